@@ -1,0 +1,60 @@
+"""Exact softmax attention over dequantized cache values, in fp64 (oracle).
+
+Test infrastructure only. Decode attention reads every cached position of a
+full-attention layer each step (offload page: decode is a bandwidth problem;
+full-attention layers read the whole KV cache every step). A QSA layer reads only
+the main-KV rows at the positions its indexer chose, so the indexer budget, not
+the context, bounds the bytes (offload page, QSA paragraph).
+
+Readings: the softmax scale defaults to 1/sqrt(D); q arrives already rotated and
+K is stored post-rotation; no mask beyond the sequence length; grouped-query
+attention maps query head h to KV head floor(h / (Hq / Hkv)). The softmax is the
+plain two-pass definition: m = max s, w = exp(s - m), out = sum w V / sum w.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """q [Hq, D] fp64, k/v [T, Hkv, D] fp64 -> out [Hq, D] fp64."""
+    hq = q.shape[0]
+    hk = k.shape[1]
+    group = hq // hk
+    out = np.zeros_like(q, dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        s = scale * (k[:, g, :] @ q[h])                 # [T]
+        m = np.max(s)
+        w = np.exp(s - m)
+        out[h] = (w @ v[:, g, :]) / np.sum(w)
+    return out
+
+
+def _q64(q_bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(q_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _scale(cache, scale):
+    return 1.0 / np.sqrt(cache.cfg["head_dim"]) if (scale is None or scale <= 0) else float(scale)
+
+
+def decode_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, scale=None) -> np.ndarray:
+    """Dense decode over positions [0, len) of each sequence: out [n_seqs, Hq, D] fp64."""
+    sc = _scale(cache, scale)
+    out = []
+    for i, sid in enumerate(seq_ids):
+        k, v = cache.dequantized(layer, sid)
+        out.append(attend(_q64(q_bits[i]), k, v, sc))
+    return np.stack(out)
+
+
+def sparse_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, positions: np.ndarray,
+                     scale=None) -> np.ndarray:
+    """Attention over positions[i] (list order; one list per sequence, shared by all KV heads)."""
+    sc = _scale(cache, scale)
+    out = []
+    for i, sid in enumerate(seq_ids):
+        k, v = cache.dequantized(layer, sid, positions[i])
+        out.append(attend(_q64(q_bits[i]), k, v, sc))
+    return np.stack(out)

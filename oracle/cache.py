@@ -1,0 +1,255 @@
+"""Cache state machine: qN_0 body, precision tail / 8-bit ring, requantization (oracle).
+
+Test infrastructure only. Follows, step by step:
+
+* qN_0 body with separate K and V widths (KVarN benchmark page, K/V pair table;
+  "Hard numbers on Qwen3.8-27B's KV cache" page, K 6-bit / V 5-bit setting D).
+* Precision tail: the newest W tokens are kept in bf16, the rest quantized as usual
+  (BeeLlama.cpp v0.4.1 page, KV cache precision tail paragraph).
+* 8-bit recent ring: the newest 2,048 positions sit in an 8-bit ring; below the
+  window the output equals a q8_0 cache (Qwen3.8-27B page, KV low-bit section).
+  Reading: ring rows are q8_0 blocks; eviction requantizes the dequantized q8_0
+  values (double quantization).
+* Tokens leaving the window are requantized into the low-bit body; this needs two
+  KV paths per layer and per-position branching (Qwen3.8-27B page, reader comment
+  on the window boundary).
+* KVarN (BeeLlama.cpp v0.4.1 page, KVarN paragraph): per-channel sigma from the
+  first appended chunk, applied to every row before block quantization.
+
+Readings: the ring holds R = W + S slots (S = slack, 512 by default, which makes
+the KV MiB table's tail rows exact); position p lives in slot p mod R. ``append``
+evicts the oldest ring rows only when the ring would overflow; tokens that are
+already behind the window after an append go to the body through the ring
+representation, so the body never depends on chunking. ``tail_evict`` drains the
+ring to the newest W. A decode step appends into the slack, then evicts.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .layout import (pack_k_rows, pack_v_tiles, pack_bf16_v_tiles, slab_layout, TILE)
+from .quant import quantize_blocks, kvarn_sigma, normalize, dequantize_blocks
+
+TAIL_NONE, TAIL_BF16, TAIL_Q8 = 0, 1, 2
+
+
+def _bf16_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+class _SeqState:
+    def __init__(self, cfg, lay):
+        hk, d = cfg["n_kv_heads"], cfg["head_dim"]
+        nb = d // 32
+        cap32 = lay["cap32"]
+        self.len = 0
+        self.body_len = 0
+        self.calibrated = False
+        self.sigma = np.zeros((hk, 2, d), dtype=np.float16)
+        self.ku = np.zeros((cap32, hk, d), dtype=np.uint8)
+        self.kd = np.zeros((cap32, hk, nb), dtype=np.float16)
+        self.vu = np.zeros((cap32, hk, d), dtype=np.uint8)
+        self.vd = np.zeros((cap32, hk, nb), dtype=np.float16)
+        r = lay["ring_slots"]
+        if cfg["tail_len"] > 0 and cfg["tail_dtype"] == TAIL_BF16:
+            self.rk = np.zeros((r, hk, d), dtype=np.uint16)
+            self.rv = np.zeros((r, hk, d), dtype=np.uint16)
+        elif cfg["tail_len"] > 0:
+            self.rku = np.zeros((r, hk, d), dtype=np.uint8)
+            self.rkd = np.zeros((r, hk, nb), dtype=np.float16)
+            self.rvu = np.zeros((r, hk, d), dtype=np.uint8)
+            self.rvd = np.zeros((r, hk, nb), dtype=np.float16)
+
+
+class OracleCache:
+    """Mirror of the library's cache semantics on the CPU, one (layer, sequence) at a time."""
+
+    def __init__(self, cfg: dict):
+        self.cfg = dict(cfg)
+        self.lay = slab_layout(self.cfg)
+        self.W = cfg["tail_len"]
+        self.R = self.lay["ring_slots"]
+        self.tail = cfg["tail_dtype"] if self.W > 0 else TAIL_NONE
+        self.state = {}
+
+    # ------------------------------------------------------------------ helpers
+    def st(self, layer: int, seq: int) -> _SeqState:
+        key = (layer, seq)
+        if key not in self.state:
+            self.state[key] = _SeqState(self.cfg, self.lay)
+        return self.state[key]
+
+    def _ring_value(self, s: _SeqState, slots) -> tuple:
+        """fp32 ring representation r(x) of K and V at ring slots: [n, Hkv, D] each."""
+        if self.tail == TAIL_BF16:
+            return _bf16_f32(s.rk[slots]), _bf16_f32(s.rv[slots])
+        k = dequantize_blocks(s.rku[slots], s.rkd[slots], 8).astype(np.float32)   # exact c * d16
+        v = dequantize_blocks(s.rvu[slots], s.rvd[slots], 8).astype(np.float32)
+        return k, v
+
+    def _ring_rep_of_input(self, k_bits, v_bits) -> tuple:
+        """r(x) for fresh inputs (what the ring would store, read back as fp32)."""
+        k = _bf16_f32(k_bits)
+        v = _bf16_f32(v_bits)
+        if self.tail == TAIL_Q8:
+            ku, kd = quantize_blocks(k, 8)
+            vu, vd = quantize_blocks(v, 8)
+            k = dequantize_blocks(ku, kd, 8).astype(np.float32)
+            v = dequantize_blocks(vu, vd, 8).astype(np.float32)
+        return k, v
+
+    def _write_body(self, s: _SeqState, pos: np.ndarray, k32, v32):
+        """Quantize fp32 rows (after the ring representation) into body positions."""
+        if len(pos) == 0:
+            return
+        if self.cfg["kvarn"]:
+            k32 = normalize(k32, s.sigma[:, 0, :])
+            v32 = normalize(v32, s.sigma[:, 1, :])
+        s.ku[pos], s.kd[pos] = quantize_blocks(k32, self.cfg["k_bits"])
+        s.vu[pos], s.vd[pos] = quantize_blocks(v32, self.cfg["v_bits"])
+
+    def _write_ring(self, s: _SeqState, pos: np.ndarray, k_bits, v_bits):
+        if len(pos) == 0:
+            return
+        slots = pos % self.R
+        if self.tail == TAIL_BF16:
+            s.rk[slots] = k_bits
+            s.rv[slots] = v_bits
+        else:
+            s.rku[slots], s.rkd[slots] = quantize_blocks(_bf16_f32(k_bits), 8)
+            s.rvu[slots], s.rvd[slots] = quantize_blocks(_bf16_f32(v_bits), 8)
+
+    def _evict_to(self, s: _SeqState, target: int):
+        """Requantize ring positions [body_len, target) into the body."""
+        if target <= s.body_len:
+            return
+        pos = np.arange(s.body_len, target)
+        k32, v32 = self._ring_value(s, pos % self.R)
+        self._write_body(s, pos, k32, v32)
+        s.body_len = target
+
+    # ------------------------------------------------------------------ the calls
+    def append(self, layer: int, seq_ids, n_new, k_bits: np.ndarray, v_bits: np.ndarray):
+        """k_bits, v_bits: bf16 bit patterns [sum(n_new), Hkv, D], sequences in order."""
+        off = 0
+        for sid, n in zip(seq_ids, n_new):
+            n = int(n)
+            kb = k_bits[off:off + n]
+            vb = v_bits[off:off + n]
+            off += n
+            s = self.st(layer, sid)
+            if s.len + n > self.cfg["capacity"]:
+                raise ValueError("capacity")
+            if n == 0:
+                continue
+            if self.cfg["kvarn"] and not s.calibrated:
+                sig_k = kvarn_sigma(_bf16_f32(kb))            # [Hkv, D]
+                sig_v = kvarn_sigma(_bf16_f32(vb))
+                s.sigma = np.stack([sig_k, sig_v], axis=1)
+                s.calibrated = True
+            new_len = s.len + n
+            pos = np.arange(s.len, new_len)
+            if self.tail == TAIL_NONE:
+                self._write_body(s, pos, _bf16_f32(kb), _bf16_f32(vb))
+                s.len = s.body_len = new_len
+                continue
+            new_body = max(s.body_len, new_len - self.R)
+            # oldest ring rows leave first (only when the ring would overflow)
+            self._evict_to(s, min(new_body, s.len))
+            # new tokens already behind the window: through the ring representation
+            direct = pos[pos < new_body]
+            if len(direct):
+                sel = direct - s.len
+                k32, v32 = self._ring_rep_of_input(kb[sel], vb[sel])
+                self._write_body(s, direct, k32, v32)
+            keep = pos[pos >= new_body]
+            self._write_ring(s, keep, kb[keep - s.len], vb[keep - s.len])
+            s.len = new_len
+            s.body_len = new_body
+
+    def tail_evict(self, layer: int, seq_ids):
+        for sid in seq_ids:
+            s = self.st(layer, sid)
+            if self.tail == TAIL_NONE:
+                continue
+            self._evict_to(s, max(s.body_len, s.len - self.W))
+
+    # ------------------------------------------------------------------ reading
+    def lengths(self, layer: int, seq: int):
+        s = self.st(layer, seq)
+        return s.len, s.body_len
+
+    def dequantized(self, layer: int, seq: int, positions=None):
+        """Exact fp64 K^, V^ [n, Hkv, D] at positions (default: all of [0, len))."""
+        s = self.st(layer, seq)
+        if positions is None:
+            positions = np.arange(s.len)
+        positions = np.asarray(positions, dtype=np.int64)
+        d = self.cfg["head_dim"]
+        hk = self.cfg["n_kv_heads"]
+        k = np.zeros((len(positions), hk, d))
+        v = np.zeros((len(positions), hk, d))
+        in_body = positions < s.body_len
+        pb = positions[in_body]
+        if len(pb):
+            kb = dequantize_blocks(s.ku[pb], s.kd[pb], self.cfg["k_bits"])
+            vb = dequantize_blocks(s.vu[pb], s.vd[pb], self.cfg["v_bits"])
+            if self.cfg["kvarn"]:
+                kb = kb * s.sigma[:, 0, :].astype(np.float64)
+                vb = vb * s.sigma[:, 1, :].astype(np.float64)
+            k[in_body], v[in_body] = kb, vb
+        pr = positions[~in_body]
+        if len(pr):
+            kr, vr = self._ring_value(s, pr % self.R)
+            k[~in_body], v[~in_body] = kr.astype(np.float64), vr.astype(np.float64)
+        return k, v
+
+    # ------------------------------------------------------------------ bytes
+    def region_bytes(self, layer: int, seq: int, region: str, head: int, lo: int, hi: int) -> np.ndarray:
+        """Packed bytes of one head's region for positions / slots [lo, hi).
+
+        k_body / k_ring: rows lo..hi-1; v_body / v_ring: tiles lo//32 .. hi//32 - 1
+        (lo, hi multiples of 32); sigma: the [2, D] fp16 block of the head."""
+        s = self.st(layer, seq)
+        kb, vb = self.cfg["k_bits"], self.cfg["v_bits"]
+        if region == "k_body":
+            return pack_k_rows(s.ku[lo:hi, head], s.kd[lo:hi, head], kb)
+        if region == "v_body":
+            assert lo % TILE == 0 and hi % TILE == 0
+            u = s.vu[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"])
+            d = s.vd[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"] // 32)
+            return pack_v_tiles(u, d, vb)
+        if region == "k_ring":
+            if self.tail == TAIL_BF16:
+                return np.ascontiguousarray(s.rk[lo:hi, head]).view(np.uint8)
+            return pack_k_rows(s.rku[lo:hi, head], s.rkd[lo:hi, head], 8)
+        if region == "v_ring":
+            assert lo % TILE == 0 and hi % TILE == 0
+            if self.tail == TAIL_BF16:
+                return pack_bf16_v_tiles(s.rv[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"]))
+            u = s.rvu[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"])
+            d = s.rvd[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"] // 32)
+            return pack_v_tiles(u, d, 8)
+        if region == "sigma":
+            return np.ascontiguousarray(s.sigma[head]).view(np.uint8).reshape(-1)
+        raise ValueError(region)
+
+    def slab_image(self, layer: int, seq: int) -> np.ndarray:
+        """The whole packed slab of one (layer, sequence), as the arena should hold it."""
+        lay = self.lay
+        img = np.zeros(lay["slab"], dtype=np.uint8)
+        hk = self.cfg["n_kv_heads"]
+        cap32 = lay["cap32"]
+        for region, n in (("k_body", cap32), ("v_body", cap32), ("k_ring", self.R), ("v_ring", self.R)):
+            off, size = lay[region]
+            if size == 0:
+                continue
+            per = size // hk
+            for h in range(hk):
+                img[off + h * per: off + (h + 1) * per] = self.region_bytes(layer, seq, region, h, 0, n).reshape(-1)
+        off, size = lay["sigma"]
+        if size:
+            per = size // hk
+            for h in range(hk):
+                img[off + h * per: off + (h + 1) * per] = self.region_bytes(layer, seq, "sigma", h, 0, 0)
+        return img

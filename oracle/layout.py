@@ -1,0 +1,262 @@
+"""Byte layout of the cache arena and its exact size (oracle; test infrastructure only).
+
+The pages fix only the *size* of a qN_0 block: N bits per value plus one fp16
+scale per 32 values (BeeLlama.cpp v0.4.1 page, KV MiB table: q4_0 / q5_0 /
+q6_0 / q8_0 at tail 0 = 1152 / 1408 / 1664 / 2176 MiB; KVarN benchmark page,
+cache-size column). Where the bits go inside the arena is a design choice made
+for the GPU consumer; this module is its plain, independent statement.
+
+Code planes. An N-bit biased code u is split into bit planes of width w:
+    N=2: [2]   N=3: [2, 1]   N=4: [4]   N=5: [4, 1]   N=6: [4, 2]
+    N=7: [4, 2, 1]   N=8: [8]
+taken from the least significant bits upward (u = sum_k plane_k << shift_k).
+
+Pieces. A piece is 8 codes e_0..e_7 of one plane. For w in {1, 2, 4}, 4/w pieces
+share a little-endian 32-bit word; element i of piece p sits at bit
+16*(i % 2) + 4*w*p + w*(i // 2). For w = 8 a piece is 8 bytes, e_i in byte i.
+
+K rows (body, and the q8_0 ring): one row per (position, KV head). For lane
+group j in 0..3 and block b, piece (j, b) holds channels 32*b + 8*j + i. A row is,
+for each plane: for j = 0..3 the pieces b = 0..NB-1; then the NB fp16 block
+scales in block order. Row bytes = NB * (4N + 2).
+
+V tiles (body, and the q8_0 ring): 32 consecutive positions of one KV head. For
+lane l in 0..63 (d16 = l % 16, j = l // 16) and n-tile n in 0..D/16-1, piece
+(l, n) holds channel 16*n + d16 at tile positions T(j, i) = 4j + i (i < 4) and
+16 + 4j + (i - 4) (i >= 4). For each plane, lane l's bytes are its pieces for
+n = 0..NT-1 (NT * w bytes); they are interleaved across lanes in units of
+u = min(16, NT * w) bytes: [chunk][lane][u]. Then the 32 x NB fp16 scales,
+[position][block]. Tile bytes = 32 * NB * (4N + 2).
+
+bf16 tail ring: K rows are the D bf16 values in channel order; V tiles of 32
+slots hold, for n-tile n and lane l, the 8 bf16 values of channel 16*n + d16 at
+tile positions T(j, i): [n][lane][8 x bf16].
+
+Arena: slabs of [layer][sequence]; each slab holds, in order and 256-byte
+aligned: K body [head][capacity32][row], V body [head][capacity32/32][tile],
+K ring [head][R][row], V ring [head][R/32][tile], KVarN sigma [head][K,V][D] fp16.
+capacity32 is the capacity rounded up to 32; R = W + S (ring slots).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+TILE = 32
+
+_PLANES = {2: [(2, 0)], 3: [(2, 0), (1, 2)], 4: [(4, 0)], 5: [(4, 0), (1, 4)],
+           6: [(4, 0), (2, 4)], 7: [(4, 0), (2, 4), (1, 6)], 8: [(8, 0)]}
+
+
+def planes(n_bits: int):
+    """[(width, shift)] bit planes of an N-bit code, least significant first."""
+    return list(_PLANES[n_bits])
+
+
+def _round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+def row_bytes(n_bits: int, head_dim: int) -> int:
+    return head_dim // BLOCK * (4 * n_bits + 2)
+
+
+def tile_positions() -> np.ndarray:
+    """T[j, i]: tile position held by lane group j at element i."""
+    t = np.zeros((4, 8), dtype=np.int64)
+    for j in range(4):
+        for i in range(8):
+            t[j, i] = 4 * j + i if i < 4 else 16 + 4 * j + (i - 4)
+    return t
+
+
+# ----------------------------------------------------------------------------- pieces
+
+def _piece_shifts(w: int) -> np.ndarray:
+    per = 4 // w
+    s = np.zeros((per, 8), dtype=np.uint64)
+    for p in range(per):
+        for i in range(8):
+            s[p, i] = 16 * (i % 2) + 4 * w * p + w * (i // 2)
+    return s
+
+
+def pack_pieces(vals: np.ndarray, w: int) -> np.ndarray:
+    """vals [..., M, 8] (each < 2^w) -> bytes [..., M * w]."""
+    vals = np.asarray(vals)
+    m = vals.shape[-2]
+    if w == 8:
+        return vals.astype(np.uint8).reshape(*vals.shape[:-2], m * 8)
+    per = 4 // w
+    assert m % per == 0
+    v = vals.astype(np.uint64).reshape(*vals.shape[:-2], m // per, per, 8)
+    words = np.sum(v << _piece_shifts(w), axis=(-2, -1)).astype(np.uint32)
+    return np.ascontiguousarray(words).view(np.uint8).reshape(*vals.shape[:-2], m * w)
+
+
+def unpack_pieces(b: np.ndarray, w: int, m: int) -> np.ndarray:
+    """Inverse of pack_pieces: bytes [..., M * w] -> vals [..., M, 8]."""
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    if w == 8:
+        return b.reshape(*b.shape[:-1], m, 8)
+    per = 4 // w
+    words = b.reshape(*b.shape[:-1], m * w // 4, 4).copy().view(np.uint32)[..., 0].astype(np.uint64)
+    v = (words[..., None, None] >> _piece_shifts(w)) & np.uint64((1 << w) - 1)
+    return v.reshape(*b.shape[:-1], m, 8).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------- K rows
+
+def pack_k_rows(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
+    """Codes u [..., D] (uint8) and scales d16 [..., D/32] -> K rows [..., row_bytes]."""
+    u = np.asarray(u, dtype=np.uint8)
+    d = u.shape[-1]
+    nb = d // BLOCK
+    pieces = u.reshape(*u.shape[:-1], nb, 4, 8)            # [.., b, j, i]
+    pieces = np.swapaxes(pieces, -3, -2)                    # [.., j, b, i]
+    parts = []
+    for w, sh in planes(n_bits):
+        v = (pieces >> sh) & ((1 << w) - 1)
+        parts.append(pack_pieces(v, w).reshape(*u.shape[:-1], 4 * nb * w))
+    parts.append(np.ascontiguousarray(np.asarray(d16, dtype=np.float16)).view(np.uint8)
+                 .reshape(*u.shape[:-1], 2 * nb))
+    return np.concatenate(parts, axis=-1)
+
+
+def unpack_k_rows(rows: np.ndarray, n_bits: int, head_dim: int):
+    """K rows [..., row_bytes] -> (u [..., D], d16 [..., D/32])."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    nb = head_dim // BLOCK
+    lead = rows.shape[:-1]
+    u = np.zeros((*lead, 4, nb, 8), dtype=np.uint8)
+    off = 0
+    for w, sh in planes(n_bits):
+        sz = 4 * nb * w
+        v = unpack_pieces(rows[..., off:off + sz].reshape(*lead, 4, nb * w), w, nb)
+        u |= (v << sh).astype(np.uint8)
+        off += sz
+    d16 = np.ascontiguousarray(rows[..., off:off + 2 * nb]).view(np.float16)
+    u = np.swapaxes(u, -3, -2).reshape(*lead, head_dim)
+    return u, d16
+
+
+# ----------------------------------------------------------------------------- V tiles
+
+def _v_gather_index(head_dim: int):
+    nt = head_dim // 16
+    tp = tile_positions()
+    lane = np.arange(64)
+    t_idx = tp[lane // 16][:, None, :].repeat(nt, axis=1)                  # [64, NT, 8]
+    d_idx = (16 * np.arange(nt)[None, :, None] + (lane % 16)[:, None, None]).repeat(8, axis=2)
+    return t_idx, d_idx
+
+
+def pack_v_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
+    """Codes u [n_tiles, 32, D] and scales [n_tiles, 32, D/32] -> tiles [n_tiles, tile_bytes]."""
+    u = np.asarray(u, dtype=np.uint8)
+    ntl, tt, d = u.shape
+    assert tt == TILE
+    nt = d // 16
+    t_idx, d_idx = _v_gather_index(d)
+    g = u[:, t_idx, d_idx]                                  # [ntl, 64, NT, 8]
+    parts = []
+    for w, sh in planes(n_bits):
+        v = (g >> sh) & ((1 << w) - 1)
+        lane_bytes = pack_pieces(v, w)                      # [ntl, 64, NT*w]
+        lb = nt * w
+        cu = min(16, lb)
+        x = lane_bytes.reshape(ntl, 64, lb // cu, cu).transpose(0, 2, 1, 3)
+        parts.append(x.reshape(ntl, 64 * lb))
+    parts.append(np.ascontiguousarray(np.asarray(d16, dtype=np.float16)).view(np.uint8).reshape(ntl, -1))
+    return np.concatenate(parts, axis=-1)
+
+
+def unpack_v_tiles(tiles: np.ndarray, n_bits: int, head_dim: int):
+    """Tiles [n_tiles, tile_bytes] -> (u [n_tiles, 32, D], d16 [n_tiles, 32, D/32])."""
+    tiles = np.asarray(tiles, dtype=np.uint8)
+    ntl = tiles.shape[0]
+    nt = head_dim // 16
+    nb = head_dim // BLOCK
+    g = np.zeros((ntl, 64, nt, 8), dtype=np.uint8)
+    off = 0
+    for w, sh in planes(n_bits):
+        lb = nt * w
+        cu = min(16, lb)
+        x = tiles[:, off:off + 64 * lb].reshape(ntl, lb // cu, 64, cu).transpose(0, 2, 1, 3)
+        v = unpack_pieces(x.reshape(ntl, 64, lb), w, nt)
+        g |= (v << sh).astype(np.uint8)
+        off += 64 * lb
+    t_idx, d_idx = _v_gather_index(head_dim)
+    u = np.zeros((ntl, TILE, head_dim), dtype=np.uint8)
+    u[:, t_idx, d_idx] = g
+    d16 = np.ascontiguousarray(tiles[:, off:off + TILE * nb * 2]).view(np.float16).reshape(ntl, TILE, nb)
+    return u, d16
+
+
+def pack_bf16_v_tiles(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits [n_tiles, 32, D] -> bf16 ring V tiles [n_tiles, 64 * D] bytes ([n][lane][8])."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    ntl, _, d = bits.shape
+    t_idx, d_idx = _v_gather_index(d)                       # [64, NT, 8]
+    g = bits[:, t_idx, d_idx]                               # [ntl, 64, NT, 8]
+    g = g.transpose(0, 2, 1, 3)                             # [ntl, NT, 64, 8]
+    return np.ascontiguousarray(g).view(np.uint8).reshape(ntl, -1)
+
+
+def unpack_bf16_v_tiles(tiles: np.ndarray, head_dim: int) -> np.ndarray:
+    tiles = np.ascontiguousarray(tiles, dtype=np.uint8)
+    ntl = tiles.shape[0]
+    nt = head_dim // 16
+    g = tiles.view(np.uint16).reshape(ntl, nt, 64, 8).transpose(0, 2, 1, 3)
+    t_idx, d_idx = _v_gather_index(head_dim)
+    out = np.zeros((ntl, TILE, head_dim), dtype=np.uint16)
+    out[:, t_idx, d_idx] = g
+    return out
+
+
+# ----------------------------------------------------------------------------- arena
+
+def ring_slots(cfg: dict) -> int:
+    return cfg["tail_len"] + cfg["tail_slack"] if cfg["tail_len"] > 0 else 0
+
+
+def slab_layout(cfg: dict) -> dict:
+    """Byte offsets and sizes of the regions of one (layer, sequence) slab."""
+    d = cfg["head_dim"]
+    hk = cfg["n_kv_heads"]
+    cap32 = _round_up(cfg["capacity"], TILE)
+    rk = row_bytes(cfg["k_bits"], d)
+    rv = row_bytes(cfg["v_bits"], d)
+    r = ring_slots(cfg)
+    if cfg["tail_len"] > 0 and cfg["tail_dtype"] == 1:
+        ring_rk = ring_rv = 2 * d
+    elif cfg["tail_len"] > 0 and cfg["tail_dtype"] == 2:
+        ring_rk = ring_rv = row_bytes(8, d)
+    else:
+        ring_rk = ring_rv = 0
+    sizes = {
+        "k_body": hk * cap32 * rk,
+        "v_body": hk * cap32 * rv,
+        "k_ring": hk * r * ring_rk,
+        "v_ring": hk * r * ring_rv,
+        "sigma": hk * 2 * d * 2 if cfg["kvarn"] else 0,
+    }
+    off = 0
+    lay = {}
+    for name in ("k_body", "v_body", "k_ring", "v_ring", "sigma"):
+        off = _round_up(off, 256)
+        lay[name] = (off, sizes[name])
+        off += sizes[name]
+    lay["slab"] = _round_up(off, 256)
+    lay["cap32"] = cap32
+    lay["row_k"] = rk
+    lay["row_v"] = rv
+    lay["ring_row_k"] = ring_rk
+    lay["ring_row_v"] = ring_rv
+    lay["ring_slots"] = r
+    return lay
+
+
+def cache_bytes(cfg: dict) -> int:
+    """Exact arena bytes: n_layers * max_seqs slabs."""
+    return cfg["n_layers"] * cfg["max_seqs"] * slab_layout(cfg)["slab"]

@@ -1,0 +1,104 @@
+"""Pins of the oracle's attention: brute force, closed forms and sparse/dense relations."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import OracleCache, attend, decode_reference, sparse_reference
+from workloads import small_tokens, small_query
+
+
+def brute(q, k, v, scale):
+    """Scalar reference with math.fsum / math.exp: q [Hq, D], k/v [T, Hkv, D] (Python floats)."""
+    hq, d = q.shape
+    t_len, hk, _ = k.shape
+    group = hq // hk
+    out = np.zeros((hq, d))
+    for h in range(hq):
+        g = h // group
+        s = [scale * math.fsum(float(q[h, i]) * float(k[t, g, i]) for i in range(d)) for t in range(t_len)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        den = math.fsum(w)
+        for i in range(d):
+            out[h, i] = math.fsum(w[t] * float(v[t, g, i]) for t in range(t_len)) / den
+    return out
+
+
+@pytest.mark.parametrize("hq,hk,t_len", [(4, 2, 7), (4, 4, 33), (8, 1, 64), (2, 2, 1)])
+def test_attend_brute_force(hq, hk, t_len):
+    rng = np.random.default_rng(hq * 100 + t_len)
+    q = rng.standard_normal((hq, 32))
+    k = rng.standard_normal((t_len, hk, 32)) * 2
+    v = rng.standard_normal((t_len, hk, 32)) * 5
+    np.testing.assert_allclose(attend(q, k, v, 0.3), brute(q, k, v, 0.3), rtol=0, atol=1e-12)
+
+
+def test_identical_keys_give_mean_of_values():
+    rng = np.random.default_rng(1)
+    k = np.repeat(rng.standard_normal((1, 2, 32)), 10, axis=0)
+    v = rng.standard_normal((10, 2, 32))
+    out = attend(rng.standard_normal((4, 32)), k, v, 1.0)
+    np.testing.assert_allclose(out[:2], np.repeat(v[:, 0].mean(0)[None], 2, 0), atol=1e-13)
+    np.testing.assert_allclose(out[2:], np.repeat(v[:, 1].mean(0)[None], 2, 0), atol=1e-13)
+
+
+def test_dominant_key_selects_its_value():
+    rng = np.random.default_rng(2)
+    q = np.zeros((2, 32))
+    q[:, 0] = 1.0
+    k = rng.standard_normal((20, 1, 32)) * 0.01
+    k[13, 0, 0] = 100.0                     # score gap > 60 at scale 1
+    v = rng.standard_normal((20, 1, 32))
+    out = attend(q, k, v, 1.0)
+    np.testing.assert_allclose(out, np.repeat(v[13:14, 0], 2, 0), atol=1e-20)
+
+
+def test_gqa_head_mapping():
+    # query heads 0,1 read KV head 0; heads 2,3 read KV head 1
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((4, 32))
+    k = rng.standard_normal((9, 2, 32))
+    v = rng.standard_normal((9, 2, 32))
+    out = attend(q, k, v, 0.5)
+    for h in range(4):
+        g = h // 2
+        np.testing.assert_allclose(out[h], attend(q[h:h + 1], k[:, g:g + 1], v[:, g:g + 1], 0.5)[0], atol=1e-14)
+
+
+def _cache(tail_len=64, tail_dtype=1, n=300):
+    c = dict(n_layers=1, max_seqs=1, capacity=512, n_q_heads=16, n_kv_heads=2, head_dim=256,
+             k_bits=6, v_bits=5, kvarn=0, tail_len=tail_len, tail_slack=32, tail_dtype=tail_dtype)
+    k, v = small_tokens(11, n, 2, 256)
+    o = OracleCache(c)
+    o.append(0, [0], [n], k, v)
+    o.tail_evict(0, [0])
+    return o, k, v, c
+
+
+def test_sparse_with_all_positions_equals_dense():
+    o, *_ = _cache()
+    q = small_query(1, 1, 16, 256)
+    dense = decode_reference(o, 0, [0], q)
+    perm = np.random.default_rng(4).permutation(300)[None, :]
+    sparse = sparse_reference(o, 0, [0], q, perm)
+    np.testing.assert_allclose(sparse, dense, atol=1e-12, rtol=0)
+
+
+def test_sparse_equals_dense_over_cache_holding_only_those_positions():
+    o, k, v, c = _cache(tail_len=0)
+    pos = np.sort(np.random.default_rng(5).choice(300, 40, replace=False))
+    q = small_query(2, 1, 16, 256)
+    sparse = sparse_reference(o, 0, [0], q, pos[None, :])
+    only = OracleCache(c)
+    only.append(0, [0], [40], k[pos], v[pos])
+    dense = decode_reference(only, 0, [0], q)
+    np.testing.assert_allclose(sparse, dense, atol=1e-12, rtol=0)
+    perm = np.random.default_rng(6).permutation(pos)
+    np.testing.assert_allclose(sparse_reference(o, 0, [0], q, perm[None, :]), sparse, atol=1e-12, rtol=0)
+
+
+def test_default_scale_is_inverse_sqrt_dim():
+    o, *_ = _cache()
+    q = small_query(3, 1, 16, 256)
+    np.testing.assert_array_equal(decode_reference(o, 0, [0], q, 0.0), decode_reference(o, 0, [0], q, 1 / 16))

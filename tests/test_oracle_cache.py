@@ -1,0 +1,162 @@
+"""Pins of the oracle's cache state machine: tail, ring, eviction and KVarN.
+
+The special cases come from the pages: a precision tail stores the newest tokens
+without loss (BeeLlama.cpp v0.4.1 page); with a context shorter than the 8-bit
+ring window the output equals a q8_0 cache (Qwen3.8-27B page). The rest are
+invariants of the semantics: chunk invariance, the ring holding exactly the newest
+W after an evict, W = 0 meaning no ring.
+"""
+import numpy as np
+import pytest
+
+from oracle import OracleCache, quant
+from oracle.layout import slab_layout
+from workloads import small_tokens, bf16_to_f32
+
+
+def cfg(**kw):
+    c = dict(n_layers=1, max_seqs=2, capacity=512, n_q_heads=4, n_kv_heads=2, head_dim=256,
+             k_bits=6, v_bits=5, kvarn=0, tail_len=64, tail_slack=32, tail_dtype=1)
+    c.update(kw)
+    return c
+
+
+def _append_all(c, k, v, chunks, seq=0, evict_after=()):
+    o = OracleCache(c)
+    off = 0
+    for idx, n in enumerate(chunks):
+        o.append(0, [seq], [n], k[off:off + n], v[off:off + n])
+        off += n
+        if idx in evict_after:
+            o.tail_evict(0, [seq])
+    return o
+
+
+def test_tail_is_lossless_below_window():
+    c = cfg(tail_len=128, tail_slack=32)
+    k, v = small_tokens(1, 100, 2, 256)
+    o = _append_all(c, k, v, [37, 63])
+    kk, vv = o.dequantized(0, 0)
+    assert o.lengths(0, 0) == (100, 0)
+    assert np.array_equal(kk, bf16_to_f32(k).astype(np.float64))
+    assert np.array_equal(vv, bf16_to_f32(v).astype(np.float64))
+
+
+def test_q8_ring_below_window_equals_q8_body():
+    k, v = small_tokens(2, 90, 2, 256, scale=np.full((2, 2, 256), 3.0, dtype=np.float32))
+    ring = _append_all(cfg(tail_len=128, tail_slack=32, tail_dtype=2), k, v, [90])
+    body = _append_all(cfg(tail_len=0, k_bits=8, v_bits=8), k, v, [90])
+    a, b = ring.dequantized(0, 0), body.dequantized(0, 0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("kvarn", [0, 1])
+def test_chunk_invariance(tail_dtype, kvarn):
+    c = cfg(tail_dtype=tail_dtype, kvarn=kvarn, tail_len=64, tail_slack=32)
+    k, v = small_tokens(3, 300, 2, 256)
+    first = 40          # KVarN calibrates on the first chunk: keep it fixed
+    ref = _append_all(c, k, v, [first] + [1] * 260)
+    for chunks, ev in (([first, 260], ()), ([first, 7, 100, 53, 100], (1, 3)), ([first] + [20] * 13, (5, 6, 9))):
+        o = _append_all(c, k, v, chunks, evict_after=ev)
+        o.tail_evict(0, [0])
+        ref.tail_evict(0, [0])
+        assert o.lengths(0, 0) == ref.lengths(0, 0) == (300, 300 - 64)
+        a, b = o.dequantized(0, 0), ref.dequantized(0, 0)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        sa, sb = o.st(0, 0), ref.st(0, 0)
+        bl = 300 - 64
+        assert np.array_equal(sa.ku[:bl], sb.ku[:bl]) and np.array_equal(sa.vd[:bl], sb.vd[:bl])
+
+
+def test_append_evicts_only_on_overflow_and_evict_drains_to_window():
+    c = cfg(tail_len=64, tail_slack=32)     # R = 96
+    k, v = small_tokens(4, 400, 2, 256)
+    o = OracleCache(c)
+    o.append(0, [0], [50], k[:50], v[:50])
+    assert o.lengths(0, 0) == (50, 0)
+    o.append(0, [0], [40], k[50:90], v[50:90])
+    assert o.lengths(0, 0) == (90, 0)       # 90 <= R: nothing leaves
+    o.append(0, [0], [20], k[90:110], v[90:110])
+    assert o.lengths(0, 0) == (110, 14)     # overflow: the oldest 14 leave
+    o.tail_evict(0, [0])
+    assert o.lengths(0, 0) == (110, 46)     # drained to the newest 64
+    o.tail_evict(0, [0])
+    assert o.lengths(0, 0) == (110, 46)
+    o.append(0, [0], [290], k[110:400], v[110:400])
+    assert o.lengths(0, 0) == (400, 400 - 96)
+
+
+@pytest.mark.parametrize("tail_dtype", [1, 2])
+def test_evicted_rows_are_requantized_ring_values(tail_dtype):
+    c = cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype)
+    k, v = small_tokens(5, 200, 2, 256)
+    o = _append_all(c, k, v, [100, 100])
+    o.tail_evict(0, [0])
+    s = o.st(0, 0)
+    kx = bf16_to_f32(k[:136])
+    if tail_dtype == 2:
+        u8, d8 = quant.quantize_blocks(kx, 8)
+        kx = quant.dequantize_blocks(u8, d8, 8).astype(np.float32)
+    u, d = quant.quantize_blocks(kx, 6)
+    assert np.array_equal(s.ku[:136], u) and np.array_equal(s.kd[:136].view(np.uint16), d.view(np.uint16))
+
+
+def test_zero_window_is_no_ring():
+    k, v = small_tokens(6, 120, 2, 256)
+    a = _append_all(cfg(tail_len=0, tail_slack=0), k, v, [60, 60])
+    b = _append_all(cfg(tail_len=0, tail_slack=512, tail_dtype=2), k, v, [120])
+    assert a.lengths(0, 0) == b.lengths(0, 0) == (120, 120)
+    assert np.array_equal(a.dequantized(0, 0)[0], b.dequantized(0, 0)[0])
+    lay = slab_layout(cfg(tail_len=0, tail_slack=512, tail_dtype=2))
+    assert lay["k_ring"][1] == 0 and lay["v_ring"][1] == 0
+
+
+def test_kvarn_unit_rms_equals_plain():
+    # first chunk with every channel of RMS exactly 1 (values +-1) -> sigma = 1
+    n = 32
+    signs = np.where(np.random.default_rng(0).random((n, 2, 256)) < 0.5, -1.0, 1.0).astype(np.float32)
+    from workloads import bf16_bits
+    kb = bf16_bits(signs)
+    k2, v2 = small_tokens(7, 100, 2, 256)
+    k = np.concatenate([kb, k2])
+    v = np.concatenate([kb, v2])
+    a = _append_all(cfg(kvarn=1, tail_len=0), k, v, [n, 100])
+    b = _append_all(cfg(kvarn=0, tail_len=0), k, v, [n, 100])
+    assert np.all(a.st(0, 0).sigma.astype(np.float32) == 1.0)
+    assert np.array_equal(a.st(0, 0).ku, b.st(0, 0).ku)
+    assert np.array_equal(a.st(0, 0).vd.view(np.uint16), b.st(0, 0).vd.view(np.uint16))
+
+
+def test_kvarn_dequant_includes_sigma():
+    sc = np.ones((2, 2, 256), dtype=np.float32)
+    sc[:, :, 3] = 16.0
+    k, v = small_tokens(8, 64, 2, 256, scale=sc)
+    o = _append_all(cfg(kvarn=1, tail_len=0), k, v, [64])
+    s = o.st(0, 0)
+    kk, _ = o.dequantized(0, 0)
+    y = quant.normalize(bf16_to_f32(k), s.sigma[:, 0, :])
+    u, d = quant.quantize_blocks(y, 6)
+    expect = quant.dequantize_blocks(u, d, 6) * s.sigma[:, 0, :].astype(np.float64)
+    assert np.array_equal(kk, expect)
+    # the per-channel scale tracks the channel's RMS: the x16 channel gets sigma ~ 16
+    assert np.all(np.abs(s.sigma[:, 0, 3].astype(np.float64) / 16.0 - 1) < 0.35)
+
+
+def test_capacity_is_enforced():
+    o = OracleCache(cfg(capacity=64, tail_len=0))
+    k, v = small_tokens(9, 65, 2, 256)
+    o.append(0, [0], [64], k[:64], v[:64])
+    with pytest.raises(ValueError):
+        o.append(0, [0], [1], k[64:], v[64:])
+
+
+def test_sequences_are_independent():
+    c = cfg()
+    k, v = small_tokens(10, 150, 2, 256)
+    o = OracleCache(c)
+    o.append(0, [1, 0], [100, 50], k, v)
+    a = _append_all(c, k[:100], v[:100], [100], seq=1)
+    b = _append_all(c, k[100:], v[100:], [50], seq=0)
+    assert np.array_equal(o.dequantized(0, 1)[0], a.dequantized(0, 1)[0])
+    assert np.array_equal(o.dequantized(0, 0)[1], b.dequantized(0, 0)[1])

@@ -1,0 +1,213 @@
+"""Pins of the oracle's qN_0 quantizer and KVarN normalization against the mathematics.
+
+Nothing here re-calls the oracle's own formula to produce an expected value: the
+expectations come from exact rational arithmetic (``fractions``), exhaustive
+search over the code levels, closed forms and invariances.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import quant
+from workloads import bf16_bits, bf16_to_f32
+
+
+def _f32(x) -> float:
+    return float(np.float32(x))
+
+
+def _round_f32(fr: Fraction) -> float:
+    """Correctly rounded fp32 of an exact rational (independent of numpy's division)."""
+    f = float(fr)                          # correctly rounded to fp64
+    c = np.float32(f)                      # may double-round; fix by checking neighbours
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - fr)
+        if best is None or err < best[0] or (err == best[0] and (np.float32(cand).view(np.uint32) & 1) == 0):
+            best = (err, cand)
+    return float(best[1])
+
+
+def _round_f16(x: float) -> float:
+    """Correctly rounded fp16 (RNE) of an fp32 value, by exhaustive neighbour search."""
+    if x == 0:
+        return 0.0
+    c = np.float16(x)
+    best = None
+    for cand in (np.nextafter(c, np.float16(-np.inf)), c, np.nextafter(c, np.float16(np.inf))):
+        if not np.isfinite(cand):
+            continue
+        err = abs(Fraction(float(cand)) - Fraction(x))
+        if best is None or err < best[0] or (err == best[0] and (np.float16(cand).view(np.uint16) & 1) == 0):
+            best = (err, cand)
+    return float(best[1])
+
+
+def _blocks(seed, n, scale=1.0, outliers=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 32)).astype(np.float32) * np.float32(scale)
+    if outliers:
+        x[:, 3] *= 20
+    return bf16_to_f32(bf16_bits(x))
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+@pytest.mark.parametrize("scale", [0.05, 1.0, 37.0])
+def test_round_trip_within_half_scale(n_bits, scale):
+    x = _blocks(n_bits * 7 + int(scale * 10), 400, scale, outliers=(n_bits % 2 == 0))
+    u, d16 = quant.quantize_blocks(x, n_bits)
+    c = u.astype(np.int64) - (1 << (n_bits - 1))
+    d = d16.astype(np.float64)[:, 0]                              # one block per row
+    assert np.all(d >= 2.0 ** -14) and np.all(d < 65504)        # normal, unsaturated scales
+    err = np.abs(x.astype(np.float64) - c * d[:, None])
+    # d16/2 from rounding to the nearest level; 2^-24 |x| from the fp32 division
+    bound = d[:, None] / 2 + 2.0 ** -24 * np.abs(x)
+    assert np.all(err <= bound)
+    assert np.all(np.abs(c) <= quant.QMAX[n_bits])
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_scale_is_rne_fp16_of_correctly_rounded_fp32_quotient(n_bits):
+    x = _blocks(100 + n_bits, 60, 3.0)
+    u, d16 = quant.quantize_blocks(x, n_bits)
+    qmax = (1 << (n_bits - 1)) - 1
+    for b in range(x.shape[0]):
+        amax = max(abs(float(v)) for v in x[b])
+        d32 = _round_f32(Fraction(amax) / qmax)
+        assert float(d16[b, 0]) == _round_f16(d32)
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_codes_are_nearest_level_by_exhaustive_search(n_bits):
+    x = _blocks(200 + n_bits, 40, 2.0)
+    u, d16 = quant.quantize_blocks(x, n_bits)
+    qmax = (1 << (n_bits - 1)) - 1
+    for b in range(x.shape[0]):
+        d = Fraction(float(d16[b, 0]))
+        for i in range(32):
+            xv = Fraction(float(x[b, i]))
+            dists = [(abs(xv - c * d), c) for c in range(-qmax, qmax + 1)]
+            dists.sort()
+            best, c_best = dists[0]
+            if dists[1][0] == best:          # an exact tie: round half to even
+                c_best = dists[0][1] if dists[0][1] % 2 == 0 else dists[1][1]
+            q = xv / d
+            frac = q - math.floor(q)
+            if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 20):
+                continue                      # fp32 division may legitimately land on the tie
+            assert int(u[b, i]) - (1 << (n_bits - 1)) == c_best, (b, i)
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_power_of_two_grid_is_exact(n_bits):
+    qmax = (1 << (n_bits - 1)) - 1
+    rng = np.random.default_rng(n_bits)
+    for k in (-10, -3, 0, 4, 9):
+        c = rng.integers(-qmax, qmax + 1, size=(8, 32))
+        c[:, 5] = qmax * np.where(rng.random(8) < 0.5, -1, 1)     # amax hits qmax
+        x = (c * 2.0 ** k).astype(np.float32)
+        u, d16 = quant.quantize_blocks(x, n_bits)
+        assert np.all(d16.astype(np.float64) == 2.0 ** k)      # one block per row
+        assert np.array_equal(u.astype(np.int64) - (1 << (n_bits - 1)), c)
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_zero_block_and_sign_symmetry(n_bits):
+    z = np.zeros((2, 32), dtype=np.float32)
+    u, d16 = quant.quantize_blocks(z, n_bits)
+    assert np.all(u == (1 << (n_bits - 1)))
+    assert np.all(d16.view(np.uint16) == 0)
+    x = _blocks(300 + n_bits, 50, 1.5)
+    u1, d1 = quant.quantize_blocks(x, n_bits)
+    u2, d2 = quant.quantize_blocks(-x, n_bits)
+    off = 1 << (n_bits - 1)
+    assert np.array_equal(d1.view(np.uint16), d2.view(np.uint16))
+    assert np.array_equal(u1.astype(int) - off, -(u2.astype(int) - off))
+
+
+def test_tiny_and_huge_scales():
+    # scale below half the smallest fp16 subnormal -> zero scale, zero codes
+    x = np.full((1, 32), 1e-9, dtype=np.float32)
+    u, d16 = quant.quantize_blocks(x, 4)
+    assert d16.view(np.uint16)[0, 0] == 0 and np.all(u == 8)
+    # saturation at 65504: codes clamp to qmax
+    x = np.full((1, 32), 3e38, dtype=np.float32)
+    u, d16 = quant.quantize_blocks(x, 8)
+    assert float(d16[0, 0]) == 65504.0 and np.all(u == 255)
+    # an fp16-subnormal scale is kept (no flush) and codes stay within range
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 1e-4
+    x[0, 1] = -3e-5
+    u, d16 = quant.quantize_blocks(x, 8)
+    assert 0 < float(d16[0, 0]) < 2.0 ** -14
+    assert int(u[0, 0]) - 128 == 127
+
+
+def test_dequantize_exact():
+    u = np.array([[0, 1, 127, 128, 255] + [128] * 27], dtype=np.uint8)
+    d = np.array([0.375], dtype=np.float16)
+    v = quant.dequantize_blocks(u, d, 8)
+    assert list(v[0, :5]) == [-48.0, -47.625, -0.375, 0.0, 47.625]
+
+
+# --------------------------------------------------------------------------- KVarN
+
+def test_kvarn_sigma_brute_force():
+    rng = np.random.default_rng(5)
+    x = bf16_to_f32(bf16_bits(rng.standard_normal((37, 2, 64)).astype(np.float32) * 3))
+    s = quant.kvarn_sigma(x)
+    for h in range(2):
+        for c in range(64):
+            col = [float(v) for v in x[:, h, c]]
+            ms = math.fsum(v * v for v in col) / len(col)
+            ref = np.float16(math.sqrt(ms))          # fp64 -> fp16 RNE
+            assert s[h, c] == ref
+
+
+def test_kvarn_sigma_closed_forms():
+    x = np.zeros((10, 1, 6), dtype=np.float32)
+    x[:, 0, 0] = 2.5                     # constant channel: sigma = |a|
+    x[:, 0, 1] = np.where(np.arange(10) % 2 == 0, 1.0, -1.0)   # +-1: sigma = 1
+    x[:, 0, 2] = 0.0                     # zero channel -> 1
+    x[:, 0, 3] = 1e-12                   # below fp16 range -> clamped to 2^-14
+    x[:, 0, 4] = 1e6                     # above fp16 range -> 65504
+    x[:, 0, 5] = -7.0
+    s = quant.kvarn_sigma(x)[0].astype(np.float64)
+    assert list(s) == [2.5, 1.0, 1.0, 2.0 ** -14, 65504.0, 7.0]
+
+
+@pytest.mark.parametrize("n_bits", [3, 4, 6, 8])
+def test_kvarn_unit_sigma_reduces_to_plain(n_bits):
+    rng = np.random.default_rng(n_bits)
+    x = bf16_to_f32(bf16_bits(rng.standard_normal((20, 1, 64)).astype(np.float32)))
+    sig = np.ones((1, 64), dtype=np.float16)
+    y = quant.normalize(x, sig)
+    assert np.array_equal(y, x)
+    assert np.array_equal(quant.quantize_blocks(y, n_bits)[0], quant.quantize_blocks(x, n_bits)[0])
+
+
+@pytest.mark.parametrize("n_bits", [4, 5, 6])
+def test_kvarn_power_of_two_channel_scaling(n_bits):
+    rng = np.random.default_rng(10 + n_bits)
+    x = bf16_to_f32(bf16_bits(rng.standard_normal((50, 1, 64)).astype(np.float32)))
+    k = rng.integers(-4, 5, size=64)
+    x2 = (x * (2.0 ** k)[None, None, :]).astype(np.float32)          # exact
+    s1, s2 = quant.kvarn_sigma(x), quant.kvarn_sigma(x2)
+    assert np.array_equal(s2.astype(np.float64), s1.astype(np.float64) * 2.0 ** k[None, :])
+    u1, d1 = quant.quantize_blocks(quant.normalize(x, s1), n_bits)
+    u2, d2 = quant.quantize_blocks(quant.normalize(x2, s2), n_bits)
+    assert np.array_equal(u1, u2) and np.array_equal(d1.view(np.uint16), d2.view(np.uint16))
+
+
+def test_kvarn_normalized_round_trip():
+    rng = np.random.default_rng(77)
+    sc = np.abs(rng.standard_t(3, size=64)).astype(np.float32)
+    x = bf16_to_f32(bf16_bits(rng.standard_normal((64, 1, 64)).astype(np.float32) * sc))
+    s = quant.kvarn_sigma(x)
+    y = quant.normalize(x, s)
+    u, d16 = quant.quantize_blocks(y, 4)
+    c = u.astype(np.float64) - 8
+    err = np.abs(y.astype(np.float64) - c * np.repeat(d16.astype(np.float64), 32, axis=-1))
+    assert np.all(err <= np.repeat(d16.astype(np.float64), 32, axis=-1) / 2 + 2.0 ** -24 * np.abs(y))
