@@ -1,0 +1,151 @@
+/*
+ * kvq — mixed-precision quantized KV cache and the decode attention that reads it (MI355X / gfx950).
+ *
+ * C ABI. Every entry point takes plain pointers and sizes; device pointers are HIP device memory owned
+ * by the caller, host pointers are ordinary host memory read during the call only. Nothing here
+ * allocates device memory. All GPU work is enqueued asynchronously on the caller's stream (a
+ * hipStream_t passed as void*; NULL = the default stream). Calls on one cache handle must be ordered
+ * on one stream; a handle is not thread-safe.
+ *
+ * Errors: every call validates its arguments and the cache state on the host before any HIP call and
+ * returns a kvq_status; no exception crosses the ABI. A launch failure returns KVQ_E_HIP. A fault
+ * inside a kernel surfaces at the caller's next stream synchronisation. kvq_last_error() returns a
+ * thread-local message describing the last failure.
+ *
+ * Passages cited: "BeeLlama.cpp v0.4.1" page (KV cache types q2_0..q8_0, KVarN, precision tail);
+ * "KV cache quant benchmarks: KVarN 6-bit matches q8_0, 4-bit matches q5_0" page (separate K and V
+ * types, cache-size column); "Hard numbers on Qwen3.8-27B's KV cache" page (K 6-bit / V 5-bit with a
+ * 2,048-position 8-bit ring; requantization when the window moves); "You can offload most of
+ * Qwen3.8-Flash-Next's KV cache to RAM" page (decode reads the whole cache of a full-attention layer;
+ * a QSA layer reads only an indexer-chosen budget of positions).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_E_INVALID = -1,   /* bad argument or configuration                                   */
+  KVQ_E_CAPACITY = -2,  /* an append would exceed the per-sequence capacity                 */
+  KVQ_E_SIZE = -3,      /* a caller buffer (arena, workspace) is too small                  */
+  KVQ_E_HIP = -4,       /* a HIP runtime call or kernel launch failed                        */
+  KVQ_E_STATE = -5      /* the call is not valid in the cache's current state (e.g. empty)   */
+} kvq_status;
+
+typedef enum {
+  KVQ_TAIL_NONE = 0,    /* no precision tail: every token goes straight to the qN_0 body          */
+  KVQ_TAIL_BF16 = 1,    /* newest tail_len tokens kept in bf16 (BeeLlama page, precision tail)     */
+  KVQ_TAIL_Q8_0 = 2     /* newest tail_len tokens kept as q8_0 (Qwen3.8-27B page, 8-bit ring)      */
+} kvq_tail_dtype;
+
+/* Maximum number of sequences one call may name. */
+#define KVQ_MAX_BATCH 64
+
+/* Cache configuration. K and V bit widths are chosen separately (KVarN benchmark page, K/V pairs). */
+typedef struct {
+  int32_t n_layers;     /* layers held by the arena                                        */
+  int32_t max_seqs;     /* sequence slots per layer; sequence ids are 0..max_seqs-1          */
+  int32_t capacity;     /* maximum positions per sequence                                    */
+  int32_t n_q_heads;    /* query heads; n_q_heads / n_kv_heads <= 8                           */
+  int32_t n_kv_heads;   /* KV heads                                                          */
+  int32_t head_dim;     /* 256 (the layout also covers 128; kernels are built for 256)       */
+  int32_t k_bits;       /* 2..8: qN_0 width of the K body                                     */
+  int32_t v_bits;       /* 2..8: qN_0 width of the V body                                     */
+  int32_t kvarn;        /* 0/1: per-channel variance normalization before block quantization */
+  int32_t tail_len;     /* W: newest tokens kept in the tail ring (0 = no ring)                */
+  int32_t tail_slack;   /* S: extra ring slots; ring capacity R = W + S must be a multiple of 32 */
+  int32_t tail_dtype;   /* kvq_tail_dtype (ignored when tail_len == 0)                          */
+} kvq_config;
+
+typedef struct kvq_cache kvq_cache;
+
+/* Regions of one (layer, sequence) slab, for kvq_region(). */
+enum { KVQ_REGION_K_BODY = 0, KVQ_REGION_V_BODY = 1, KVQ_REGION_K_RING = 2, KVQ_REGION_V_RING = 3,
+       KVQ_REGION_SIGMA = 4, KVQ_REGION_SLAB = 5 };
+
+/* Validate a configuration (host only). */
+kvq_status kvq_config_validate(const kvq_config* cfg);
+
+/* Exact arena size in bytes for cfg (0 if cfg is invalid). The body costs N bits per value plus one
+ * fp16 scale per 32 values; a tail ring costs R slots of bf16 or q8_0 rows; KVarN adds D fp16 scales
+ * per (layer, sequence, KV head, K/V). At 16 layers x 4 KV heads x 256 x 65,536 positions this gives the
+ * BeeLlama page's KV MiB column for q4_0..q8_0 at tail 0 / 1024 / 2048. */
+size_t kvq_cache_bytes(const kvq_config* cfg);
+
+/* Byte offset and size of a region of the (layer, seq) slab inside the arena (host only). */
+kvq_status kvq_region(const kvq_config* cfg, int32_t layer, int32_t seq, int32_t region,
+                      size_t* offset, size_t* bytes);
+
+/* Create a host handle over a caller-owned device arena of at least kvq_cache_bytes(cfg) bytes
+ * (256-byte aligned). The arena is zero-filled on `stream`; every sequence starts empty. The handle
+ * records the arena pointer, the configuration and per-(layer, sequence) lengths; it owns no device
+ * memory. */
+kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_arena, size_t arena_bytes, void* stream,
+                          kvq_cache** out);
+
+/* Free the host handle (the arena stays the caller's). */
+void kvq_cache_destroy(kvq_cache* cache);
+
+/* Forget the contents of sequences (lengths and KVarN calibration back to zero) and zero their slabs
+ * for the given layer (layer = -1: every layer). seq_ids: host int32[n_seqs]. */
+kvq_status kvq_seq_reset(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                         void* stream);
+
+/* Host-side lengths of a (layer, seq): positions held (len) and positions in the qN_0 body. */
+kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t seq, int32_t* len,
+                           int32_t* body_len);
+
+/* Workspace bytes needed by kvq_decode_attn / kvq_sparse_decode_attn for n_seqs sequences of at most
+ * max_len positions (sparse: max_len = budget). */
+size_t kvq_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t max_len);
+
+/* Append n_new[i] tokens to sequence seq_ids[i] of `layer` (a1-a4).
+ * seq_ids, n_new: host int32[n_seqs] (distinct ids). k_bf16, v_bf16: device bf16 [sum n_new][Hkv][D],
+ * sequences packed in call order. The first non-empty append of a (layer, seq) calibrates the KVarN
+ * scales from its tokens (BeeLlama page, KVarN). With a tail ring the new tokens enter the ring; when
+ * the ring (R = W + S slots) would overflow, its oldest rows are first requantized into the body
+ * (Qwen3.8-27B page, window boundary), and new tokens already behind the window go to the body through
+ * the ring representation, so the body never depends on how tokens were chunked. Without a ring tokens
+ * are quantized straight into the body. Errors: KVQ_E_CAPACITY if len + n_new > capacity. */
+kvq_status kvq_append(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                      const int32_t* n_new, const void* k_bf16, const void* v_bf16, void* stream);
+
+/* Requantize ring rows older than the newest tail_len into the body (a4; Qwen3.8-27B page: blocks are
+ * requantized when the window boundary moves). After the call the ring holds exactly the newest
+ * min(len, W) positions. No-op without a ring. seq_ids: host int32[n_seqs]. */
+kvq_status kvq_tail_evict(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                          void* stream);
+
+/* Dense decode attention (a5 + a6; offload page: each step reads the whole cache of a full-attention
+ * layer). For each sequence i: out[i][h][:] = softmax(scale * q[i][h] . K^[t]) over t in [0, len) of V^,
+ * with K^, V^ the dequantized body rows (t < body_len) or ring rows. q_bf16: device bf16
+ * [n_seqs][Hq][D]; out: device fp32 [n_seqs][Hq][D]; softmax_scale <= 0 means 1/sqrt(D); workspace:
+ * device, at least kvq_workspace_bytes(cache, n_seqs, max len) bytes, 256-byte aligned.
+ * Errors: KVQ_E_STATE if a sequence is empty; KVQ_E_SIZE if the workspace is too small. */
+kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                           const void* q_bf16, float* out, float softmax_scale, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/* Sparse decode attention over an indexer budget (a7; offload page, QSA: the layer reads only the
+ * main-KV rows at the positions the indexer chose, so the budget, not the context, bounds the bytes).
+ * positions: device int32 [n_seqs][budget], one list per sequence shared by all KV heads; entries must
+ * be distinct and in [0, len) (entries outside are skipped). 1 <= budget <= len of every sequence.
+ * Other arguments as kvq_decode_attn. */
+kvq_status kvq_sparse_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                  const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
+                                  float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
+
+/* Thread-local text of the last error (never NULL). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

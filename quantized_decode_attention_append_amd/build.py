@@ -1,0 +1,65 @@
+"""Build libkvq.so (the HIP library behind include/kvq.h) in-tree for gfx950.
+
+Each translation unit is compiled by hipcc in parallel, then linked into a shared library that sits
+next to this file. Flags:
+* ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed fp32 instructions are generated.
+* ``-fhip-fp32-correctly-rounded-divide-sqrt`` and, for the append kernels, ``-ffp-contract=off``: the
+  quantizer's fp32 division and rounding are plain IEEE operations, bit-identical to a CPU evaluation.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libkvq.so")
+BUILD = os.path.join(HERE, "_build")
+
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wno-unused-command-line-argument"]
+
+UNITS = [
+    ("kvq_host.cpp", ["-ffp-contract=off"]),
+    ("kvq_append.hip", ["-ffp-contract=off"]),
+    ("kvq_decode.hip", ["-ffp-contract=fast"]),
+]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the kvq HIP library cannot be built")
+
+
+def _compile(src: str, extra) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(UNITS)) as ex:
+        objs = list(ex.map(lambda u: _compile(*u), UNITS))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"[kvq] built {LIB}", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

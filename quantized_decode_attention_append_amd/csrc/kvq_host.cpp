@@ -1,0 +1,456 @@
+// Host side of the kvq C ABI: validation, per-(layer, sequence) bookkeeping, work planning and launches.
+// Every entry point validates on the host before any HIP call; no exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_kernels.h"
+
+using kvq::SlabLayout;
+
+struct kvq_cache {
+  kvq_config cfg;
+  SlabLayout lay;
+  uint8_t* arena;
+  size_t arena_bytes;
+  std::vector<int32_t> len, body_len;
+  std::vector<uint8_t> calibrated;
+  int idx(int layer, int seq) const { return layer * cfg.max_seqs + seq; }
+};
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+kvq_status fail(kvq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kvq_status fail(kvq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+SlabLayout layout_of(const kvq_config& c) {
+  return kvq::slab_layout(c.capacity, c.n_kv_heads, c.head_dim, c.k_bits, c.v_bits, c.kvarn, c.tail_len,
+                          c.tail_slack, c.tail_dtype);
+}
+
+kvq_status validate(const kvq_config* c) {
+  if (!c) return fail(KVQ_E_INVALID, "config is NULL");
+  if (c->n_layers < 1) return fail(KVQ_E_INVALID, "n_layers must be >= 1 (got %d)", c->n_layers);
+  if (c->max_seqs < 1) return fail(KVQ_E_INVALID, "max_seqs must be >= 1 (got %d)", c->max_seqs);
+  if (c->capacity < 1 || c->capacity > (1 << 28))
+    return fail(KVQ_E_INVALID, "capacity must be in [1, 2^28] (got %d)", c->capacity);
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+    return fail(KVQ_E_INVALID, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > kvq::kPartialHeads)
+    return fail(KVQ_E_INVALID, "query group n_q_heads / n_kv_heads must be <= 8 (got %d)",
+                c->n_q_heads / c->n_kv_heads);
+  if (c->head_dim != 256) return fail(KVQ_E_INVALID, "head_dim must be 256 (got %d)", c->head_dim);
+  if (c->k_bits < 2 || c->k_bits > 8 || c->v_bits < 2 || c->v_bits > 8)
+    return fail(KVQ_E_INVALID, "k_bits and v_bits must be in [2, 8] (got %d, %d)", c->k_bits, c->v_bits);
+  if (c->kvarn != 0 && c->kvarn != 1) return fail(KVQ_E_INVALID, "kvarn must be 0 or 1");
+  if (c->tail_len < 0 || c->tail_slack < 0) return fail(KVQ_E_INVALID, "tail_len and tail_slack must be >= 0");
+  if (c->tail_len > 0) {
+    if (c->tail_dtype != KVQ_TAIL_BF16 && c->tail_dtype != KVQ_TAIL_Q8_0)
+      return fail(KVQ_E_INVALID, "tail_dtype must be KVQ_TAIL_BF16 or KVQ_TAIL_Q8_0 when tail_len > 0");
+    const long r = (long)c->tail_len + c->tail_slack;
+    if (r % kvq::kTile != 0) return fail(KVQ_E_INVALID, "tail_len + tail_slack must be a multiple of 32 (got %ld)", r);
+    if (r > (1 << 24)) return fail(KVQ_E_INVALID, "tail_len + tail_slack too large");
+  }
+  return KVQ_OK;
+}
+
+kvq::Geometry geometry(const kvq_cache* c) {
+  kvq::Geometry g{};
+  g.arena = c->arena;
+  g.slab_bytes = c->lay.slab;
+  g.k_body = c->lay.k_body;
+  g.v_body = c->lay.v_body;
+  g.k_ring = c->lay.k_ring;
+  g.v_ring = c->lay.v_ring;
+  g.sigma = c->lay.sigma;
+  g.cap32 = c->lay.cap32;
+  g.row_k = c->lay.row_k;
+  g.row_v = c->lay.row_v;
+  g.tile_v = kvq::kTile * c->lay.row_v;
+  g.ring_row_k = c->lay.ring_row_k;
+  g.ring_tile_v = kvq::kTile * c->lay.ring_row_v;
+  g.ring_slots = c->lay.ring_slots;
+  g.n_kv_heads = c->cfg.n_kv_heads;
+  g.head_dim = c->cfg.head_dim;
+  g.k_bits = c->cfg.k_bits;
+  g.v_bits = c->cfg.v_bits;
+  g.kvarn = c->cfg.kvarn;
+  g.tail_dtype = c->cfg.tail_len > 0 ? c->cfg.tail_dtype : 0;
+  return g;
+}
+
+size_t slab_offset(const kvq_cache* c, int layer, int seq) {
+  return ((size_t)layer * c->cfg.max_seqs + seq) * c->lay.slab;
+}
+
+kvq_status check_seqs(const kvq_cache* c, int layer, int n_seqs, const int32_t* ids) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVQ_E_INVALID, "layer %d out of range", layer);
+  if (n_seqs < 1 || n_seqs > KVQ_MAX_BATCH)
+    return fail(KVQ_E_INVALID, "n_seqs must be in [1, %d] (got %d)", KVQ_MAX_BATCH, n_seqs);
+  if (!ids) return fail(KVQ_E_INVALID, "seq_ids is NULL");
+  for (int i = 0; i < n_seqs; ++i) {
+    if (ids[i] < 0 || ids[i] >= c->cfg.max_seqs) return fail(KVQ_E_INVALID, "seq id %d out of range", ids[i]);
+    for (int j = 0; j < i; ++j)
+      if (ids[j] == ids[i]) return fail(KVQ_E_INVALID, "seq id %d repeated", ids[i]);
+  }
+  return KVQ_OK;
+}
+
+int tiles_of(int p0, int p1) { return p1 > p0 ? (p1 - 1) / kvq::kTile - p0 / kvq::kTile + 1 : 0; }
+
+// Split planning shared by kvq_workspace_bytes and kvq_decode_attn.
+constexpr int kTargetWgs = 512;
+constexpr int kMinTilesPerSplit = 4;
+constexpr size_t kPartialFloats(int d) { return (size_t)kvq::kPartialHeads * (d + 2); }
+
+struct SplitPlan {
+  int tiles_per_split;
+  int max_splits;
+};
+
+SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out) {
+  long total = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int bt = (body_len[i] + kvq::kTile - 1) / kvq::kTile;
+    const int rt = len[i] > body_len[i] ? (len[i] + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
+    total += (long)c->cfg.n_kv_heads * (bt + rt);
+  }
+  long t = (total + kTargetWgs - 1) / kTargetWgs;
+  t = (t + 3) / 4 * 4;
+  if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
+  SplitPlan p{(int)t, 1};
+  for (int i = 0; i < n_seqs; ++i) {
+    const int bt = (body_len[i] + kvq::kTile - 1) / kvq::kTile;
+    const int rt = len[i] > body_len[i] ? (len[i] + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
+    const int nb = (bt + p.tiles_per_split - 1) / p.tiles_per_split;
+    const int nr = (rt + p.tiles_per_split - 1) / p.tiles_per_split;
+    if (out) {
+      out[i].len = len[i];
+      out[i].body_len = body_len[i];
+      out[i].n_body_splits = nb;
+      out[i].n_ring_splits = nr;
+      out[i].ring_tile0 = body_len[i] / kvq::kTile;
+    }
+    p.max_splits = std::max(p.max_splits, nb + nr);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+kvq_status kvq_config_validate(const kvq_config* cfg) { return validate(cfg); }
+
+size_t kvq_cache_bytes(const kvq_config* cfg) {
+  if (validate(cfg) != KVQ_OK) return 0;
+  return (size_t)cfg->n_layers * cfg->max_seqs * layout_of(*cfg).slab;
+}
+
+kvq_status kvq_region(const kvq_config* cfg, int32_t layer, int32_t seq, int32_t region, size_t* offset,
+                      size_t* bytes) {
+  kvq_status s = validate(cfg);
+  if (s != KVQ_OK) return s;
+  if (!offset || !bytes) return fail(KVQ_E_INVALID, "offset/bytes is NULL");
+  if (layer < 0 || layer >= cfg->n_layers || seq < 0 || seq >= cfg->max_seqs)
+    return fail(KVQ_E_INVALID, "layer/seq out of range");
+  const SlabLayout L = layout_of(*cfg);
+  const size_t base = ((size_t)layer * cfg->max_seqs + seq) * L.slab;
+  switch (region) {
+    case KVQ_REGION_K_BODY: *offset = base + L.k_body; *bytes = L.k_body_sz; break;
+    case KVQ_REGION_V_BODY: *offset = base + L.v_body; *bytes = L.v_body_sz; break;
+    case KVQ_REGION_K_RING: *offset = base + L.k_ring; *bytes = L.k_ring_sz; break;
+    case KVQ_REGION_V_RING: *offset = base + L.v_ring; *bytes = L.v_ring_sz; break;
+    case KVQ_REGION_SIGMA: *offset = base + L.sigma; *bytes = L.sigma_sz; break;
+    case KVQ_REGION_SLAB: *offset = base; *bytes = L.slab; break;
+    default: return fail(KVQ_E_INVALID, "unknown region %d", region);
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_arena, size_t arena_bytes, void* stream,
+                          kvq_cache** out) {
+  kvq_status s = validate(cfg);
+  if (s != KVQ_OK) return s;
+  if (!out) return fail(KVQ_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!dev_arena) return fail(KVQ_E_INVALID, "arena is NULL");
+  if (((uintptr_t)dev_arena) % 256 != 0) return fail(KVQ_E_INVALID, "arena must be 256-byte aligned");
+  const size_t need = kvq_cache_bytes(cfg);
+  if (arena_bytes < need) return fail(KVQ_E_SIZE, "arena has %zu bytes, needs %zu", arena_bytes, need);
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return fail(KVQ_E_INVALID, "out of host memory");
+  c->cfg = *cfg;
+  c->lay = layout_of(*cfg);
+  c->arena = (uint8_t*)dev_arena;
+  c->arena_bytes = arena_bytes;
+  const size_t n = (size_t)cfg->n_layers * cfg->max_seqs;
+  c->len.assign(n, 0);
+  c->body_len.assign(n, 0);
+  c->calibrated.assign(n, 0);
+  hipError_t e = kvq::launch_fill_zero(dev_arena, need, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "zero-fill of the arena");
+  }
+  *out = c;
+  return KVQ_OK;
+}
+
+void kvq_cache_destroy(kvq_cache* cache) { delete cache; }
+
+kvq_status kvq_seq_reset(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (layer < -1 || layer >= c->cfg.n_layers) return fail(KVQ_E_INVALID, "layer %d out of range", layer);
+  kvq_status s = check_seqs(c, layer < 0 ? 0 : layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->cfg.n_layers : layer + 1;
+  for (int l = l0; l < l1; ++l)
+    for (int i = 0; i < n_seqs; ++i) {
+      hipError_t e = kvq::launch_fill_zero(c->arena + slab_offset(c, l, seq_ids[i]), c->lay.slab, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "zero-fill of a slab");
+      const int k = c->idx(l, seq_ids[i]);
+      c->len[k] = c->body_len[k] = 0;
+      c->calibrated[k] = 0;
+    }
+  return KVQ_OK;
+}
+
+kvq_status kvq_seq_lengths(const kvq_cache* c, int32_t layer, int32_t seq, int32_t* len, int32_t* body_len) {
+  if (!c || !len || !body_len) return fail(KVQ_E_INVALID, "NULL argument");
+  if (layer < 0 || layer >= c->cfg.n_layers || seq < 0 || seq >= c->cfg.max_seqs)
+    return fail(KVQ_E_INVALID, "layer/seq out of range");
+  *len = c->len[c->idx(layer, seq)];
+  *body_len = c->body_len[c->idx(layer, seq)];
+  return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) {
+  if (!c || n_seqs < 1 || max_len < 1) return 0;
+  // splits per (seq, head) never exceed the tiles of one sequence / 4 + 2, nor the work-group target + 2
+  const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 2;
+  long splits = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit + 2;
+  splits = std::min<long>(splits, kTargetWgs + 2);
+  return (size_t)n_seqs * c->cfg.n_kv_heads * splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
+}
+
+kvq_status kvq_append(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                      const void* k_bf16, const void* v_bf16, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (!n_new) return fail(KVQ_E_INVALID, "n_new is NULL");
+  long total = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (n_new[i] < 0) return fail(KVQ_E_INVALID, "n_new[%d] is negative", i);
+    const int k = c->idx(layer, seq_ids[i]);
+    if ((long)c->len[k] + n_new[i] > c->cfg.capacity)
+      return fail(KVQ_E_CAPACITY, "seq %d: %d + %d positions exceed capacity %d", seq_ids[i], c->len[k], n_new[i],
+                  c->cfg.capacity);
+    total += n_new[i];
+  }
+  if (total == 0) return KVQ_OK;
+  if (!k_bf16 || !v_bf16) return fail(KVQ_E_INVALID, "k/v input is NULL");
+
+  const kvq::Geometry g = geometry(c);
+  const hipStream_t st = (hipStream_t)stream;
+  const int W = c->cfg.tail_len;
+  const int R = c->lay.ring_slots;
+
+  kvq::CalibArgs ca{};
+  ca.g = g;
+  ca.k_in = (const uint16_t*)k_bf16;
+  ca.v_in = (const uint16_t*)v_bf16;
+  kvq::WriteArgs body{}, ring{}, ring2{};
+  body.g = ring.g = ring2.g = g;
+  body.k_in = ring.k_in = ring2.k_in = (const uint16_t*)k_bf16;
+  body.v_in = ring.v_in = ring2.v_in = (const uint16_t*)v_bf16;
+  body.dst_ring = 0;
+  ring.dst_ring = ring2.dst_ring = 1;
+  int body_wgs = 0, ring_wgs = 0, ring2_wgs = 0;
+  std::vector<int> new_len(n_seqs), new_body(n_seqs);
+
+  int row = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    const int n = n_new[i];
+    const int len = c->len[k], bl = c->body_len[k];
+    const size_t slab = slab_offset(c, layer, seq_ids[i]);
+    new_len[i] = len + n;
+    new_body[i] = bl;
+    if (n == 0) continue;
+    if (c->cfg.kvarn && !c->calibrated[k]) ca.items[ca.n_items++] = kvq::CalibItem{slab, row, n};
+    int b0, b1, r0 = 0, r1 = 0;
+    if (W == 0) {
+      b0 = len;
+      b1 = len + n;
+      new_body[i] = len + n;
+    } else {
+      const int nb = std::max(bl, len + n - R);
+      b0 = bl;
+      b1 = nb;
+      r0 = std::max(len, nb);
+      r1 = len + n;
+      new_body[i] = nb;
+    }
+    if (b1 > b0) {
+      kvq::WriteItem& it = body.items[body.n_items++];
+      it = kvq::WriteItem{slab, b0, b1, len, row, b0 / kvq::kTile, body_wgs};
+      body_wgs += tiles_of(b0, b1);
+    }
+    if (r1 > r0) {
+      // A ring write of up to R positions spans at most R/32 + 1 position tiles; when it does, its first
+      // and last tiles land in the same ring tile. The q8_0 ring updates V tiles by read-modify-write, so
+      // the last tile then goes to a second, stream-ordered launch.
+      int r_split = r1;
+      if (c->cfg.tail_dtype == KVQ_TAIL_Q8_0 && tiles_of(r0, r1) > R / kvq::kTile)
+        r_split = (r1 - 1) / kvq::kTile * kvq::kTile;
+      kvq::WriteItem& it = ring.items[ring.n_items++];
+      it = kvq::WriteItem{slab, r0, r_split, len, row, r0 / kvq::kTile, ring_wgs};
+      ring_wgs += tiles_of(r0, r_split);
+      if (r_split < r1) {
+        kvq::WriteItem& it2 = ring2.items[ring2.n_items++];
+        it2 = kvq::WriteItem{slab, r_split, r1, len, row, r_split / kvq::kTile, ring2_wgs};
+        ring2_wgs += tiles_of(r_split, r1);
+      }
+    }
+    row += n;
+  }
+
+  hipError_t e;
+  if (ca.n_items) {
+    e = kvq::launch_calibrate(ca, ca.n_items, st);
+    if (e != hipSuccess) return hip_fail(e, "calibrate launch");
+  }
+  if (body_wgs) {
+    e = kvq::launch_body_write(body, body_wgs, st);
+    if (e != hipSuccess) return hip_fail(e, "body write launch");
+  }
+  if (ring_wgs) {
+    e = (c->cfg.tail_dtype == KVQ_TAIL_BF16) ? kvq::launch_bf16_ring_write(ring, ring_wgs, st)
+                                             : kvq::launch_body_write(ring, ring_wgs, st);
+    if (e != hipSuccess) return hip_fail(e, "ring write launch");
+  }
+  if (ring2_wgs) {
+    e = kvq::launch_body_write(ring2, ring2_wgs, st);
+    if (e != hipSuccess) return hip_fail(e, "ring write launch");
+  }
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    if (n_new[i] > 0 && c->cfg.kvarn) c->calibrated[k] = 1;
+    c->len[k] = new_len[i];
+    c->body_len[k] = new_body[i];
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_tail_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  const int W = c->cfg.tail_len;
+  if (W == 0) return KVQ_OK;
+  kvq::WriteArgs body{};
+  body.g = geometry(c);
+  body.dst_ring = 0;
+  int wgs = 0;
+  std::vector<int> target(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    const int len = c->len[k], bl = c->body_len[k];
+    target[i] = std::max(bl, len - W);
+    if (target[i] > bl) {
+      kvq::WriteItem& it = body.items[body.n_items++];
+      it = kvq::WriteItem{slab_offset(c, layer, seq_ids[i]), bl, target[i], len, 0, bl / kvq::kTile, wgs};
+      wgs += tiles_of(bl, target[i]);
+    }
+  }
+  if (wgs) {
+    hipError_t e = kvq::launch_body_write(body, wgs, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "evict launch");
+  }
+  for (int i = 0; i < n_seqs; ++i) c->body_len[c->idx(layer, seq_ids[i])] = target[i];
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
+                           float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (!q_bf16 || !out || !workspace) return fail(KVQ_E_INVALID, "q/out/workspace is NULL");
+  if (((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
+  int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    len[i] = c->len[k];
+    bl[i] = c->body_len[k];
+    if (len[i] < 1) return fail(KVQ_E_STATE, "seq %d of layer %d is empty", seq_ids[i], layer);
+  }
+  kvq::DecodeArgs a{};
+  a.g = geometry(c);
+  const SplitPlan p = plan_splits(c, n_seqs, len, bl, a.seqs);
+  const size_t need = (size_t)n_seqs * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  for (int i = 0; i < n_seqs; ++i) a.seqs[i].slab = slab_offset(c, layer, seq_ids[i]);
+  a.q = (const uint16_t*)q_bf16;
+  a.out = out;
+  a.partials = (float*)workspace;
+  a.n_seqs = n_seqs;
+  a.n_q_heads = c->cfg.n_q_heads;
+  a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  a.max_splits = p.max_splits;
+  a.tiles_per_split = p.tiles_per_split;
+  a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
+  hipError_t e = kvq::launch_decode(a, p.max_splits, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  kvq::CombineArgs cb{};
+  cb.out = out;
+  cb.partials = (const float*)workspace;
+  cb.n_seqs = n_seqs;
+  cb.n_q_heads = c->cfg.n_q_heads;
+  cb.n_kv_heads = c->cfg.n_kv_heads;
+  cb.group = a.group;
+  cb.head_dim = c->cfg.head_dim;
+  cb.max_splits = p.max_splits;
+  for (int i = 0; i < n_seqs; ++i) cb.n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
+  e = kvq::launch_combine(cb, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_sparse_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                  const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
+                                  float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  (void)q_bf16; (void)positions; (void)budget; (void)out; (void)softmax_scale; (void)workspace; (void)ws_bytes;
+  (void)stream;
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  return fail(KVQ_E_INVALID, "sparse decode is not built yet");
+}
+
+}  // extern "C"

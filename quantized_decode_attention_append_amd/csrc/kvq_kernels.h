@@ -1,0 +1,106 @@
+// Kernel argument blocks and launch wrappers shared by the kvq host code and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvq_format.h"
+
+namespace kvq {
+
+constexpr int kMaxBatch = 64;      // sequences per call (kernel arguments are passed by value)
+constexpr int kPartialHeads = 8;   // query heads per KV head handled by one decode work-group
+
+// Geometry of one (layer) of the arena, as the kernels need it.
+struct Geometry {
+  uint8_t* arena;
+  size_t slab_bytes;
+  size_t k_body, v_body, k_ring, v_ring, sigma;   // region offsets within a slab
+  int cap32, row_k, row_v, tile_v, ring_row_k, ring_tile_v, ring_slots;
+  int n_kv_heads, head_dim, k_bits, v_bits, kvarn, tail_dtype;
+};
+
+// ---------------------------------------------------------------- append side
+
+// KVarN calibration: per (item, KV head, K/V) sum of squares over the item's first chunk.
+struct CalibItem {
+  size_t slab;       // byte offset of the (layer, seq) slab
+  int src_row;       // first input row of the chunk
+  int n;             // tokens in the chunk
+};
+struct CalibArgs {
+  Geometry g;
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  int n_items;
+  CalibItem items[kMaxBatch];
+};
+
+// Body write (quantize into the qN_0 body), one work-group per (item, tile, KV head).
+// Position p in [p0, p1): from input row src_row + (p - len_old) when p >= len_old (through the ring
+// representation when the ring is q8_0), otherwise from ring slot p mod R.
+// The same kernel writes q8_0 ring rows (dst_ring = 1: destination is the ring, source is the input).
+struct WriteItem {
+  size_t slab;
+  int p0, p1;        // positions written
+  int len_old;       // positions >= len_old come from the input
+  int src_row;       // input row of position len_old
+  int tile0;         // first position tile (p0 / 32)
+  int wg_begin;      // first work-group of this item (prefix over items)
+};
+struct WriteArgs {
+  Geometry g;
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  int dst_ring;      // 0: body; 1: q8_0 ring
+  int n_items;
+  WriteItem items[kMaxBatch];
+};
+
+// ---------------------------------------------------------------- decode side
+
+struct DecodeSeq {
+  size_t slab;
+  int len, body_len;
+  int n_body_splits, n_ring_splits;
+  int ring_tile0;    // first position tile of the ring range (body_len / 32)
+};
+struct DecodeArgs {
+  Geometry g;
+  const uint16_t* q;           // [n_seqs][Hq][D] bf16
+  float* out;                  // [n_seqs][Hq][D]
+  float* partials;             // [n_seqs][Hkv][max_splits][8 * (D + 2)]
+  int n_seqs, n_q_heads, group, max_splits, tiles_per_split;
+  float scale;                 // softmax scale
+  DecodeSeq seqs[kMaxBatch];
+};
+
+struct SparseArgs {
+  Geometry g;
+  const uint16_t* q;
+  const int32_t* positions;    // [n_seqs][budget]
+  float* out;
+  float* partials;
+  int n_seqs, n_q_heads, group, budget, max_splits, pos_per_split;
+  float scale;
+  DecodeSeq seqs[kMaxBatch];
+};
+
+struct CombineArgs {
+  float* out;
+  const float* partials;
+  int n_seqs, n_q_heads, n_kv_heads, group, head_dim, max_splits;
+  int n_splits[kMaxBatch];
+};
+
+// Launch wrappers (return the launch status).
+hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s);
+hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s);
+hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_sparse(const SparseArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,215 @@
+"""Thin Python binding of the kvq C ABI (include/kvq.h).
+
+Argument marshalling only: every step of the cache and of attention runs in the HIP library
+(``libkvq.so`` next to this file). PyTorch provides device memory (tensors' ``data_ptr()``) and streams
+(``torch.cuda.current_stream().cuda_stream``). If the library is missing this module raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_E_INVALID, KVQ_E_CAPACITY, KVQ_E_SIZE, KVQ_E_HIP, KVQ_E_STATE = 0, -1, -2, -3, -4, -5
+TAIL_NONE, TAIL_BF16, TAIL_Q8_0 = 0, 1, 2
+REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab": 5}
+MAX_BATCH = 64
+
+_FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits",
+           "kvarn", "tail_len", "tail_slack", "tail_dtype")
+
+SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
+           "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
+           "kvq_decode_attn", "kvq_sparse_decode_attn", "kvq_last_error")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in _FIELDS]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"kvq error {status}: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"kvq HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    CP = ctypes.POINTER(Config)
+    IP = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "kvq_config_validate": (I32, [CP]),
+        "kvq_cache_bytes": (SZ, [CP]),
+        "kvq_region": (I32, [CP, I32, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "kvq_cache_init": (I32, [CP, P, SZ, P, ctypes.POINTER(P)]),
+        "kvq_cache_destroy": (None, [P]),
+        "kvq_seq_reset": (I32, [P, I32, I32, IP, P]),
+        "kvq_seq_lengths": (I32, [P, I32, I32, IP, IP]),
+        "kvq_workspace_bytes": (SZ, [P, I32, I32]),
+        "kvq_append": (I32, [P, I32, I32, IP, IP, P, P, P]),
+        "kvq_tail_evict": (I32, [P, I32, I32, IP, P]),
+        "kvq_decode_attn": (I32, [P, I32, I32, IP, P, P, F, P, SZ, P]),
+        "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
+        "kvq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != KVQ_OK:
+        raise KvqError(status, _lib.kvq_last_error().decode())
+
+
+def make_config(cfg: Dict[str, int]) -> Config:
+    return Config(*[int(cfg[f]) for f in _FIELDS])
+
+
+def config_validate(cfg: Dict[str, int]) -> None:
+    c = make_config(cfg)
+    _check(_lib.kvq_config_validate(ctypes.byref(c)))
+
+
+def cache_bytes(cfg: Dict[str, int]) -> int:
+    c = make_config(cfg)
+    return int(_lib.kvq_cache_bytes(ctypes.byref(c)))
+
+
+def region(cfg: Dict[str, int], layer: int, seq: int, name: str):
+    c = make_config(cfg)
+    off, size = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.kvq_region(ctypes.byref(c), layer, seq, REGION[name], ctypes.byref(off), ctypes.byref(size)))
+    return off.value, size.value
+
+
+def _ids(seq_ids: Sequence[int]):
+    arr = (ctypes.c_int32 * len(seq_ids))(*[int(s) for s in seq_ids])
+    return arr
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Cache:
+    """A quantized KV cache over a torch-allocated device arena (the arena is owned by this object)."""
+
+    def __init__(self, cfg: Dict[str, int], arena: Optional[torch.Tensor] = None, stream=None):
+        self.cfg = dict(cfg)
+        self._c = make_config(self.cfg)
+        nbytes = cache_bytes(self.cfg)
+        if nbytes == 0:
+            config_validate(self.cfg)
+        if arena is None:
+            arena = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.arena = arena
+        h = ctypes.c_void_p()
+        _check(_lib.kvq_cache_init(ctypes.byref(self._c), _dev(arena, torch.uint8, "arena"), arena.numel(),
+                                   ctypes.c_void_p(_stream(stream)), ctypes.byref(h)))
+        self._h = h
+        self.hq = self.cfg["n_q_heads"]
+        self.hk = self.cfg["n_kv_heads"]
+        self.d = self.cfg["head_dim"]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.kvq_cache_destroy(h)
+            self._h = None
+
+    # ---------------------------------------------------------------- state
+    def lengths(self, layer: int, seq: int):
+        ln, bl = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.kvq_seq_lengths(self._h, layer, seq, ctypes.byref(ln), ctypes.byref(bl)))
+        return ln.value, bl.value
+
+    def seq_reset(self, layer: int, seq_ids: Sequence[int], stream=None):
+        _check(_lib.kvq_seq_reset(self._h, layer, len(seq_ids), _ids(seq_ids), ctypes.c_void_p(_stream(stream))))
+
+    def workspace_bytes(self, n_seqs: int, max_len: int) -> int:
+        return int(_lib.kvq_workspace_bytes(self._h, n_seqs, max_len))
+
+    def workspace(self, n_seqs: int, max_len: int) -> torch.Tensor:
+        n = self.workspace_bytes(n_seqs, max_len)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+
+    # ---------------------------------------------------------------- the calls
+    def append(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor,
+               v: torch.Tensor, stream=None):
+        """k, v: bf16 (or int16/uint16 bit patterns) [sum(n_new), Hkv, D] on the device."""
+        total = int(sum(int(n) for n in n_new))
+        for name, t in (("k", k), ("v", v)):
+            if t.numel() != total * self.hk * self.d:
+                raise ValueError(f"{name} has {t.numel()} elements, expected {total * self.hk * self.d}")
+        kp = _dev(k, k.dtype, "k") if total else ctypes.c_void_p(0)
+        vp = _dev(v, v.dtype, "v") if total else ctypes.c_void_p(0)
+        if total and k.element_size() != 2:
+            raise ValueError("k/v must hold 16-bit bf16 values")
+        nn = (ctypes.c_int32 * len(n_new))(*[int(n) for n in n_new])
+        _check(_lib.kvq_append(self._h, layer, len(seq_ids), _ids(seq_ids), nn, kp, vp,
+                               ctypes.c_void_p(_stream(stream))))
+
+    def tail_evict(self, layer: int, seq_ids: Sequence[int], stream=None):
+        _check(_lib.kvq_tail_evict(self._h, layer, len(seq_ids), _ids(seq_ids), ctypes.c_void_p(_stream(stream))))
+
+    def decode_attn(self, layer: int, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None):
+        n = len(seq_ids)
+        if q.numel() != n * self.hq * self.d or q.element_size() != 2:
+            raise ValueError("q must be bf16 [n_seqs, Hq, D]")
+        if out is None:
+            out = torch.empty((n, self.hq, self.d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            max_len = max(self.lengths(layer, s)[0] for s in seq_ids)
+            workspace = self.workspace(n, max(1, max_len))
+        _check(_lib.kvq_decode_attn(self._h, layer, n, _ids(seq_ids), _dev(q, q.dtype, "q"),
+                                    _dev(out, torch.float32, "out"), float(softmax_scale),
+                                    _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                    ctypes.c_void_p(_stream(stream))))
+        return out
+
+    def sparse_decode_attn(self, layer: int, seq_ids: Sequence[int], q: torch.Tensor, positions: torch.Tensor,
+                           out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+        n = len(seq_ids)
+        if q.numel() != n * self.hq * self.d or q.element_size() != 2:
+            raise ValueError("q must be bf16 [n_seqs, Hq, D]")
+        if positions.dim() != 2 or positions.shape[0] != n:
+            raise ValueError("positions must be int32 [n_seqs, budget]")
+        budget = positions.shape[1]
+        if out is None:
+            out = torch.empty((n, self.hq, self.d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(n, budget)
+        _check(_lib.kvq_sparse_decode_attn(self._h, layer, n, _ids(seq_ids), _dev(q, q.dtype, "q"),
+                                           _dev(positions, torch.int32, "positions"), budget,
+                                           _dev(out, torch.float32, "out"), float(softmax_scale),
+                                           _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                           ctypes.c_void_p(_stream(stream))))
+        return out

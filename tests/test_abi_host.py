@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every symbol include/kvq.h declares, and its host-only logic
+(validation, exact arena size, region offsets, workspace sizing) agrees with the oracle. No GPU calls."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.layout import slab_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "quantized_decode_attention_append_amd", "libkvq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkvq.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    import ctypes
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    from quantized_decode_attention_append_amd import kvq
+    assert set(kvq.SYMBOLS) == set(names)
+
+
+def _cfg(**kw):
+    c = dict(n_layers=2, max_seqs=3, capacity=1000, n_q_heads=16, n_kv_heads=2, head_dim=256, k_bits=6,
+             v_bits=5, kvarn=0, tail_len=64, tail_slack=32, tail_dtype=1)
+    c.update(kw)
+    return c
+
+
+def _random_cfgs(n=60):
+    rng = np.random.default_rng(0)
+    for _ in range(n):
+        hk = int(rng.choice([1, 2, 4, 8]))
+        w = int(rng.choice([0, 32, 1024, 2048]))
+        yield _cfg(n_layers=int(rng.integers(1, 17)), max_seqs=int(rng.integers(1, 9)),
+                   capacity=int(rng.integers(1, 300000)), n_kv_heads=hk, n_q_heads=hk * int(rng.integers(1, 9)),
+                   k_bits=int(rng.integers(2, 9)), v_bits=int(rng.integers(2, 9)), kvarn=int(rng.integers(0, 2)),
+                   tail_len=w, tail_slack=int(rng.choice([0, 32, 512])) if w else 0,
+                   tail_dtype=int(rng.integers(1, 3)))
+
+
+def test_cache_bytes_and_regions_match_oracle():
+    from quantized_decode_attention_append_amd import kvq
+    for c in _random_cfgs():
+        assert kvq.cache_bytes(c) == oracle.cache_bytes(c), c
+        lay = slab_layout(c)
+        for layer, seq in ((0, 0), (c["n_layers"] - 1, c["max_seqs"] - 1)):
+            base = (layer * c["max_seqs"] + seq) * lay["slab"]
+            for name in ("k_body", "v_body", "k_ring", "v_ring", "sigma"):
+                off, size = kvq.region(c, layer, seq, name)
+                assert (off, size) == (base + lay[name][0], lay[name][1]), (c, name)
+            assert kvq.region(c, layer, seq, "slab") == (base, lay["slab"])
+
+
+def test_kv_mib_table_through_the_library():
+    from quantized_decode_attention_append_amd import kvq
+    for n, t, mib in ((4, 0, 1152), (5, 1024, 1504), (6, 2048, 1824), (8, 1024, 2272)):
+        c = _cfg(n_layers=16, max_seqs=1, capacity=65536, n_q_heads=32, n_kv_heads=4, k_bits=n, v_bits=n,
+                 tail_len=t, tail_slack=512)
+        assert kvq.cache_bytes(c) == mib * 2 ** 20
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_layers=0), dict(max_seqs=0), dict(capacity=0), dict(n_q_heads=15), dict(n_q_heads=32),
+    dict(head_dim=100), dict(k_bits=1), dict(v_bits=9), dict(kvarn=2), dict(tail_len=-1),
+    dict(tail_len=64, tail_slack=31), dict(tail_len=64, tail_dtype=0), dict(tail_len=64, tail_dtype=3),
+])
+def test_validation_rejects(bad):
+    from quantized_decode_attention_append_amd import kvq
+    c = _cfg(**bad)
+    assert kvq.cache_bytes(c) == 0
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.config_validate(c)
+    assert e.value.status == kvq.KVQ_E_INVALID
+
+
+def test_validation_accepts_no_ring_with_any_dtype():
+    from quantized_decode_attention_append_amd import kvq
+    kvq.config_validate(_cfg(tail_len=0, tail_slack=7, tail_dtype=9))
+
+
+def test_region_rejects_out_of_range():
+    from quantized_decode_attention_append_amd import kvq
+    with pytest.raises(kvq.KvqError):
+        kvq.region(_cfg(), 2, 0, "k_body")
+    with pytest.raises(kvq.KvqError):
+        kvq.region(_cfg(), 0, 3, "k_body")

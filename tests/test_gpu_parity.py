@@ -1,0 +1,157 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Codes, scales, ring contents and KVarN scales must match byte for byte (whole slabs are compared, so
+the layout of every region is checked too); attention outputs must be within 2e-3 absolute of the
+oracle's fp64 result over the same dequantized values.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import Pair, TOL, max_err
+from workloads import small_tokens, small_query, channel_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg(**kw):
+    c = dict(n_layers=2, max_seqs=3, capacity=512, n_q_heads=16, n_kv_heads=2, head_dim=256, k_bits=6,
+             v_bits=5, kvarn=0, tail_len=0, tail_slack=0, tail_dtype=0)
+    c.update(kw)
+    return c
+
+
+def scales(seed, kind):
+    rng = np.random.default_rng(seed)
+    if kind == "loguniform":
+        return (10.0 ** rng.uniform(-1, 1, size=(2, 2, 256))).astype(np.float32)
+    if kind == "student":
+        return np.abs(rng.standard_t(3, size=(2, 2, 256))).astype(np.float32)
+    s = np.ones((2, 2, 256), dtype=np.float32)
+    s[:, 0, [3, 77, 130, 201]] = 20.0
+    return s
+
+
+@pytest.mark.parametrize("nk,nv", list(itertools.product(range(2, 9), range(2, 9))))
+def test_body_bytes_and_decode_no_tail(nk, nv):
+    p = Pair(cfg(k_bits=nk, v_bits=nv))
+    k, v = small_tokens(nk * 10 + nv, 300, 2, 256, scale=scales(nk, "outlier"))
+    p.append(1, [2], [37], k[:37], v[:37])
+    p.append(1, [2, 0], [64, 70], k[37:171], v[37:171])
+    p.append(1, [2], [1], k[171:172], v[171:172])
+    p.lengths_match(1, 2)
+    p.assert_slab_equal(1, 2)
+    p.assert_slab_equal(1, 0)
+    q = small_query(nk + nv, 2, 16, 256)
+    got, want = p.decode(1, [2, 0], q)
+    assert max_err(got, want) <= TOL
+
+
+@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("kvarn", [0, 1])
+def test_tail_ring_bytes_evict_and_decode(tail_dtype, kvarn):
+    c = cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=6, v_bits=5)
+    p = Pair(c)
+    k, v = small_tokens(40 + tail_dtype + 2 * kvarn, 400, 2, 256, scale=scales(5, "student"))
+    off = 0
+    q = small_query(3, 1, 16, 256)
+    # below the window, over the window, then decode-style steps, then a big chunk that overflows
+    for n, ev in ((40, False), (30, False), (1, False), (50, True), (1, True), (1, True), (1, True), (150, False),
+                  (3, True), (90, False)):
+        p.append(0, [1], [n], k[off:off + n], v[off:off + n])
+        off += n
+        if ev:
+            p.evict(0, [1])
+        p.lengths_match(0, 1)
+        p.assert_slab_equal(0, 1)
+        got, want = p.decode(0, [1], q)
+        assert max_err(got, want) <= TOL, (n, ev)
+
+
+def test_kvarn_calibrates_on_first_chunk_only():
+    c = cfg(kvarn=1, k_bits=4, v_bits=4)
+    p = Pair(c)
+    k, v = small_tokens(77, 200, 2, 256, scale=scales(7, "student"))
+    p.append(0, [0, 1], [50, 20], k[:70], v[:70])
+    p.append(0, [0], [130], k[70:200], v[70:200])
+    for s in (0, 1):
+        p.assert_slab_equal(0, s)
+    got, want = p.decode(0, [0, 1], small_query(9, 2, 16, 256))
+    assert max_err(got, want) <= TOL
+
+
+@pytest.mark.parametrize("length", [1, 2, 31, 32, 33, 95, 129])
+def test_decode_short_and_ragged(length):
+    p = Pair(cfg(k_bits=8, v_bits=8))
+    k, v = small_tokens(length, length, 2, 256)
+    p.append(0, [0], [length], k, v)
+    got, want = p.decode(0, [0], small_query(length, 1, 16, 256))
+    assert max_err(got, want) <= TOL
+
+
+@pytest.mark.parametrize("tail_dtype", [1, 2])
+def test_ring_only_equals_lossless_or_q8(tail_dtype):
+    # context below the window: a bf16 tail is lossless, an 8-bit ring behaves as q8_0 (pages' special cases)
+    p = Pair(cfg(tail_len=256, tail_slack=32, tail_dtype=tail_dtype))
+    k, v = small_tokens(11, 200, 2, 256, scale=scales(2, "loguniform"))
+    p.append(0, [0], [200], k, v)
+    p.evict(0, [0])
+    assert p.gpu.lengths(0, 0) == (200, 0)
+    got, want = p.decode(0, [0], small_query(5, 1, 16, 256))
+    assert max_err(got, want) <= TOL
+
+
+def test_mixed_batch_lengths_and_heads():
+    c = cfg(max_seqs=5, capacity=2048, tail_len=96, tail_slack=32, tail_dtype=1, k_bits=4, v_bits=4)
+    p = Pair(c)
+    lens = [1500, 7, 300, 96, 1]
+    k, v = small_tokens(99, sum(lens), 2, 256, scale=scales(3, "loguniform"))
+    p.append(0, [4, 0, 2, 1, 3], [lens[4], lens[0], lens[2], lens[1], lens[3]], k, v)
+    p.evict(0, [0, 1, 2, 3, 4])
+    for s in range(5):
+        p.lengths_match(0, s)
+        p.assert_slab_equal(0, s)
+    got, want = p.decode(0, [3, 1, 0, 2, 4], small_query(8, 5, 16, 256))
+    assert max_err(got, want) <= TOL
+
+
+def test_softmax_scale_and_peaked_scores():
+    p = Pair(cfg(k_bits=6, v_bits=5))
+    k, v = small_tokens(5, 400, 2, 256, scale=scales(4, "loguniform"))
+    p.append(0, [0], [400], k, v)
+    q = small_query(6, 1, 16, 256, std=3.0)
+    for sc in (0.0, 0.01, 0.5):
+        got, want = p.decode(0, [0], q, sc)
+        assert max_err(got, want) <= TOL, sc
+
+
+def test_gqa_group_sizes():
+    for hq in (2, 8, 16):
+        p = Pair(cfg(n_q_heads=hq, k_bits=5, v_bits=4))
+        k, v = small_tokens(hq, 100, 2, 256)
+        p.append(0, [0], [100], k, v)
+        got, want = p.decode(0, [0], small_query(hq, 1, hq, 256))
+        assert max_err(got, want) <= TOL, hq
+
+
+def test_errors_from_the_host():
+    from quantized_decode_attention_append_amd import kvq
+    p = Pair(cfg(capacity=64))
+    k, v = small_tokens(1, 65, 2, 256)
+    with pytest.raises(kvq.KvqError) as e:
+        p.gpu.decode_attn(0, [0], __import__("tests.gpu_util", fromlist=["dev"]).dev(small_query(0, 1, 16, 256)))
+    assert e.value.status == kvq.KVQ_E_STATE
+    p.append(0, [0], [64], k[:64], v[:64])
+    from tests.gpu_util import dev
+    with pytest.raises(kvq.KvqError) as e:
+        p.gpu.append(0, [0], [1], dev(k[64:]), dev(v[64:]))
+    assert e.value.status == kvq.KVQ_E_CAPACITY
+    with pytest.raises(kvq.KvqError) as e:
+        p.gpu.append(0, [0, 0], [0, 0], dev(k[:0]), dev(v[:0]))
+    assert e.value.status == kvq.KVQ_E_INVALID
+    import torch
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:
+        p.gpu.decode_attn(0, [0], dev(small_query(0, 1, 16, 256)), workspace=ws)
+    assert e.value.status == kvq.KVQ_E_SIZE
