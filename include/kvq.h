@@ -105,7 +105,7 @@ kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t seq, i
  * max_len positions (sparse: max_len = budget). */
 size_t kvq_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t max_len);
 
-/* Append n_new[i] tokens to sequence seq_ids[i] of `layer` (a1-a4).
+/* Append n_new[i] tokens to sequence seq_ids[i] of `layer`.
  * seq_ids, n_new: host int32[n_seqs] (distinct ids). k_bf16, v_bf16: device bf16 [sum n_new][Hkv][D],
  * sequences packed in call order. The first non-empty append of a (layer, seq) calibrates the KVarN
  * scales from its tokens (BeeLlama page, KVarN). With a tail ring the new tokens enter the ring; when
@@ -116,23 +116,26 @@ size_t kvq_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t max_l
 kvq_status kvq_append(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                       const int32_t* n_new, const void* k_bf16, const void* v_bf16, void* stream);
 
-/* Requantize ring rows older than the newest tail_len into the body (a4; Qwen3.8-27B page: blocks are
+/* Requantize ring rows older than the newest tail_len into the body (Qwen3.8-27B page: blocks are
  * requantized when the window boundary moves). After the call the ring holds exactly the newest
  * min(len, W) positions. No-op without a ring. seq_ids: host int32[n_seqs]. */
 kvq_status kvq_tail_evict(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                           void* stream);
 
-/* Dense decode attention (a5 + a6; offload page: each step reads the whole cache of a full-attention
+/* Dense decode attention (offload page: each step reads the whole cache of a full-attention
  * layer). For each sequence i: out[i][h][:] = softmax(scale * q[i][h] . K^[t]) over t in [0, len) of V^,
  * with K^, V^ the dequantized body rows (t < body_len) or ring rows. q_bf16: device bf16
  * [n_seqs][Hq][D]; out: device fp32 [n_seqs][Hq][D]; softmax_scale <= 0 means 1/sqrt(D); workspace:
- * device, at least kvq_workspace_bytes(cache, n_seqs, max len) bytes, 256-byte aligned.
+ * device, at least kvq_workspace_bytes(cache, n_seqs, max len) bytes, 256-byte aligned, no initial
+ * contents needed. Work-groups over (position split, KV head, sequence) write partial (max, sum, output)
+ * records to the workspace; a second kernel merges them with a log-sum-exp. Calls that may run
+ * concurrently must not share a workspace.
  * Errors: KVQ_E_STATE if a sequence is empty; KVQ_E_SIZE if the workspace is too small. */
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                            const void* q_bf16, float* out, float softmax_scale, void* workspace,
                            size_t ws_bytes, void* stream);
 
-/* Sparse decode attention over an indexer budget (a7; offload page, QSA: the layer reads only the
+/* Sparse decode attention over an indexer budget (offload page, QSA: the layer reads only the
  * main-KV rows at the positions the indexer chose, so the budget, not the context, bounds the bytes).
  * positions: device int32 [n_seqs][budget], one list per sequence shared by all KV heads; entries must
  * be distinct and in [0, len) (entries outside are skipped). 1 <= budget <= len of every sequence.

@@ -25,8 +25,7 @@ What it computes, and where the pages fix it (pages cited by title and passage):
                   positions (offload page, QSA paragraph).
 * ``sizes``     - algorithmic bytes read per decode call.
 
-Readings where the pages are silent are listed in the design doc; the functions say
-which one they take. The quantizer emulates fp32 arithmetic exactly (numpy
+Where the pages are silent the functions state the reading they take. The quantizer emulates fp32 arithmetic exactly (numpy
 float32 operations are IEEE round-to-nearest-even, with no contraction), and
 attention is evaluated in fp64.
 """

@@ -16,7 +16,7 @@
 // * P.V = MFMA with A = P * dv16 split into fp16 hi (rows 0-7) and lo (rows 8-15) parts, so the product
 //   with the integer codes is accumulated to ~22 bits in fp32 (the hi/lo rows are summed at the end);
 // * the bf16 tail uses bf16 MFMA directly on the stored values (hi/lo bf16 P).
-// A second small kernel merges the partials (log-sum-exp).
+// A second, fully parallel kernel merges the split partials (log-sum-exp).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -66,12 +66,12 @@ constexpr int pair_pre_shift(int w, int slot, int k) { return (pair_offset(w, sl
 // Pair k (elements 2k, 2k+1) of a w<8 piece held in `word` at slot `slot`: two fp16 magic values
 // 1024 + 2^q * v. Returns the packed halves and the scale exponent q.
 template <int W, int SLOT, int K>
-__device__ inline uint32_t extract_pair(uint32_t word) {
+__device__ inline uint32_t extract_pair(uint32_t word, uint32_t magic) {
   constexpr int q = pair_offset(W, SLOT, K) - pair_pre_shift(W, SLOT, K);
   constexpr uint32_t m = ((1u << W) - 1) << q;
   constexpr uint32_t mask = m | (m << 16);
   constexpr int s = pair_pre_shift(W, SLOT, K);
-  return ((word >> s) & mask) | kMagic;
+  return ((word >> s) & mask) | magic;      // one v_and_or_b32 (mask from an SGPR, magic from a VGPR)
 }
 template <int W, int SLOT, int K>
 constexpr int pair_q() { return pair_offset(W, SLOT, K) - pair_pre_shift(W, SLOT, K); }
@@ -84,7 +84,7 @@ struct PieceWords {
 // Decode one piece (8 codes) into exact fp16 signed values c = u - 2^(N-1). SLOTS are the piece's slot
 // index in each plane's word (0 for w >= 4).
 template <int N, int S1, int S2>
-__device__ inline half8 decode_piece(const PieceWords& pw) {
+__device__ inline half8 decode_piece(const PieceWords& pw, uint32_t magic) {
   constexpr int off = 1 << (N - 1);
   u32x4 r;
   if constexpr (N == 8) {
@@ -110,7 +110,7 @@ __device__ inline half8 decode_piece(const PieceWords& pw) {
     {                                                                                                 \
       constexpr int s0 = (w0 == 4) ? 0 : S1;                                                          \
       constexpr int q0 = pair_q<w0, s0, K>();                                                         \
-      const uint32_t h0 = extract_pair<w0, s0, K>(pw.w[0]);                                           \
+      const uint32_t h0 = extract_pair<w0, s0, K>(pw.w[0], magic);                                           \
       constexpr float f0 = 1.0f / (float)(1 << q0);                                                   \
       if constexpr (np == 1) {                                                                        \
         constexpr float c0 = -(1024.0f * f0 + (float)off);                                           \
@@ -120,7 +120,7 @@ __device__ inline half8 decode_piece(const PieceWords& pw) {
       } else if constexpr (np == 2) {                                                                 \
         constexpr int s1 = (w0 == 4) ? S1 : S2;                                                       \
         constexpr int q1 = pair_q<w1, s1, K>();                                                       \
-        const uint32_t h1 = extract_pair<w1, s1, K>(pw.w[1]);                                         \
+        const uint32_t h1 = extract_pair<w1, s1, K>(pw.w[1], magic);                                         \
         constexpr float f1 = (float)(1 << sh1) / (float)(1 << q1);                                    \
         constexpr float c1 = -(1024.0f * (f0 + f1) + (float)off);                                     \
         half2v acc = __builtin_elementwise_fma(as_h2(h1), half2v{(_Float16)f1, (_Float16)f1},          \
@@ -130,8 +130,8 @@ __device__ inline half8 decode_piece(const PieceWords& pw) {
       } else {                                                                                        \
         constexpr int q1 = pair_q<w1, S1, K>();                                                       \
         constexpr int q2 = pair_q<w2, S2, K>();                                                       \
-        const uint32_t h1 = extract_pair<w1, S1, K>(pw.w[1]);                                         \
-        const uint32_t h2 = extract_pair<w2, S2, K>(pw.w[2]);                                         \
+        const uint32_t h1 = extract_pair<w1, S1, K>(pw.w[1], magic);                                         \
+        const uint32_t h2 = extract_pair<w2, S2, K>(pw.w[2], magic);                                         \
         constexpr float f1 = (float)(1 << sh1) / (float)(1 << q1);                                    \
         constexpr float f2 = (float)(1 << sh2) / (float)(1 << q2);                                    \
         constexpr float c12 = -(1024.0f * (f0 + f1) + (float)off);                                    \
@@ -155,13 +155,14 @@ __device__ inline half8 decode_piece(const PieceWords& pw) {
 // Decode piece index `i` (block b for K, n-tile n for V) given the per-plane runs of words.
 // run0 holds plane 0's words, run1 plane 1's, run2 plane 2's (indexed in 32-bit words).
 template <int N, int I>
-__device__ inline half8 decode_run_piece(const uint32_t* run0, const uint32_t* run1, const uint32_t* run2) {
+__device__ inline half8 decode_run_piece(const uint32_t* run0, const uint32_t* run1, const uint32_t* run2,
+                                         uint32_t magic) {
   PieceWords pw;
   if constexpr (N == 8) {
     pw.w[0] = run0[2 * I];
     pw.w[1] = run0[2 * I + 1];
     pw.w[2] = 0;
-    return decode_piece<8, 0, 0>(pw);
+    return decode_piece<8, 0, 0>(pw, magic);
   } else {
     constexpr int w0 = Planes<N>::w[0];
     constexpr int w1 = Planes<N>::w[1];
@@ -173,13 +174,13 @@ __device__ inline half8 decode_run_piece(const uint32_t* run0, const uint32_t* r
       if constexpr (Planes<N>::n >= 3) pw.w[2] = run2[I / (4 / w2)];
       constexpr int s1 = (Planes<N>::n >= 2) ? I % (4 / (w1 ? w1 : 4)) : 0;
       constexpr int s2 = (Planes<N>::n >= 3) ? I % (4 / (w2 ? w2 : 4)) : 0;
-      return decode_piece<N, s1, s2>(pw);
+      return decode_piece<N, s1, s2>(pw, magic);
     } else {
       // w0 == 2 (N = 2 or 3): plane 0 slot = I % 2, plane 1 (w = 1) slot = I % 4
       if constexpr (Planes<N>::n >= 2) pw.w[1] = run1[I / 4];
       constexpr int s0 = I % 2;
       constexpr int s1 = (Planes<N>::n >= 2) ? I % 4 : 0;
-      return decode_piece<N, s0, s1>(pw);
+      return decode_piece<N, s0, s1>(pw, magic);
     }
   }
 }
@@ -221,133 +222,201 @@ struct WaveState {
   float l;         // running sum of p over this lane's positions
 };
 
-// One 32-position tile of a qN_0 store (body, or the q8_0 ring).
-//   krow(pos) gives the K row of a position; vt is the V tile; [lo, hi) the valid positions.
+// Raw bytes of one 32-position tile of a qN_0 store, as this lane loads them. The tile's fp16 scales
+// (32 K rows x 16 bytes, 32 V positions x 16 bytes) are loaded one 16-byte chunk per lane and staged
+// through LDS, because each lane needs the scales of 4 K rows and 8 V positions.
 template <int NK, int NV>
-__device__ inline void tile_quant(WaveState& st, const half8* qb, float qmul, const uint8_t* kbase, int row_k,
-                                  bool ring, int R, const uint8_t* vt, int tile, int lo, int hi, bool lo_lane) {
-  constexpr int D = 256, NB = 8, NT = 16;
+struct TileRaw {
+  static constexpr int NB = 8, NT = 16;
+  static constexpr int w0k = Planes<NK>::w[0], w1k = Planes<NK>::w[1], w2k = Planes<NK>::w[2];
+  static constexpr int w0v = Planes<NV>::w[0], w1v = Planes<NV>::w[1], w2v = Planes<NV>::w[2];
+  static constexpr int nk0 = NB * w0k / 4, nk1 = w1k ? NB * w1k / 4 : 1, nk2 = w2k ? NB * w2k / 4 : 1;
+  static constexpr int nv0 = NT * w0v / 4, nv1 = w1v ? NT * w1v / 4 : 1, nv2 = w2v ? NT * w2v / 4 : 1;
+  uint32_t k0[2][nk0], k1[2][nk1], k2[2][nk2];   // K pieces of this lane's row in each 16-row subtile
+  uint32_t v0[nv0], v1[nv1], v2[nv2];             // V pieces of this lane (16 n-tiles)
+  u32x4 sc;                                       // lanes 0-31: K scales of row `lane`; 32-63: V scales of position lane-32
+};
+
+template <int NK, int NV>
+__device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kbase, int row_k, bool ring, int R,
+                                 const uint8_t* vt, int tile) {
+  using T = TileRaw<NK, NV>;
+  constexpr int NB = 8, NT = 16, D = 256;
   const int lane = threadIdx.x & 63;
   const int m16 = lane & 15;
   const int g = lane >> 4;
-  constexpr int w0k = Planes<NK>::w[0], w1k = Planes<NK>::w[1], w2k = Planes<NK>::w[2];
-  constexpr int w0v = Planes<NV>::w[0], w1v = Planes<NV>::w[1], w2v = Planes<NV>::w[2];
-
-  // ---- scores for the two 16-position subtiles
-  float sc[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int pos = tile * kTile + 16 * s + m16;
     const uint8_t* row = kbase + (size_t)(ring ? pos % R : pos) * row_k;
-    uint32_t k0[NB * w0k / 4 + 1], k1[(w1k ? NB * w1k / 4 : 1) + 1], k2[(w2k ? NB * w2k / 4 : 1) + 1];
-    load_words<0>(row + g * NB * w0k, k0, NB * w0k / 4);
-    if constexpr (w1k) load_words<0>(row + 4 * NB * w0k + g * NB * w1k, k1, NB * w1k / 4);
-    if constexpr (w2k) load_words<0>(row + 4 * NB * (w0k + w1k) + g * NB * w2k, k2, NB * w2k / 4);
-    // scales of rows 4g + r
-    u32x4 dk[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pr = tile * kTile + 16 * s + 4 * g + r;
-      const uint8_t* rr = kbase + (size_t)(ring ? pr % R : pr) * row_k;
-      dk[r] = *(const u32x4*)(rr + NB * 4 * NK);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[s][r] = 0.0f;
-#define KVQ_QK(B)                                                                                 \
-    {                                                                                             \
-      half8 a = decode_run_piece<NK, B>(k0, k1, k2);                                              \
-      floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[B], floatx4{0, 0, 0, 0}, 0, 0, 0);  \
-      _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                             \
-        const uint32_t wd = dk[r][B >> 1];                                                        \
-        const float d = h2f((uint16_t)((B & 1) ? (wd >> 16) : (wd & 0xFFFF)));                    \
-        sc[s][r] = fmaf(c[r], d, sc[s][r]);                                                       \
-      }                                                                                           \
-    }
-    KVQ_QK(0) KVQ_QK(1) KVQ_QK(2) KVQ_QK(3) KVQ_QK(4) KVQ_QK(5) KVQ_QK(6) KVQ_QK(7)
-#undef KVQ_QK
+    load_words<0>(row + g * NB * T::w0k, t.k0[s], T::nk0);
+    if constexpr (T::w1k > 0) load_words<0>(row + 4 * NB * T::w0k + g * NB * T::w1k, t.k1[s], T::nk1);
+    if constexpr (T::w2k > 0) load_words<0>(row + 4 * NB * (T::w0k + T::w1k) + g * NB * T::w2k, t.k2[s], T::nk2);
   }
+#pragma unroll
+  for (int c = 0; c < NT * T::w0v / 16; ++c) {
+    u32x4 x = *(const u32x4*)(vt + c * 1024 + lane * 16);
+    t.v0[4 * c] = x[0]; t.v0[4 * c + 1] = x[1]; t.v0[4 * c + 2] = x[2]; t.v0[4 * c + 3] = x[3];
+  }
+  if constexpr (T::w1v > 0) {
+    const uint8_t* p1 = vt + 64 * NT * T::w0v;
+#pragma unroll
+    for (int c = 0; c < NT * T::w1v / 16; ++c) {
+      u32x4 x = *(const u32x4*)(p1 + c * 1024 + lane * 16);
+      t.v1[4 * c] = x[0]; t.v1[4 * c + 1] = x[1]; t.v1[4 * c + 2] = x[2]; t.v1[4 * c + 3] = x[3];
+    }
+  }
+  if constexpr (T::w2v > 0) {
+    u32x4 x = *(const u32x4*)(vt + 64 * NT * (T::w0v + T::w1v) + lane * 16);
+    t.v2[0] = x[0]; t.v2[1] = x[1]; t.v2[2] = x[2]; t.v2[3] = x[3];
+  }
+  if (lane < 32) {
+    const int pr = tile * kTile + lane;
+    t.sc = *(const u32x4*)(kbase + (size_t)(ring ? pr % R : pr) * row_k + NB * 4 * NK);
+  } else {
+    t.sc = *(const u32x4*)(vt + 4 * D * NV + (lane - 32) * NB * 2);
+  }
+}
 
-  // ---- V codes and scales of this lane (positions T(g, i))
-  uint32_t v0[NT * w0v / 4], v1[(w1v ? NT * w1v / 4 : 1)], v2[(w2v ? NT * w2v / 4 : 1)];
-  {
-    const int run0 = NT * w0v;        // bytes per lane
-#pragma unroll
-    for (int c = 0; c < run0 / 16; ++c) {
-      u32x4 x = *(const u32x4*)(vt + c * 1024 + lane * 16);
-      v0[4 * c] = x[0]; v0[4 * c + 1] = x[1]; v0[4 * c + 2] = x[2]; v0[4 * c + 3] = x[3];
-    }
-    if constexpr (w1v) {
-      const uint8_t* p1 = vt + 64 * NT * w0v;
-#pragma unroll
-      for (int c = 0; c < NT * w1v / 16; ++c) {
-        u32x4 x = *(const u32x4*)(p1 + c * 1024 + lane * 16);
-        v1[4 * c] = x[0]; v1[4 * c + 1] = x[1]; v1[4 * c + 2] = x[2]; v1[4 * c + 3] = x[3];
-      }
-    }
-    if constexpr (w2v) {
-      const uint8_t* p2 = vt + 64 * NT * (w0v + w1v);
-      u32x4 x = *(const u32x4*)(p2 + lane * 16);
-      v2[0] = x[0]; v2[1] = x[1]; v2[2] = x[2]; v2[3] = x[3];
-    }
-  }
-  u32x4 dv[8];
-  {
-    const uint8_t* sp = vt + 4 * D * NV;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dv[i] = *(const u32x4*)(sp + tile_pos(g, i) * NB * 2);
-  }
+#define KVQ_SB __builtin_amdgcn_sched_barrier(0);
 
-  // ---- softmax update
-  float x[8];
+__device__ inline float lo_h(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ inline float hi_h(uint32_t w) { return (float)as_h2(w)[1]; }
+
+// Online-softmax update for this lane's 8 scores x[] (exp2 domain, -inf for masked positions).
+// Returns p[] and rescales the accumulators only when some lane's running max moved.
+__device__ inline void softmax_update(WaveState& st, const float* x, float* p) {
   float tmax = kNegBig;
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float full = sc[s][r] + dpp_ror8(sc[s][r]);
-      const int pos = tile * kTile + 16 * s + 4 * g + r;
-      const float v = (pos >= lo && pos < hi) ? full * qmul : -INFINITY;
-      x[4 * s + r] = v;
-      tmax = fmaxf(tmax, v);
-    }
+  for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
   tmax = wave_max_16_32(tmax);
   const float m_new = fmaxf(st.m, tmax);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
-  float p[8];
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
     psum += p[i];
   }
-  st.l = st.l * alpha + psum;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    st.l *= alpha;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) st.o[n] *= alpha;
+    for (int n = 0; n < 16; ++n) st.o[n] *= alpha;
+  }
+  st.l += psum;
+}
 
-  // ---- P.V: per block b, A = P * dv16 (hi rows / lo rows), B = V codes of n-tiles 2b, 2b+1
-  const float kf = lo_lane ? 1.0f : 0.0f;
+// One 32-position tile of a qN_0 store (body, or the q8_0 ring). [lo, hi) are the valid positions.
+// lane_mask is 0 on the hi-part lanes (rows 0-7 of the P operand) and ~0 on the lo-part lanes.
+// s_sc: this wave's LDS copy of the tile's scales: K as [block][row], then V as [block][position].
+template <int NK, int NV>
+__device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, const u32x4* s_sc, const half8* qb,
+                                    float qmul, int tile, int lo, int hi, uint32_t lane_mask, uint32_t magic) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  float sc[2][4];
+  // K scales, transposed in LDS to [block][row]: the 4 rows 4g..4g+3 of a subtile are 8 contiguous bytes
+  const uint16_t* s_dk = (const uint16_t*)s_sc;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[s][r] = 0.0f;
+    // block B's MFMA is issued before block B+1 is decoded, and its result consumed after that, so the
+    // MFMA latency is covered by the next block's decode
+    half8 a_cur = decode_run_piece<NK, 0>(t.k0[s], t.k1[s], t.k2[s], magic);
+#define KVQ_QK(B)                                                                                 \
+    {                                                                                             \
+      const half8 qv = qb[B * 64 + lane];                                                         \
+      floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, qv, floatx4{0, 0, 0, 0}, 0, 0, 0); \
+      if constexpr (B < 7) a_cur = decode_run_piece<NK, (B < 7 ? B + 1 : 0)>(t.k0[s], t.k1[s], t.k2[s], magic); \
+      const u32x2 dk = *(const u32x2*)(s_dk + B * 32 + 16 * s + 4 * g);                           \
+      sc[s][0] = fmaf(c[0], lo_h(dk[0]), sc[s][0]);                                               \
+      sc[s][1] = fmaf(c[1], hi_h(dk[0]), sc[s][1]);                                               \
+      sc[s][2] = fmaf(c[2], lo_h(dk[1]), sc[s][2]);                                               \
+      sc[s][3] = fmaf(c[3], hi_h(dk[1]), sc[s][3]);                                               \
+    }
+    // one block at a time (sched barriers): bounds the live decoded operands
+    KVQ_QK(0) KVQ_SB KVQ_QK(1) KVQ_SB KVQ_QK(2) KVQ_SB KVQ_QK(3) KVQ_SB
+    KVQ_QK(4) KVQ_SB KVQ_QK(5) KVQ_SB KVQ_QK(6) KVQ_SB KVQ_QK(7) KVQ_SB
+#undef KVQ_QK
+  }
+  float x[8], p[8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float full = sc[s][r] + dpp_ror8(sc[s][r]);
+      const int pos = tile * kTile + 16 * s + 4 * g + r;
+      x[4 * s + r] = (pos >= lo && pos < hi) ? full * qmul : -INFINITY;
+    }
+  softmax_update(st, x, p);
+  // V scales, transposed in LDS to [block][position]: this lane's positions T(g, 0..3) and T(g, 4..7)
+  // are two runs of 4 fp16 values per block.
+  const uint16_t* s_dv = (const uint16_t*)(s_sc + 32);
+  // P.V: for block b, A = P * dv16 as fp16 hi (lane_mask = 0) or lo (lane_mask = ~0) parts
 #define KVQ_PV(B)                                                                                   \
   {                                                                                                 \
+    const u32x2 d0 = *(const u32x2*)(s_dv + B * 32 + 4 * g);                                         \
+    const u32x2 d1 = *(const u32x2*)(s_dv + B * 32 + 16 + 4 * g);                                    \
+    const uint32_t dw[4] = {d0[0], d0[1], d1[0], d1[1]};                                             \
     half8 a;                                                                                        \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                 \
-      const uint32_t wd = dv[i][B >> 1];                                                            \
-      const float d = h2f((uint16_t)((B & 1) ? (wd >> 16) : (wd & 0xFFFF)));                        \
-      const float xv = p[i] * d;                                                                    \
-      const _Float16 h = (_Float16)xv;                                                              \
-      const float y = fmaf(-kf, (float)h, xv);                                                      \
-      a[i] = (_Float16)y;                                                                           \
+      const uint32_t wd = dw[i >> 1];                                                               \
+      const uint32_t wk = wd & lane_mask;                                                           \
+      const float d = (i & 1) ? hi_h(wd) : lo_h(wd);                                                \
+      const float dm = (i & 1) ? hi_h(wk) : lo_h(wk);                                               \
+      const _Float16 h = (_Float16)(p[i] * dm);                                                     \
+      a[i] = (_Float16)fmaf(p[i], d, -(float)h);                                                    \
     }                                                                                               \
-    half8 b0 = decode_run_piece<NV, 2 * B>(v0, v1, v2);                                             \
+    half8 b0 = decode_run_piece<NV, 2 * B>(t.v0, t.v1, t.v2, magic);                                \
     st.o[2 * B] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, st.o[2 * B], 0, 0, 0);              \
-    half8 b1 = decode_run_piece<NV, 2 * B + 1>(v0, v1, v2);                                         \
+    half8 b1 = decode_run_piece<NV, 2 * B + 1>(t.v0, t.v1, t.v2, magic);                            \
     st.o[2 * B + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b1, st.o[2 * B + 1], 0, 0, 0);      \
   }
-  KVQ_PV(0) KVQ_PV(1) KVQ_PV(2) KVQ_PV(3) KVQ_PV(4) KVQ_PV(5) KVQ_PV(6) KVQ_PV(7)
+  KVQ_PV(0) KVQ_SB KVQ_PV(1) KVQ_SB KVQ_PV(2) KVQ_SB KVQ_PV(3) KVQ_SB
+  KVQ_PV(4) KVQ_SB KVQ_PV(5) KVQ_SB KVQ_PV(6) KVQ_SB KVQ_PV(7) KVQ_SB
 #undef KVQ_PV
 }
 
-// One 32-position tile of the bf16 tail ring.
+__device__ inline const uint8_t* tile_ptr(const uint8_t* vbase, int tile_v, bool ring, int R, int t) {
+  return vbase + (size_t)(ring ? ((t * kTile) % R) / kTile : t) * tile_v;
+}
+
+// Loop over this wave's contiguous tiles [t, tile_end) of a qN_0 store. On entry `cur` holds tile t and
+// `nxt` tile t+1 (both requested before the query set-up); during the compute of tile i the loads of tile
+// i+1 are in flight. s_buf: this wave's two 1-KiB LDS buffers for tile scales.
+template <int NK, int NV>
+__device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, TileRaw<NK, NV>& nxt, const half8* qb,
+                                       float qmul, const uint8_t* kbase, int row_k, bool ring, int R,
+                                       const uint8_t* vbase, int tile_v, int t, int tile_end, int lo, int hi,
+                                       uint32_t lane_mask, u32x4* s_buf) {
+  const int lane = threadIdx.x & 63;
+  if (t >= tile_end) return;
+  uint32_t magic = kMagic;
+  asm volatile("" : "+v"(magic));   // keep the fp16 magic in a VGPR (the mask takes the SGPR operand)
+  // Stage one tile's scales into a wave-private LDS buffer (no work-group barrier needed).
+  auto stage = [&](const TileRaw<NK, NV>& tr, u32x4* sb) {
+    // lanes 0-31 hold the 8 block scales of K row `lane`, lanes 32-63 those of V position lane-32:
+    // both are stored transposed, [block][row] at sb and [block][position] at sb + 32
+    uint16_t* dst = (uint16_t*)(sb + (lane < 32 ? 0 : 32));
+    const int tp = lane & 31;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) dst[b * 32 + tp] = (uint16_t)(tr.sc[b >> 1] >> (16 * (b & 1)));
+  };
+  int buf = 0;
+  for (;;) {
+    u32x4* sb = s_buf + 64 * buf;
+    stage(cur, sb);
+    if (t + 1 < tile_end) load_tile<NK, NV>(nxt, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, t + 1), t + 1);
+    compute_tile<NK, NV>(st, cur, sb, qb, qmul, t, lo, hi, lane_mask, magic);
+    if (++t >= tile_end) break;
+    cur = nxt;
+    buf ^= 1;
+  }
+}
+
+// One 32-position tile of the bf16 tail ring. qb: the bf16 query B operands in LDS ([block][lane]).
 __device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, const uint8_t* kring, int R,
                                  const uint8_t* vt, int tile, int lo, int hi, bool lo_lane) {
   constexpr int D = 256, NT = 16;
@@ -359,92 +428,166 @@ __device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, co
   for (int s = 0; s < 2; ++s) {
     const int pos = tile * kTile + 16 * s + m16;
     const uint8_t* row = kring + (size_t)(pos % R) * (2 * D);
+    bf16x8 kk[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) kk[b] = *(const bf16x8*)(row + (32 * b + 8 * g) * 2);
     floatx4 c = {0, 0, 0, 0};
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      bf16x8 a = *(const bf16x8*)(row + (32 * b + 8 * g) * 2);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[b], c, 0, 0, 0);
-    }
+    for (int b = 0; b < 8; ++b) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[b], qb[b * 64 + lane], c, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[s][r] = c[r];
   }
-  bf16x8 vv[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) vv[n] = *(const bf16x8*)(vt + n * 1024 + lane * 16);
-
-  float x[8];
-  float tmax = kNegBig;
+  float x[8], p[8];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pos = tile * kTile + 16 * s + 4 * g + r;
-      const float v = (pos >= lo && pos < hi) ? sc[s][r] * qmul : -INFINITY;
-      x[4 * s + r] = v;
-      tmax = fmaxf(tmax, v);
+      x[4 * s + r] = (pos >= lo && pos < hi) ? sc[s][r] * qmul : -INFINITY;
     }
-  tmax = wave_max_16_32(tmax);
-  const float m_new = fmaxf(st.m, tmax);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  st.m = m_new;
-  float psum = 0.0f;
+  softmax_update(st, x, p);
   bf16x8 a;
   const float kf = lo_lane ? 1.0f : 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float p = __builtin_amdgcn_exp2f(x[i] - m_new);
-    psum += p;
-    const __bf16 h = (__bf16)p;
-    const float y = fmaf(-kf, (float)h, p);
-    a[i] = (__bf16)y;
+    const __bf16 h = (__bf16)p[i];
+    a[i] = (__bf16)fmaf(-kf, (float)h, p[i]);
   }
-  st.l = st.l * alpha + psum;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    st.o[n] *= alpha;
-    st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vv[n], st.o[n], 0, 0, 0);
+  for (int n0 = 0; n0 < NT; n0 += 4) {
+    bf16x8 vv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vv[k] = *(const bf16x8*)(vt + (n0 + k) * 1024 + lane * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      st.o[n0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vv[k], st.o[n0 + k], 0, 0, 0);
   }
 }
 
 // ------------------------------------------------------------------ the split kernel
 
-template <int NK, int NV>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  constexpr int D = 256, NB = 8, NT = 16;
-  __shared__ float s_o[4][kPartialHeads][D];
-  __shared__ float s_ml[4][2][kPartialHeads];
+struct QArgs {
+  const uint16_t* qrow;   // this lane's query head (bf16)
+  const uint16_t* sig;    // KVarN sigma of this KV head ([K,V][D] fp16)
+  bool use_sigma, head_ok, lo_lane;
+  float scale;
+};
 
-  const int split = blockIdx.x;
-  const int head = blockIdx.y;
-  const int si = blockIdx.z;
+// A qN_0 store path (body, or q8_0 ring): issue the first tile's loads, build the exponent-shifted query
+// operands (times KVarN sigma) in LDS, then run the tile loop. All waves of the work-group call this.
+template <int NK, int NV>
+__device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, const uint8_t* kbase, int row_k,
+                                  bool ring, int R, const uint8_t* vbase, int tile_v, int wb, int we, int lo, int hi,
+                                  uint32_t lane_mask, u32x4* sbuf) {
+  constexpr int NB = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int gq = lane >> 4;
+  TileRaw<NK, NV> cur, nxt;
+  // the first two tiles' loads go out before the query set-up
+  if (wb < we) load_tile<NK, NV>(cur, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, wb), wb);
+  // exponent-shifted query, split into fp16 hi (cols 0-7) and lo (cols 8-15); two passes over the
+  // (cached) query keep the live registers low while the first tiles' loads are in flight
+  auto q_block = [&](int b, float* x) {
+    const u32x4 raw = *(const u32x4*)(qa.qrow + 32 * b + 8 * gq);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(raw[k] << 16);
+      x[2 * k + 1] = __uint_as_float(raw[k] & 0xFFFF0000u);
+    }
+    if (qa.use_sigma) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] *= h2f(qa.sig[32 * b + 8 * gq + i]);   // exact (8 + 11 bits)
+    }
+  };
+  float amax = 0.0f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float x[8];
+    q_block(b, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  }
+  amax = wave_max_16_32(amax);
+  const int e = amax > 0.0f ? ilogbf(amax) - 14 : 0;
+  if (wave == 0) {   // the B operand of every block goes to LDS (read back per block and subtile)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float x[8];
+      q_block(b, x);
+      half8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xs = ldexpf(x[i], -e);
+        const _Float16 h = (_Float16)xs;
+        const _Float16 l = (_Float16)(xs - (float)h);
+        v[i] = qa.head_ok ? (qa.lo_lane ? l : h) : (_Float16)0.0f;
+      }
+      s_qb[b * 64 + lane] = v;
+    }
+  }
+  __syncthreads();
+  const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e);
+  run_quant_tiles<NK, NV>(st, cur, nxt, s_qb, qmul, kbase, row_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
+                          sbuf);
+}
+
+// One work-group of 8 waves (two per SIMD) per split; the host sizes the splits so that there is about one
+// work-group per CU. Each wave takes a contiguous share of the split's tiles (extra tiles go to waves 0-3,
+// which sit on different SIMDs); the waves' partial results are merged in LDS into one partial record.
+template <int NK, int NV>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+  constexpr int D = 256, NB = 8, NT = 16, NW = 8;
+  __shared__ float s_o[NW][kPartialHeads][D];
+  __shared__ float s_ml[NW][2][kPartialHeads];
+  __shared__ u32x4 s_scales[NW][2][64];   // per wave, double-buffered tile scales
+  __shared__ half8 s_qb[8 * 64];           // QK B operands (per block, per lane)
+
+  // flattened grid: (sequence, KV head, split)
+  const Geometry& g = a.g;
+  int rem = blockIdx.x;
+  int si = 0;
+  for (;;) {
+    const int n = g.n_kv_heads * (a.seqs[si].n_body_splits + a.seqs[si].n_ring_splits);
+    if (rem < n || si + 1 >= a.n_seqs) break;
+    rem -= n;
+    ++si;
+  }
   const DecodeSeq S = a.seqs[si];
   const int n_splits = S.n_body_splits + S.n_ring_splits;
-  if (split >= n_splits) return;
-  const Geometry& g = a.g;
+  const int head = rem / n_splits;
+  const int split = rem % n_splits;
   const bool is_ring = split >= S.n_body_splits;
   const int tail = g.tail_dtype;
   const int R = g.ring_slots;
   const uint8_t* slab = g.arena + S.slab;
 
-  int tile_begin, tile_end, lo, hi;
+  int seg_begin, seg_tiles, nsp, sp, lo, hi;
   if (!is_ring) {
-    const int body_tiles = (S.body_len + kTile - 1) / kTile;
-    tile_begin = split * a.tiles_per_split;
-    tile_end = min(body_tiles, tile_begin + a.tiles_per_split);
+    seg_begin = 0;
+    seg_tiles = (S.body_len + kTile - 1) / kTile;
+    nsp = S.n_body_splits;
+    sp = split;
     lo = 0;
     hi = S.body_len;
   } else {
-    const int rs = split - S.n_body_splits;
-    const int ring_end = (S.len + kTile - 1) / kTile;
-    tile_begin = S.ring_tile0 + rs * a.tiles_per_split;
-    tile_end = min(ring_end, tile_begin + a.tiles_per_split);
+    seg_begin = S.ring_tile0;
+    seg_tiles = (S.len + kTile - 1) / kTile - S.ring_tile0;
+    nsp = S.n_ring_splits;
+    sp = split - S.n_body_splits;
     lo = S.body_len;
     hi = S.len;
   }
-
+  // this split's tiles, then this wave's share
+  const int tb = seg_begin + (int)((long)sp * seg_tiles / nsp);
+  const int te = seg_begin + (int)((long)(sp + 1) * seg_tiles / nsp);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int nt = te - tb, qw = nt / NW, rw = nt % NW;
+  const int wb = tb + wave * qw + min(wave, rw);
+  const int we = wb + qw + (wave < rw ? 1 : 0);
+
   const int m16 = lane & 15;
   const int gq = lane >> 4;
   const int hh = m16 & 7;
@@ -463,65 +606,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   // channels of this lane's B operand: 32b + 8*gq + i
   if (is_ring && tail == 1) {
-    bf16x8 qb[NB];
+    bf16x8* qb = (bf16x8*)s_qb;
+    if (wave == 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // columns 8-15 repeat heads 0-7 so the lo-part lanes see the same scores
-      bf16x8 v = *(const bf16x8*)(qrow + 32 * b + 8 * gq);
-      if (!head_ok) v = bf16x8{};
-      qb[b] = v;
+      for (int b = 0; b < NB; ++b) {
+        // columns 8-15 repeat heads 0-7 so the lo-part lanes see the same scores
+        bf16x8 v = *(const bf16x8*)(qrow + 32 * b + 8 * gq);
+        if (!head_ok) v = bf16x8{};
+        qb[b * 64 + lane] = v;
+      }
     }
+    __syncthreads();
     const float qmul = a.scale * kLog2e;
     const uint8_t* kring = slab + g.k_ring + (size_t)head * R * (2 * D);
-    for (int t = tile_begin + wave; t < tile_end; t += 4) {
+    for (int t = wb; t < we; ++t) {
       const uint8_t* vt = slab + g.v_ring + ((size_t)head * (R / kTile) + ((t * kTile) % R) / kTile) * g.ring_tile_v;
       tile_bf16(st, qb, qmul, kring, R, vt, t, lo, hi, lo_lane);
     }
   } else {
-    // exponent-shifted query (times KVarN sigma), split into fp16 hi (cols 0-7) and lo (cols 8-15)
-    float xq[NB][8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      u32x4 raw = *(const u32x4*)(qrow + 32 * b + 8 * gq);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        xq[b][2 * k] = __uint_as_float(raw[k] << 16);
-        xq[b][2 * k + 1] = __uint_as_float(raw[k] & 0xFFFF0000u);
-      }
-      if (use_sigma) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xq[b][i] *= h2f(sig[32 * b + 8 * gq + i]);   // exact (8 + 11 bits)
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(xq[b][i]));
-    }
-    amax = wave_max_16_32(amax);
-    const int e = amax > 0.0f ? ilogbf(amax) - 14 : 0;
-    half8 qb[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xs = ldexpf(xq[b][i], -e);
-        const _Float16 h = (_Float16)xs;
-        const _Float16 l = (_Float16)(xs - (float)h);
-        qb[b][i] = head_ok ? (lo_lane ? l : h) : (_Float16)0.0f;
-      }
-    }
-    const float qmul = a.scale * kLog2e * ldexpf(1.0f, e);
+    const uint32_t lane_mask = lo_lane ? 0xFFFFFFFFu : 0u;
+    const QArgs qa{qrow, sig, use_sigma, head_ok, lo_lane, a.scale};
+    u32x4* sbuf = &s_scales[wave][0][0];
     if (!is_ring) {
       const uint8_t* kbase = slab + g.k_body + (size_t)head * g.cap32 * g.row_k;
-      for (int t = tile_begin + wave; t < tile_end; t += 4) {
-        const uint8_t* vt = slab + g.v_body + ((size_t)head * (g.cap32 / kTile) + t) * g.tile_v;
-        tile_quant<NK, NV>(st, qb, qmul, kbase, g.row_k, false, 1, vt, t, lo, hi, lo_lane);
-      }
+      const uint8_t* vbase = slab + g.v_body + (size_t)head * (g.cap32 / kTile) * g.tile_v;
+      quant_path<NK, NV>(st, qa, s_qb, kbase, g.row_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask, sbuf);
     } else {
       const uint8_t* kbase = slab + g.k_ring + (size_t)head * R * g.ring_row_k;
-      for (int t = tile_begin + wave; t < tile_end; t += 4) {
-        const uint8_t* vt = slab + g.v_ring + ((size_t)head * (R / kTile) + ((t * kTile) % R) / kTile) * g.ring_tile_v;
-        tile_quant<8, 8>(st, qb, qmul, kbase, g.ring_row_k, true, R, vt, t, lo, hi, lo_lane);
-      }
+      const uint8_t* vbase = slab + g.v_ring + (size_t)head * (R / kTile) * g.ring_tile_v;
+      quant_path<8, 8>(st, qa, s_qb, kbase, g.ring_row_k, true, R, vbase, g.ring_tile_v, wb, we, lo, hi, lane_mask,
+                       sbuf);
     }
   }
 
@@ -545,55 +659,86 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- merge the 4 waves and write the partial of this split
+  // ---- merge the waves and write the partial of this split (512 threads: 2 heads x 256 channels per pass)
   float* part = a.partials + (((size_t)si * g.n_kv_heads + head) * a.max_splits + split) * (kPartialHeads * (D + 2));
-  const float vs = (use_sigma) ? h2f(sig[D + tid]) : 1.0f;
-  for (int h = 0; h < kPartialHeads; ++h) {
+  const int c = tid & 255;
+  const float vs = use_sigma ? h2f(sig[D + c]) : 1.0f;
+  for (int h = tid >> 8; h < kPartialHeads; h += 2) {
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);
     float L = 0.0f, O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(s_ml[w][0][h] - M);
       L += s_ml[w][1][h] * f;
-      O += s_o[w][h][tid] * f;
+      O += s_o[w][h][c] * f;
     }
-    part[2 * kPartialHeads + h * D + tid] = O * vs;
-    if (tid == 0) {
+    part[2 * kPartialHeads + h * D + c] = O * vs;
+    if (c == 0) {
       part[h] = M;
       part[kPartialHeads + h] = L;
     }
   }
 }
 
-// ------------------------------------------------------------------ combine
+// ------------------------------------------------------------------ merge of the split partials
 
+// One work-group per (sequence, KV head, query head, 16-channel chunk): 16 groups of 16 threads each sum
+// a strided share of the splits for the 16 channels, then the groups are added. Log-sum-exp:
+// out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s with M = max_s m_s (exp2 domain).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int D = 256;
+  constexpr size_t rec = kPartialHeads * (D + 2);
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_acc[16][17];
+  __shared__ float s_red[2][4];
   const int si = blockIdx.x / a.n_kv_heads;
   const int head = blockIdx.x % a.n_kv_heads;
-  const int D = a.head_dim;
+  const int h = blockIdx.y;
+  const int c0 = blockIdx.z * 16;
+  const int tid = threadIdx.x;
   const int ns = a.n_splits[si];
-  const float* base = a.partials + ((size_t)si * a.n_kv_heads + head) * a.max_splits * (kPartialHeads * (D + 2));
-  const size_t rec = kPartialHeads * (D + 2);
-  for (int h = 0; h < a.group; ++h) {
-    float M = kNegBig;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * rec + h]);
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-      float L = 0.0f, O = 0.0f;
-      for (int s = 0; s < ns; ++s) {
-        const float f = __builtin_amdgcn_exp2f(base[s * rec + h] - M);
-        L += base[s * rec + kPartialHeads + h] * f;
-        O += base[s * rec + 2 * kPartialHeads + h * D + c] * f;
-      }
-      a.out[((size_t)si * a.n_q_heads + head * a.group + h) * D + c] = O / L;
-    }
+  const float* base = a.partials + ((size_t)si * a.n_kv_heads + head) * a.max_splits * rec;
+  float mx = kNegBig;
+  for (int sp = tid; sp < ns; sp += 256) {
+    const float m = base[sp * rec + h];
+    s_w[sp] = m;
+    mx = fmaxf(mx, m);
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) s_red[0][tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  float lsum = 0.0f;
+  for (int sp = tid; sp < ns; sp += 256) {
+    const float w = __builtin_amdgcn_exp2f(s_w[sp] - M);
+    s_w[sp] = w;
+    lsum += w * base[sp * rec + kPartialHeads + h];
+  }
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+  if ((tid & 63) == 0) s_red[1][tid >> 6] = lsum;
+  __syncthreads();
+  const float L = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+  const int c = c0 + (tid & 15);
+  const int grp = tid >> 4;
+  const float* po = base + 2 * kPartialHeads + h * D + c;
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int sp = grp; sp < ns; sp += 16) acc += s_w[sp] * po[sp * rec];
+  s_acc[grp][tid & 15] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float o = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o += s_acc[k][tid];
+    a.out[((size_t)si * a.n_q_heads + head * a.group + h) * D + c] = o / L;
   }
 }
 
 template <int NK, int NV>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<NK, NV>), dim3(grid_x, a.g.n_kv_heads, a.n_seqs), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<NK, NV>), dim3(grid_x), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -609,8 +754,9 @@ hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.n_seqs * a.n_kv_heads), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.n_seqs * a.n_kv_heads, a.group, a.head_dim / 16), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

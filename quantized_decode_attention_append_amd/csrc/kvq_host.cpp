@@ -23,6 +23,7 @@ struct kvq_cache {
   size_t arena_bytes;
   std::vector<int32_t> len, body_len;
   std::vector<uint8_t> calibrated;
+  int n_cu = 256;            // compute units of the device (split planning)
   int idx(int layer, int seq) const { return layer * cfg.max_seqs + seq; }
 };
 
@@ -122,40 +123,56 @@ kvq_status check_seqs(const kvq_cache* c, int layer, int n_seqs, const int32_t* 
 
 int tiles_of(int p0, int p1) { return p1 > p0 ? (p1 - 1) / kvq::kTile - p0 / kvq::kTile + 1 : 0; }
 
-// Split planning shared by kvq_workspace_bytes and kvq_decode_attn.
-constexpr int kTargetWgs = 512;
-constexpr int kMinTilesPerSplit = 4;
+// Split planning. The decode kernel runs one 8-wave work-group per split and the plan aims at about one
+// work-group per CU: each (sequence, body|ring) segment gets a share of the CU budget proportional to
+// its tiles (at least one), leftover work-groups go to the segments with the most tiles per work-group.
+constexpr int kMaxWgBudget = 1024;
 constexpr size_t kPartialFloats(int d) { return (size_t)kvq::kPartialHeads * (d + 2); }
 
 struct SplitPlan {
-  int tiles_per_split;
-  int max_splits;
+  int max_splits;   // per (sequence, KV head)
+  int total_wgs;
 };
 
 SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out) {
+  const int hk = c->cfg.n_kv_heads;
+  const int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
+  int tiles[2 * KVQ_MAX_BATCH], nwg[2 * KVQ_MAX_BATCH];
   long total = 0;
   for (int i = 0; i < n_seqs; ++i) {
-    const int bt = (body_len[i] + kvq::kTile - 1) / kvq::kTile;
-    const int rt = len[i] > body_len[i] ? (len[i] + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
-    total += (long)c->cfg.n_kv_heads * (bt + rt);
+    tiles[2 * i] = (body_len[i] + kvq::kTile - 1) / kvq::kTile;
+    tiles[2 * i + 1] =
+        len[i] > body_len[i] ? (len[i] + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
+    total += tiles[2 * i] + tiles[2 * i + 1];
   }
-  long t = (total + kTargetWgs - 1) / kTargetWgs;
-  t = (t + 3) / 4 * 4;
-  if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
-  SplitPlan p{(int)t, 1};
+  int used = 0;
+  for (int k = 0; k < 2 * n_seqs; ++k) {
+    nwg[k] = tiles[k] ? std::max(1, (int)((long)budget_h * tiles[k] / std::max(total, 1L))) : 0;
+    nwg[k] = std::min(nwg[k], tiles[k]);
+    used += nwg[k];
+  }
+  for (; used < budget_h; ++used) {   // leftover: the segment with the most tiles per work-group
+    int best = -1;
+    double best_r = 1.0;
+    for (int k = 0; k < 2 * n_seqs; ++k)
+      if (nwg[k] && nwg[k] < tiles[k] && (double)tiles[k] / nwg[k] > best_r) {
+        best_r = (double)tiles[k] / nwg[k];
+        best = k;
+      }
+    if (best < 0) break;
+    ++nwg[best];
+  }
+  SplitPlan p{1, 0};
   for (int i = 0; i < n_seqs; ++i) {
-    const int bt = (body_len[i] + kvq::kTile - 1) / kvq::kTile;
-    const int rt = len[i] > body_len[i] ? (len[i] + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
-    const int nb = (bt + p.tiles_per_split - 1) / p.tiles_per_split;
-    const int nr = (rt + p.tiles_per_split - 1) / p.tiles_per_split;
     if (out) {
       out[i].len = len[i];
       out[i].body_len = body_len[i];
-      out[i].n_body_splits = nb;
-      out[i].n_ring_splits = nr;
+      out[i].n_body_splits = nwg[2 * i];
+      out[i].n_ring_splits = nwg[2 * i + 1];
       out[i].ring_tile0 = body_len[i] / kvq::kTile;
     }
-    p.max_splits = std::max(p.max_splits, nb + nr);
+    p.max_splits = std::max(p.max_splits, nwg[2 * i] + nwg[2 * i + 1]);
+    p.total_wgs += hk * (nwg[2 * i] + nwg[2 * i + 1]);
   }
   return p;
 }
@@ -214,6 +231,10 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_arena, size_t arena_b
   c->len.assign(n, 0);
   c->body_len.assign(n, 0);
   c->calibrated.assign(n, 0);
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+    c->n_cu = ncu;
   hipError_t e = kvq::launch_fill_zero(dev_arena, need, (hipStream_t)stream);
   if (e != hipSuccess) {
     delete c;
@@ -253,10 +274,10 @@ kvq_status kvq_seq_lengths(const kvq_cache* c, int32_t layer, int32_t seq, int32
 
 size_t kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) {
   if (!c || n_seqs < 1 || max_len < 1) return 0;
-  // splits per (seq, head) never exceed the tiles of one sequence / 4 + 2, nor the work-group target + 2
-  const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 2;
-  long splits = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit + 2;
-  splits = std::min<long>(splits, kTargetWgs + 2);
+  // splits per (sequence, KV head) never exceed the tiles of a sequence (+1 for the body/ring boundary
+  // tile) nor the per-head work-group budget
+  const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 1;
+  const long splits = std::min<long>(tiles, std::max(1, std::min(c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads));
   return (size_t)n_seqs * c->cfg.n_kv_heads * splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
 }
 
@@ -414,6 +435,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   kvq::DecodeArgs a{};
   a.g = geometry(c);
   const SplitPlan p = plan_splits(c, n_seqs, len, bl, a.seqs);
+  if (p.max_splits > kvq::kMaxSplits) return fail(KVQ_E_INVALID, "too many splits (%d)", p.max_splits);
   const size_t need = (size_t)n_seqs * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   for (int i = 0; i < n_seqs; ++i) a.seqs[i].slab = slab_offset(c, layer, seq_ids[i]);
@@ -424,9 +446,8 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   a.n_q_heads = c->cfg.n_q_heads;
   a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
   a.max_splits = p.max_splits;
-  a.tiles_per_split = p.tiles_per_split;
   a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
-  hipError_t e = kvq::launch_decode(a, p.max_splits, (hipStream_t)stream);
+  hipError_t e = kvq::launch_decode(a, p.total_wgs, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   kvq::CombineArgs cb{};
   cb.out = out;
@@ -439,7 +460,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   cb.max_splits = p.max_splits;
   for (int i = 0; i < n_seqs; ++i) cb.n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
   e = kvq::launch_combine(cb, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return KVQ_OK;
 }
 

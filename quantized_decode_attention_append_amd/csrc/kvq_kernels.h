@@ -11,6 +11,7 @@ namespace kvq {
 
 constexpr int kMaxBatch = 64;      // sequences per call (kernel arguments are passed by value)
 constexpr int kPartialHeads = 8;   // query heads per KV head handled by one decode work-group
+constexpr int kMaxSplits = 1024;   // split partials per (sequence, KV head)
 
 // Geometry of one (layer) of the arena, as the kernels need it.
 struct Geometry {
@@ -71,7 +72,7 @@ struct DecodeArgs {
   const uint16_t* q;           // [n_seqs][Hq][D] bf16
   float* out;                  // [n_seqs][Hq][D]
   float* partials;             // [n_seqs][Hkv][max_splits][8 * (D + 2)]
-  int n_seqs, n_q_heads, group, max_splits, tiles_per_split;
+  int n_seqs, n_q_heads, group, max_splits;
   float scale;                 // softmax scale
   DecodeSeq seqs[kMaxBatch];
 };

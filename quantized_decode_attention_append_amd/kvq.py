@@ -156,8 +156,14 @@ class Cache:
         return int(_lib.kvq_workspace_bytes(self._h, n_seqs, max_len))
 
     def workspace(self, n_seqs: int, max_len: int) -> torch.Tensor:
-        n = self.workspace_bytes(n_seqs, max_len)
-        return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        """A workspace for n_seqs sequences of up to max_len positions (kept by the cache and grown on
+        demand, so repeated calls return the same memory)."""
+        n = max(self.workspace_bytes(n_seqs, max_len), 256)
+        ws = getattr(self, "_ws", None)
+        if ws is None or ws.numel() < n:
+            ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+            self._ws = ws
+        return ws
 
     # ---------------------------------------------------------------- the calls
     def append(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor,

@@ -155,3 +155,22 @@ def test_errors_from_the_host():
     with pytest.raises(kvq.KvqError) as e:
         p.gpu.decode_attn(0, [0], dev(small_query(0, 1, 16, 256)), workspace=ws)
     assert e.value.status == kvq.KVQ_E_SIZE
+
+
+def test_workspace_reused_across_calls_and_allocations():
+    # many calls on one workspace, with unrelated allocations in between, must all be right
+    import torch
+    p = Pair(cfg(k_bits=4, v_bits=4, capacity=4096))
+    k, v = small_tokens(3, 3000, 2, 256)
+    p.append(0, [0], [3000], k, v)
+    ws = p.gpu.workspace(1, 3000)
+    for i in range(6):
+        junk = torch.full((1 << 20,), 7, dtype=torch.int32, device="cuda")
+        q = small_query(100 + i, 1, 16, 256)
+        from tests.gpu_util import dev
+        import oracle
+        got = p.gpu.decode_attn(0, [0], dev(q), workspace=ws).cpu().numpy()
+        want = oracle.decode_reference(p.ora, 0, [0], q)
+        assert max_err(got, want) <= TOL, i
+        del junk
+
