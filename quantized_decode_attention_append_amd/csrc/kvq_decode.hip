@@ -198,17 +198,21 @@ __device__ inline float wave_max_16_32(float x) {
   return x;
 }
 
+// Cache rows are read once per decode call: streaming (nontemporal) loads keep them from displacing
+// other lines and sustain a much higher read rate on gfx950 than ordinary loads.
+__device__ inline u32x4 ldnt(const uint8_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+
 template <int W>
 __device__ inline void load_words(const uint8_t* p, uint32_t* dst, int n_words) {
   // n_words is a compile-time multiple of 2 or 4 at every call site
   if (n_words % 4 == 0) {
     for (int k = 0; k < n_words; k += 4) {
-      u32x4 v = *(const u32x4*)(p + 4 * k);
+      u32x4 v = ldnt(p + 4 * k);
       dst[k] = v[0]; dst[k + 1] = v[1]; dst[k + 2] = v[2]; dst[k + 3] = v[3];
     }
   } else {
     for (int k = 0; k < n_words; k += 2) {
-      u32x2 v = *(const u32x2*)(p + 4 * k);
+      u32x2 v = __builtin_nontemporal_load((const u32x2*)(p + 4 * k));
       dst[k] = v[0]; dst[k + 1] = v[1];
     }
   }
@@ -237,48 +241,54 @@ struct TileRaw {
   u32x4 sc;                                       // lanes 0-31: K scales of row `lane`; 32-63: V scales of position lane-32
 };
 
+// Issue the loads of one tile into `t`. With live = false every lane reads the same 16 bytes at the start
+// of kbase / vt instead (a placeholder that costs one cache line per instruction): the loads are then
+// issued on every path, which keeps the compiler's memory-counter waits exact across the tile loop.
 template <int NK, int NV>
 __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kbase, int row_k, bool ring, int R,
-                                 const uint8_t* vt, int tile) {
+                                 const uint8_t* vt, int tile, bool live) {
   using T = TileRaw<NK, NV>;
   constexpr int NB = 8, NT = 16, D = 256;
   const int lane = threadIdx.x & 63;
   const int m16 = lane & 15;
   const int g = lane >> 4;
+  const int gl = live ? g : 0;
+  const int ll = live ? lane : 0;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int pos = tile * kTile + 16 * s + m16;
-    const uint8_t* row = kbase + (size_t)(ring ? pos % R : pos) * row_k;
-    load_words<0>(row + g * NB * T::w0k, t.k0[s], T::nk0);
-    if constexpr (T::w1k > 0) load_words<0>(row + 4 * NB * T::w0k + g * NB * T::w1k, t.k1[s], T::nk1);
-    if constexpr (T::w2k > 0) load_words<0>(row + 4 * NB * (T::w0k + T::w1k) + g * NB * T::w2k, t.k2[s], T::nk2);
+    const uint8_t* row = live ? kbase + (size_t)(ring ? pos % R : pos) * row_k : kbase;
+    load_words<0>(row + gl * NB * T::w0k, t.k0[s], T::nk0);
+    if constexpr (T::w1k > 0) load_words<0>(row + 4 * NB * T::w0k + gl * NB * T::w1k, t.k1[s], T::nk1);
+    if constexpr (T::w2k > 0) load_words<0>(row + 4 * NB * (T::w0k + T::w1k) + gl * NB * T::w2k, t.k2[s], T::nk2);
   }
 #pragma unroll
   for (int c = 0; c < NT * T::w0v / 16; ++c) {
-    u32x4 x = *(const u32x4*)(vt + c * 1024 + lane * 16);
+    u32x4 x = ldnt(vt + c * 1024 + ll * 16);
     t.v0[4 * c] = x[0]; t.v0[4 * c + 1] = x[1]; t.v0[4 * c + 2] = x[2]; t.v0[4 * c + 3] = x[3];
   }
   if constexpr (T::w1v > 0) {
     const uint8_t* p1 = vt + 64 * NT * T::w0v;
 #pragma unroll
     for (int c = 0; c < NT * T::w1v / 16; ++c) {
-      u32x4 x = *(const u32x4*)(p1 + c * 1024 + lane * 16);
+      u32x4 x = ldnt(p1 + c * 1024 + ll * 16);
       t.v1[4 * c] = x[0]; t.v1[4 * c + 1] = x[1]; t.v1[4 * c + 2] = x[2]; t.v1[4 * c + 3] = x[3];
     }
   }
   if constexpr (T::w2v > 0) {
-    u32x4 x = *(const u32x4*)(vt + 64 * NT * (T::w0v + T::w1v) + lane * 16);
+    u32x4 x = ldnt(vt + 64 * NT * (T::w0v + T::w1v) + ll * 16);
     t.v2[0] = x[0]; t.v2[1] = x[1]; t.v2[2] = x[2]; t.v2[3] = x[3];
   }
-  if (lane < 32) {
-    const int pr = tile * kTile + lane;
-    t.sc = *(const u32x4*)(kbase + (size_t)(ring ? pr % R : pr) * row_k + NB * 4 * NK);
-  } else {
-    t.sc = *(const u32x4*)(vt + 4 * D * NV + (lane - 32) * NB * 2);
-  }
+  const int pr = tile * kTile + (lane & 31);
+  const uint8_t* ksc = live ? kbase + (size_t)(ring ? pr % R : pr) * row_k + NB * 4 * NK : kbase;
+  const uint8_t* vsc = live ? vt + 4 * D * NV + (lane - 32) * NB * 2 : vt;
+  t.sc = ldnt(lane < 32 ? ksc : vsc);
 }
 
 #define KVQ_SB __builtin_amdgcn_sched_barrier(0);
+#ifndef TRACE_QLOADED
+#define TRACE_QLOADED
+#endif
 
 __device__ inline float lo_h(uint32_t w) { return (float)as_h2(w)[0]; }
 __device__ inline float hi_h(uint32_t w) { return (float)as_h2(w)[1]; }
@@ -361,13 +371,14 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
     const u32x2 d1 = *(const u32x2*)(s_dv + B * 32 + 16 + 4 * g);                                    \
     const uint32_t dw[4] = {d0[0], d0[1], d1[0], d1[1]};                                             \
     half8 a;                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                 \
-      const uint32_t wd = dw[i >> 1];                                                               \
-      const uint32_t wk = wd & lane_mask;                                                           \
-      const float d = (i & 1) ? hi_h(wd) : lo_h(wd);                                                \
-      const float dm = (i & 1) ? hi_h(wk) : lo_h(wk);                                               \
-      const _Float16 h = (_Float16)(p[i] * dm);                                                     \
-      a[i] = (_Float16)fmaf(p[i], d, -(float)h);                                                    \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                 \
+      const half2v d = as_h2(dw[j]);                                                                \
+      const half2v dm = as_h2(dw[j] & lane_mask);                                                   \
+      /* fma with +0 (not a product) so that it maps to a mixed-precision fma */                    \
+      const _Float16 h0 = (_Float16)fmaf(p[2 * j], (float)dm[0], 0.0f);                             \
+      const _Float16 h1 = (_Float16)fmaf(p[2 * j + 1], (float)dm[1], 0.0f);                         \
+      a[2 * j] = (_Float16)fmaf(p[2 * j], (float)d[0], -(float)h0);                                 \
+      a[2 * j + 1] = (_Float16)fmaf(p[2 * j + 1], (float)d[1], -(float)h1);                         \
     }                                                                                               \
     half8 b0 = decode_run_piece<NV, 2 * B>(t.v0, t.v1, t.v2, magic);                                \
     st.o[2 * B] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, st.o[2 * B], 0, 0, 0);              \
@@ -379,18 +390,26 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
 #undef KVQ_PV
 }
 
+// Next tile of the work-group's range for this wave: the waves of a work-group take tiles from a shared
+// LDS counter, so a wave that gets fewer issue slots on its SIMD simply processes fewer tiles.
+__device__ inline int grab_tile(int* s_next) {
+  int v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(s_next, 1);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 __device__ inline const uint8_t* tile_ptr(const uint8_t* vbase, int tile_v, bool ring, int R, int t) {
   return vbase + (size_t)(ring ? ((t * kTile) % R) / kTile : t) * tile_v;
 }
 
-// Loop over this wave's contiguous tiles [t, tile_end) of a qN_0 store. On entry `cur` holds tile t and
-// `nxt` tile t+1 (both requested before the query set-up); during the compute of tile i the loads of tile
-// i+1 are in flight. s_buf: this wave's two 1-KiB LDS buffers for tile scales.
+// Loop over tiles of a qN_0 store: this wave starts with tile t (already requested in `cur`) and then takes
+// further tiles below tile_end from the work-group counter. During the compute of one tile the loads of
+// the next are in flight. s_buf: this wave's two 1-KiB LDS buffers for tile scales.
 template <int NK, int NV>
 __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, TileRaw<NK, NV>& nxt, const half8* qb,
                                        float qmul, const uint8_t* kbase, int row_k, bool ring, int R,
                                        const uint8_t* vbase, int tile_v, int t, int tile_end, int lo, int hi,
-                                       uint32_t lane_mask, u32x4* s_buf) {
+                                       uint32_t lane_mask, u32x4* s_buf, int* s_next) {
   const int lane = threadIdx.x & 63;
   if (t >= tile_end) return;
   uint32_t magic = kMagic;
@@ -407,10 +426,14 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
   int buf = 0;
   for (;;) {
     u32x4* sb = s_buf + 64 * buf;
+    // the next tile's loads go out before this tile's scales are staged (which waits for this tile only)
+    const int nt = grab_tile(s_next);
+    const bool more = nt < tile_end;
+    load_tile<NK, NV>(nxt, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), more ? nt : t, more);
     stage(cur, sb);
-    if (t + 1 < tile_end) load_tile<NK, NV>(nxt, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, t + 1), t + 1);
     compute_tile<NK, NV>(st, cur, sb, qb, qmul, t, lo, hi, lane_mask, magic);
-    if (++t >= tile_end) break;
+    if (nt >= tile_end) break;
+    t = nt;
     cur = nxt;
     buf ^= 1;
   }
@@ -430,7 +453,7 @@ __device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, co
     const uint8_t* row = kring + (size_t)(pos % R) * (2 * D);
     bf16x8 kk[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) kk[b] = *(const bf16x8*)(row + (32 * b + 8 * g) * 2);
+    for (int b = 0; b < 8; ++b) kk[b] = __builtin_nontemporal_load((const bf16x8*)(row + (32 * b + 8 * g) * 2));
     floatx4 c = {0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[b], qb[b * 64 + lane], c, 0, 0, 0);
@@ -457,7 +480,7 @@ __device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, co
   for (int n0 = 0; n0 < NT; n0 += 4) {
     bf16x8 vv[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vv[k] = *(const bf16x8*)(vt + (n0 + k) * 1024 + lane * 16);
+    for (int k = 0; k < 4; ++k) vv[k] = __builtin_nontemporal_load((const bf16x8*)(vt + (n0 + k) * 1024 + lane * 16));
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       st.o[n0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vv[k], st.o[n0 + k], 0, 0, 0);
@@ -475,66 +498,62 @@ struct QArgs {
 
 // A qN_0 store path (body, or q8_0 ring): issue the first tile's loads, build the exponent-shifted query
 // operands (times KVarN sigma) in LDS, then run the tile loop. All waves of the work-group call this.
-template <int NK, int NV>
+template <int NK, int NV, bool EARLY>
 __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, const uint8_t* kbase, int row_k,
                                   bool ring, int R, const uint8_t* vbase, int tile_v, int wb, int we, int lo, int hi,
-                                  uint32_t lane_mask, u32x4* sbuf) {
+                                  uint32_t lane_mask, u32x4* sbuf, int* s_next, float* s_amax) {
   constexpr int NB = 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int gq = lane >> 4;
   TileRaw<NK, NV> cur, nxt;
-  // the first two tiles' loads go out before the query set-up
-  if (wb < we) load_tile<NK, NV>(cur, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, wb), wb);
-  // exponent-shifted query, split into fp16 hi (cols 0-7) and lo (cols 8-15); two passes over the
-  // (cached) query keep the live registers low while the first tiles' loads are in flight
-  auto q_block = [&](int b, float* x) {
-    const u32x4 raw = *(const u32x4*)(qa.qrow + 32 * b + 8 * gq);
+  // Wave w prepares block w of the query operand. Its query (and KVarN sigma) loads go out before the
+  // first tile's: issued behind the tile loads they would wait for the work-group's tile traffic.
+  const u32x4 qraw = *(const u32x4*)(qa.qrow + 32 * wave + 8 * gq);
+  u32x4 sraw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
+  if (qa.use_sigma) sraw = *(const u32x4*)(qa.sig + 32 * wave + 8 * gq);
+  KVQ_SB
+  const int t0 = wb < we ? wb : we - 1;
+  if constexpr (EARLY) load_tile<NK, NV>(cur, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, t0), t0, wb < we);
+  float x[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __uint_as_float(raw[k] << 16);
-      x[2 * k + 1] = __uint_as_float(raw[k] & 0xFFFF0000u);
-    }
-    if (qa.use_sigma) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] *= h2f(qa.sig[32 * b + 8 * gq + i]);   // exact (8 + 11 bits)
-    }
-  };
+  for (int k = 0; k < 4; ++k) {   // q times sigma is exact in fp32 (8 + 11 bits)
+    x[2 * k] = __uint_as_float(qraw[k] << 16) * lo_h(sraw[k]);
+    x[2 * k + 1] = __uint_as_float(qraw[k] & 0xFFFF0000u) * hi_h(sraw[k]);
+  }
   float amax = 0.0f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float x[8];
-    q_block(b, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  }
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  TRACE_QLOADED
   amax = wave_max_16_32(amax);
+  if (lane < 16) s_amax[wave * 16 + lane] = amax;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) amax = fmaxf(amax, s_amax[w * 16 + (lane & 15)]);
+  // exponent-shifted query of this lane's head, split into fp16 hi (cols 0-7) and lo (cols 8-15)
   const int e = amax > 0.0f ? ilogbf(amax) - 14 : 0;
-  if (wave == 0) {   // the B operand of every block goes to LDS (read back per block and subtile)
+  {
+    half8 v;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float x[8];
-      q_block(b, x);
-      half8 v;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xs = ldexpf(x[i], -e);
-        const _Float16 h = (_Float16)xs;
-        const _Float16 l = (_Float16)(xs - (float)h);
-        v[i] = qa.head_ok ? (qa.lo_lane ? l : h) : (_Float16)0.0f;
-      }
-      s_qb[b * 64 + lane] = v;
+    for (int i = 0; i < 8; ++i) {
+      const float xs = ldexpf(x[i], -e);
+      const _Float16 h = (_Float16)xs;
+      const _Float16 l = (_Float16)(xs - (float)h);
+      v[i] = qa.head_ok ? (qa.lo_lane ? l : h) : (_Float16)0.0f;
     }
+    s_qb[wave * 64 + lane] = v;
   }
   __syncthreads();
+  if constexpr (!EARLY) load_tile<NK, NV>(cur, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, t0), t0, wb < we);
   const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e);
   run_quant_tiles<NK, NV>(st, cur, nxt, s_qb, qmul, kbase, row_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
-                          sbuf);
+                          sbuf, s_next);
 }
 
 // One work-group of 8 waves (two per SIMD) per split; the host sizes the splits so that there is about one
-// work-group per CU. Each wave takes a contiguous share of the split's tiles (extra tiles go to waves 0-3,
-// which sit on different SIMDs); the waves' partial results are merged in LDS into one partial record.
+// work-group per CU. The waves claim the split's tiles one at a time from an LDS counter (the two waves of
+// a SIMD do not get equal issue slots, so a static share would leave one of them finishing late); the
+// waves' partial results are merged in LDS into one partial record.
 template <int NK, int NV>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int D = 256, NB = 8, NT = 16, NW = 8;
@@ -542,6 +561,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float s_ml[NW][2][kPartialHeads];
   __shared__ u32x4 s_scales[NW][2][64];   // per wave, double-buffered tile scales
   __shared__ half8 s_qb[8 * 64];           // QK B operands (per block, per lane)
+  __shared__ int s_next;                   // next unclaimed tile of this split
+  __shared__ float s_amax[8 * 16];         // per wave: |q| maximum of each head over the wave's block
 
   // flattened grid: (sequence, KV head, split)
   const Geometry& g = a.g;
@@ -578,15 +599,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lo = S.body_len;
     hi = S.len;
   }
-  // this split's tiles, then this wave's share
+  // this split's tiles [tb, te): wave w starts with tile tb + w, further tiles come from s_next
   const int tb = seg_begin + (int)((long)sp * seg_tiles / nsp);
   const int te = seg_begin + (int)((long)(sp + 1) * seg_tiles / nsp);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int nt = te - tb, qw = nt / NW, rw = nt % NW;
-  const int wb = tb + wave * qw + min(wave, rw);
-  const int we = wb + qw + (wave < rw ? 1 : 0);
+  const int wb = tb + wave;
+  const int we = te;
+  if (tid == 0) s_next = tb + NW;   // published by the work-group barrier before the first tile loop
 
   const int m16 = lane & 15;
   const int gq = lane >> 4;
@@ -619,7 +640,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     const float qmul = a.scale * kLog2e;
     const uint8_t* kring = slab + g.k_ring + (size_t)head * R * (2 * D);
-    for (int t = wb; t < we; ++t) {
+    for (int t = wb; t < we; t = grab_tile(&s_next)) {
       const uint8_t* vt = slab + g.v_ring + ((size_t)head * (R / kTile) + ((t * kTile) % R) / kTile) * g.ring_tile_v;
       tile_bf16(st, qb, qmul, kring, R, vt, t, lo, hi, lo_lane);
     }
@@ -630,12 +651,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (!is_ring) {
       const uint8_t* kbase = slab + g.k_body + (size_t)head * g.cap32 * g.row_k;
       const uint8_t* vbase = slab + g.v_body + (size_t)head * (g.cap32 / kTile) * g.tile_v;
-      quant_path<NK, NV>(st, qa, s_qb, kbase, g.row_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask, sbuf);
+      // waves 0-3 (one per SIMD) request their first tile at once, waves 4-7 only once the query is set
+      // up: a smaller first burst reaches every SIMD sooner
+      if (wave < 4)
+        quant_path<NK, NV, true>(st, qa, s_qb, kbase, g.row_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
+                                 sbuf, &s_next, s_amax);
+      else
+        quant_path<NK, NV, false>(st, qa, s_qb, kbase, g.row_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
+                                  sbuf, &s_next, s_amax);
     } else {
       const uint8_t* kbase = slab + g.k_ring + (size_t)head * R * g.ring_row_k;
       const uint8_t* vbase = slab + g.v_ring + (size_t)head * (R / kTile) * g.ring_tile_v;
-      quant_path<8, 8>(st, qa, s_qb, kbase, g.ring_row_k, true, R, vbase, g.ring_tile_v, wb, we, lo, hi, lane_mask,
-                       sbuf);
+      quant_path<8, 8, true>(st, qa, s_qb, kbase, g.ring_row_k, true, R, vbase, g.ring_tile_v, wb, we, lo, hi,
+                             lane_mask, sbuf, &s_next, s_amax);
     }
   }
 
