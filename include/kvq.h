@@ -44,6 +44,13 @@ typedef enum {
   KVQ_TAIL_Q8_0 = 2     /* newest tail_len tokens kept as q8_0 (Qwen3.8-27B page, 8-bit ring)      */
 } kvq_tail_dtype;
 
+typedef enum {
+  KVQ_LAYOUT_TILES = 0, /* V (and q8_0 ring V) stored in 32-position tiles ordered for the decode kernel's
+                           matrix operands: the fastest dense decode; no sparse decode              */
+  KVQ_LAYOUT_ROWS = 1   /* every K and V position stored as one contiguous row, so that a sparse
+                           layer gathers exactly the rows it attends (offload page, QSA paragraph)  */
+} kvq_layout;
+
 /* Maximum number of sequences one call may name. */
 #define KVQ_MAX_BATCH 64
 
@@ -61,6 +68,7 @@ typedef struct {
   int32_t tail_len;     /* W: newest tokens kept in the tail ring (0 = no ring)                */
   int32_t tail_slack;   /* S: extra ring slots; ring capacity R = W + S must be a multiple of 32 */
   int32_t tail_dtype;   /* kvq_tail_dtype (ignored when tail_len == 0)                          */
+  int32_t layout;       /* kvq_layout: placement of V rows (both layouts have the same size)       */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache;
@@ -123,7 +131,7 @@ kvq_status kvq_tail_evict(kvq_cache* cache, int32_t layer, int32_t n_seqs, const
                           void* stream);
 
 /* Dense decode attention (offload page: each step reads the whole cache of a full-attention
- * layer). For each sequence i: out[i][h][:] = softmax(scale * q[i][h] . K^[t]) over t in [0, len) of V^,
+ * layer). With KVQ_LAYOUT_ROWS the rows are read by the same gather kernel as sparse decode. For each sequence i: out[i][h][:] = softmax(scale * q[i][h] . K^[t]) over t in [0, len) of V^,
  * with K^, V^ the dequantized body rows (t < body_len) or ring rows. q_bf16: device bf16
  * [n_seqs][Hq][D]; out: device fp32 [n_seqs][Hq][D]; softmax_scale <= 0 means 1/sqrt(D); workspace:
  * device, at least kvq_workspace_bytes(cache, n_seqs, max len) bytes, 256-byte aligned, no initial
@@ -137,9 +145,11 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
 
 /* Sparse decode attention over an indexer budget (offload page, QSA: the layer reads only the
  * main-KV rows at the positions the indexer chose, so the budget, not the context, bounds the bytes).
- * positions: device int32 [n_seqs][budget], one list per sequence shared by all KV heads; entries must
- * be distinct and in [0, len) (entries outside are skipped). 1 <= budget <= len of every sequence.
- * Other arguments as kvq_decode_attn. */
+ * positions: device int32 [n_seqs][budget], one list per sequence shared by all KV heads; entries are
+ * expected to be distinct and in [0, len): entries outside [0, len) are skipped, a repeated entry counts
+ * as often as it appears. If no entry of a sequence is valid its output is zero. 1 <= budget.
+ * The cache must use KVQ_LAYOUT_ROWS (KVQ_E_INVALID otherwise). Other arguments as kvq_decode_attn;
+ * the workspace must hold kvq_workspace_bytes(cache, n_seqs, budget) bytes. */
 kvq_status kvq_sparse_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                   const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
                                   float softmax_scale, void* workspace, size_t ws_bytes, void* stream);

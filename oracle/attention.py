@@ -51,10 +51,20 @@ def decode_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, scale=None)
 
 def sparse_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, positions: np.ndarray,
                      scale=None) -> np.ndarray:
-    """Attention over positions[i] (list order; one list per sequence, shared by all KV heads)."""
+    """Attention over positions[i] (list order; one list per sequence, shared by all KV heads).
+
+    Reading (the pages say only that the layer reads the rows the indexer chose): an entry
+    outside [0, len) names no row and is skipped; a repeated entry is attended as often as it
+    appears; a list with no valid entry gives a zero output."""
     sc = _scale(cache, scale)
     out = []
     for i, sid in enumerate(seq_ids):
-        k, v = cache.dequantized(layer, sid, positions[i])
+        n, _ = cache.lengths(layer, sid)
+        pos = np.asarray(positions[i], dtype=np.int64)
+        pos = pos[(pos >= 0) & (pos < n)]
+        if len(pos) == 0:
+            out.append(np.zeros((q_bits.shape[1], cache.cfg["head_dim"])))
+            continue
+        k, v = cache.dequantized(layer, sid, pos)
         out.append(attend(_q64(q_bits[i]), k, v, sc))
     return np.stack(out)

@@ -31,6 +31,7 @@ from .layout import (pack_k_rows, pack_v_tiles, pack_bf16_v_tiles, slab_layout, 
 from .quant import quantize_blocks, kvarn_sigma, normalize, dequantize_blocks
 
 TAIL_NONE, TAIL_BF16, TAIL_Q8 = 0, 1, 2
+LAYOUT_TILES, LAYOUT_ROWS = 0, 1
 
 
 def _bf16_f32(bits):
@@ -70,6 +71,7 @@ class OracleCache:
         self.W = cfg["tail_len"]
         self.R = self.lay["ring_slots"]
         self.tail = cfg["tail_dtype"] if self.W > 0 else TAIL_NONE
+        self.rows = cfg.get("layout", LAYOUT_TILES) == LAYOUT_ROWS   # V stored as rows, like K
         self.state = {}
 
     # ------------------------------------------------------------------ helpers
@@ -209,11 +211,18 @@ class OracleCache:
         """Packed bytes of one head's region for positions / slots [lo, hi).
 
         k_body / k_ring: rows lo..hi-1; v_body / v_ring: tiles lo//32 .. hi//32 - 1
-        (lo, hi multiples of 32); sigma: the [2, D] fp16 block of the head."""
+        (lo, hi multiples of 32), or rows lo..hi-1 in the row layout; sigma: the [2, D]
+        fp16 block of the head."""
         s = self.st(layer, seq)
         kb, vb = self.cfg["k_bits"], self.cfg["v_bits"]
         if region == "k_body":
             return pack_k_rows(s.ku[lo:hi, head], s.kd[lo:hi, head], kb)
+        if region == "v_body" and self.rows:
+            return pack_k_rows(s.vu[lo:hi, head], s.vd[lo:hi, head], vb)
+        if region == "v_ring" and self.rows:
+            if self.tail == TAIL_BF16:
+                return np.ascontiguousarray(s.rv[lo:hi, head]).view(np.uint8)
+            return pack_k_rows(s.rvu[lo:hi, head], s.rvd[lo:hi, head], 8)
         if region == "v_body":
             assert lo % TILE == 0 and hi % TILE == 0
             u = s.vu[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"])

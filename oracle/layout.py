@@ -32,6 +32,11 @@ bf16 tail ring: K rows are the D bf16 values in channel order; V tiles of 32
 slots hold, for n-tile n and lane l, the 8 bf16 values of channel 16*n + d16 at
 tile positions T(j, i): [n][lane][8 x bf16].
 
+Row layout (a cache option for sparse layers): V is stored exactly like K, one
+row per position (body and q8_0 ring: the K row format above; bf16 ring: the D
+bf16 values), so a position is one contiguous K row and one V row. The region
+sizes equal those of the tile layout.
+
 Arena: slabs of [layer][sequence]; each slab holds, in order and 256-byte
 aligned: K body [head][capacity32][row], V body [head][capacity32/32][tile],
 K ring [head][R][row], V ring [head][R/32][tile], KVarN sigma [head][K,V][D] fp16.

@@ -27,6 +27,7 @@ UNITS = [
     ("kvq_host.cpp", ["-ffp-contract=off"]),
     ("kvq_append.hip", ["-ffp-contract=off"]),
     ("kvq_decode.hip", ["-ffp-contract=fast"]),
+    ("kvq_gather.hip", ["-ffp-contract=fast"]),
 ]
 
 

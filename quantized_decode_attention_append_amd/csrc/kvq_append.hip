@@ -105,13 +105,14 @@ __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int k
   const int lane = 16 * ((t % 16) / 4) + (c % 16);
   const int e = (t % 4) + 4 * (t / 16);
   if (g.tail_dtype == 1) {
-    if (kv == 0) return bf16_to_f32(((const uint16_t*)(slab + g.k_ring))[((size_t)head * R + slot) * D + c]);
+    if (kv == 0 || g.layout == 1)
+      return bf16_to_f32(((const uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c]);
     const uint8_t* tile = slab + g.v_ring + ((size_t)head * (R / kTile) + slot / kTile) * g.ring_tile_v;
     return bf16_to_f32(*((const uint16_t*)(tile + (size_t)(c / 16) * 64 * 16 + lane * 16) + e));
   }
   const int b = c / kBlock;
-  if (kv == 0) {
-    const uint8_t* row = slab + g.k_ring + ((size_t)head * R + slot) * g.ring_row_k;
+  if (kv == 0 || g.layout == 1) {
+    const uint8_t* row = slab + (kv ? g.v_ring : g.k_ring) + ((size_t)head * R + slot) * g.ring_row_k;
     const int j = (c % kBlock) / 8;
     const float dh = f16_to_f32(((const uint16_t*)(row + NB * 32))[b]);
     return (float)((int)row[(j * NB + b) * 8 + (c % 8)] - 128) * dh;
@@ -138,19 +139,25 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
   const int R = g.ring_slots;
   uint8_t* slab = g.arena + w.slab;
 
-  int row_k;
+  const bool vrows = g.layout == 1;
+  int row_k, row_v;
   uint8_t* kbase;
-  uint8_t* vtile;
+  uint8_t* vbase;   // row layout: V rows of this head
+  uint8_t* vtile;   // tile layout: this work-group's V tile
   if (a.dst_ring) {
-    row_k = g.ring_row_k;
+    row_k = row_v = g.ring_row_k;
     kbase = slab + g.k_ring + (size_t)head * R * row_k;
+    vbase = slab + g.v_ring + (size_t)head * R * row_v;
     vtile = slab + g.v_ring + ((size_t)head * (R / kTile) + ((tile * kTile) % R) / kTile) * g.ring_tile_v;
   } else {
     row_k = g.row_k;
+    row_v = g.row_v;
     kbase = slab + g.k_body + (size_t)head * g.cap32 * row_k;
+    vbase = slab + g.v_body + (size_t)head * g.cap32 * row_v;
     vtile = slab + g.v_body + ((size_t)head * (g.cap32 / kTile) + tile) * g.tile_v;
   }
   auto krow_of = [&](int p) { return kbase + (size_t)(a.dst_ring ? p % R : p) * row_k; };
+  auto vrow_of = [&](int p) { return vbase + (size_t)(a.dst_ring ? p % R : p) * row_v; };
   const int t0 = max(w.p0 - tile * kTile, 0);
   const int t1 = min(w.p1 - tile * kTile, kTile);
 
@@ -178,24 +185,28 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
     codes[kv][t][c] = (uint8_t)quant_lane(x, nb, &dq);
     if ((c % kBlock) == 0) {
       if (kv == 0) ((uint16_t*)(krow_of(p) + NB * 4 * NK))[b] = dq;
+      else if (vrows) ((uint16_t*)(vrow_of(p) + NB * 4 * NV))[b] = dq;
       else ((uint16_t*)(vtile + 4 * D * NV))[t * NB + b] = dq;
     }
   }
   __syncthreads();
 
-  // ---- phase 2a: K rows of the written positions, one 32-bit word per work item
-  const int words_per_row = NB * NK;           // sum over planes of 4 * NB * w / 4
+  // ---- phase 2a: K rows (and, in the row layout, V rows) of the written positions, one 32-bit word per
+  // work item
+  for (int rkv = 0; rkv < (vrows ? 2 : 1); ++rkv) {
+  const int NR = rkv ? NV : NK;
+  const int words_per_row = NB * NR;           // sum over planes of 4 * NB * w / 4
   for (int item = tid; item < (t1 - t0) * words_per_row; item += 512) {
     const int t = t0 + item / words_per_row;
     int widx = item % words_per_row;
     int pl = 0, plane_off = 0;
-    while (widx >= NB * plane_width(NK, pl)) {
-      widx -= NB * plane_width(NK, pl);
-      plane_off += 4 * NB * plane_width(NK, pl);
+    while (widx >= NB * plane_width(NR, pl)) {
+      widx -= NB * plane_width(NR, pl);
+      plane_off += 4 * NB * plane_width(NR, pl);
       ++pl;
     }
-    const int wdt = plane_width(NK, pl);
-    const int sh = plane_shift(NK, pl);
+    const int wdt = plane_width(NR, pl);
+    const int sh = plane_shift(NR, pl);
     const uint32_t m = (1u << wdt) - 1;
     const int wpj = NB * wdt / 4;               // words per lane group j in this plane
     const int j = widx / wpj;
@@ -204,19 +215,22 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
     if (wdt == 8) {
       const int bb = k / 2, e0 = 4 * (k & 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bits |= (uint32_t)codes[0][t][32 * bb + 8 * j + e0 + e] << (8 * e);
+      for (int e = 0; e < 4; ++e) bits |= (uint32_t)codes[rkv][t][32 * bb + 8 * j + e0 + e] << (8 * e);
     } else {
       const int per = 4 / wdt;
       for (int sl = 0; sl < per; ++sl) {
         const int bb = k * per + sl;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          bits |= ((uint32_t)(codes[0][t][32 * bb + 8 * j + e] >> sh) & m)
+          bits |= ((uint32_t)(codes[rkv][t][32 * bb + 8 * j + e] >> sh) & m)
                   << (16 * (e & 1) + 4 * wdt * sl + wdt * (e >> 1));
       }
     }
-    *(uint32_t*)(krow_of(tile * kTile + t) + plane_off + 4 * widx) = bits;   // = j * NB * w + 4k
+    uint8_t* row = rkv ? vrow_of(tile * kTile + t) : krow_of(tile * kTile + t);
+    *(uint32_t*)(row + plane_off + 4 * widx) = bits;   // = j * NB * w + 4k
   }
+  }
+  if (vrows) return;
 
   // ---- phase 2b: V tile words touched by this call (read-modify-write where partly covered)
   const int lane = tid & 63;
@@ -315,8 +329,8 @@ __global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
     const int p = tile * kTile + t;
     const uint16_t v = in[((size_t)(w.src_row + p - w.len_old) * g.n_kv_heads + head) * D + c];
     const int slot = p % R;
-    if (kv == 0) {
-      ((uint16_t*)(slab + g.k_ring))[((size_t)head * R + slot) * D + c] = v;
+    if (kv == 0 || g.layout == 1) {
+      ((uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c] = v;
     } else {
       uint8_t* vt = slab + g.v_ring + ((size_t)head * (R / kTile) + slot / kTile) * g.ring_tile_v;
       const int ts = slot % kTile;

@@ -760,7 +760,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     float o = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) o += s_acc[k][tid];
-    a.out[((size_t)si * a.n_q_heads + head * a.group + h) * D + c] = o / L;
+    a.out[((size_t)si * a.n_q_heads + head * a.group + h) * D + c] = L > 0.0f ? o / L : 0.0f;
   }
 }
 
@@ -788,6 +788,5 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse(const SparseArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace kvq

@@ -18,6 +18,9 @@
 //   min(16, NT*w) bytes ([chunk][lane][unit]); then the 32 x NB fp16 scales [position][block].
 // * bf16 tail ring: K rows are plain bf16; V tiles hold, per n-tile and lane, the 8 bf16 values of
 //   channel 16n+d16 at positions T(j,i): [n][lane][8 x bf16].
+// * Row layout (a cache option for sparse layers): V is stored exactly like K, one row per position
+//   (body, q8_0 ring) or plain bf16 rows (bf16 ring), so every position is one contiguous row of K and
+//   one of V. Region sizes are the same in both layouts.
 // * Arena: [layer][seq] slabs; a slab holds (256-byte aligned) K body [head][cap32][row],
 //   V body [head][cap32/32][tile], K ring [head][R][row], V ring [head][R/32][tile],
 //   KVarN sigma [head][K,V][D] fp16.

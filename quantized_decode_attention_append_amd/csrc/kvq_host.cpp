@@ -68,6 +68,8 @@ kvq_status validate(const kvq_config* c) {
     return fail(KVQ_E_INVALID, "k_bits and v_bits must be in [2, 8] (got %d, %d)", c->k_bits, c->v_bits);
   if (c->kvarn != 0 && c->kvarn != 1) return fail(KVQ_E_INVALID, "kvarn must be 0 or 1");
   if (c->tail_len < 0 || c->tail_slack < 0) return fail(KVQ_E_INVALID, "tail_len and tail_slack must be >= 0");
+  if (c->layout != KVQ_LAYOUT_TILES && c->layout != KVQ_LAYOUT_ROWS)
+    return fail(KVQ_E_INVALID, "layout must be KVQ_LAYOUT_TILES or KVQ_LAYOUT_ROWS (got %d)", c->layout);
   if (c->tail_len > 0) {
     if (c->tail_dtype != KVQ_TAIL_BF16 && c->tail_dtype != KVQ_TAIL_Q8_0)
       return fail(KVQ_E_INVALID, "tail_dtype must be KVQ_TAIL_BF16 or KVQ_TAIL_Q8_0 when tail_len > 0");
@@ -93,7 +95,9 @@ kvq::Geometry geometry(const kvq_cache* c) {
   g.tile_v = kvq::kTile * c->lay.row_v;
   g.ring_row_k = c->lay.ring_row_k;
   g.ring_tile_v = kvq::kTile * c->lay.ring_row_v;
+  g.ring_row_v = c->lay.ring_row_v;
   g.ring_slots = c->lay.ring_slots;
+  g.layout = c->cfg.layout;
   g.n_kv_heads = c->cfg.n_kv_heads;
   g.head_dim = c->cfg.head_dim;
   g.k_bits = c->cfg.k_bits;
@@ -175,6 +179,80 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
     p.total_wgs += hk * (nwg[2 * i] + nwg[2 * i + 1]);
   }
   return p;
+}
+
+// Gather decode: list entries per work-group are at least kGatherMin; about two work-groups per CU over all
+// (sequence, KV head) pairs.
+constexpr int kGatherMin = 64;
+int gather_budget_h(const kvq_cache* c) {
+  return std::max(1, std::min(2 * c->n_cu, kvq::kMaxSplits) / c->cfg.n_kv_heads);
+}
+int plan_gather(const kvq_cache* c, int n_seqs, const int* n_list, kvq::GatherSeq* out, int* total_wgs) {
+  long total = 0;
+  for (int i = 0; i < n_seqs; ++i) total += n_list[i];
+  const int budget = gather_budget_h(c);
+  int max_splits = 1;
+  *total_wgs = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int by_size = (n_list[i] + kGatherMin - 1) / kGatherMin;
+    const int by_share = (int)std::max(1L, (long)budget * n_list[i] / std::max(total, 1L));
+    const int ns = std::max(1, std::min(by_size, by_share));
+    out[i].n_splits = ns;
+    max_splits = std::max(max_splits, ns);
+    *total_wgs += c->cfg.n_kv_heads * ns;
+  }
+  return max_splits;
+}
+
+kvq_status launch_combine_for(kvq_cache* c, int n_seqs, const int* n_splits, int max_splits, float* out,
+                              void* workspace, hipStream_t stream) {
+  kvq::CombineArgs cb{};
+  cb.out = out;
+  cb.partials = (const float*)workspace;
+  cb.n_seqs = n_seqs;
+  cb.n_q_heads = c->cfg.n_q_heads;
+  cb.n_kv_heads = c->cfg.n_kv_heads;
+  cb.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  cb.head_dim = c->cfg.head_dim;
+  cb.max_splits = max_splits;
+  for (int i = 0; i < n_seqs; ++i) cb.n_splits[i] = n_splits[i];
+  hipError_t e = kvq::launch_combine(cb, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return KVQ_OK;
+}
+
+// The gather path shared by sparse decode and dense decode of a row-layout cache. positions: device
+// [n_seqs][pos_stride] or nullptr (entry i = position i, n_list[i] = len).
+kvq_status run_gather(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
+                      const int32_t* positions, int pos_stride, const int* n_list, float* out, float softmax_scale,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  kvq::GatherArgs a{};
+  a.g = geometry(c);
+  int total_wgs = 0;
+  const int max_splits = plan_gather(c, n_seqs, n_list, a.seqs, &total_wgs);
+  const size_t need = (size_t)n_seqs * c->cfg.n_kv_heads * max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  int n_splits[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    a.seqs[i].slab = slab_offset(c, layer, seq_ids[i]);
+    a.seqs[i].len = c->len[k];
+    a.seqs[i].body_len = c->body_len[k];
+    a.seqs[i].n_list = n_list[i];
+    n_splits[i] = a.seqs[i].n_splits;
+  }
+  a.q = (const uint16_t*)q_bf16;
+  a.positions = positions;
+  a.pos_stride = pos_stride;
+  a.partials = (float*)workspace;
+  a.n_seqs = n_seqs;
+  a.n_q_heads = c->cfg.n_q_heads;
+  a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  a.max_splits = max_splits;
+  a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
+  hipError_t e = kvq::launch_gather(a, total_wgs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return launch_combine_for(c, n_seqs, n_splits, max_splits, out, workspace, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -277,7 +355,10 @@ size_t kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) 
   // splits per (sequence, KV head) never exceed the tiles of a sequence (+1 for the body/ring boundary
   // tile) nor the per-head work-group budget
   const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 1;
-  const long splits = std::min<long>(tiles, std::max(1, std::min(c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads));
+  long splits = std::min<long>(tiles, std::max(1, std::min(c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads));
+  // the gather path (sparse decode, and dense decode of a row-layout cache)
+  const long gsplits = std::min<long>((max_len + kGatherMin - 1) / kGatherMin, gather_budget_h(c));
+  splits = std::max(splits, std::max(1L, gsplits));
   return (size_t)n_seqs * c->cfg.n_kv_heads * splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
 }
 
@@ -432,6 +513,9 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
     bl[i] = c->body_len[k];
     if (len[i] < 1) return fail(KVQ_E_STATE, "seq %d of layer %d is empty", seq_ids[i], layer);
   }
+  if (c->cfg.layout == KVQ_LAYOUT_ROWS)
+    return run_gather(c, layer, n_seqs, seq_ids, q_bf16, nullptr, 0, len, out, softmax_scale, workspace, ws_bytes,
+                      stream);
   kvq::DecodeArgs a{};
   a.g = geometry(c);
   const SplitPlan p = plan_splits(c, n_seqs, len, bl, a.seqs);
@@ -449,29 +533,27 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
   hipError_t e = kvq::launch_decode(a, p.total_wgs, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  kvq::CombineArgs cb{};
-  cb.out = out;
-  cb.partials = (const float*)workspace;
-  cb.n_seqs = n_seqs;
-  cb.n_q_heads = c->cfg.n_q_heads;
-  cb.n_kv_heads = c->cfg.n_kv_heads;
-  cb.group = a.group;
-  cb.head_dim = c->cfg.head_dim;
-  cb.max_splits = p.max_splits;
-  for (int i = 0; i < n_seqs; ++i) cb.n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
-  e = kvq::launch_combine(cb, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
-  return KVQ_OK;
+  int n_splits[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
+  return launch_combine_for(c, n_seqs, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
 }
 
 kvq_status kvq_sparse_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                   const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
                                   float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
-  (void)q_bf16; (void)positions; (void)budget; (void)out; (void)softmax_scale; (void)workspace; (void)ws_bytes;
-  (void)stream;
   kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != KVQ_OK) return s;
-  return fail(KVQ_E_INVALID, "sparse decode is not built yet");
+  if (c->cfg.layout != KVQ_LAYOUT_ROWS)
+    return fail(KVQ_E_INVALID, "sparse decode reads whole rows: the cache must use KVQ_LAYOUT_ROWS");
+  if (!q_bf16 || !out || !workspace || !positions) return fail(KVQ_E_INVALID, "q/positions/out/workspace is NULL");
+  if (((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
+  if (((uintptr_t)positions) % 4 != 0) return fail(KVQ_E_INVALID, "positions must be 4-byte aligned");
+  if (budget < 1 || budget > (1 << 28)) return fail(KVQ_E_INVALID, "budget must be in [1, 2^28] (got %d)", budget);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
+  int n_list[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) n_list[i] = budget;
+  return run_gather(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, n_list, out, softmax_scale, workspace,
+                    ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -18,8 +18,9 @@ struct Geometry {
   uint8_t* arena;
   size_t slab_bytes;
   size_t k_body, v_body, k_ring, v_ring, sigma;   // region offsets within a slab
-  int cap32, row_k, row_v, tile_v, ring_row_k, ring_tile_v, ring_slots;
+  int cap32, row_k, row_v, tile_v, ring_row_k, ring_row_v, ring_tile_v, ring_slots;
   int n_kv_heads, head_dim, k_bits, v_bits, kvarn, tail_dtype;
+  int layout;                                      // 0: V tiles, 1: V rows
 };
 
 // ---------------------------------------------------------------- append side
@@ -77,15 +78,23 @@ struct DecodeArgs {
   DecodeSeq seqs[kMaxBatch];
 };
 
-struct SparseArgs {
+// Gather decode over a list of positions of a row-layout cache (sparse decode), or over all positions
+// (dense decode of a row-layout cache: positions == nullptr, entry i is position i).
+struct GatherSeq {
+  size_t slab;
+  int len, body_len;
+  int n_list;        // list entries of this sequence (budget, or len)
+  int n_splits;      // work-groups per KV head
+};
+struct GatherArgs {
   Geometry g;
-  const uint16_t* q;
-  const int32_t* positions;    // [n_seqs][budget]
-  float* out;
-  float* partials;
-  int n_seqs, n_q_heads, group, budget, max_splits, pos_per_split;
+  const uint16_t* q;           // [n_seqs][Hq][D] bf16
+  const int32_t* positions;    // [n_seqs][pos_stride] or nullptr
+  int pos_stride;
+  float* partials;             // [n_seqs][Hkv][max_splits][8 * (D + 2)]
+  int n_seqs, n_q_heads, group, max_splits;
   float scale;
-  DecodeSeq seqs[kMaxBatch];
+  GatherSeq seqs[kMaxBatch];
 };
 
 struct CombineArgs {
@@ -101,7 +110,7 @@ hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s);
 hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_sparse(const SparseArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_E_INVALID, KVQ_E_CAPACITY, KVQ_E_SIZE, KVQ_E_HIP, KVQ_E_STATE = 0, -1, -2, -3, -4, -5
 TAIL_NONE, TAIL_BF16, TAIL_Q8_0 = 0, 1, 2
+LAYOUT_TILES, LAYOUT_ROWS = 0, 1
 REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab": 5}
 MAX_BATCH = 64
 
 _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits",
-           "kvarn", "tail_len", "tail_slack", "tail_dtype")
+           "kvarn", "tail_len", "tail_slack", "tail_dtype", "layout")
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
@@ -76,7 +77,8 @@ def _check(status: int):
 
 
 def make_config(cfg: Dict[str, int]) -> Config:
-    return Config(*[int(cfg[f]) for f in _FIELDS])
+    """kvq_config from a dict; "layout" defaults to LAYOUT_TILES."""
+    return Config(*[int(cfg.get(f, 0) if f == "layout" else cfg[f]) for f in _FIELDS])
 
 
 def config_validate(cfg: Dict[str, int]) -> None:

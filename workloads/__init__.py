@@ -63,6 +63,7 @@ class Workload:
     budget: int = 0           # sparse positions per step (0 = dense decode)
     recent: int = 0           # of the budget, this many newest positions
     capacity: int = 0         # positions per sequence the cache is sized for
+    layout: int = 0           # 0: V tiles (dense decode), 1: rows (sparse decode)
 
     def cache_config(self, capacity: Optional[int] = None) -> dict:
         cap = capacity if capacity is not None else self.capacity
@@ -70,7 +71,7 @@ class Workload:
                     n_q_heads=self.n_q_heads, n_kv_heads=self.n_kv_heads,
                     head_dim=self.head_dim, k_bits=self.k_bits, v_bits=self.v_bits,
                     kvarn=self.kvarn, tail_len=self.tail_len, tail_slack=self.tail_slack,
-                    tail_dtype=self.tail_dtype)
+                    tail_dtype=self.tail_dtype, layout=self.layout)
 
 
 def _round_up(x: int, m: int) -> int:
@@ -101,7 +102,7 @@ def workload(cfg: int, capacity_extra: int = 64) -> Workload:
     if cfg == 5:
         return Workload(5, "sparse q8_0, budget 2048 of ctx 262144, 12 layers", 12, 1, 16, 2, 256, 8, 8, 0,
                         0, 0, 0, [262144], 64, budget=2048, recent=512,
-                        capacity=262144 + capacity_extra)
+                        capacity=262144 + capacity_extra, layout=1)
     raise ValueError(cfg)
 
 
