@@ -1,21 +1,27 @@
 """Decode-attention benchmark of the quantized KV cache on one MI355X.
 
-A step is one pass of the hot path over every layer of the workload: append one token (tail-ring write),
-evict the oldest tail token (requantize into the qN_0 body) and run decode attention over the whole
-cache. Inputs (decode tokens, queries) are resident in HBM before the timed region starts.
+A step is one pass of the hot path over every layer of the workload, with inputs already in HBM:
+per layer, append one token per sequence (tail-ring write), evict the oldest tail token (requantize
+into the qN_0 body) and run decode attention over the whole cache; sparse workloads append and then
+run sparse decode over the step's position list.
 
 Default workload: 16 layers, batch 1, context 65,536, 16 query / 2 KV heads x 256, K 6-bit / V 5-bit
 body with a 2,048-token bf16 precision tail, 64 decode steps (synthetic Gaussian K/V with per-channel
 standard deviations log-uniform in [0.1, 10]).
 
-Prints one JSON line: effective KV GB/s of decode attention over the step (algorithmic KV bytes read by
-the decode calls / step time), attended tokens/s per layer, the roofline of the decode kernel (bytes per
-launch / average launch time from HIP events on the launch stream, against 8 TB/s HBM3E) and the CPU
+Prints one JSON line. `value` is the effective KV GB/s of decode attention over the whole step
+(algorithmic KV bytes read by the decode calls / step time). `roofline` is the decode kernel's rate:
+algorithmic bytes per launch / average kernel time, from HIP events that the kernel dispatches stamp
+with their start and end (library launch timing, measured on a second run of the same number of steps),
+against 8 TB/s HBM3E. `traffic` is the HBM bytes per launch measured with
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by the copy-kernel calibration stored with them),
+used only while the kernel source still matches the one that was measured. `cpu_baseline` is the CPU
 oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (AMD specification)
 BLOCK = 32
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "quantized_decode_attention_append_amd", "csrc", "kvq_decode.hip")
+GATHER_SRC = os.path.join(ROOT, "quantized_decode_attention_append_amd", "csrc", "kvq_gather.hip")
 
 
 def log(msg: str) -> None:
@@ -38,14 +47,18 @@ def row_bytes(n_bits: int, d: int) -> int:
     return d // BLOCK * (4 * n_bits + 2)
 
 
+def ring_row_bytes(cfg: dict) -> int:
+    if cfg["tail_len"] == 0:
+        return 0
+    return 2 * cfg["head_dim"] if cfg["tail_dtype"] == 1 else row_bytes(8, cfg["head_dim"])
+
+
 def decode_call_bytes(cfg: dict, lens, bodies) -> int:
-    """Algorithmic KV bytes one decode call reads: every attended body row and ring row, K and V."""
+    """Algorithmic KV bytes of one dense decode call: every attended body row and ring row, K and V,
+    plus the KVarN scales."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
     body = hk * (row_bytes(cfg["k_bits"], d) + row_bytes(cfg["v_bits"], d))
-    if cfg["tail_len"] > 0:
-        ring = hk * 2 * (2 * d if cfg["tail_dtype"] == 1 else row_bytes(8, d))
-    else:
-        ring = 0
+    ring = hk * 2 * ring_row_bytes(cfg)
     total = 0
     for ln, bl in zip(lens, bodies):
         total += bl * body + (ln - bl) * ring
@@ -54,32 +67,97 @@ def decode_call_bytes(cfg: dict, lens, bodies) -> int:
     return total
 
 
+def sparse_call_bytes(cfg: dict, budget: int, n_seqs: int) -> int:
+    """Algorithmic KV bytes of one sparse decode call over a body-only cache: budget K and V rows."""
+    hk, d = cfg["n_kv_heads"], cfg["head_dim"]
+    return n_seqs * budget * hk * (row_bytes(cfg["k_bits"], d) + row_bytes(cfg["v_bits"], d))
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str, src: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it covers this workload and
+    kernel source; else None."""
+    path = os.path.join(PROFILES, "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            rec = json.loads(line)
+            if rec.get("workload") == workload and rec.get("kernel") == kernel \
+                    and rec.get("source_sha256") == source_digest(src):
+                kib = rec["fetch_kib_per_launch"] * rec["fetch_factor"] + rec["write_kib_per_launch"] * rec["write_factor"]
+                return int(round(kib * 1024))
+    return None
+
+
 def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
-    """The oracle (plain NumPy, fp64 attention) on layer 0 of the workload, single BLAS thread."""
+    """The oracle (plain NumPy, fp64 attention) on layer 0 of the workload, one BLAS thread."""
+    import contextlib
     try:
         from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        threadpool_limits = None
+        limit = contextlib.nullcontext()
     import oracle
     import workloads as W
     cfg1 = dict(wl.cache_config(), n_layers=1, max_seqs=1)
     ctx = wl.contexts[0]
+    if wl.budget:
+        # body-only rows depend on their own token only: a cache holding just the step's listed tokens
+        # attends over the same rows as the full cache
+        t_total, nbytes, steps = 0.0, 0, 0
+        with limit:
+            while t_total < budget_s and steps < wl.decode_steps:
+                n = ctx + steps + 1
+                pos = W.sparse_positions(wl.cfg, 0, 0, steps, n, wl.budget, wl.recent)
+                k = np.zeros((wl.budget, wl.n_kv_heads, wl.head_dim), dtype=np.uint16)
+                v = np.zeros_like(k)
+                chunks = {}
+                for i, p in enumerate(pos):
+                    p = int(p)
+                    if p >= ctx:
+                        kk, vv = W.decode_token(wl.cfg, 0, 0, p - ctx)
+                        k[i], v[i] = kk[0], vv[0]
+                    else:
+                        c0 = (p // W.CHUNK) * W.CHUNK
+                        if c0 not in chunks:
+                            chunks[c0] = W.kv_tokens(wl.cfg, 0, 0, c0, min(W.CHUNK, ctx - c0))
+                        k[i], v[i] = chunks[c0][0][p - c0], chunks[c0][1][p - c0]
+                q = W.query(wl.cfg, 0, 0, steps)[None]
+                cfg_s = dict(cfg1, capacity=wl.budget)
+                t0 = time.perf_counter()
+                o = oracle.OracleCache(cfg_s)
+                o.append(0, [0], [wl.budget], k, v)
+                oracle.decode_reference(o, 0, [0], q)
+                t_total += time.perf_counter() - t0
+                nbytes += sparse_call_bytes(cfg1, wl.budget, 1)
+                steps += 1
+        return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"layer 0: {steps} sparse decode steps over {wl.budget} listed positions (quantize the "
+                          f"listed tokens, fp64 attention), {t_total:.1f} s, one BLAS thread",
+                "tok_per_s_per_layer": round(steps * wl.budget / t_total, 1)}
     log(f"cpu baseline: oracle prefill of {ctx} tokens (not timed)")
     o = oracle.OracleCache(cfg1)
     for s in range(0, ctx, W.CHUNK):
         k, v = W.kv_tokens(wl.cfg, 0, 0, s, min(W.CHUNK, ctx - s))
         o.append(0, [0], [k.shape[0]], k, v)
     o.tail_evict(0, [0])
-    import contextlib
-    limit = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
     t_total, nbytes, steps = 0.0, 0, 0
     with limit:
-        while t_total < budget_s and steps < wl.decode_steps:
-            k, v = W.decode_token(wl.cfg, 0, 0, steps)
+        while t_total < budget_s and steps < max(wl.decode_steps, 1):
             q = W.query(wl.cfg, 0, 0, steps)[None]
             t0 = time.perf_counter()
-            o.append(0, [0], [1], k, v)
-            o.tail_evict(0, [0])
+            if wl.decode_steps:
+                k, v = W.decode_token(wl.cfg, 0, 0, steps)
+                o.append(0, [0], [1], k, v)
+                o.tail_evict(0, [0])
             oracle.decode_reference(o, 0, [0], q)
             t_total += time.perf_counter() - t0
             ln, bl = o.lengths(0, 0)
@@ -87,7 +165,7 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
             steps += 1
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"layer 0 of the workload at context {ctx}: {steps} decode steps (append 1, evict, "
-                      f"fp64 attention over the dequantized cache), {t_total:.1f} s, single BLAS thread",
+                      f"fp64 attention over the dequantized cache), {t_total:.1f} s, one BLAS thread",
             "tok_per_s_per_layer": round(steps * (ctx + steps / 2) / t_total, 1)}
 
 
@@ -96,13 +174,15 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="1: q8_0 4k single layer; 2: K6/V5 + bf16 tail, 64k, 16 layers (default); 3: KVarN "
+                         "K4/V4, 8 streams; 4: K6/V5 + q8_0 ring, 262k; 5: sparse q8_0, budget 2048 of 262k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import torch
@@ -110,16 +190,18 @@ def main() -> int:
     from quantized_decode_attention_append_amd import kvq
 
     wl = W.workload(args.config)
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + 2 * args.steps   # warmup, timed steps, then as many steps with kernel timing
     ctx = list(wl.contexts)
     cfg = wl.cache_config(capacity=((max(ctx) + total_steps + 8 + 31) // 32) * 32)
     L, B = wl.n_layers, wl.batch
+    sparse = wl.budget > 0
+    appends = wl.decode_steps > 0
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}; arena {kvq.cache_bytes(cfg) / 2**30:.2f} GiB")
     cache = kvq.Cache(cfg)
 
-    # ---- prefill (setup, not timed): 4096-token chunks per (layer, sequence), then drain the ring to W
+    # ---- prefill (set-up, not timed): 4096-token chunks per (layer, sequence), then drain the ring to W
     t0 = time.time()
     for layer in range(L):
         for seq in range(B):
@@ -133,22 +215,28 @@ def main() -> int:
             torch.cuda.synchronize()
             log(f"prefill layers 0..{layer} done ({time.time() - t0:.1f} s)")
 
-    # ---- decode inputs resident in HBM before timing
-    kin = np.zeros((total_steps, L, B, 2, 256), dtype=np.uint16)
+    # ---- step inputs resident in HBM before timing
+    kin = np.zeros((total_steps, L, B, wl.n_kv_heads, wl.head_dim), dtype=np.uint16)
     vin = np.zeros_like(kin)
-    qin = np.zeros((total_steps, L, B, wl.n_q_heads, 256), dtype=np.uint16)
+    qin = np.zeros((total_steps, L, B, wl.n_q_heads, wl.head_dim), dtype=np.uint16)
+    pin = np.zeros((total_steps, L, B, max(wl.budget, 1)), dtype=np.int32)
     for st in range(total_steps):
         for layer in range(L):
             for seq in range(B):
-                k, v = W.decode_token(wl.cfg, layer, seq, st)
-                kin[st, layer, seq], vin[st, layer, seq] = k[0], v[0]
+                if appends:
+                    k, v = W.decode_token(wl.cfg, layer, seq, st)
+                    kin[st, layer, seq], vin[st, layer, seq] = k[0], v[0]
                 qin[st, layer, seq] = W.query(wl.cfg, layer, seq, st)
+                if sparse:
+                    pin[st, layer, seq] = W.sparse_positions(wl.cfg, layer, seq, st, ctx[seq] + st + 1,
+                                                             wl.budget, wl.recent)
     kin_d = torch.from_numpy(kin.view(np.int16)).to(dev)
     vin_d = torch.from_numpy(vin.view(np.int16)).to(dev)
     qin_d = torch.from_numpy(qin.view(np.int16)).to(dev)
+    pin_d = torch.from_numpy(pin).to(dev)
     seqs = list(range(B))
-    ws = cache.workspace(B, max(ctx) + total_steps + 1)
-    out = torch.empty((L, B, wl.n_q_heads, 256), dtype=torch.float32, device=dev)
+    ws = cache.workspace(B, max(max(ctx) + total_steps + 1, wl.budget))
+    out = torch.empty((L, B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     ones = [1] * B
 
     if args.copy_calibration_mib:
@@ -160,43 +248,57 @@ def main() -> int:
         log(f"copy calibration: one device copy of {nb} bytes")
         del src, dst
 
-    def step(st, events=None, nbytes=None):
+    def step(st, nbytes=None):
         for layer in range(L):
-            cache.append(layer, seqs, ones, kin_d[st, layer], vin_d[st, layer])
-            cache.tail_evict(layer, seqs)
-            if nbytes is not None:
-                lens = [cache.lengths(layer, s) for s in seqs]
-                nbytes.append(decode_call_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens]))
-            if events is not None:
-                events[layer][0].record()
-            cache.decode_attn(layer, seqs, qin_d[st, layer], out=out[layer], workspace=ws)
-            if events is not None:
-                events[layer][1].record()
+            if appends:
+                cache.append(layer, seqs, ones, kin_d[st, layer], vin_d[st, layer])
+            if sparse:
+                if nbytes is not None:
+                    nbytes.append(sparse_call_bytes(cfg, wl.budget, B))
+                cache.sparse_decode_attn(layer, seqs, qin_d[st, layer], pin_d[st, layer], out=out[layer],
+                                         workspace=ws)
+            else:
+                if appends:
+                    cache.tail_evict(layer, seqs)
+                if nbytes is not None:
+                    lens = [cache.lengths(layer, s) for s in seqs]
+                    nbytes.append(decode_call_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens]))
+                cache.decode_attn(layer, seqs, qin_d[st, layer], out=out[layer], workspace=ws)
 
     for st in range(args.warmup):
         step(st)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
-          for _ in range(args.steps)]
     nbytes = []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, ev[i], nbytes)
+        step(args.warmup + i, nbytes)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    call_ms = [ev[i][layer][0].elapsed_time(ev[i][layer][1]) for i in range(args.steps) for layer in range(L)]
     log(f"timed {args.steps} steps in {elapsed:.3f} s")
+    # kernel durations: the same number of further steps with every launch stamped by its dispatch
+    kbytes = []
+    cache.timing(True)
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, kbytes)
+    torch.cuda.synchronize()
+    times = {k: cache.timing_read(k) for k in ("decode", "gather", "combine", "append", "evict")}
+    cache.timing(False)
 
+    main_kernel = "gather" if (sparse or cfg.get("layout", 0) == 1) else "decode"
+    ms, n = times[main_kernel]
+    avg_s = ms / 1e3 / max(n, 1)
     total_bytes = float(sum(nbytes))
-    ms_per_step = elapsed * 1e3 / args.steps
+    bytes_per_launch = float(sum(kbytes)) / max(len(kbytes), 1)
+    achieved = bytes_per_launch / avg_s / 1e9
     value = total_bytes / elapsed / 1e9
-    avg_call_s = float(np.mean(call_ms)) / 1e3
-    bytes_per_call = total_bytes / len(nbytes)
-    achieved = bytes_per_call / avg_call_s / 1e9
-    attended = sum(cache.lengths(0, s)[0] for s in seqs)
+    ms_per_step = elapsed * 1e3 / args.steps
+    attended = wl.budget * B if sparse else sum(cache.lengths(0, s)[0] for s in seqs)
+    kname = (f"gather_kernel<{wl.k_bits},{wl.v_bits}>" if main_kernel == "gather"
+             else f"decode_kernel<{wl.k_bits},{wl.v_bits}>")
+    traffic = measured_traffic(wl.name, kname, GATHER_SRC if main_kernel == "gather" else DECODE_SRC)
     res = {
         "metric": "decode-attn effective KV GB/s (and % of HBM peak; attended tok/s per layer)",
         "value": round(value, 2),
@@ -210,18 +312,21 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": L, "batch": B,
-                   "context": ctx if B > 1 else ctx[0], "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
-                   "head_dim": wl.head_dim, "k_bits": wl.k_bits, "v_bits": wl.v_bits, "kvarn": wl.kvarn,
-                   "tail": wl.tail_len, "tail_dtype": ["none", "bf16", "q8_0"][wl.tail_dtype],
-                   "step": "per layer: append 1 token, evict 1 tail token, decode attention"},
+        "config": {"workload": wl.name, "layers": L, "batch": B, "context": ctx if B > 1 else ctx[0],
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "k_bits": wl.k_bits, "v_bits": wl.v_bits, "kvarn": wl.kvarn, "tail": wl.tail_len,
+                   "tail_dtype": ["none", "bf16", "q8_0"][wl.tail_dtype], "budget": wl.budget,
+                   "layout": ["tiles", "rows"][cfg.get("layout", 0)],
+                   "step": ("per layer: append 1 token, sparse decode over the step's position list" if sparse
+                            else "per layer: append 1 token, evict 1 tail token, decode attention" if appends
+                            else "per layer: decode attention")},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attended_tok_per_s_per_layer": round(attended * args.steps / elapsed, 1),
-        "decode_call_us": round(avg_call_s * 1e6, 3),
+        "kernel_us": {k: round(v[0] * 1e3 / v[1], 3) for k, v in times.items() if v[1]},
+        "launches": {k: v[1] for k, v in times.items() if v[1]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel (one launch per decode call)",
-                     "bytes_per_launch": int(bytes_per_call)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": kname, "bytes_per_launch": int(bytes_per_launch)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -154,6 +154,26 @@ kvq_status kvq_sparse_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seq
                                   const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
                                   float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
 
+/* Kernel kinds for launch timing. */
+typedef enum {
+  KVQ_KERNEL_DECODE = 0,   /* split kernel of dense decode (tile layout)                      */
+  KVQ_KERNEL_GATHER = 1,   /* gather kernel of sparse decode / dense decode of a row layout     */
+  KVQ_KERNEL_COMBINE = 2,  /* merge of the split partials                                      */
+  KVQ_KERNEL_APPEND = 3,   /* append kernels (calibration, body and ring writes)               */
+  KVQ_KERNEL_EVICT = 4,    /* tail-evict requantization                                         */
+  KVQ_KERNEL_COUNT = 5
+} kvq_kernel;
+
+/* Launch timing, for measuring kernels against the memory roofline. While enabled, every launch the
+ * handle makes carries a pair of HIP events that the dispatch itself stamps with the kernel's start and
+ * end time (hipExtLaunchKernel; host-side objects, no device memory). Enabling or disabling drops earlier
+ * records. At most 65,536 launches per kind are recorded; later ones run untimed. */
+kvq_status kvq_timing_enable(kvq_cache* cache, int32_t enable);
+
+/* Sum of the recorded launch durations of one kernel kind, in ms, and the number of launches. Waits for
+ * the recorded events to complete. */
+kvq_status kvq_timing_read(kvq_cache* cache, int32_t kernel, double* total_ms, int32_t* launches);
+
 /* Thread-local text of the last error (never NULL). */
 const char* kvq_last_error(void);
 

@@ -348,19 +348,16 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16) {
 
 }  // namespace
 
-hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s) {
-  hipLaunchKernelGGL(calibrate_kernel, dim3(n_items, a.g.n_kv_heads, 2), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(calibrate_kernel, dim3(n_items, a.g.n_kv_heads, 2), dim3(256), s, e0, e1, a);
 }
 
-hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s) {
-  hipLaunchKernelGGL(body_write_kernel, dim3(n_wgs, a.g.n_kv_heads), dim3(512), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(body_write_kernel, dim3(n_wgs, a.g.n_kv_heads), dim3(512), s, e0, e1, a);
 }
 
-hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s) {
-  hipLaunchKernelGGL(bf16_ring_write_kernel, dim3(n_wgs, a.g.n_kv_heads), dim3(512), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(bf16_ring_write_kernel, dim3(n_wgs, a.g.n_kv_heads), dim3(512), s, e0, e1, a);
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

@@ -765,16 +765,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 template <int NK, int NV>
-hipError_t launch_decode_t(const DecodeArgs& a, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<NK, NV>), dim3(grid_x), dim3(512), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_decode_t(const DecodeArgs& a, int grid_x, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(decode_kernel<NK, NV>, dim3(grid_x), dim3(512), s, e0, e1, a);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int nk = a.g.k_bits, nv = a.g.v_bits;
-#define KVQ_CASE(K, V) if (nk == K && nv == V) return launch_decode_t<K, V>(a, grid_x, s);
+#define KVQ_CASE(K, V) if (nk == K && nv == V) return launch_decode_t<K, V>(a, grid_x, s, e0, e1);
 #define KVQ_ROW(K) KVQ_CASE(K, 2) KVQ_CASE(K, 3) KVQ_CASE(K, 4) KVQ_CASE(K, 5) KVQ_CASE(K, 6) KVQ_CASE(K, 7) KVQ_CASE(K, 8)
   KVQ_ROW(2) KVQ_ROW(3) KVQ_ROW(4) KVQ_ROW(5) KVQ_ROW(6) KVQ_ROW(7) KVQ_ROW(8)
 #undef KVQ_ROW
@@ -783,9 +782,8 @@ hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s) {
 }
 
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.n_seqs * a.n_kv_heads, a.group, a.head_dim / 16), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(combine_kernel, dim3(a.n_seqs * a.n_kv_heads, a.group, a.head_dim / 16), dim3(256), s, e0, e1, a);
 }
 
 

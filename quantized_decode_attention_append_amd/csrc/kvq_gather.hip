@@ -395,16 +395,15 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 }
 
 template <int NK, int NV>
-hipError_t launch_gather_t(const GatherArgs& a, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL((gather_kernel<NK, NV>), dim3(grid_x), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_gather_t(const GatherArgs& a, int grid_x, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(gather_kernel<NK, NV>, dim3(grid_x), dim3(256), s, e0, e1, a);
 }
 
 }  // namespace
 
-hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s) {
+hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int nk = a.g.k_bits, nv = a.g.v_bits;
-#define KVQ_CASE(K, V) if (nk == K && nv == V) return launch_gather_t<K, V>(a, grid_x, s);
+#define KVQ_CASE(K, V) if (nk == K && nv == V) return launch_gather_t<K, V>(a, grid_x, s, e0, e1);
 #define KVQ_ROW(K) KVQ_CASE(K, 2) KVQ_CASE(K, 3) KVQ_CASE(K, 4) KVQ_CASE(K, 5) KVQ_CASE(K, 6) KVQ_CASE(K, 7) KVQ_CASE(K, 8)
   KVQ_ROW(2) KVQ_ROW(3) KVQ_ROW(4) KVQ_ROW(5) KVQ_ROW(6) KVQ_ROW(7) KVQ_ROW(8)
 #undef KVQ_ROW

@@ -16,8 +16,16 @@
 
 using kvq::SlabLayout;
 
+// Per-kernel launch timing (kvq_timing_enable): HIP event pairs recorded on the launch stream around
+// each launch, read back by kvq_timing_read.
+struct KernelTimes {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> used, spare;
+};
+
 struct kvq_cache {
   kvq_config cfg;
+  bool timing = false;
+  KernelTimes times[KVQ_KERNEL_COUNT];
   SlabLayout lay;
   uint8_t* arena;
   size_t arena_bytes;
@@ -25,6 +33,12 @@ struct kvq_cache {
   std::vector<uint8_t> calibrated;
   int n_cu = 256;            // compute units of the device (split planning)
   int idx(int layer, int seq) const { return layer * cfg.max_seqs + seq; }
+  ~kvq_cache() {
+    for (auto& t : times) {
+      for (auto& e : t.used) { (void)hipEventDestroy(e.first); (void)hipEventDestroy(e.second); }
+      for (auto& e : t.spare) { (void)hipEventDestroy(e.first); (void)hipEventDestroy(e.second); }
+    }
+  }
 };
 
 namespace {
@@ -44,6 +58,31 @@ kvq_status fail(kvq_status s, const char* fmt, ...) {
 
 kvq_status hip_fail(hipError_t e, const char* what) {
   return fail(KVQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kMaxTimedLaunches = 1 << 16;   // per kernel kind between two kvq_timing_enable calls
+
+// Run `launch(e0, e1)`; with timing on, e0 / e1 are events that the launch fills with the kernel's start
+// and end time (null otherwise).
+template <typename F>
+hipError_t timed(kvq_cache* c, int kind, hipStream_t stream, F launch) {
+  (void)stream;
+  if (!c->timing || c->times[kind].used.size() >= kMaxTimedLaunches) return launch(nullptr, nullptr);
+  KernelTimes& t = c->times[kind];
+  std::pair<hipEvent_t, hipEvent_t> ev;
+  if (!t.spare.empty()) {
+    ev = t.spare.back();
+    t.spare.pop_back();
+  } else {
+    hipError_t e = hipEventCreate(&ev.first);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&ev.second);
+    if (e != hipSuccess) { (void)hipEventDestroy(ev.first); return e; }
+  }
+  hipError_t e = launch(ev.first, ev.second);
+  if (e == hipSuccess) t.used.push_back(ev);
+  else t.spare.push_back(ev);
+  return e;
 }
 
 SlabLayout layout_of(const kvq_config& c) {
@@ -216,7 +255,7 @@ kvq_status launch_combine_for(kvq_cache* c, int n_seqs, const int* n_splits, int
   cb.head_dim = c->cfg.head_dim;
   cb.max_splits = max_splits;
   for (int i = 0; i < n_seqs; ++i) cb.n_splits[i] = n_splits[i];
-  hipError_t e = kvq::launch_combine(cb, stream);
+  hipError_t e = timed(c, KVQ_KERNEL_COMBINE, stream, [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_combine(cb, stream, e0, e1); });
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return KVQ_OK;
 }
@@ -250,7 +289,8 @@ kvq_status run_gather(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
   a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
   a.max_splits = max_splits;
   a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
-  hipError_t e = kvq::launch_gather(a, total_wgs, (hipStream_t)stream);
+  hipError_t e = timed(c, KVQ_KERNEL_GATHER, (hipStream_t)stream,
+                       [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_gather(a, total_wgs, (hipStream_t)stream, e0, e1); });
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   return launch_combine_for(c, n_seqs, n_splits, max_splits, out, workspace, (hipStream_t)stream);
 }
@@ -260,6 +300,34 @@ kvq_status run_gather(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
 extern "C" {
 
 const char* kvq_last_error(void) { return g_err.c_str(); }
+
+kvq_status kvq_timing_enable(kvq_cache* c, int32_t enable) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (enable != 0 && enable != 1) return fail(KVQ_E_INVALID, "enable must be 0 or 1");
+  for (auto& t : c->times) {   // records of earlier launches are dropped (their events are reused)
+    t.spare.insert(t.spare.end(), t.used.begin(), t.used.end());
+    t.used.clear();
+  }
+  c->timing = enable != 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_timing_read(kvq_cache* c, int32_t kernel, double* total_ms, int32_t* launches) {
+  if (!c || !total_ms || !launches) return fail(KVQ_E_INVALID, "cache/total_ms/launches is NULL");
+  if (kernel < 0 || kernel >= KVQ_KERNEL_COUNT) return fail(KVQ_E_INVALID, "unknown kernel kind %d", kernel);
+  double sum = 0.0;
+  for (const auto& ev : c->times[kernel].used) {
+    hipError_t e = hipEventSynchronize(ev.second);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, ev.first, ev.second);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int32_t)c->times[kernel].used.size();
+  return KVQ_OK;
+}
 
 kvq_status kvq_config_validate(const kvq_config* cfg) { return validate(cfg); }
 
@@ -446,20 +514,22 @@ kvq_status kvq_append(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
 
   hipError_t e;
   if (ca.n_items) {
-    e = kvq::launch_calibrate(ca, ca.n_items, st);
+    e = timed(c, KVQ_KERNEL_APPEND, st, [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_calibrate(ca, ca.n_items, st, e0, e1); });
     if (e != hipSuccess) return hip_fail(e, "calibrate launch");
   }
   if (body_wgs) {
-    e = kvq::launch_body_write(body, body_wgs, st);
+    e = timed(c, KVQ_KERNEL_APPEND, st, [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_body_write(body, body_wgs, st, e0, e1); });
     if (e != hipSuccess) return hip_fail(e, "body write launch");
   }
   if (ring_wgs) {
-    e = (c->cfg.tail_dtype == KVQ_TAIL_BF16) ? kvq::launch_bf16_ring_write(ring, ring_wgs, st)
-                                             : kvq::launch_body_write(ring, ring_wgs, st);
+    e = timed(c, KVQ_KERNEL_APPEND, st, [&](hipEvent_t e0, hipEvent_t e1) {
+      return (c->cfg.tail_dtype == KVQ_TAIL_BF16) ? kvq::launch_bf16_ring_write(ring, ring_wgs, st, e0, e1)
+                                                  : kvq::launch_body_write(ring, ring_wgs, st, e0, e1);
+    });
     if (e != hipSuccess) return hip_fail(e, "ring write launch");
   }
   if (ring2_wgs) {
-    e = kvq::launch_body_write(ring2, ring2_wgs, st);
+    e = timed(c, KVQ_KERNEL_APPEND, st, [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_body_write(ring2, ring2_wgs, st, e0, e1); });
     if (e != hipSuccess) return hip_fail(e, "ring write launch");
   }
   for (int i = 0; i < n_seqs; ++i) {
@@ -492,7 +562,8 @@ kvq_status kvq_tail_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const int
     }
   }
   if (wgs) {
-    hipError_t e = kvq::launch_body_write(body, wgs, (hipStream_t)stream);
+    hipError_t e = timed(c, KVQ_KERNEL_EVICT, (hipStream_t)stream,
+                         [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_body_write(body, wgs, (hipStream_t)stream, e0, e1); });
     if (e != hipSuccess) return hip_fail(e, "evict launch");
   }
   for (int i = 0; i < n_seqs; ++i) c->body_len[c->idx(layer, seq_ids[i])] = target[i];
@@ -531,7 +602,8 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
   a.max_splits = p.max_splits;
   a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
-  hipError_t e = kvq::launch_decode(a, p.total_wgs, (hipStream_t)stream);
+  hipError_t e = timed(c, KVQ_KERNEL_DECODE, (hipStream_t)stream,
+                       [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_decode(a, p.total_wgs, (hipStream_t)stream, e0, e1); });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   int n_splits[KVQ_MAX_BATCH];
   for (int i = 0; i < n_seqs; ++i) n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;

@@ -1,6 +1,7 @@
 // Kernel argument blocks and launch wrappers shared by the kvq host code and its kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -104,13 +105,27 @@ struct CombineArgs {
   int n_splits[kMaxBatch];
 };
 
-// Launch wrappers (return the launch status).
-hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s);
-hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s);
-hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s);
+// Launch wrappers (return the launch status). With non-null events e0 / e1 the launch records the kernel's
+// start and end time in them (hipExtLaunchKernel: timestamps of the dispatch itself).
+hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s, hipEvent_t e0 = nullptr,
+                            hipEvent_t e1 = nullptr);
+hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0 = nullptr,
+                             hipEvent_t e1 = nullptr);
+hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0 = nullptr,
+                                  hipEvent_t e1 = nullptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s, hipEvent_t e0 = nullptr,
+                         hipEvent_t e1 = nullptr);
+hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s, hipEvent_t e0 = nullptr,
+                         hipEvent_t e1 = nullptr);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+
+// Plain or timed launch of a kernel with one by-value argument block.
+template <typename K, typename A>
+inline hipError_t launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const A& a) {
+  if (e0) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, a);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace kvq

@@ -26,7 +26,8 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_decode_attn", "kvq_sparse_decode_attn", "kvq_last_error")
+           "kvq_decode_attn", "kvq_sparse_decode_attn", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4}
 
 
 class Config(ctypes.Structure):
@@ -59,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "kvq_tail_evict": (I32, [P, I32, I32, IP, P]),
         "kvq_decode_attn": (I32, [P, I32, I32, IP, P, P, F, P, SZ, P]),
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
+        "kvq_timing_enable": (I32, [P, I32]),
+        "kvq_timing_read": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), IP]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -166,6 +169,17 @@ class Cache:
             ws = torch.empty(n, dtype=torch.uint8, device="cuda")
             self._ws = ws
         return ws
+
+    # ---------------------------------------------------------------- launch timing
+    def timing(self, enable: bool = True):
+        """Bracket every launch of this cache with HIP events on its stream (drops earlier records)."""
+        _check(_lib.kvq_timing_enable(self._h, 1 if enable else 0))
+
+    def timing_read(self, kernel: str):
+        """(total ms, launches) recorded for a kernel kind: decode, gather, combine, append, evict."""
+        ms, n = ctypes.c_double(), ctypes.c_int32()
+        _check(_lib.kvq_timing_read(self._h, KERNEL[kernel], ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     # ---------------------------------------------------------------- the calls
     def append(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor,
