@@ -298,6 +298,18 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
     }
     if (plane_ok) vplane_off += 64 * NT * wdt;
   }
+  if (!a.dst_ring) {
+    // Body positions are written once after the slab was zeroed, so their bits in a shared word are still
+    // zero: OR them in without reading the word first.
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k)
+      if (use[k] && mask[k]) {
+        if (mask[k] == 0xFFFFFFFFu) *dst[k] = bits[k];
+        else atomicOr(dst[k], bits[k]);
+      }
+    return;
+  }
+  // ring slots are reused: read-modify-write
   uint32_t old[kSlots];
 #pragma unroll
   for (int k = 0; k < kSlots; ++k) old[k] = (use[k] && mask[k] != 0xFFFFFFFFu) ? *dst[k] : 0u;

@@ -712,55 +712,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ------------------------------------------------------------------ merge of the split partials
 
-// One work-group per (sequence, KV head, query head, 16-channel chunk): 16 groups of 16 threads each sum
-// a strided share of the splits for the 16 channels, then the groups are added. Log-sum-exp:
-// out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s with M = max_s m_s (exp2 domain).
+// One work-group per (sequence, KV head, query head, 16-channel chunk): 16 groups of 16 threads each fold a
+// strided share of the splits into a running (max, sum, output) in one pass (online log-sum-exp, exp2
+// domain), then the 16 groups are merged: out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int D = 256;
   constexpr size_t rec = kPartialHeads * (D + 2);
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_acc[16][17];
-  __shared__ float s_red[2][4];
+  __shared__ float s_m[16], s_l[16], s_o[16][17];
   const int si = blockIdx.x / a.n_kv_heads;
   const int head = blockIdx.x % a.n_kv_heads;
   const int h = blockIdx.y;
-  const int c0 = blockIdx.z * 16;
   const int tid = threadIdx.x;
+  const int c = blockIdx.z * 16 + (tid & 15);
+  const int grp = tid >> 4;
   const int ns = a.n_splits[si];
   const float* base = a.partials + ((size_t)si * a.n_kv_heads + head) * a.max_splits * rec;
-  float mx = kNegBig;
-  for (int sp = tid; sp < ns; sp += 256) {
-    const float m = base[sp * rec + h];
-    s_w[sp] = m;
-    mx = fmaxf(mx, m);
-  }
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if ((tid & 63) == 0) s_red[0][tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-  float lsum = 0.0f;
-  for (int sp = tid; sp < ns; sp += 256) {
-    const float w = __builtin_amdgcn_exp2f(s_w[sp] - M);
-    s_w[sp] = w;
-    lsum += w * base[sp * rec + kPartialHeads + h];
-  }
-  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
-  if ((tid & 63) == 0) s_red[1][tid >> 6] = lsum;
-  __syncthreads();
-  const float L = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-  const int c = c0 + (tid & 15);
-  const int grp = tid >> 4;
-  const float* po = base + 2 * kPartialHeads + h * D + c;
-  float acc = 0.0f;
+  float M = kNegBig, L = 0.0f, O = 0.0f;
 #pragma unroll 4
-  for (int sp = grp; sp < ns; sp += 16) acc += s_w[sp] * po[sp * rec];
-  s_acc[grp][tid & 15] = acc;
+  for (int sp = grp; sp < ns; sp += 16) {
+    const float* pr = base + sp * rec;
+    const float m = pr[h], l = pr[kPartialHeads + h], o = pr[2 * kPartialHeads + h * D + c];
+    const float mn = fmaxf(M, m);
+    const float fa = __builtin_amdgcn_exp2f(M - mn), fb = __builtin_amdgcn_exp2f(m - mn);
+    L = L * fa + l * fb;
+    O = O * fa + o * fb;
+    M = mn;
+  }
+  if ((tid & 15) == 0) {
+    s_m[grp] = M;
+    s_l[grp] = L;
+  }
+  s_o[grp][tid & 15] = O;
   __syncthreads();
   if (tid < 16) {
-    float o = 0.0f;
+    float Mx = kNegBig;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o += s_acc[k][tid];
-    a.out[((size_t)si * a.n_q_heads + head * a.group + h) * D + c] = L > 0.0f ? o / L : 0.0f;
+    for (int k = 0; k < 16; ++k) Mx = fmaxf(Mx, s_m[k]);
+    float Ls = 0.0f, Os = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float f = __builtin_amdgcn_exp2f(s_m[k] - Mx);
+      Ls += s_l[k] * f;
+      Os += s_o[k][tid] * f;
+    }
+    a.out[((size_t)si * a.n_q_heads + head * a.group + h) * D + blockIdx.z * 16 + tid] = Ls > 0.0f ? Os / Ls : 0.0f;
   }
 }
 
