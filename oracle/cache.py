@@ -27,7 +27,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layout import (pack_k_rows, pack_v_tiles, pack_bf16_v_tiles, slab_layout, TILE)
+from .layout import (pack_k_rows, pack_k_tiles, pack_bf16_k_tiles, pack_v_tiles, pack_bf16_v_tiles,
+                     slab_layout, TILE)
 from .quant import quantize_blocks, kvarn_sigma, normalize, dequantize_blocks
 
 TAIL_NONE, TAIL_BF16, TAIL_Q8 = 0, 1, 2
@@ -210,11 +211,19 @@ class OracleCache:
     def region_bytes(self, layer: int, seq: int, region: str, head: int, lo: int, hi: int) -> np.ndarray:
         """Packed bytes of one head's region for positions / slots [lo, hi).
 
-        k_body / k_ring: rows lo..hi-1; v_body / v_ring: tiles lo//32 .. hi//32 - 1
-        (lo, hi multiples of 32), or rows lo..hi-1 in the row layout; sigma: the [2, D]
-        fp16 block of the head."""
+        Tile layout: tiles lo//32 .. hi//32 - 1 (lo, hi multiples of 32) of every region;
+        row layout: rows lo..hi-1. sigma: the [2, D] fp16 block of the head."""
         s = self.st(layer, seq)
         kb, vb = self.cfg["k_bits"], self.cfg["v_bits"]
+        d = self.cfg["head_dim"]
+        if region == "k_body" and not self.rows:
+            assert lo % TILE == 0 and hi % TILE == 0
+            return pack_k_tiles(s.ku[lo:hi, head].reshape(-1, TILE, d), s.kd[lo:hi, head].reshape(-1, TILE, d // 32), kb)
+        if region == "k_ring" and not self.rows:
+            assert lo % TILE == 0 and hi % TILE == 0
+            if self.tail == TAIL_BF16:
+                return pack_bf16_k_tiles(s.rk[lo:hi, head].reshape(-1, TILE, d))
+            return pack_k_tiles(s.rku[lo:hi, head].reshape(-1, TILE, d), s.rkd[lo:hi, head].reshape(-1, TILE, d // 32), 8)
         if region == "k_body":
             return pack_k_rows(s.ku[lo:hi, head], s.kd[lo:hi, head], kb)
         if region == "v_body" and self.rows:

@@ -20,26 +20,37 @@ group j in 0..3 and block b, piece (j, b) holds channels 32*b + 8*j + i. A row i
 for each plane: for j = 0..3 the pieces b = 0..NB-1; then the NB fp16 block
 scales in block order. Row bytes = NB * (4N + 2).
 
+K tiles (tile layout; body and q8_0 ring): the K rows of 32 consecutive positions of
+one KV head, rearranged so that a wave reads them with 1 KiB contiguous loads. For
+subtile s in 0..1 (positions 16s..16s+15) and each plane, lane l = 16j + m (row
+16s + m, lane group j) holds the row's bytes of that plane for lane group j (the
+NB pieces (j, b), NB * w bytes); lanes are interleaved in units of
+min(16, NB * w) bytes: [chunk][lane][unit]. Subtile s, plane p starts at byte
+512 * (N * s + sum of the widths before p). Then the NB x 32 fp16 scales,
+[block][position]. Tile bytes = 32 * NB * (4N + 2).
+
 V tiles (body, and the q8_0 ring): 32 consecutive positions of one KV head. For
 lane l in 0..63 (d16 = l % 16, j = l // 16) and n-tile n in 0..D/16-1, piece
 (l, n) holds channel 16*n + d16 at tile positions T(j, i) = 4j + i (i < 4) and
 16 + 4j + (i - 4) (i >= 4). For each plane, lane l's bytes are its pieces for
 n = 0..NT-1 (NT * w bytes); they are interleaved across lanes in units of
-u = min(16, NT * w) bytes: [chunk][lane][u]. Then the 32 x NB fp16 scales,
-[position][block]. Tile bytes = 32 * NB * (4N + 2).
+u = min(16, NT * w) bytes: [chunk][lane][u]. Then the NB x 32 fp16 scales,
+[block][position]. Tile bytes = 32 * NB * (4N + 2).
 
-bf16 tail ring: K rows are the D bf16 values in channel order; V tiles of 32
-slots hold, for n-tile n and lane l, the 8 bf16 values of channel 16*n + d16 at
-tile positions T(j, i): [n][lane][8 x bf16].
+bf16 tail ring (tile layout): K tiles of 32 slots hold, for subtile s and block b,
+lane l = 16j + m's 8 bf16 values of channels 32b + 8j .. +7 of slot 16s + m:
+[s][b][lane][8 x bf16]; V tiles hold, for n-tile n and lane l, the 8 bf16 values
+of channel 16*n + d16 at tile positions T(j, i): [n][lane][8 x bf16].
 
 Row layout (a cache option for sparse layers): V is stored exactly like K, one
-row per position (body and q8_0 ring: the K row format above; bf16 ring: the D
-bf16 values), so a position is one contiguous K row and one V row. The region
-sizes equal those of the tile layout.
+row per position, and K stays in rows (body and q8_0 ring: the K row format
+above; bf16 ring: the D bf16 values), so a position is one contiguous K row and
+one V row. The region sizes equal those of the tile layout.
 
 Arena: slabs of [layer][sequence]; each slab holds, in order and 256-byte
-aligned: K body [head][capacity32][row], V body [head][capacity32/32][tile],
-K ring [head][R][row], V ring [head][R/32][tile], KVarN sigma [head][K,V][D] fp16.
+aligned: K body [head][capacity32/32][tile], V body [head][capacity32/32][tile],
+K ring [head][R/32][tile], V ring [head][R/32][tile] (row layout: [head][.][row]
+for K, and for V as well), KVarN sigma [head][K,V][D] fp16.
 capacity32 is the capacity rounded up to 32; R = W + S (ring slots).
 """
 from __future__ import annotations
@@ -145,6 +156,79 @@ def unpack_k_rows(rows: np.ndarray, n_bits: int, head_dim: int):
     return u, d16
 
 
+# ----------------------------------------------------------------------------- K tiles
+
+def _k_tile_parts(n_bits: int, head_dim: int):
+    """[(subtile, row byte offset of the plane, lane run bytes NB * w)] in tile order."""
+    nb = head_dim // BLOCK
+    parts = []
+    for s in range(2):
+        off = 0
+        for w, _ in planes(n_bits):
+            parts.append((s, off, nb * w))
+            off += 4 * nb * w
+    return parts
+
+
+def pack_k_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
+    """Codes u [n_tiles, 32, D] and scales [n_tiles, 32, D/32] -> K tiles [n_tiles, tile_bytes]."""
+    u = np.asarray(u, dtype=np.uint8)
+    ntl, tt, d = u.shape
+    assert tt == TILE
+    nb = d // BLOCK
+    rows = pack_k_rows(u, d16, n_bits)                       # [ntl, 32, row_bytes]
+    out = []
+    for s, off, lb in _k_tile_parts(n_bits, d):
+        sub = rows[:, 16 * s:16 * s + 16, :]                 # [ntl, m, row]
+        # lane l = 16 j + m takes row m's run of lane group j: bytes off + j*lb .. + lb
+        runs = np.stack([sub[:, :, off + j * lb: off + (j + 1) * lb] for j in range(4)], axis=1)  # [ntl, j, m, lb]
+        runs = runs.reshape(ntl, 64, lb)
+        cu = min(16, lb)
+        out.append(runs.reshape(ntl, 64, lb // cu, cu).transpose(0, 2, 1, 3).reshape(ntl, 64 * lb))
+    sc = np.ascontiguousarray(np.asarray(d16, dtype=np.float16).transpose(0, 2, 1))   # [ntl, b, t]
+    out.append(sc.view(np.uint8).reshape(ntl, 2 * nb * TILE))
+    return np.concatenate(out, axis=-1)
+
+
+def unpack_k_tiles(tiles: np.ndarray, n_bits: int, head_dim: int):
+    """K tiles [n_tiles, tile_bytes] -> (u [n_tiles, 32, D], d16 [n_tiles, 32, D/32])."""
+    tiles = np.asarray(tiles, dtype=np.uint8)
+    ntl = tiles.shape[0]
+    nb = head_dim // BLOCK
+    rb = row_bytes(n_bits, head_dim)
+    rows = np.zeros((ntl, TILE, rb), dtype=np.uint8)
+    pos = 0
+    for s, off, lb in _k_tile_parts(n_bits, head_dim):
+        cu = min(16, lb)
+        x = tiles[:, pos:pos + 64 * lb].reshape(ntl, lb // cu, 64, cu).transpose(0, 2, 1, 3).reshape(ntl, 4, 16, lb)
+        for j in range(4):
+            rows[:, 16 * s:16 * s + 16, off + j * lb: off + (j + 1) * lb] = x[:, j]
+        pos += 64 * lb
+    d16 = np.ascontiguousarray(tiles[:, pos:pos + 2 * nb * TILE]).view(np.float16).reshape(ntl, nb, TILE)
+    d16 = np.ascontiguousarray(d16.transpose(0, 2, 1))
+    rows[:, :, 4 * nb * n_bits:] = np.ascontiguousarray(d16).view(np.uint8).reshape(ntl, TILE, 2 * nb)
+    u, _ = unpack_k_rows(rows, n_bits, head_dim)
+    return u, d16
+
+
+def pack_bf16_k_tiles(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits [n_tiles, 32, D] -> bf16 ring K tiles [n_tiles, 64 * D] bytes ([s][b][lane][8])."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    ntl, _, d = bits.shape
+    nb = d // BLOCK
+    x = bits.reshape(ntl, 2, 16, nb, 4, 8)                   # [ntl, s, m, b, j, i]
+    x = x.transpose(0, 1, 3, 4, 2, 5)                        # [ntl, s, b, j, m, i] -> lane = 16 j + m
+    return np.ascontiguousarray(x).view(np.uint8).reshape(ntl, -1)
+
+
+def unpack_bf16_k_tiles(tiles: np.ndarray, head_dim: int) -> np.ndarray:
+    tiles = np.ascontiguousarray(tiles, dtype=np.uint8)
+    ntl = tiles.shape[0]
+    nb = head_dim // BLOCK
+    x = tiles.view(np.uint16).reshape(ntl, 2, nb, 4, 16, 8).transpose(0, 1, 4, 2, 3, 5)
+    return np.ascontiguousarray(x).reshape(ntl, TILE, head_dim)
+
+
 # ----------------------------------------------------------------------------- V tiles
 
 def _v_gather_index(head_dim: int):
@@ -172,7 +256,8 @@ def pack_v_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
         cu = min(16, lb)
         x = lane_bytes.reshape(ntl, 64, lb // cu, cu).transpose(0, 2, 1, 3)
         parts.append(x.reshape(ntl, 64 * lb))
-    parts.append(np.ascontiguousarray(np.asarray(d16, dtype=np.float16)).view(np.uint8).reshape(ntl, -1))
+    sc = np.ascontiguousarray(np.asarray(d16, dtype=np.float16).transpose(0, 2, 1))   # [ntl, b, t]
+    parts.append(sc.view(np.uint8).reshape(ntl, -1))
     return np.concatenate(parts, axis=-1)
 
 
@@ -194,8 +279,8 @@ def unpack_v_tiles(tiles: np.ndarray, n_bits: int, head_dim: int):
     t_idx, d_idx = _v_gather_index(head_dim)
     u = np.zeros((ntl, TILE, head_dim), dtype=np.uint8)
     u[:, t_idx, d_idx] = g
-    d16 = np.ascontiguousarray(tiles[:, off:off + TILE * nb * 2]).view(np.float16).reshape(ntl, TILE, nb)
-    return u, d16
+    d16 = np.ascontiguousarray(tiles[:, off:off + TILE * nb * 2]).view(np.float16).reshape(ntl, nb, TILE)
+    return u, np.ascontiguousarray(d16.transpose(0, 2, 1))
 
 
 def pack_bf16_v_tiles(bits: np.ndarray) -> np.ndarray:

@@ -104,21 +104,32 @@ __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int k
   const int t = slot % kTile;
   const int lane = 16 * ((t % 16) / 4) + (c % 16);
   const int e = (t % 4) + 4 * (t / 16);
+  const int b = c / kBlock;
+  const int j = (c % kBlock) / 8;
+  const int klane = 16 * j + (t % 16);   // K tile lane of (slot, channel)
+  const size_t rt = (size_t)head * (R / kTile) + slot / kTile;   // ring tile (tile layout)
   if (g.tail_dtype == 1) {
-    if (kv == 0 || g.layout == 1)
+    if (g.layout == 1)
       return bf16_to_f32(((const uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c]);
-    const uint8_t* tile = slab + g.v_ring + ((size_t)head * (R / kTile) + slot / kTile) * g.ring_tile_v;
+    if (kv == 0) {
+      const uint16_t* kt = (const uint16_t*)(slab + g.k_ring + rt * g.ring_tile_k);
+      return bf16_to_f32(kt[(((t / 16) * NB + b) * 64 + klane) * 8 + (c % 8)]);
+    }
+    const uint8_t* tile = slab + g.v_ring + rt * g.ring_tile_v;
     return bf16_to_f32(*((const uint16_t*)(tile + (size_t)(c / 16) * 64 * 16 + lane * 16) + e));
   }
-  const int b = c / kBlock;
-  if (kv == 0 || g.layout == 1) {
+  if (g.layout == 1) {
     const uint8_t* row = slab + (kv ? g.v_ring : g.k_ring) + ((size_t)head * R + slot) * g.ring_row_k;
-    const int j = (c % kBlock) / 8;
     const float dh = f16_to_f32(((const uint16_t*)(row + NB * 32))[b]);
     return (float)((int)row[(j * NB + b) * 8 + (c % 8)] - 128) * dh;
   }
-  const uint8_t* tile = slab + g.v_ring + ((size_t)head * (R / kTile) + slot / kTile) * g.ring_tile_v;
-  const float dh = f16_to_f32(((const uint16_t*)(tile + 32 * D))[t * NB + b]);
+  if (kv == 0) {
+    const uint8_t* kt = slab + g.k_ring + rt * g.ring_tile_k;
+    const float dh = f16_to_f32(((const uint16_t*)(kt + 32 * D))[b * kTile + t]);
+    return (float)((int)kt[512 * 8 * (t / 16) + lane_run_byte(klane, NB * 8 * 0 + 8 * b + (c % 8), NB * 8)] - 128) * dh;
+  }
+  const uint8_t* tile = slab + g.v_ring + rt * g.ring_tile_v;
+  const float dh = f16_to_f32(((const uint16_t*)(tile + 32 * D))[b * kTile + t]);
   return (float)((int)tile[vtile_lane_byte(lane, (c / 16) * 8 + e, NT, 8)] - 128) * dh;
 }
 
@@ -144,16 +155,20 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
   uint8_t* kbase;
   uint8_t* vbase;   // row layout: V rows of this head
   uint8_t* vtile;   // tile layout: this work-group's V tile
+  uint8_t* ktile;   // tile layout: this work-group's K tile
   if (a.dst_ring) {
     row_k = row_v = g.ring_row_k;
     kbase = slab + g.k_ring + (size_t)head * R * row_k;
     vbase = slab + g.v_ring + (size_t)head * R * row_v;
-    vtile = slab + g.v_ring + ((size_t)head * (R / kTile) + ((tile * kTile) % R) / kTile) * g.ring_tile_v;
+    const size_t rt = (size_t)head * (R / kTile) + ((tile * kTile) % R) / kTile;
+    ktile = slab + g.k_ring + rt * g.ring_tile_k;
+    vtile = slab + g.v_ring + rt * g.ring_tile_v;
   } else {
     row_k = g.row_k;
     row_v = g.row_v;
     kbase = slab + g.k_body + (size_t)head * g.cap32 * row_k;
     vbase = slab + g.v_body + (size_t)head * g.cap32 * row_v;
+    ktile = slab + g.k_body + ((size_t)head * (g.cap32 / kTile) + tile) * g.tile_k;
     vtile = slab + g.v_body + ((size_t)head * (g.cap32 / kTile) + tile) * g.tile_v;
   }
   auto krow_of = [&](int p) { return kbase + (size_t)(a.dst_ring ? p % R : p) * row_k; };
@@ -184,9 +199,9 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
     uint16_t dq;
     codes[kv][t][c] = (uint8_t)quant_lane(x, nb, &dq);
     if ((c % kBlock) == 0) {
-      if (kv == 0) ((uint16_t*)(krow_of(p) + NB * 4 * NK))[b] = dq;
-      else if (vrows) ((uint16_t*)(vrow_of(p) + NB * 4 * NV))[b] = dq;
-      else ((uint16_t*)(vtile + 4 * D * NV))[t * NB + b] = dq;
+      if (vrows) ((uint16_t*)(kv ? vrow_of(p) + NB * 4 * NV : krow_of(p) + NB * 4 * NK))[b] = dq;
+      else if (kv == 0) ((uint16_t*)(ktile + 4 * D * NK))[b * kTile + t] = dq;   // [block][position]
+      else ((uint16_t*)(vtile + 4 * D * NV))[b * kTile + t] = dq;
     }
   }
   __syncthreads();
@@ -226,8 +241,14 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
                   << (16 * (e & 1) + 4 * wdt * sl + wdt * (e >> 1));
       }
     }
-    uint8_t* row = rkv ? vrow_of(tile * kTile + t) : krow_of(tile * kTile + t);
-    *(uint32_t*)(row + plane_off + 4 * widx) = bits;   // = j * NB * w + 4k
+    if (vrows) {
+      uint8_t* row = rkv ? vrow_of(tile * kTile + t) : krow_of(tile * kTile + t);
+      *(uint32_t*)(row + plane_off + 4 * widx) = bits;   // = j * NB * w + 4k
+    } else {
+      // K tile: subtile t / 16, lane 16 j + t % 16, byte 4k of the lane's run of this plane
+      *(uint32_t*)(ktile + 512 * (NR * (t / 16)) + 16 * plane_off + lane_run_byte(16 * j + t % 16, 4 * k, NB * wdt)) =
+          bits;
+    }
   }
   }
   if (vrows) return;
@@ -341,8 +362,13 @@ __global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
     const int p = tile * kTile + t;
     const uint16_t v = in[((size_t)(w.src_row + p - w.len_old) * g.n_kv_heads + head) * D + c];
     const int slot = p % R;
-    if (kv == 0 || g.layout == 1) {
+    if (g.layout == 1) {
       ((uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c] = v;
+    } else if (kv == 0) {
+      // [s][b][lane][8]: lane 16 j + slot % 16 holds channels 32b + 8j .. +7
+      const int ts = slot % kTile;
+      uint16_t* kt = (uint16_t*)(slab + g.k_ring + ((size_t)head * (R / kTile) + slot / kTile) * g.ring_tile_k);
+      kt[(((ts / 16) * (D / kBlock) + c / kBlock) * 64 + 16 * ((c % kBlock) / 8) + ts % 16) * 8 + c % 8] = v;
     } else {
       uint8_t* vt = slab + g.v_ring + ((size_t)head * (R / kTile) + slot / kTile) * g.ring_tile_v;
       const int ts = slot % kTile;

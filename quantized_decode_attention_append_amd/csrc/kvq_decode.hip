@@ -238,29 +238,41 @@ struct TileRaw {
   static constexpr int nv0 = NT * w0v / 4, nv1 = w1v ? NT * w1v / 4 : 1, nv2 = w2v ? NT * w2v / 4 : 1;
   uint32_t k0[2][nk0], k1[2][nk1], k2[2][nk2];   // K pieces of this lane's row in each 16-row subtile
   uint32_t v0[nv0], v1[nv1], v2[nv2];             // V pieces of this lane (16 n-tiles)
-  u32x4 sc;                                       // lanes 0-31: K scales of row `lane`; 32-63: V scales of position lane-32
+  u32x4 sc;                                       // 16 bytes of the K (lanes 0-31) or V (32-63) tile scales
 };
 
-// Issue the loads of one tile into `t`. With live = false every lane reads the same 16 bytes at the start
-// of kbase / vt instead (a placeholder that costs one cache line per instruction): the loads are then
-// issued on every path, which keeps the compiler's memory-counter waits exact across the tile loop.
+// Issue the loads of one tile into `t` (kt: the K tile, vt: the V tile). Every load reads 1 KiB (or 512 B)
+// contiguous per wave: lane l's run of a K plane sits at [chunk][lane][16 B], like the V tile. With
+// live = false every lane reads the same 16 bytes at the start of kt / vt instead (a placeholder that costs
+// one cache line per instruction): the loads are then issued on every path, which keeps the compiler's
+// memory-counter waits exact across the tile loop.
+template <int W>
+__device__ inline void load_run(const uint8_t* part, int ll, uint32_t* dst) {
+  constexpr int words = 8 * W / 4;      // NB pieces of W bits x 8 codes
+  if constexpr (words >= 4) {
+#pragma unroll
+    for (int c = 0; c < words / 4; ++c) {
+      const u32x4 x = ldnt(part + c * 1024 + ll * 16);
+      dst[4 * c] = x[0]; dst[4 * c + 1] = x[1]; dst[4 * c + 2] = x[2]; dst[4 * c + 3] = x[3];
+    }
+  } else {
+    const u32x2 x = __builtin_nontemporal_load((const u32x2*)(part + ll * 8));
+    dst[0] = x[0]; dst[1] = x[1];
+  }
+}
+
 template <int NK, int NV>
-__device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kbase, int row_k, bool ring, int R,
-                                 const uint8_t* vt, int tile, bool live) {
+__device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, const uint8_t* vt, bool live) {
   using T = TileRaw<NK, NV>;
-  constexpr int NB = 8, NT = 16, D = 256;
+  constexpr int NT = 16, D = 256;
   const int lane = threadIdx.x & 63;
-  const int m16 = lane & 15;
-  const int g = lane >> 4;
-  const int gl = live ? g : 0;
   const int ll = live ? lane : 0;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int pos = tile * kTile + 16 * s + m16;
-    const uint8_t* row = live ? kbase + (size_t)(ring ? pos % R : pos) * row_k : kbase;
-    load_words<0>(row + gl * NB * T::w0k, t.k0[s], T::nk0);
-    if constexpr (T::w1k > 0) load_words<0>(row + 4 * NB * T::w0k + gl * NB * T::w1k, t.k1[s], T::nk1);
-    if constexpr (T::w2k > 0) load_words<0>(row + 4 * NB * (T::w0k + T::w1k) + gl * NB * T::w2k, t.k2[s], T::nk2);
+    const uint8_t* sub = kt + 512 * NK * s;
+    load_run<T::w0k>(sub, ll, t.k0[s]);
+    if constexpr (T::w1k > 0) load_run<T::w1k>(sub + 512 * T::w0k, ll, t.k1[s]);
+    if constexpr (T::w2k > 0) load_run<T::w2k>(sub + 512 * (T::w0k + T::w1k), ll, t.k2[s]);
   }
 #pragma unroll
   for (int c = 0; c < NT * T::w0v / 16; ++c) {
@@ -279,9 +291,9 @@ __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kbase, int r
     u32x4 x = ldnt(vt + 64 * NT * (T::w0v + T::w1v) + ll * 16);
     t.v2[0] = x[0]; t.v2[1] = x[1]; t.v2[2] = x[2]; t.v2[3] = x[3];
   }
-  const int pr = tile * kTile + (lane & 31);
-  const uint8_t* ksc = live ? kbase + (size_t)(ring ? pr % R : pr) * row_k + NB * 4 * NK : kbase;
-  const uint8_t* vsc = live ? vt + 4 * D * NV + (lane - 32) * NB * 2 : vt;
+  // scales, [block][position] fp16 in both tiles: lanes 0-31 take the K tile's 512 bytes, 32-63 the V tile's
+  const uint8_t* ksc = live ? kt + 4 * D * NK + 16 * lane : kt;
+  const uint8_t* vsc = live ? vt + 4 * D * NV + 16 * (lane - 32) : vt;
   t.sc = ldnt(lane < 32 ? ksc : vsc);
 }
 
@@ -407,7 +419,7 @@ __device__ inline const uint8_t* tile_ptr(const uint8_t* vbase, int tile_v, bool
 // the next are in flight. s_buf: this wave's two 1-KiB LDS buffers for tile scales.
 template <int NK, int NV>
 __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, TileRaw<NK, NV>& nxt, const half8* qb,
-                                       float qmul, const uint8_t* kbase, int row_k, bool ring, int R,
+                                       float qmul, const uint8_t* kbase, int tile_k, bool ring, int R,
                                        const uint8_t* vbase, int tile_v, int t, int tile_end, int lo, int hi,
                                        uint32_t lane_mask, u32x4* s_buf, int* s_next) {
   const int lane = threadIdx.x & 63;
@@ -416,12 +428,8 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
   asm volatile("" : "+v"(magic));   // keep the fp16 magic in a VGPR (the mask takes the SGPR operand)
   // Stage one tile's scales into a wave-private LDS buffer (no work-group barrier needed).
   auto stage = [&](const TileRaw<NK, NV>& tr, u32x4* sb) {
-    // lanes 0-31 hold the 8 block scales of K row `lane`, lanes 32-63 those of V position lane-32:
-    // both are stored transposed, [block][row] at sb and [block][position] at sb + 32
-    uint16_t* dst = (uint16_t*)(sb + (lane < 32 ? 0 : 32));
-    const int tp = lane & 31;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) dst[b * 32 + tp] = (uint16_t)(tr.sc[b >> 1] >> (16 * (b & 1)));
+    // the tiles hold their scales as [block][position]: K at sb[0..31], V at sb[32..63]
+    sb[lane] = tr.sc;
   };
   int buf = 0;
   for (;;) {
@@ -429,7 +437,8 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     // the next tile's loads go out before this tile's scales are staged (which waits for this tile only)
     const int nt = grab_tile(s_next);
     const bool more = nt < tile_end;
-    load_tile<NK, NV>(nxt, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), more ? nt : t, more);
+    load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+                      more);
     stage(cur, sb);
     compute_tile<NK, NV>(st, cur, sb, qb, qmul, t, lo, hi, lane_mask, magic);
     if (nt >= tile_end) break;
@@ -439,21 +448,20 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
   }
 }
 
-// One 32-position tile of the bf16 tail ring. qb: the bf16 query B operands in LDS ([block][lane]).
-__device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, const uint8_t* kring, int R,
+// One 32-position tile of the bf16 tail ring (kt, vt: its K and V tiles). qb: the bf16 query B operands in
+// LDS ([block][lane]).
+__device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, const uint8_t* kt,
                                  const uint8_t* vt, int tile, int lo, int hi, bool lo_lane) {
   constexpr int D = 256, NT = 16;
   const int lane = threadIdx.x & 63;
-  const int m16 = lane & 15;
   const int g = lane >> 4;
   float sc[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int pos = tile * kTile + 16 * s + m16;
-    const uint8_t* row = kring + (size_t)(pos % R) * (2 * D);
+    // [s][b][lane][8 bf16]: lane (g, m16) holds channels 32b + 8g .. +7 of slot 16s + m16
     bf16x8 kk[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) kk[b] = __builtin_nontemporal_load((const bf16x8*)(row + (32 * b + 8 * g) * 2));
+    for (int b = 0; b < 8; ++b) kk[b] = __builtin_nontemporal_load((const bf16x8*)(kt + ((s * 8 + b) * 64 + lane) * 16));
     floatx4 c = {0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[b], qb[b * 64 + lane], c, 0, 0, 0);
@@ -499,7 +507,7 @@ struct QArgs {
 // A qN_0 store path (body, or q8_0 ring): issue the first tile's loads, build the exponent-shifted query
 // operands (times KVarN sigma) in LDS, then run the tile loop. All waves of the work-group call this.
 template <int NK, int NV, bool EARLY>
-__device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, const uint8_t* kbase, int row_k,
+__device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, const uint8_t* kbase, int tile_k,
                                   bool ring, int R, const uint8_t* vbase, int tile_v, int wb, int we, int lo, int hi,
                                   uint32_t lane_mask, u32x4* sbuf, int* s_next, float* s_amax) {
   constexpr int NB = 8;
@@ -514,7 +522,8 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   if (qa.use_sigma) sraw = *(const u32x4*)(qa.sig + 32 * wave + 8 * gq);
   KVQ_SB
   const int t0 = wb < we ? wb : we - 1;
-  if constexpr (EARLY) load_tile<NK, NV>(cur, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, t0), t0, wb < we);
+  if constexpr (EARLY)
+    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_ptr(vbase, tile_v, ring, R, t0), wb < we);
   float x[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {   // q times sigma is exact in fp32 (8 + 11 bits)
@@ -544,9 +553,10 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
     s_qb[wave * 64 + lane] = v;
   }
   __syncthreads();
-  if constexpr (!EARLY) load_tile<NK, NV>(cur, kbase, row_k, ring, R, tile_ptr(vbase, tile_v, ring, R, t0), t0, wb < we);
+  if constexpr (!EARLY)
+    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_ptr(vbase, tile_v, ring, R, t0), wb < we);
   const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e);
-  run_quant_tiles<NK, NV>(st, cur, nxt, s_qb, qmul, kbase, row_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
+  run_quant_tiles<NK, NV>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
                           sbuf, s_next);
 }
 
@@ -639,30 +649,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
     const float qmul = a.scale * kLog2e;
-    const uint8_t* kring = slab + g.k_ring + (size_t)head * R * (2 * D);
     for (int t = wb; t < we; t = grab_tile(&s_next)) {
-      const uint8_t* vt = slab + g.v_ring + ((size_t)head * (R / kTile) + ((t * kTile) % R) / kTile) * g.ring_tile_v;
-      tile_bf16(st, qb, qmul, kring, R, vt, t, lo, hi, lo_lane);
+      const size_t rt = (size_t)head * (R / kTile) + ((t * kTile) % R) / kTile;
+      tile_bf16(st, qb, qmul, slab + g.k_ring + rt * g.ring_tile_k, slab + g.v_ring + rt * g.ring_tile_v, t, lo, hi,
+                lo_lane);
     }
   } else {
     const uint32_t lane_mask = lo_lane ? 0xFFFFFFFFu : 0u;
     const QArgs qa{qrow, sig, use_sigma, head_ok, lo_lane, a.scale};
     u32x4* sbuf = &s_scales[wave][0][0];
     if (!is_ring) {
-      const uint8_t* kbase = slab + g.k_body + (size_t)head * g.cap32 * g.row_k;
+      const uint8_t* kbase = slab + g.k_body + (size_t)head * (g.cap32 / kTile) * g.tile_k;
       const uint8_t* vbase = slab + g.v_body + (size_t)head * (g.cap32 / kTile) * g.tile_v;
       // waves 0-3 (one per SIMD) request their first tile at once, waves 4-7 only once the query is set
       // up: a smaller first burst reaches every SIMD sooner
       if (wave < 4)
-        quant_path<NK, NV, true>(st, qa, s_qb, kbase, g.row_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
+        quant_path<NK, NV, true>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
                                  sbuf, &s_next, s_amax);
       else
-        quant_path<NK, NV, false>(st, qa, s_qb, kbase, g.row_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
+        quant_path<NK, NV, false>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
                                   sbuf, &s_next, s_amax);
     } else {
-      const uint8_t* kbase = slab + g.k_ring + (size_t)head * R * g.ring_row_k;
+      const uint8_t* kbase = slab + g.k_ring + (size_t)head * (R / kTile) * g.ring_tile_k;
       const uint8_t* vbase = slab + g.v_ring + (size_t)head * (R / kTile) * g.ring_tile_v;
-      quant_path<8, 8, true>(st, qa, s_qb, kbase, g.ring_row_k, true, R, vbase, g.ring_tile_v, wb, we, lo, hi,
+      quant_path<8, 8, true>(st, qa, s_qb, kbase, g.ring_tile_k, true, R, vbase, g.ring_tile_v, wb, we, lo, hi,
                              lane_mask, sbuf, &s_next, s_amax);
     }
   }

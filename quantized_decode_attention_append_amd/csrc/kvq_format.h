@@ -10,20 +10,25 @@
 //   little-endian word and element i of piece p sits at bit 16*(i&1) + 4*w*p + w*(i>>1), so that the
 //   pair (e_2k, e_2k+1) always lands in the two 16-bit halves at the same offset (one AND-OR forms two
 //   fp16 "1024 + value" magic numbers). For w = 8 a piece is 8 bytes, e_i in byte i.
-// * K rows (body and q8_0 ring), one per (position, KV head): per plane, for lane group j = 0..3 the
-//   pieces of blocks b = 0..NB-1 (piece (j,b) = channels 32b+8j+i), then NB fp16 scales.
+// * K rows, one per (position, KV head): per plane, for lane group j = 0..3 the pieces of blocks
+//   b = 0..NB-1 (piece (j,b) = channels 32b+8j+i), then NB fp16 scales. The row layout stores them as is.
+// * K tiles (tile layout, body and q8_0 ring): the K rows of 32 positions rearranged for 1 KiB loads: for
+//   subtile s (positions 16s..16s+15) and plane p, lane l = 16j + m holds row 16s+m's run of lane group j
+//   (NB*w bytes) as [chunk][lane][min(16, NB*w)] starting at byte 512*(N*s + widths before p); then the
+//   NB x 32 fp16 scales [block][position].
 // * V tiles (body and q8_0 ring), 32 positions of one KV head: per plane, lane l (d16 = l&15,
 //   j = l>>4) owns pieces n = 0..NT-1, piece (l,n) = channel 16n+d16 at tile positions
 //   T(j,i) = 4j+i (i<4), 16+4j+i-4 (i>=4); lanes' bytes are interleaved in units of
-//   min(16, NT*w) bytes ([chunk][lane][unit]); then the 32 x NB fp16 scales [position][block].
-// * bf16 tail ring: K rows are plain bf16; V tiles hold, per n-tile and lane, the 8 bf16 values of
-//   channel 16n+d16 at positions T(j,i): [n][lane][8 x bf16].
+//   min(16, NT*w) bytes ([chunk][lane][unit]); then the NB x 32 fp16 scales [block][position].
+// * bf16 tail ring: K tiles hold, per subtile s and block b, lane (j, m)'s 8 bf16 values of channels
+//   32b+8j.. of slot 16s+m: [s][b][lane][8 x bf16]; V tiles hold, per n-tile and lane, the 8 bf16 values
+//   of channel 16n+d16 at positions T(j,i): [n][lane][8 x bf16].
 // * Row layout (a cache option for sparse layers): V is stored exactly like K, one row per position
 //   (body, q8_0 ring) or plain bf16 rows (bf16 ring), so every position is one contiguous row of K and
 //   one of V. Region sizes are the same in both layouts.
-// * Arena: [layer][seq] slabs; a slab holds (256-byte aligned) K body [head][cap32][row],
-//   V body [head][cap32/32][tile], K ring [head][R][row], V ring [head][R/32][tile],
-//   KVarN sigma [head][K,V][D] fp16.
+// * Arena: [layer][seq] slabs; a slab holds (256-byte aligned) K body [head][cap32/32][tile],
+//   V body [head][cap32/32][tile], K ring [head][R/32][tile], V ring [head][R/32][tile] (row layout:
+//   [head][positions][row] for K and V), KVarN sigma [head][K,V][D] fp16.
 #pragma once
 
 #include <stddef.h>
@@ -75,6 +80,13 @@ KVQ_HD size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 KVQ_HD int row_bytes(int n_bits, int head_dim) { return head_dim / kBlock * (4 * n_bits + 2); }
 KVQ_HD int tile_bytes(int n_bits, int head_dim) { return kTile * row_bytes(n_bits, head_dim); }
 KVQ_HD int tile_pos(int j, int i) { return i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4); }
+
+// Offset of lane l's byte `b` of its run of `lb` bytes in a lane-interleaved tile part: runs are stored in
+// units of min(16, lb) bytes, [unit index][lane][unit].
+KVQ_HD int lane_run_byte(int lane, int b, int lb) {
+  int unit = lb < 16 ? lb : 16;
+  return (b / unit) * 64 * unit + lane * unit + (b % unit);
+}
 
 // Offset of lane l's byte `b` (within its per-plane run of nt*w bytes) in a V tile's plane.
 KVQ_HD int vtile_lane_byte(int lane, int b, int nt, int w) {

@@ -131,8 +131,10 @@ kvq::Geometry geometry(const kvq_cache* c) {
   g.cap32 = c->lay.cap32;
   g.row_k = c->lay.row_k;
   g.row_v = c->lay.row_v;
+  g.tile_k = kvq::kTile * c->lay.row_k;
   g.tile_v = kvq::kTile * c->lay.row_v;
   g.ring_row_k = c->lay.ring_row_k;
+  g.ring_tile_k = kvq::kTile * c->lay.ring_row_k;
   g.ring_tile_v = kvq::kTile * c->lay.ring_row_v;
   g.ring_row_v = c->lay.ring_row_v;
   g.ring_slots = c->lay.ring_slots;

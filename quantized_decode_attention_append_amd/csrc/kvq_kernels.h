@@ -19,7 +19,7 @@ struct Geometry {
   uint8_t* arena;
   size_t slab_bytes;
   size_t k_body, v_body, k_ring, v_ring, sigma;   // region offsets within a slab
-  int cap32, row_k, row_v, tile_v, ring_row_k, ring_row_v, ring_tile_v, ring_slots;
+  int cap32, row_k, row_v, tile_k, tile_v, ring_row_k, ring_row_v, ring_tile_k, ring_tile_v, ring_slots;
   int n_kv_heads, head_dim, k_bits, v_bits, kvarn, tail_dtype;
   int layout;                                      // 0: V tiles, 1: V rows
 };

@@ -84,6 +84,7 @@ def test_row_and_tile_sizes(n_bits):
         s = np.zeros((1, 32, d // 32), dtype=np.float16)
         assert layout.pack_v_tiles(u, s, n_bits).shape == (1, 32 * layout.row_bytes(n_bits, d))
         assert layout.pack_k_rows(u[0], s[0], n_bits).shape == (32, layout.row_bytes(n_bits, d))
+        assert layout.pack_k_tiles(u, s, n_bits).shape == (1, 32 * layout.row_bytes(n_bits, d))
 
 
 def test_piece_bits_worked_examples():
@@ -144,6 +145,43 @@ def test_v_tile_worked_example():
         assert np.array_equal(tile, expect)
 
 
+def test_k_tile_worked_example():
+    # D = 256, N = 5: nibble plane (32 B per lane run, two 16-byte chunks), then 1-bit plane (8 B per lane)
+    d, n = 256, 5
+    for (t, b, j, i, val, sc) in [(0, 0, 0, 0, 0x1F, 1.5), (17, 5, 2, 3, 0x13, -2.0), (31, 7, 3, 7, 0x0A, 0.25),
+                                  (14, 2, 1, 6, 0x10, 3.0)]:
+        u = np.zeros((1, 32, d), dtype=np.uint8)
+        u[0, t, 32 * b + 8 * j + i] = val
+        d16 = np.zeros((1, 32, 8), dtype=np.float16)
+        d16[0, t, b] = sc
+        tile = layout.pack_k_tiles(u, d16, n)[0]
+        expect = np.zeros(32 * layout.row_bytes(n, d), dtype=np.uint8)
+        s, m = t // 16, t % 16
+        lane = 16 * j + m
+        # subtile s starts at 512 * N * s; nibble plane: lane run byte 4b, 16-byte chunks over 64 lanes
+        rb = 4 * b
+        off = 512 * n * s + (rb // 16) * 1024 + lane * 16 + rb % 16
+        w0 = (val & 0xF) << (16 * (i % 2) + 4 * (i // 2))
+        expect[off:off + 4] |= np.frombuffer(np.uint32(w0).tobytes(), dtype=np.uint8)
+        # 1-bit plane after 512 * 4 bytes of the subtile: 8 bytes per lane, 4 pieces per word
+        off = 512 * n * s + 2048 + lane * 8 + (b // 4) * 4
+        w1 = (val >> 4) << (16 * (i % 2) + 4 * (b % 4) + i // 2)
+        expect[off:off + 4] |= np.frombuffer(np.uint32(w1).tobytes(), dtype=np.uint8)
+        # scales [block][position] after the codes
+        off = 1024 * n + 2 * (32 * b + t)
+        expect[off:off + 2] = np.frombuffer(np.float16(sc).tobytes(), dtype=np.uint8)
+        assert np.array_equal(tile, expect), (t, b, j, i)
+
+
+def test_bf16_k_tile_worked_example():
+    bits = np.zeros((1, 32, 256), dtype=np.uint16)
+    bits[0, 19, 32 * 6 + 8 * 2 + 5] = 0xBEEF
+    tile = layout.pack_bf16_k_tiles(bits)[0].view(np.uint16)
+    # [s][b][lane][8]: s = 1, b = 6, lane = 16 * 2 + 3, element 5
+    idx = ((1 * 8 + 6) * 64 + (16 * 2 + 3)) * 8 + 5
+    assert tile[idx] == 0xBEEF and np.count_nonzero(tile) == 1
+
+
 @pytest.mark.parametrize("n_bits", range(2, 9))
 def test_pack_unpack_round_trip(n_bits):
     rng = np.random.default_rng(n_bits)
@@ -156,8 +194,11 @@ def test_pack_unpack_round_trip(n_bits):
         s = rng.standard_normal((3, 32, d // 32)).astype(np.float16)
         u2, s2 = layout.unpack_v_tiles(layout.pack_v_tiles(u, s, n_bits), n_bits, d)
         assert np.array_equal(u, u2) and np.array_equal(s.view(np.uint16), s2.view(np.uint16))
+        u2, s2 = layout.unpack_k_tiles(layout.pack_k_tiles(u, s, n_bits), n_bits, d)
+        assert np.array_equal(u, u2) and np.array_equal(s.view(np.uint16), s2.view(np.uint16))
     b = rng.integers(0, 1 << 16, size=(2, 32, 256)).astype(np.uint16)
     assert np.array_equal(layout.unpack_bf16_v_tiles(layout.pack_bf16_v_tiles(b), 256), b)
+    assert np.array_equal(layout.unpack_bf16_k_tiles(layout.pack_bf16_k_tiles(b), 256), b)
 
 
 def test_slab_regions_are_disjoint_and_aligned():
