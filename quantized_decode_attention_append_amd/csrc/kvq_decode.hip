@@ -185,6 +185,65 @@ __device__ inline half8 decode_run_piece(const uint32_t* run0, const uint32_t* r
   }
 }
 
+// ------------------------------------------------------------------ K planes as fp16 denormals
+//
+// For QK each bit plane of a K piece goes to the MFMA on its own, as fp16 denormal numbers: an AND of
+// the plane word leaves the field of pair k in both 16-bit halves at bit offset q_k, i.e. the half is the
+// exact denormal field * 2^(q_k - 24). The query operand of that plane carries the compensating weight
+// 2^(plane shift - q_k) per element, so the plane MFMAs add up to 2^-24 * sum(u * q) for the biased code u;
+// the bias is removed by one more MFMA of a constant operand (-2^(N-1) * 2^(q_k - 24), also exact) with
+// the plane-0 query operand. gfx950's MFMA treats fp16 denormal inputs exactly. Fields at bits 8 and above are shifted down by 8 first so that every field stays in the
+// mantissa (bits 0-9).
+
+// Bit offset q of the field of element i after the extraction below (plane width W, piece slot SLOT).
+__device__ inline int dn_bitpos(int w, int slot, int i) {
+  const int k = i >> 1;
+  return w == 8 ? 0 : w == 4 ? 4 * (k & 1) : w == 2 ? 2 * k : 4 * (slot & 1) + k;
+}
+
+template <int W, int SLOT>
+__device__ inline half8 dn_extract(uint32_t word) {
+  u32x4 r;
+  if constexpr (W == 4) {
+    const uint32_t w8 = word >> 8;
+    r[0] = word & 0x000F000Fu;
+    r[1] = word & 0x00F000F0u;
+    r[2] = w8 & 0x000F000Fu;
+    r[3] = w8 & 0x00F000F0u;
+  } else if constexpr (W == 2) {
+    const uint32_t ws = SLOT ? word >> 8 : word;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = ws & (0x00030003u << (2 * k));
+  } else {
+    const uint32_t ws = SLOT >= 2 ? word >> 8 : word;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = ws & (0x00010001u << (4 * (SLOT & 1) + k));
+  }
+  return __builtin_bit_cast(half8, r);
+}
+
+// The plane operands of K piece B (block B) from the lane's runs of plane words.
+template <int N> struct KPlanes { half8 a[Planes<N>::n]; };
+
+template <int N, int B>
+__device__ inline void dn_piece(const uint32_t* run0, const uint32_t* run1, const uint32_t* run2, KPlanes<N>& kp) {
+  if constexpr (N == 8) {
+    // bytes -> halves (0x00, byte): the byte itself as a denormal
+    const uint32_t lo = run0[2 * B], hi = run0[2 * B + 1];
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(0u, lo, 0x0C010C00u);
+    r[1] = __builtin_amdgcn_perm(0u, lo, 0x0C030C02u);
+    r[2] = __builtin_amdgcn_perm(0u, hi, 0x0C010C00u);
+    r[3] = __builtin_amdgcn_perm(0u, hi, 0x0C030C02u);
+    kp.a[0] = __builtin_bit_cast(half8, r);
+  } else {
+    constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
+    kp.a[0] = dn_extract<w0, B % (4 / w0)>(run0[(B * w0) / 4]);
+    if constexpr (Planes<N>::n >= 2) kp.a[1] = dn_extract<w1, B % (4 / w1)>(run1[(B * w1) / 4]);
+    if constexpr (Planes<N>::n >= 3) kp.a[2] = dn_extract<w2, B % (4 / w2)>(run2[(B * w2) / 4]);
+  }
+}
+
 // ------------------------------------------------------------------ small helpers
 
 __device__ inline float dpp_ror8(float x) {
@@ -329,6 +388,10 @@ __device__ inline void softmax_update(WaveState& st, const float* x, float* p) {
   st.l += psum;
 }
 
+// LDS of the QK B operands: one [block][lane] array per K bit plane.
+constexpr int kQbPlanes = 3;
+constexpr int kQbHalf8 = kQbPlanes * 8 * 64;
+
 // One 32-position tile of a qN_0 store (body, or the q8_0 ring). [lo, hi) are the valid positions.
 // lane_mask is 0 on the hi-part lanes (rows 0-7 of the P operand) and ~0 on the lo-part lanes.
 // s_sc: this wave's LDS copy of the tile's scales: K as [block][row], then V as [block][position].
@@ -340,18 +403,30 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
   float sc[2][4];
   // K scales, transposed in LDS to [block][row]: the 4 rows 4g..4g+3 of a subtile are 8 contiguous bytes
   const uint16_t* s_dk = (const uint16_t*)s_sc;
+  half8 kbias;   // -2^(N-1) * 2^(q_k - 24) per element: with the plane-0 query operand, minus the code bias
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    kbias[i] = (_Float16)(-ldexpf(1.0f, NK - 1 + dn_bitpos(Planes<NK>::w[0], 0, i) - 24));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[s][r] = 0.0f;
-    // block B's MFMA is issued before block B+1 is decoded, and its result consumed after that, so the
+    // block B's MFMAs are issued before block B+1 is decoded, and their result consumed after that, so the
     // MFMA latency is covered by the next block's decode
-    half8 a_cur = decode_run_piece<NK, 0>(t.k0[s], t.k1[s], t.k2[s], magic);
+    KPlanes<NK> a_cur;
+    dn_piece<NK, 0>(t.k0[s], t.k1[s], t.k2[s], a_cur);
 #define KVQ_QK(B)                                                                                 \
     {                                                                                             \
-      const half8 qv = qb[B * 64 + lane];                                                         \
-      floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, qv, floatx4{0, 0, 0, 0}, 0, 0, 0); \
-      if constexpr (B < 7) a_cur = decode_run_piece<NK, (B < 7 ? B + 1 : 0)>(t.k0[s], t.k1[s], t.k2[s], magic); \
+      const half8 q0 = qb[B * 64 + lane];                                                         \
+      floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbias, q0, floatx4{0, 0, 0, 0}, 0, 0, 0);  \
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur.a[0], q0, c, 0, 0, 0);                     \
+      if constexpr (Planes<NK>::n >= 2 && NK != 8)                                                \
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur.a[Planes<NK>::n >= 2 && NK != 8 ? 1 : 0], \
+                                                   qb[512 + B * 64 + lane], c, 0, 0, 0);          \
+      if constexpr (Planes<NK>::n >= 3)                                                           \
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur.a[Planes<NK>::n >= 3 ? 2 : 0],            \
+                                                   qb[1024 + B * 64 + lane], c, 0, 0, 0);         \
+      if constexpr (B < 7) dn_piece<NK, (B < 7 ? B + 1 : 0)>(t.k0[s], t.k1[s], t.k2[s], a_cur);   \
       const u32x2 dk = *(const u32x2*)(s_dk + B * 32 + 16 * s + 4 * g);                           \
       sc[s][0] = fmaf(c[0], lo_h(dk[0]), sc[s][0]);                                               \
       sc[s][1] = fmaf(c[1], hi_h(dk[0]), sc[s][1]);                                               \
@@ -539,23 +614,34 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < 8; ++w) amax = fmaxf(amax, s_amax[w * 16 + (lane & 15)]);
-  // exponent-shifted query of this lane's head, split into fp16 hi (cols 0-7) and lo (cols 8-15)
-  const int e = amax > 0.0f ? ilogbf(amax) - 14 : 0;
+  // exponent-shifted query of this lane's head (|q| < 2^9, so that the plane weights of up to 2^6 stay in
+  // fp16 range), split into fp16 hi (cols 0-7) and lo (cols 8-15); one weighted copy per K bit plane
+  const int e = amax > 0.0f ? ilogbf(amax) - 8 : 0;
   {
-    half8 v;
+    float part[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float xs = ldexpf(x[i], -e);
       const _Float16 h = (_Float16)xs;
       const _Float16 l = (_Float16)(xs - (float)h);
-      v[i] = qa.head_ok ? (qa.lo_lane ? l : h) : (_Float16)0.0f;
+      part[i] = qa.head_ok ? (float)(qa.lo_lane ? l : h) : 0.0f;
     }
-    s_qb[wave * 64 + lane] = v;
+#pragma unroll
+    for (int p = 0; p < Planes<NK>::n; ++p) {
+      half8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int w = Planes<NK>::w[p];
+        const int slot = w == 8 ? 0 : wave % (4 / w);
+        v[i] = (_Float16)ldexpf(part[i], Planes<NK>::sh[p] - dn_bitpos(w, slot, i));   // exact: power of two
+      }
+      s_qb[p * 512 + wave * 64 + lane] = v;
+    }
   }
   __syncthreads();
   if constexpr (!EARLY)
     load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_ptr(vbase, tile_v, ring, R, t0), wb < we);
-  const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e);
+  const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e + 24);
   run_quant_tiles<NK, NV>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
                           sbuf, s_next);
 }
@@ -570,7 +656,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float s_o[NW][kPartialHeads][D];
   __shared__ float s_ml[NW][2][kPartialHeads];
   __shared__ u32x4 s_scales[NW][2][64];   // per wave, double-buffered tile scales
-  __shared__ half8 s_qb[8 * 64];           // QK B operands (per block, per lane)
+  __shared__ half8 s_qb[kQbHalf8];         // QK B operands (per plane, block and lane)
   __shared__ int s_next;                   // next unclaimed tile of this split
   __shared__ float s_amax[8 * 16];         // per wave: |q| maximum of each head over the wave's block
 
