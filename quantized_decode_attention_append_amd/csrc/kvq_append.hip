@@ -133,6 +133,53 @@ __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int k
   return (float)((int)tile[vtile_lane_byte(lane, (c / 16) * 8 + e, NT, 8)] - 128) * dh;
 }
 
+// OR one biased code u of (tile position t, channel c) into the body words that hold it. Body positions are
+// written once after the slab was zeroed, so the target bits are zero and no read is needed; every word of
+// a K tile / row belongs to one position, a V tile word is shared by up to 8 positions (hence the atomics).
+// row: K (kv = 0) or V row of the position (row layout); tile: the position's K or V tile (tile layout).
+__device__ inline void or_code(uint8_t* row, uint8_t* tile, bool rows, int kv, int n_bits, int t, int c, uint32_t u,
+                               int D) {
+  const int NB = D / kBlock, NT = D / 16;
+  int row_off = 0, tile_off = 0;
+  for (int p = 0; p < plane_count(n_bits); ++p) {
+    const int w = plane_width(n_bits, p);
+    const uint32_t field = (u >> plane_shift(n_bits, p)) & ((1u << w) - 1);
+    int wbyte, bit, lane, e = 0;
+    if (kv == 0 || rows) {
+      const int b = c / kBlock, j = (c % kBlock) / 8, i = c % 8;
+      if (w == 8) {
+        wbyte = (8 * b + i) & ~3;
+        bit = 8 * (i & 3);
+      } else {
+        wbyte = 4 * ((b * w) / 4);
+        bit = 16 * (i & 1) + 4 * w * (b % (4 / w)) + w * (i >> 1);
+      }
+      lane = 16 * j + t % 16;
+      uint8_t* dst = rows ? row + row_off + j * NB * w + wbyte
+                          : tile + 512 * (n_bits * (t / 16)) + 16 * row_off + lane_run_byte(lane, wbyte, NB * w);
+      if (field) atomicOr((uint32_t*)dst, field << bit);
+    } else {
+      const int n = c / 16;
+      e = t % 4 + 4 * (t / 16);
+      lane = 16 * ((t % 16) / 4) + c % 16;
+      if (w == 8) {
+        wbyte = (8 * n + e) & ~3;
+        bit = 8 * (e & 3);
+      } else {
+        wbyte = 4 * ((n * w) / 4);
+        bit = 16 * (e & 1) + 4 * w * (n % (4 / w)) + w * (e >> 1);
+      }
+      uint8_t* dst = tile + tile_off + vtile_lane_byte(lane, wbyte, NT, w);
+      if (field) atomicOr((uint32_t*)dst, field << bit);
+    }
+    row_off += 4 * NB * w;
+    tile_off += 64 * NT * w;
+  }
+}
+
+// A work-group with at most this many positions ORs its codes straight into the body (no LDS staging).
+constexpr int kDirectPositions = 4;
+
 __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
   __shared__ uint8_t codes[2][kTile][256];     // [K,V][tile position][channel]
   const Geometry& g = a.g;
@@ -186,6 +233,8 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
   const float sig = (!a.dst_ring && g.kvarn)
                         ? f16_to_f32(((const uint16_t*)(slab + g.sigma))[((size_t)head * 2 + kv) * D + c])
                         : 1.0f;
+  // few positions of the body (a decode step's evict): OR the codes in directly, no LDS round trip
+  const bool direct = !a.dst_ring && t1 - t0 <= kDirectPositions;
   for (int t = t0; t < t1; ++t) {
     const int p = tile * kTile + t;
     float x;
@@ -197,13 +246,16 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
     }
     if (!a.dst_ring && g.kvarn) x = x / sig;
     uint16_t dq;
-    codes[kv][t][c] = (uint8_t)quant_lane(x, nb, &dq);
+    const uint32_t u = quant_lane(x, nb, &dq);
+    if (direct) or_code(kv ? vrow_of(p) : krow_of(p), kv ? vtile : ktile, vrows, kv, nb, t, c, u, D);
+    else codes[kv][t][c] = (uint8_t)u;
     if ((c % kBlock) == 0) {
       if (vrows) ((uint16_t*)(kv ? vrow_of(p) + NB * 4 * NV : krow_of(p) + NB * 4 * NK))[b] = dq;
       else if (kv == 0) ((uint16_t*)(ktile + 4 * D * NK))[b * kTile + t] = dq;   // [block][position]
       else ((uint16_t*)(vtile + 4 * D * NV))[b * kTile + t] = dq;
     }
   }
+  if (direct) return;   // uniform over the work-group
   __syncthreads();
 
   // ---- phase 2a: K rows (and, in the row layout, V rows) of the written positions, one 32-bit word per

@@ -326,6 +326,12 @@ __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, const ui
   constexpr int NT = 16, D = 256;
   const int lane = threadIdx.x & 63;
   const int ll = live ? lane : 0;
+  // scales first, then K, then V: the loads return in order, so staging the scales, QK and P.V each wait
+  // only for their own part of the tile
+  // scales, [block][position] fp16 in both tiles: lanes 0-31 take the K tile's 512 bytes, 32-63 the V tile's
+  const uint8_t* ksc = live ? kt + 4 * D * NK + 16 * lane : kt;
+  const uint8_t* vsc = live ? vt + 4 * D * NV + 16 * (lane - 32) : vt;
+  t.sc = ldnt(lane < 32 ? ksc : vsc);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const uint8_t* sub = kt + 512 * NK * s;
@@ -350,10 +356,6 @@ __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, const ui
     u32x4 x = ldnt(vt + 64 * NT * (T::w0v + T::w1v) + ll * 16);
     t.v2[0] = x[0]; t.v2[1] = x[1]; t.v2[2] = x[2]; t.v2[3] = x[3];
   }
-  // scales, [block][position] fp16 in both tiles: lanes 0-31 take the K tile's 512 bytes, 32-63 the V tile's
-  const uint8_t* ksc = live ? kt + 4 * D * NK + 16 * lane : kt;
-  const uint8_t* vsc = live ? vt + 4 * D * NV + 16 * (lane - 32) : vt;
-  t.sc = ldnt(lane < 32 ? ksc : vsc);
 }
 
 #define KVQ_SB __builtin_amdgcn_sched_barrier(0);
@@ -752,9 +754,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (wave < 4)
         quant_path<NK, NV, true>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
                                  sbuf, &s_next, s_amax);
-      else
+      else {
+        // the later-starting wave of each SIMD gets issue priority, so that both finish together
+        __builtin_amdgcn_s_setprio(1);
         quant_path<NK, NV, false>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
                                   sbuf, &s_next, s_amax);
+        __builtin_amdgcn_s_setprio(0);
+      }
     } else {
       const uint8_t* kbase = slab + g.k_ring + (size_t)head * (R / kTile) * g.ring_tile_k;
       const uint8_t* vbase = slab + g.v_ring + (size_t)head * (R / kTile) * g.ring_tile_v;
