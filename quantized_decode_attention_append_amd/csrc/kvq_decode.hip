@@ -251,11 +251,28 @@ __device__ inline float dpp_ror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
 
-__device__ inline float wave_max_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions across the four 16-lane rows of the wave with gfx950's lane-swap instructions, without LDS
+// traffic: with both operands equal, v_permlane16_swap returns (rows 0,0,2,2) and (rows 1,1,3,3) of x, and
+// v_permlane32_swap returns (lanes 0-31 twice) and (lanes 32-63 twice), so combining the two results gives
+// x op x[lane ^ 16] (or ^ 32) in every lane.
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float wave_max_16_32(float x) { return max_xor32(max_xor16(x)); }
 
 // Cache rows are read once per decode call: streaming (nontemporal) loads keep them from displacing
 // other lines and sustain a much higher read rate on gfx950 than ordinary loads.
@@ -366,26 +383,40 @@ __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, const ui
 __device__ inline float lo_h(uint32_t w) { return (float)as_h2(w)[0]; }
 __device__ inline float hi_h(uint32_t w) { return (float)as_h2(w)[1]; }
 
-// Online-softmax update for this lane's 8 scores x[] (exp2 domain, -inf for masked positions).
-// Returns p[] and rescales the accumulators only when some lane's running max moved.
+// Online-softmax update for this lane's 8 scores x[] (exp2 domain, -inf for masked positions); returns p[].
+// The scores are exponentiated against a reference max that moves only when some score of the wave exceeds it
+// by more than kLazy: until then p <= 2^kLazy, well inside the range of the fp32 accumulators and of the fp16 /
+// bf16 P.V operands, and the accumulators need no rescale (the split merge uses whatever reference a partial
+// carries).
+constexpr float kLazy = 8.0f;
+
 __device__ inline void softmax_update(WaveState& st, const float* x, float* p) {
   float tmax = kNegBig;
 #pragma unroll
   for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
   tmax = wave_max_16_32(tmax);
-  const float m_new = fmaxf(st.m, tmax);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  st.m = m_new;
+  if (__builtin_amdgcn_ballot_w64(tmax > st.m + kLazy)) {
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+    // The accumulator rows of lane (g, m16) are rows 4g..4g+3 of the P.V tile, i.e. heads 4g..4g+3 (hi parts for
+    // g < 2, lo parts for g >= 2), not the lane's own score column m16: take those heads' factors from the lanes
+    // of this 16-lane row that hold columns 4g..4g+3.
+    const int lane = threadIdx.x & 63;
+    const int src = (lane & 48) + ((lane >> 4) << 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((src + r) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+      for (int n = 0; n < 16; ++n) st.o[n][r] *= ar;
+    }
+  }
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+    p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
     psum += p[i];
-  }
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-    st.l *= alpha;
-#pragma unroll
-    for (int n = 0; n < 16; ++n) st.o[n] *= alpha;
   }
   st.l += psum;
 }
@@ -444,12 +475,21 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float full = sc[s][r] + dpp_ror8(sc[s][r]);
-      const int pos = tile * kTile + 16 * s + 4 * g + r;
-      x[4 * s + r] = (pos >= lo && pos < hi) ? full * qmul : -INFINITY;
-    }
+    for (int r = 0; r < 4; ++r) x[4 * s + r] = (sc[s][r] + dpp_ror8(sc[s][r])) * qmul;
+  if (tile * kTile < lo || tile * kTile + kTile > hi) {   // a tile at either end of the range: mask positions
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = tile * kTile + 16 * s + 4 * g + r;
+        if (pos < lo || pos >= hi) x[4 * s + r] = -INFINITY;
+      }
+  }
   softmax_update(st, x, p);
+  // P masked to zero on the hi-part lanes: there the hi part below is P * dv itself
+  float pm[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pm[i] = __uint_as_float(__float_as_uint(p[i]) & lane_mask);
   // V scales, transposed in LDS to [block][position]: this lane's positions T(g, 0..3) and T(g, 4..7)
   // are two runs of 4 fp16 values per block.
   const uint16_t* s_dv = (const uint16_t*)(s_sc + 32);
@@ -462,10 +502,9 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
     half8 a;                                                                                        \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                 \
       const half2v d = as_h2(dw[j]);                                                                \
-      const half2v dm = as_h2(dw[j] & lane_mask);                                                   \
       /* fma with +0 (not a product) so that it maps to a mixed-precision fma */                    \
-      const _Float16 h0 = (_Float16)fmaf(p[2 * j], (float)dm[0], 0.0f);                             \
-      const _Float16 h1 = (_Float16)fmaf(p[2 * j + 1], (float)dm[1], 0.0f);                         \
+      const _Float16 h0 = (_Float16)fmaf(pm[2 * j], (float)d[0], 0.0f);                             \
+      const _Float16 h1 = (_Float16)fmaf(pm[2 * j + 1], (float)d[1], 0.0f);                         \
       a[2 * j] = (_Float16)fmaf(p[2 * j], (float)d[0], -(float)h0);                                 \
       a[2 * j + 1] = (_Float16)fmaf(p[2 * j + 1], (float)d[1], -(float)h1);                         \
     }                                                                                               \
@@ -494,7 +533,7 @@ __device__ inline const uint8_t* tile_ptr(const uint8_t* vbase, int tile_v, bool
 // Loop over tiles of a qN_0 store: this wave starts with tile t (already requested in `cur`) and then takes
 // further tiles below tile_end from the work-group counter. During the compute of one tile the loads of
 // the next are in flight. s_buf: this wave's two 1-KiB LDS buffers for tile scales.
-template <int NK, int NV>
+template <int NK, int NV, bool UNROLL>
 __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, TileRaw<NK, NV>& nxt, const half8* qb,
                                        float qmul, const uint8_t* kbase, int tile_k, bool ring, int R,
                                        const uint8_t* vbase, int tile_v, int t, int tile_end, int lo, int hi,
@@ -508,6 +547,27 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     // the tiles hold their scales as [block][position]: K at sb[0..31], V at sb[32..63]
     sb[lane] = tr.sc;
   };
+  if constexpr (UNROLL) {
+    for (;;) {
+      int nt = grab_tile(s_next);
+      bool more = nt < tile_end;
+      load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+                        more);
+      stage(cur, s_buf);
+      compute_tile<NK, NV>(st, cur, s_buf, qb, qmul, t, lo, hi, lane_mask, magic);
+      if (!more) break;
+      t = nt;
+      nt = grab_tile(s_next);
+      more = nt < tile_end;
+      load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+                        more);
+      stage(nxt, s_buf + 64);
+      compute_tile<NK, NV>(st, nxt, s_buf + 64, qb, qmul, t, lo, hi, lane_mask, magic);
+      if (!more) break;
+      t = nt;
+    }
+    return;
+  }
   int buf = 0;
   for (;;) {
     u32x4* sb = s_buf + 64 * buf;
@@ -524,6 +584,10 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     buf ^= 1;
   }
 }
+
+// Whether the tile loop runs two tiles per trip (swapping the roles of the two register buffers instead of
+// copying the prefetched one): only where both buffers and the decode temporaries fit in 256 VGPRs.
+constexpr bool unroll_tiles(int nk, int nv) { return nk != 8 && nv <= 6 && nk + nv <= 11; }
 
 // One 32-position tile of the bf16 tail ring (kt, vt: its K and V tiles). qb: the bf16 query B operands in
 // LDS ([block][lane]).
@@ -644,7 +708,7 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   if constexpr (!EARLY)
     load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_ptr(vbase, tile_v, ring, R, t0), wb < we);
   const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e + 24);
-  run_quant_tiles<NK, NV>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
+  run_quant_tiles<NK, NV, unroll_tiles(NK, NV)>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
                           sbuf, s_next);
 }
 
@@ -770,13 +834,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- wave epilogue: l over the lanes of a head; o = hi rows + lo rows
-  float lsum = lo_lane ? 0.0f : st.l;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  const float lsum = sum_xor32(sum_xor16(lo_lane ? 0.0f : st.l));
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st.o[n][r] += __shfl_xor(st.o[n][r], 32);
+    for (int r = 0; r < 4; ++r) st.o[n][r] = sum_xor32(st.o[n][r]);
   if (gq < 2) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
