@@ -250,16 +250,14 @@ def main() -> int:
 
     def step(st, nbytes=None):
         for layer in range(L):
-            if appends:
-                cache.append(layer, seqs, ones, kin_d[st, layer], vin_d[st, layer])
+            if appends:   # append one token and requantize the one leaving the window: one launch
+                cache.append_evict(layer, seqs, ones, kin_d[st, layer], vin_d[st, layer])
             if sparse:
                 if nbytes is not None:
                     nbytes.append(sparse_call_bytes(cfg, wl.budget, B))
                 cache.sparse_decode_attn(layer, seqs, qin_d[st, layer], pin_d[st, layer], out=out[layer],
                                          workspace=ws)
             else:
-                if appends:
-                    cache.tail_evict(layer, seqs)
                 if nbytes is not None:
                     lens = [cache.lengths(layer, s) for s in seqs]
                     nbytes.append(decode_call_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens]))
@@ -284,7 +282,7 @@ def main() -> int:
     for i in range(args.steps):
         step(args.warmup + args.steps + i, kbytes)
     torch.cuda.synchronize()
-    times = {k: cache.timing_read(k) for k in ("decode", "gather", "combine", "append", "evict")}
+    times = {k: cache.timing_read(k) for k in ("decode", "gather", "combine", "append", "evict", "append_evict")}
     cache.timing(False)
 
     main_kernel = "gather" if (sparse or cfg.get("layout", 0) == 1) else "decode"

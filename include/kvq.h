@@ -130,6 +130,13 @@ kvq_status kvq_append(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int
 kvq_status kvq_tail_evict(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                           void* stream);
 
+/* kvq_append followed by kvq_tail_evict on the same sequences, with the same result. When every sequence's
+ * evicted positions were already in the ring before the call and the new tokens fit the ring beside them
+ * (a decode step: append one token, requantize the one leaving the window), both run in a single kernel
+ * launch; otherwise the two calls run in turn. Arguments and errors as kvq_append. */
+kvq_status kvq_append_evict(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                            const int32_t* n_new, const void* k_bf16, const void* v_bf16, void* stream);
+
 /* Dense decode attention (offload page: each step reads the whole cache of a full-attention
  * layer). With KVQ_LAYOUT_ROWS the rows are read by the same gather kernel as sparse decode. For each sequence i: out[i][h][:] = softmax(scale * q[i][h] . K^[t]) over t in [0, len) of V^,
  * with K^, V^ the dequantized body rows (t < body_len) or ring rows. q_bf16: device bf16
@@ -161,7 +168,8 @@ typedef enum {
   KVQ_KERNEL_COMBINE = 2,  /* merge of the split partials                                      */
   KVQ_KERNEL_APPEND = 3,   /* append kernels (calibration, body and ring writes)               */
   KVQ_KERNEL_EVICT = 4,    /* tail-evict requantization                                         */
-  KVQ_KERNEL_COUNT = 5
+  KVQ_KERNEL_APPEND_EVICT = 5, /* fused append + evict of kvq_append_evict                        */
+  KVQ_KERNEL_COUNT = 6
 } kvq_kernel;
 
 /* Launch timing, for measuring kernels against the memory roofline. While enabled, every launch the

@@ -180,11 +180,13 @@ __device__ inline void or_code(uint8_t* row, uint8_t* tile, bool rows, int kv, i
 // A work-group with at most this many positions ORs its codes straight into the body (no LDS staging).
 constexpr int kDirectPositions = 4;
 
-__global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
+// One work-group of 512 threads per (position tile, KV head): thread (kv, c) quantizes channel c of K (kv = 0)
+// or V (kv = 1) for every position of the tile that the call writes. A: WriteArgs, or one role of StepArgs
+// (the kernel argument itself, so that the item list is read in place).
+template <class A>
+__device__ inline void body_write_wg(const A& a, int wg, int head) {
   __shared__ uint8_t codes[2][kTile][256];     // [K,V][tile position][channel]
   const Geometry& g = a.g;
-  const int wg = blockIdx.x;
-  const int head = blockIdx.y;
   int it = 0;
   while (it + 1 < a.n_items && a.items[it + 1].wg_begin <= wg) ++it;
   const WriteItem& w = a.items[it];
@@ -394,10 +396,9 @@ __global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
 // ------------------------------------------------------------------------------ bf16 ring write
 
 // One work-group of 512 threads per (position tile, KV head): thread (kv, c) copies channel c.
-__global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
+template <class A>
+__device__ inline void bf16_ring_write_wg(const A& a, int wg, int head) {
   const Geometry& g = a.g;
-  const int wg = blockIdx.x;
-  const int head = blockIdx.y;
   int it = 0;
   while (it + 1 < a.n_items && a.items[it + 1].wg_begin <= wg) ++it;
   const WriteItem& w = a.items[it];
@@ -430,6 +431,25 @@ __global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
   }
 }
 
+__global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) { body_write_wg(a, blockIdx.x, blockIdx.y); }
+
+__global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
+  bf16_ring_write_wg(a, blockIdx.x, blockIdx.y);
+}
+
+// A decode step's append and evict in one launch: work-groups [0, ring_wgs) write the new tokens into the
+// ring, the rest requantize ring rows that were already there into the body. The two touch disjoint bytes
+// (the host only fuses calls whose evicted positions precede the appended ones and fit the ring together).
+__global__ __launch_bounds__(512) void step_write_kernel(StepArgs a) {
+  const int x = blockIdx.x;
+  if (x < a.ring_wgs) {
+    if (a.ring.g.tail_dtype == 1) bf16_ring_write_wg(a.ring, x, blockIdx.y);
+    else body_write_wg(a.ring, x, blockIdx.y);
+  } else {
+    body_write_wg(a.body, x - a.ring_wgs, blockIdx.y);
+  }
+}
+
 __global__ void fill_zero_kernel(uint4* p, size_t n16) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -448,6 +468,10 @@ hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEv
 
 hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   return launch_k(bf16_ring_write_kernel, dim3(n_wgs, a.g.n_kv_heads), dim3(512), s, e0, e1, a);
+}
+
+hipError_t launch_step_write(const StepArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_k(step_write_kernel, dim3(n_wgs, a.ring.g.n_kv_heads), dim3(512), s, e0, e1, a);
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

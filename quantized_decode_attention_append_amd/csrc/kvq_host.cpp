@@ -572,6 +572,70 @@ kvq_status kvq_tail_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const int
   return KVQ_OK;
 }
 
+kvq_status kvq_append_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                            const void* k_bf16, const void* v_bf16, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (!n_new) return fail(KVQ_E_INVALID, "n_new is NULL");
+  const int W = c->cfg.tail_len;
+  const int R = c->lay.ring_slots;
+  // One launch only for a pure ring write plus an evict of rows that were in the ring before the call:
+  // then the ring writes and the body writes touch disjoint bytes and neither reads what the other writes.
+  bool fuse = W > 0 && n_seqs <= kvq::kStepBatch;
+  long total = 0;
+  for (int i = 0; i < n_seqs && fuse; ++i) {
+    if (n_new[i] < 0) { fuse = false; break; }   // reported by kvq_append
+    const int k = c->idx(layer, seq_ids[i]);
+    const int len = c->len[k], bl = c->body_len[k], n = n_new[i];
+    total += n;
+    if ((long)len + n > c->cfg.capacity) fuse = false;                      // reported by kvq_append
+    else if (n > 0 && c->cfg.kvarn && !c->calibrated[k]) fuse = false;       // calibration comes first
+    else if (len + n - bl > R) fuse = false;                                 // the append would evict itself
+    else if (std::max(bl, len + n - W) > len) fuse = false;                  // would evict rows of this call
+    else if (c->cfg.tail_dtype == KVQ_TAIL_Q8_0 && tiles_of(len, len + n) > R / kvq::kTile) fuse = false;
+  }
+  if (!fuse || total == 0 || !k_bf16 || !v_bf16) {
+    s = kvq_append(c, layer, n_seqs, seq_ids, n_new, k_bf16, v_bf16, stream);
+    return s != KVQ_OK ? s : kvq_tail_evict(c, layer, n_seqs, seq_ids, stream);
+  }
+  kvq::StepArgs a{};
+  a.ring.g = a.body.g = geometry(c);
+  a.ring.k_in = a.body.k_in = (const uint16_t*)k_bf16;
+  a.ring.v_in = a.body.v_in = (const uint16_t*)v_bf16;
+  a.ring.dst_ring = 1;
+  a.body.dst_ring = 0;
+  int ring_wgs = 0, body_wgs = 0, row = 0;
+  std::vector<int> target(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    const int len = c->len[k], bl = c->body_len[k], n = n_new[i];
+    const size_t slab = slab_offset(c, layer, seq_ids[i]);
+    target[i] = std::max(bl, len + n - W);
+    if (n > 0) {
+      a.ring.items[a.ring.n_items++] = kvq::WriteItem{slab, len, len + n, len, row, len / kvq::kTile, ring_wgs};
+      ring_wgs += tiles_of(len, len + n);
+    }
+    if (target[i] > bl) {
+      a.body.items[a.body.n_items++] = kvq::WriteItem{slab, bl, target[i], len + n, 0, bl / kvq::kTile, body_wgs};
+      body_wgs += tiles_of(bl, target[i]);
+    }
+    row += n;
+  }
+  a.ring_wgs = ring_wgs;
+  if (ring_wgs + body_wgs) {
+    hipError_t e = timed(c, KVQ_KERNEL_APPEND_EVICT, (hipStream_t)stream, [&](hipEvent_t e0, hipEvent_t e1) {
+      return kvq::launch_step_write(a, ring_wgs + body_wgs, (hipStream_t)stream, e0, e1);
+    });
+    if (e != hipSuccess) return hip_fail(e, "append/evict launch");
+  }
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    c->len[k] += n_new[i];
+    c->body_len[k] = target[i];
+  }
+  return KVQ_OK;
+}
+
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
                            float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
   kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);

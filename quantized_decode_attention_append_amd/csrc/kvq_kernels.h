@@ -61,6 +61,22 @@ struct WriteArgs {
   WriteItem items[kMaxBatch];
 };
 
+// A decode step's append (ring writes) and evict (body writes) in one launch; up to kStepBatch sequences.
+constexpr int kStepBatch = 32;
+struct StepRole {    // the members of WriteArgs, with room for kStepBatch items
+  Geometry g;
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  int dst_ring;
+  int n_items;
+  WriteItem items[kStepBatch];
+};
+struct StepArgs {
+  StepRole ring;     // ring writes of the new tokens (dst_ring = 1)
+  StepRole body;     // evict: ring rows requantized into the body (dst_ring = 0)
+  int ring_wgs;      // work-groups of the ring writes (the rest are body writes)
+};
+
 // ---------------------------------------------------------------- decode side
 
 struct DecodeSeq {
@@ -113,6 +129,8 @@ hipError_t launch_body_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEv
                              hipEvent_t e1 = nullptr);
 hipError_t launch_bf16_ring_write(const WriteArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0 = nullptr,
                                   hipEvent_t e1 = nullptr);
+hipError_t launch_step_write(const StepArgs& a, int n_wgs, hipStream_t s, hipEvent_t e0 = nullptr,
+                             hipEvent_t e1 = nullptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s, hipEvent_t e0 = nullptr,
                          hipEvent_t e1 = nullptr);

@@ -26,8 +26,8 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_decode_attn", "kvq_sparse_decode_attn", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
-KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4}
+           "kvq_append_evict", "kvq_decode_attn", "kvq_sparse_decode_attn", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5}
 
 
 class Config(ctypes.Structure):
@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "kvq_seq_lengths": (I32, [P, I32, I32, IP, IP]),
         "kvq_workspace_bytes": (SZ, [P, I32, I32]),
         "kvq_append": (I32, [P, I32, I32, IP, IP, P, P, P]),
+        "kvq_append_evict": (I32, [P, I32, I32, IP, IP, P, P, P]),
         "kvq_tail_evict": (I32, [P, I32, I32, IP, P]),
         "kvq_decode_attn": (I32, [P, I32, I32, IP, P, P, F, P, SZ, P]),
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
@@ -185,6 +186,14 @@ class Cache:
     def append(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor,
                v: torch.Tensor, stream=None):
         """k, v: bf16 (or int16/uint16 bit patterns) [sum(n_new), Hkv, D] on the device."""
+        self._append(_lib.kvq_append, layer, seq_ids, n_new, k, v, stream)
+
+    def append_evict(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor,
+                     v: torch.Tensor, stream=None):
+        """append() then tail_evict() on the same sequences (one kernel launch for a decode step)."""
+        self._append(_lib.kvq_append_evict, layer, seq_ids, n_new, k, v, stream)
+
+    def _append(self, fn, layer, seq_ids, n_new, k, v, stream):
         total = int(sum(int(n) for n in n_new))
         for name, t in (("k", k), ("v", v)):
             if t.numel() != total * self.hk * self.d:
@@ -194,8 +203,7 @@ class Cache:
         if total and k.element_size() != 2:
             raise ValueError("k/v must hold 16-bit bf16 values")
         nn = (ctypes.c_int32 * len(n_new))(*[int(n) for n in n_new])
-        _check(_lib.kvq_append(self._h, layer, len(seq_ids), _ids(seq_ids), nn, kp, vp,
-                               ctypes.c_void_p(_stream(stream))))
+        _check(fn(self._h, layer, len(seq_ids), _ids(seq_ids), nn, kp, vp, ctypes.c_void_p(_stream(stream))))
 
     def tail_evict(self, layer: int, seq_ids: Sequence[int], stream=None):
         _check(_lib.kvq_tail_evict(self._h, layer, len(seq_ids), _ids(seq_ids), ctypes.c_void_p(_stream(stream))))

@@ -44,8 +44,12 @@ def test_dense_decode_full_size(cfg_id):
     for st in range(max(1, min(2, wl.decode_steps))):
         k, v, q = step_inputs(wl, 0, st)
         if wl.decode_steps:   # the single-layer q8_0 workload decodes its prefill as is
-            p.append(0, seqs, [1] * wl.batch, k, v)
-            p.evict(0, seqs)
+            p.gpu.append_evict(0, seqs, [1] * wl.batch, dev(k), dev(v))
+            p.ora.append(0, seqs, [1] * wl.batch, k, v)
+            p.ora.tail_evict(0, seqs)
+            for seq in seqs:
+                p.lengths_match(0, seq)
+            p.assert_slab_equal(0, 0)
         got, want = p.decode(0, seqs, q)
         err = max_err(got, want)
         assert err <= TOL, f"{wl.name} step {st}: max abs error {err:.3e}"

@@ -9,7 +9,7 @@ import itertools
 import numpy as np
 import pytest
 
-from tests.gpu_util import Pair, TOL, max_err
+from tests.gpu_util import Pair, TOL, dev, max_err
 from workloads import small_tokens, small_query, channel_scales
 
 pytestmark = pytest.mark.gpu
@@ -174,3 +174,39 @@ def test_workspace_reused_across_calls_and_allocations():
         assert max_err(got, want) <= TOL, i
         del junk
 
+
+
+@pytest.mark.parametrize("tail_dtype,kvarn", [(1, 0), (2, 0), (1, 1), (0, 0)])
+def test_append_evict_matches_append_then_evict(tail_dtype, kvarn):
+    """kvq_append_evict against the oracle doing the two calls: decode steps (one launch), a batch with an
+    empty sequence, a chunk that evicts its own rows and the first (calibrating) append (two launches)."""
+    tail = 64 if tail_dtype else 0
+    c = cfg(tail_len=tail, tail_slack=32 if tail else 0, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=5, v_bits=4)
+    p = Pair(c)
+    k, v = small_tokens(70 + tail_dtype + 3 * kvarn, 600, 2, 256, scale=scales(9, "loguniform"))
+    q = small_query(11, 2, 16, 256)
+    off = 0
+
+    def step(seq_ids, ns):
+        nonlocal off
+        tot = sum(ns)
+        p.gpu.append_evict(1, seq_ids, ns, dev(k[off:off + tot]), dev(v[off:off + tot]))
+        p.ora.append(1, seq_ids, ns, k[off:off + tot], v[off:off + tot])
+        p.ora.tail_evict(1, seq_ids)
+        off += tot
+        for s in seq_ids:
+            p.lengths_match(1, s)
+            p.assert_slab_equal(1, s)
+
+    p.gpu.timing(True)             # counts the launches of each kernel kind
+    step([0, 2], [90, 5])          # first append: calibration, body writes, ring overflow
+    for _ in range(4):
+        step([0, 2], [1, 1])       # decode steps
+    step([2, 0], [0, 1])           # one sequence without a token
+    step([0], [100])               # a chunk longer than the window evicts rows of its own
+    step([0, 2], [1, 3])
+    fused = p.gpu.timing_read("append_evict")[1]
+    p.gpu.timing(False)
+    assert fused == (6 if tail_dtype else 0), fused   # the decode-style steps took the single launch
+    got, want = p.decode(1, [0, 2], q)
+    assert max_err(got, want) <= TOL
