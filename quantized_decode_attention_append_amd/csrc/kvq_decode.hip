@@ -317,60 +317,78 @@ struct TileRaw {
   u32x4 sc;                                       // 16 bytes of the K (lanes 0-31) or V (32-63) tile scales
 };
 
-// Issue the loads of one tile into `t` (kt: the K tile, vt: the V tile). Every load reads 1 KiB (or 512 B)
-// contiguous per wave: lane l's run of a K plane sits at [chunk][lane][16 B], like the V tile. With
-// live = false every lane reads the same 16 bytes at the start of kt / vt instead (a placeholder that costs
-// one cache line per instruction): the loads are then issued on every path, which keeps the compiler's
-// memory-counter waits exact across the tile loop.
+// Tile loads go through buffer resources: the tile's base address and size sit in SGPRs and every lane's
+// offset is fixed, so issuing the next tile's loads writes no VGPR besides their destinations (with VGPR
+// addresses the compiler reused registers of loads still in flight and had to wait for them first). A
+// resource of size 0 makes every load return zero without touching memory: the placeholder loads that keep
+// the compiler's memory-counter waits exact when a wave has no next tile.
+constexpr int kAuxNT = 2;                  // nontemporal (streaming) loads
+constexpr int kOutOfRange = 0x7FFFFFF0;    // lane offset beyond any tile: the load returns zero
+
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ inline u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxNT));
+}
+__device__ inline u32x2 bld8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAuxNT));
+}
+
+// One plane run of a K subtile: lane l's run is [chunk][lane][min(16, 8w) B] from byte `off` of the tile.
 template <int W>
-__device__ inline void load_run(const uint8_t* part, int ll, uint32_t* dst) {
+__device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int off, int lane, uint32_t* dst) {
   constexpr int words = 8 * W / 4;      // NB pieces of W bits x 8 codes
   if constexpr (words >= 4) {
 #pragma unroll
     for (int c = 0; c < words / 4; ++c) {
-      const u32x4 x = ldnt(part + c * 1024 + ll * 16);
+      const u32x4 x = bld16(r, lane * 16, off + c * 1024);
       dst[4 * c] = x[0]; dst[4 * c + 1] = x[1]; dst[4 * c + 2] = x[2]; dst[4 * c + 3] = x[3];
     }
   } else {
-    const u32x2 x = __builtin_nontemporal_load((const u32x2*)(part + ll * 8));
+    const u32x2 x = bld8(r, lane * 8, off);
     dst[0] = x[0]; dst[1] = x[1];
   }
 }
 
+// Issue the loads of one tile into `t` (kt / vt: the K and V tiles, kbytes / vbytes their sizes; live = false:
+// placeholder loads that return zero). Every load reads 1 KiB (or 512 B) contiguous per wave. Scales first,
+// then K, then V: the loads return in order, so staging the scales, QK and P.V each wait only for their own
+// part of the tile.
 template <int NK, int NV>
-__device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, const uint8_t* vt, bool live) {
+__device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, int kbytes, const uint8_t* vt, int vbytes,
+                                 bool live) {
   using T = TileRaw<NK, NV>;
   constexpr int NT = 16, D = 256;
   const int lane = threadIdx.x & 63;
-  const int ll = live ? lane : 0;
-  // scales first, then K, then V: the loads return in order, so staging the scales, QK and P.V each wait
-  // only for their own part of the tile
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, live ? kbytes : 0);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, live ? vbytes : 0);
   // scales, [block][position] fp16 in both tiles: lanes 0-31 take the K tile's 512 bytes, 32-63 the V tile's
-  const uint8_t* ksc = live ? kt + 4 * D * NK + 16 * lane : kt;
-  const uint8_t* vsc = live ? vt + 4 * D * NV + 16 * (lane - 32) : vt;
-  t.sc = ldnt(lane < 32 ? ksc : vsc);
+  const int sck = lane < 32 ? 4 * D * NK + 16 * lane : kOutOfRange;
+  const int scv = lane >= 32 ? 4 * D * NV + 16 * (lane - 32) : kOutOfRange;
+  t.sc = bld16(rk, sck, 0) | bld16(rv, scv, 0);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const uint8_t* sub = kt + 512 * NK * s;
-    load_run<T::w0k>(sub, ll, t.k0[s]);
-    if constexpr (T::w1k > 0) load_run<T::w1k>(sub + 512 * T::w0k, ll, t.k1[s]);
-    if constexpr (T::w2k > 0) load_run<T::w2k>(sub + 512 * (T::w0k + T::w1k), ll, t.k2[s]);
+    const int sub = 512 * NK * s;
+    load_run<T::w0k>(rk, sub, lane, t.k0[s]);
+    if constexpr (T::w1k > 0) load_run<T::w1k>(rk, sub + 512 * T::w0k, lane, t.k1[s]);
+    if constexpr (T::w2k > 0) load_run<T::w2k>(rk, sub + 512 * (T::w0k + T::w1k), lane, t.k2[s]);
   }
 #pragma unroll
   for (int c = 0; c < NT * T::w0v / 16; ++c) {
-    u32x4 x = ldnt(vt + c * 1024 + ll * 16);
+    const u32x4 x = bld16(rv, lane * 16, c * 1024);
     t.v0[4 * c] = x[0]; t.v0[4 * c + 1] = x[1]; t.v0[4 * c + 2] = x[2]; t.v0[4 * c + 3] = x[3];
   }
   if constexpr (T::w1v > 0) {
-    const uint8_t* p1 = vt + 64 * NT * T::w0v;
+    const int p1 = 64 * NT * T::w0v;
 #pragma unroll
     for (int c = 0; c < NT * T::w1v / 16; ++c) {
-      u32x4 x = ldnt(p1 + c * 1024 + ll * 16);
+      const u32x4 x = bld16(rv, lane * 16, p1 + c * 1024);
       t.v1[4 * c] = x[0]; t.v1[4 * c + 1] = x[1]; t.v1[4 * c + 2] = x[2]; t.v1[4 * c + 3] = x[3];
     }
   }
   if constexpr (T::w2v > 0) {
-    u32x4 x = ldnt(vt + 64 * NT * (T::w0v + T::w1v) + ll * 16);
+    const u32x4 x = bld16(rv, lane * 16, 64 * NT * (T::w0v + T::w1v));
     t.v2[0] = x[0]; t.v2[1] = x[1]; t.v2[2] = x[2]; t.v2[3] = x[3];
   }
 }
@@ -551,7 +569,7 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     for (;;) {
       int nt = grab_tile(s_next);
       bool more = nt < tile_end;
-      load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+      load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
                         more);
       stage(cur, s_buf);
       compute_tile<NK, NV>(st, cur, s_buf, qb, qmul, t, lo, hi, lane_mask, magic);
@@ -559,7 +577,7 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
       t = nt;
       nt = grab_tile(s_next);
       more = nt < tile_end;
-      load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+      load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
                         more);
       stage(nxt, s_buf + 64);
       compute_tile<NK, NV>(st, nxt, s_buf + 64, qb, qmul, t, lo, hi, lane_mask, magic);
@@ -574,7 +592,7 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     // the next tile's loads go out before this tile's scales are staged (which waits for this tile only)
     const int nt = grab_tile(s_next);
     const bool more = nt < tile_end;
-    load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+    load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
                       more);
     stage(cur, sb);
     compute_tile<NK, NV>(st, cur, sb, qb, qmul, t, lo, hi, lane_mask, magic);
@@ -653,7 +671,7 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
                                   uint32_t lane_mask, u32x4* sbuf, int* s_next, float* s_amax) {
   constexpr int NB = 8;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile addresses stay scalar
   const int gq = lane >> 4;
   TileRaw<NK, NV> cur, nxt;
   // Wave w prepares block w of the query operand. Its query (and KVarN sigma) loads go out before the
@@ -664,7 +682,7 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   KVQ_SB
   const int t0 = wb < we ? wb : we - 1;
   if constexpr (EARLY)
-    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_ptr(vbase, tile_v, ring, R, t0), wb < we);
+    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
   float x[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {   // q times sigma is exact in fp32 (8 + 11 bits)
@@ -706,7 +724,7 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   }
   __syncthreads();
   if constexpr (!EARLY)
-    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_ptr(vbase, tile_v, ring, R, t0), wb < we);
+    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
   const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e + 24);
   run_quant_tiles<NK, NV, unroll_tiles(NK, NV)>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
                           sbuf, s_next);
@@ -765,7 +783,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tb = seg_begin + (int)((long)sp * seg_tiles / nsp);
   const int te = seg_begin + (int)((long)(sp + 1) * seg_tiles / nsp);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses stay scalar
   const int lane = tid & 63;
   const int wb = tb + wave;
   const int we = te;
@@ -839,38 +857,48 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int r = 0; r < 4; ++r) st.o[n][r] = sum_xor32(st.o[n][r]);
-  if (gq < 2) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[wave][4 * gq + r][16 * n + m16] = st.o[n][r];
-  }
   if (lane < 8) {
     s_ml[wave][0][lane] = st.m;
     s_ml[wave][1][lane] = lsum;
   }
   __syncthreads();
+  // this wave's factor 2^(m_w - M) for the heads of its accumulator rows (4 gq + r), M = max over the waves
+  if (gq < 2) {
+    float f[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * gq + r;
+      float M = kNegBig;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);
+      f[r] = __builtin_amdgcn_exp2f(s_ml[wave][0][h] - M);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[wave][4 * gq + r][16 * n + m16] = st.o[n][r] * f[r];
+  }
+  __syncthreads();
 
-  // ---- merge the waves and write the partial of this split (512 threads: 2 heads x 256 channels per pass)
+  // ---- sum the waves' scaled outputs and write the partial of this split (512 threads: 2 heads x 256 channels)
   float* part = a.partials + (((size_t)si * g.n_kv_heads + head) * a.max_splits + split) * (kPartialHeads * (D + 2));
   const int c = tid & 255;
   const float vs = use_sigma ? h2f(sig[D + c]) : 1.0f;
+#pragma unroll
   for (int h = tid >> 8; h < kPartialHeads; h += 2) {
-    float M = kNegBig;
+    float O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_ml[w][0][h] - M);
-      L += s_ml[w][1][h] * f;
-      O += s_o[w][h][c] * f;
-    }
+    for (int w = 0; w < NW; ++w) O += s_o[w][h][c];
     part[2 * kPartialHeads + h * D + c] = O * vs;
-    if (c == 0) {
-      part[h] = M;
-      part[kPartialHeads + h] = L;
-    }
+  }
+  if (tid < kPartialHeads) {
+    float M = kNegBig, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][tid]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += s_ml[w][1][tid] * __builtin_amdgcn_exp2f(s_ml[w][0][tid] - M);
+    part[tid] = M;
+    part[kPartialHeads + tid] = L;
   }
 }
 
