@@ -356,7 +356,7 @@ __device__ inline void load_run(__amdgpu_buffer_rsrc_t r, int off, int lane, uin
 // then K, then V: the loads return in order, so staging the scales, QK and P.V each wait only for their own
 // part of the tile.
 template <int NK, int NV>
-__device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, int kbytes, const uint8_t* vt, int vbytes,
+__device__ inline void load_tile_k(TileRaw<NK, NV>& t, const uint8_t* kt, int kbytes, const uint8_t* vt, int vbytes,
                                  bool live) {
   using T = TileRaw<NK, NV>;
   constexpr int NT = 16, D = 256;
@@ -366,7 +366,7 @@ __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, int kbyt
   // scales, [block][position] fp16 in both tiles: lanes 0-31 take the K tile's 512 bytes, 32-63 the V tile's
   const int sck = lane < 32 ? 4 * D * NK + 16 * lane : kOutOfRange;
   const int scv = lane >= 32 ? 4 * D * NV + 16 * (lane - 32) : kOutOfRange;
-  t.sc = bld16(rk, sck, 0) | bld16(rv, scv, 0);
+  t.sc = bld16(rk, sck, 0);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int sub = 512 * NK * s;
@@ -374,6 +374,19 @@ __device__ inline void load_tile(TileRaw<NK, NV>& t, const uint8_t* kt, int kbyt
     if constexpr (T::w1k > 0) load_run<T::w1k>(rk, sub + 512 * T::w0k, lane, t.k1[s]);
     if constexpr (T::w2k > 0) load_run<T::w2k>(rk, sub + 512 * (T::w0k + T::w1k), lane, t.k2[s]);
   }
+}
+
+template <int NK, int NV>
+__device__ inline void load_tile_v(TileRaw<NK, NV>& t, const uint8_t* kt, int kbytes, const uint8_t* vt, int vbytes,
+                                 bool live) {
+  using T = TileRaw<NK, NV>;
+  constexpr int NT = 16, D = 256;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, live ? kbytes : 0);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, live ? vbytes : 0);
+  // scales, [block][position] fp16 in both tiles: lanes 0-31 take the K tile's 512 bytes, 32-63 the V tile's
+  const int scv = lane >= 32 ? 4 * D * NV + 16 * (lane - 32) : kOutOfRange;
+  t.sc |= bld16(rv, scv, 0);
 #pragma unroll
   for (int c = 0; c < NT * T::w0v / 16; ++c) {
     const u32x4 x = bld16(rv, lane * 16, c * 1024);
@@ -447,8 +460,8 @@ constexpr int kQbHalf8 = kQbPlanes * 8 * 64;
 // lane_mask is 0 on the hi-part lanes (rows 0-7 of the P operand) and ~0 on the lo-part lanes.
 // s_sc: this wave's LDS copy of the tile's scales: K as [block][row], then V as [block][position].
 template <int NK, int NV>
-__device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, const u32x4* s_sc, const half8* qb,
-                                    float qmul, int tile, int lo, int hi, uint32_t lane_mask, uint32_t magic) {
+__device__ inline void qk_part(const TileRaw<NK, NV>& t, const u32x4* s_sc, const half8* qb,
+                                    float qmul, int tile, int lo, int hi, float* x) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   float sc[2][4];
@@ -459,37 +472,51 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
   for (int i = 0; i < 8; ++i)
     kbias[i] = (_Float16)(-ldexpf(1.0f, NK - 1 + dn_bitpos(Planes<NK>::w[0], 0, i) - 24));
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[s][r] = 0.0f;
-    // block B's MFMAs are issued before block B+1 is decoded, and their result consumed after that, so the
-    // MFMA latency is covered by the next block's decode
-    KPlanes<NK> a_cur;
-    dn_piece<NK, 0>(t.k0[s], t.k1[s], t.k2[s], a_cur);
+  // Both 16-row subtiles block by block: one query operand read and one bias product serve both, and the two
+  // subtiles' MFMA chains are independent, so each covers the other's latency. Block B's MFMAs are issued
+  // before block B+1 is decoded, and their results consumed after that.
+  KPlanes<NK> a0, a1;
+  dn_piece<NK, 0>(t.k0[0], t.k1[0], t.k2[0], a0);
+  dn_piece<NK, 0>(t.k0[1], t.k1[1], t.k2[1], a1);
 #define KVQ_QK(B)                                                                                 \
-    {                                                                                             \
-      const half8 q0 = qb[B * 64 + lane];                                                         \
-      floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbias, q0, floatx4{0, 0, 0, 0}, 0, 0, 0);  \
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur.a[0], q0, c, 0, 0, 0);                     \
-      if constexpr (Planes<NK>::n >= 2 && NK != 8)                                                \
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur.a[Planes<NK>::n >= 2 && NK != 8 ? 1 : 0], \
-                                                   qb[512 + B * 64 + lane], c, 0, 0, 0);          \
-      if constexpr (Planes<NK>::n >= 3)                                                           \
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur.a[Planes<NK>::n >= 3 ? 2 : 0],            \
-                                                   qb[1024 + B * 64 + lane], c, 0, 0, 0);         \
-      if constexpr (B < 7) dn_piece<NK, (B < 7 ? B + 1 : 0)>(t.k0[s], t.k1[s], t.k2[s], a_cur);   \
-      const u32x2 dk = *(const u32x2*)(s_dk + B * 32 + 16 * s + 4 * g);                           \
-      sc[s][0] = fmaf(c[0], lo_h(dk[0]), sc[s][0]);                                               \
-      sc[s][1] = fmaf(c[1], hi_h(dk[0]), sc[s][1]);                                               \
-      sc[s][2] = fmaf(c[2], lo_h(dk[1]), sc[s][2]);                                               \
-      sc[s][3] = fmaf(c[3], hi_h(dk[1]), sc[s][3]);                                               \
-    }
-    // one block at a time (sched barriers): bounds the live decoded operands
-    KVQ_QK(0) KVQ_SB KVQ_QK(1) KVQ_SB KVQ_QK(2) KVQ_SB KVQ_QK(3) KVQ_SB
-    KVQ_QK(4) KVQ_SB KVQ_QK(5) KVQ_SB KVQ_QK(6) KVQ_SB KVQ_QK(7) KVQ_SB
-#undef KVQ_QK
+  {                                                                                               \
+    const half8 q0 = qb[B * 64 + lane];                                                           \
+    floatx4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbias, q0, floatx4{0, 0, 0, 0}, 0, 0, 0); \
+    floatx4 c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbias, q0, floatx4{0, 0, 0, 0}, 0, 0, 0); \
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.a[0], q0, c0, 0, 0, 0);                        \
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.a[0], q0, c1, 0, 0, 0);                        \
+    if constexpr (Planes<NK>::n >= 2 && NK != 8) {                                                \
+      const half8 q1 = qb[512 + B * 64 + lane];                                                   \
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.a[Planes<NK>::n >= 2 && NK != 8 ? 1 : 0], q1, c0, 0, 0, 0); \
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.a[Planes<NK>::n >= 2 && NK != 8 ? 1 : 0], q1, c1, 0, 0, 0); \
+    }                                                                                             \
+    if constexpr (Planes<NK>::n >= 3) {                                                           \
+      const half8 q2 = qb[1024 + B * 64 + lane];                                                  \
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.a[Planes<NK>::n >= 3 ? 2 : 0], q2, c0, 0, 0, 0); \
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.a[Planes<NK>::n >= 3 ? 2 : 0], q2, c1, 0, 0, 0); \
+    }                                                                                             \
+    if constexpr (B < 7) {                                                                        \
+      dn_piece<NK, (B < 7 ? B + 1 : 0)>(t.k0[0], t.k1[0], t.k2[0], a0);                           \
+      dn_piece<NK, (B < 7 ? B + 1 : 0)>(t.k0[1], t.k1[1], t.k2[1], a1);                           \
+    }                                                                                             \
+    const u32x2 dk0 = *(const u32x2*)(s_dk + B * 32 + 4 * g);                                     \
+    const u32x2 dk1 = *(const u32x2*)(s_dk + B * 32 + 16 + 4 * g);                                \
+    sc[0][0] = fmaf(c0[0], lo_h(dk0[0]), sc[0][0]);                                               \
+    sc[0][1] = fmaf(c0[1], hi_h(dk0[0]), sc[0][1]);                                               \
+    sc[0][2] = fmaf(c0[2], lo_h(dk0[1]), sc[0][2]);                                               \
+    sc[0][3] = fmaf(c0[3], hi_h(dk0[1]), sc[0][3]);                                               \
+    sc[1][0] = fmaf(c1[0], lo_h(dk1[0]), sc[1][0]);                                               \
+    sc[1][1] = fmaf(c1[1], hi_h(dk1[0]), sc[1][1]);                                               \
+    sc[1][2] = fmaf(c1[2], lo_h(dk1[1]), sc[1][2]);                                               \
+    sc[1][3] = fmaf(c1[3], hi_h(dk1[1]), sc[1][3]);                                               \
   }
-  float x[8], p[8];
+  // one block at a time (sched barriers): bounds the live decoded operands
+  KVQ_QK(0) KVQ_SB KVQ_QK(1) KVQ_SB KVQ_QK(2) KVQ_SB KVQ_QK(3) KVQ_SB
+  KVQ_QK(4) KVQ_SB KVQ_QK(5) KVQ_SB KVQ_QK(6) KVQ_SB KVQ_QK(7) KVQ_SB
+#undef KVQ_QK
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -503,7 +530,13 @@ __device__ inline void compute_tile(WaveState& st, const TileRaw<NK, NV>& t, con
         if (pos < lo || pos >= hi) x[4 * s + r] = -INFINITY;
       }
   }
-  softmax_update(st, x, p);
+}
+
+template <int NK, int NV>
+__device__ inline void pv_part(WaveState& st, const TileRaw<NK, NV>& t, const u32x4* s_sc, const float* p, uint32_t lane_mask, uint32_t magic) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+
   // P masked to zero on the hi-part lanes: there the hi part below is P * dv itself
   float pm[8];
 #pragma unroll
@@ -569,18 +602,32 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     for (;;) {
       int nt = grab_tile(s_next);
       bool more = nt < tile_end;
-      load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
-                        more);
+      load_tile_k<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
+                          more);
       stage(cur, s_buf);
-      compute_tile<NK, NV>(st, cur, s_buf, qb, qmul, t, lo, hi, lane_mask, magic);
+      {
+        float x[8], p[8];
+        qk_part<NK, NV>(cur, s_buf, qb, qmul, t, lo, hi, x);
+        load_tile_v<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+                            tile_v, more);
+        softmax_update(st, x, p);
+        pv_part<NK, NV>(st, cur, s_buf, p, lane_mask, magic);
+      }
       if (!more) break;
       t = nt;
       nt = grab_tile(s_next);
       more = nt < tile_end;
-      load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
-                        more);
+      load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
+                          more);
       stage(nxt, s_buf + 64);
-      compute_tile<NK, NV>(st, nxt, s_buf + 64, qb, qmul, t, lo, hi, lane_mask, magic);
+      {
+        float x[8], p[8];
+        qk_part<NK, NV>(nxt, s_buf + 64, qb, qmul, t, lo, hi, x);
+        load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+                            tile_v, more);
+        softmax_update(st, x, p);
+        pv_part<NK, NV>(st, nxt, s_buf + 64, p, lane_mask, magic);
+      }
       if (!more) break;
       t = nt;
     }
@@ -592,10 +639,17 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     // the next tile's loads go out before this tile's scales are staged (which waits for this tile only)
     const int nt = grab_tile(s_next);
     const bool more = nt < tile_end;
-    load_tile<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
-                      more);
+    load_tile_k<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
+                        more);
     stage(cur, sb);
-    compute_tile<NK, NV>(st, cur, sb, qb, qmul, t, lo, hi, lane_mask, magic);
+    {
+      float x[8], p[8];
+      qk_part<NK, NV>(cur, sb, qb, qmul, t, lo, hi, x);
+      load_tile_v<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+                          tile_v, more);
+      softmax_update(st, x, p);
+      pv_part<NK, NV>(st, cur, sb, p, lane_mask, magic);
+    }
     if (nt >= tile_end) break;
     t = nt;
     cur = nxt;
@@ -681,8 +735,10 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   if (qa.use_sigma) sraw = *(const u32x4*)(qa.sig + 32 * wave + 8 * gq);
   KVQ_SB
   const int t0 = wb < we ? wb : we - 1;
-  if constexpr (EARLY)
-    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+  if constexpr (EARLY) {
+    load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+    load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+  }
   float x[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {   // q times sigma is exact in fp32 (8 + 11 bits)
@@ -723,8 +779,10 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
     }
   }
   __syncthreads();
-  if constexpr (!EARLY)
-    load_tile<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+  if constexpr (!EARLY) {
+    load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+    load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+  }
   const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e + 24);
   run_quant_tiles<NK, NV, unroll_tiles(NK, NV)>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
                           sbuf, s_next);

@@ -182,26 +182,32 @@ struct SplitPlan {
 SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out) {
   const int hk = c->cfg.n_kv_heads;
   const int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
+  // Cost of a tile in a work-group's time: a qN_0 tile (body or q8_0 ring) is decode- and MFMA-bound, a bf16
+  // ring tile carries 2.7x the bytes of a K6/V5 tile with little decode and no prefetch: it counts double.
+  const double ring_w = c->cfg.tail_dtype == KVQ_TAIL_BF16 ? 2.0 : 1.0;
   int tiles[2 * KVQ_MAX_BATCH], nwg[2 * KVQ_MAX_BATCH];
-  long total = 0;
+  double wt[2 * KVQ_MAX_BATCH];
+  double total = 0;
   for (int i = 0; i < n_seqs; ++i) {
     tiles[2 * i] = (body_len[i] + kvq::kTile - 1) / kvq::kTile;
     tiles[2 * i + 1] =
         len[i] > body_len[i] ? (len[i] + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
-    total += tiles[2 * i] + tiles[2 * i + 1];
+    wt[2 * i] = tiles[2 * i];
+    wt[2 * i + 1] = ring_w * tiles[2 * i + 1];
+    total += wt[2 * i] + wt[2 * i + 1];
   }
   int used = 0;
   for (int k = 0; k < 2 * n_seqs; ++k) {
-    nwg[k] = tiles[k] ? std::max(1, (int)((long)budget_h * tiles[k] / std::max(total, 1L))) : 0;
+    nwg[k] = tiles[k] ? std::max(1, (int)(budget_h * wt[k] / std::max(total, 1.0))) : 0;
     nwg[k] = std::min(nwg[k], tiles[k]);
     used += nwg[k];
   }
-  for (; used < budget_h; ++used) {   // leftover: the segment with the most tiles per work-group
+  for (; used < budget_h; ++used) {   // leftover: the segment with the most cost per work-group
     int best = -1;
-    double best_r = 1.0;
+    double best_r = 0.0;
     for (int k = 0; k < 2 * n_seqs; ++k)
-      if (nwg[k] && nwg[k] < tiles[k] && (double)tiles[k] / nwg[k] > best_r) {
-        best_r = (double)tiles[k] / nwg[k];
+      if (nwg[k] && nwg[k] < tiles[k] && wt[k] / nwg[k] > best_r) {
+        best_r = wt[k] / nwg[k];
         best = k;
       }
     if (best < 0) break;
