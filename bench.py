@@ -248,8 +248,19 @@ def main() -> int:
         log(f"copy calibration: one device copy of {nb} bytes")
         del src, dst
 
+    fused = appends and not sparse and wl.tail_len > 0 and cfg.get("layout", 0) == 0
+
     def step(st, nbytes=None):
         for layer in range(L):
+            if fused:   # append one token, requantize the one leaving the window and attend: one call
+                if nbytes is not None:
+                    lens = [cache.lengths(layer, s) for s in seqs]
+                    W_ = wl.tail_len
+                    nbytes.append(decode_call_bytes(cfg, [x[0] + 1 for x in lens],
+                                                    [max(x[1], x[0] + 1 - W_) for x in lens]))
+                cache.decode_step(layer, seqs, kin_d[st, layer], vin_d[st, layer], qin_d[st, layer], out=out[layer],
+                                  workspace=ws)
+                continue
             if appends:   # append one token and requantize the one leaving the window: one launch
                 cache.append_evict(layer, seqs, ones, kin_d[st, layer], vin_d[st, layer])
             if sparse:
@@ -316,7 +327,8 @@ def main() -> int:
                    "tail_dtype": ["none", "bf16", "q8_0"][wl.tail_dtype], "budget": wl.budget,
                    "layout": ["tiles", "rows"][cfg.get("layout", 0)],
                    "step": ("per layer: append 1 token, sparse decode over the step's position list" if sparse
-                            else "per layer: append 1 token, evict 1 tail token, decode attention" if appends
+                            else "per layer: append 1 token, evict 1 tail token, decode attention (one call)"
+                            if fused else "per layer: append 1 token, evict 1 tail token, decode attention" if appends
                             else "per layer: decode attention")},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attended_tok_per_s_per_layer": round(attended * args.steps / elapsed, 1),

@@ -150,6 +150,16 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
                            const void* q_bf16, float* out, float softmax_scale, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* One decode step of every listed sequence: append one token each (k_bf16, v_bf16: device bf16
+ * [n_seqs][Hkv][D]) and requantize the ring rows that leave the window, then dense decode attention, with
+ * the results of kvq_append_evict (n_new = 1 each) followed by kvq_decode_attn. With the tile layout and a
+ * ring, when the step is a ring write plus the requantization of rows that were in the ring before the call
+ * (every step after the prefill), the writes are done inside the decode launch by the work-groups that read
+ * those tiles, before they read them; otherwise the calls run in turn. Arguments and errors as those calls. */
+kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                           const void* k_bf16, const void* v_bf16, const void* q_bf16, float* out,
+                           float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
+
 /* Sparse decode attention over an indexer budget (offload page, QSA: the layer reads only the
  * main-KV rows at the positions the indexer chose, so the budget, not the context, bounds the bytes).
  * positions: device int32 [n_seqs][budget], one list per sequence shared by all KV heads; entries are

@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include "kvq_kernels.h"
+#include "kvq_write.h"
 
 namespace kvq {
 namespace {
@@ -788,6 +789,38 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
                           sbuf, s_next);
 }
 
+// One write of a fused decode step, with the members the shared write code reads.
+struct StepWriteView {
+  const Geometry& g;
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  int dst_ring;
+  int n_items;
+  WriteItem items[1];
+};
+
+// The writes of a fused decode step that fall to this work-group, done by all its threads before any of them
+// reads the cache: the last ring split writes the appended token into the ring, the last body split
+// requantizes the ring rows leaving the window into the body (the tiles they land in belong to that split).
+__device__ inline void step_writes(const DecodeArgs& a, const DecodeSeq& S, int si, int head, int split, bool is_ring) {
+  const int n_splits = S.n_body_splits + S.n_ring_splits;
+  if (is_ring && split == n_splits - 1 && S.app_pos >= 0) {
+    const StepWriteView w{a.g, a.k_in, a.v_in, 1, 1,
+                          {WriteItem{S.slab, S.app_pos, S.app_pos + 1, S.app_pos, si, S.app_pos / kTile, 0}}};
+    if (a.g.tail_dtype == 1) bf16_ring_write_wg(w, 0, head);
+    else body_write_wg(w, 0, head);
+  } else if (!is_ring && split == S.n_body_splits - 1 && S.ev1 > S.ev0) {
+    const StepWriteView w{a.g, a.k_in, a.v_in, 0, 1,
+                          {WriteItem{S.slab, S.ev0, S.ev1, S.len, 0, S.ev0 / kTile, 0}}};
+    body_write_wg(w, 0, head);
+  } else {
+    return;
+  }
+  // the writes are complete (and visible to this work-group) before its waves load any tile
+  __threadfence_block();
+  __syncthreads();
+}
+
 // One work-group of 8 waves (two per SIMD) per split; the host sizes the splits so that there is about one
 // work-group per CU. The waves claim the split's tiles one at a time from an LDS counter (the two waves of
 // a SIMD do not get equal issue slots, so a static share would leave one of them finishing late); the
@@ -817,6 +850,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int head = rem / n_splits;
   const int split = rem % n_splits;
   const bool is_ring = split >= S.n_body_splits;
+  if (a.step) step_writes(a, S, si, head, split, is_ring);
   const int tail = g.tail_dtype;
   const int R = g.ring_slots;
   const uint8_t* slab = g.arena + S.slab;
@@ -837,9 +871,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lo = S.body_len;
     hi = S.len;
   }
-  // this split's tiles [tb, te): wave w starts with tile tb + w, further tiles come from s_next
-  const int tb = seg_begin + (int)((long)sp * seg_tiles / nsp);
-  const int te = seg_begin + (int)((long)(sp + 1) * seg_tiles / nsp);
+  // this split's tiles [tb, te): wave w starts with tile tb + w, further tiles come from s_next. A body split
+  // that also requantizes rows of a fused decode step starts late: the last body split then takes the tiles
+  // from last_tb on and the others share [0, last_tb) evenly.
+  int tb, te;
+  if (!is_ring && S.last_tb > 0 && nsp > 1) {
+    tb = sp == nsp - 1 ? S.last_tb : (int)((long)sp * S.last_tb / (nsp - 1));
+    te = sp == nsp - 1 ? seg_tiles : (int)((long)(sp + 1) * S.last_tb / (nsp - 1));
+  } else {
+    tb = seg_begin + (int)((long)sp * seg_tiles / nsp);
+    te = seg_begin + (int)((long)(sp + 1) * seg_tiles / nsp);
+  }
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses stay scalar
   const int lane = tid & 63;

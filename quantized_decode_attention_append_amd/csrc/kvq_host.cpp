@@ -682,6 +682,86 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   return launch_combine_for(c, n_seqs, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
 }
 
+// Tiles the work-group that requantizes a decode step's evicted rows gives up (about the time those writes take).
+constexpr int kStepHandicap = 4;
+
+kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* k_bf16,
+                           const void* v_bf16, const void* q_bf16, float* out, float softmax_scale, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  const int W = c->cfg.tail_len;
+  const int R = c->lay.ring_slots;
+  // One launch when every sequence's step is a ring write plus the requantization of at most the rows of one
+  // position tile that were in the ring before the call (the tiles the writes touch then belong to the last
+  // ring split and the last body split, which write before they read); otherwise the calls run in turn.
+  bool fuse = W > 0 && c->cfg.layout == KVQ_LAYOUT_TILES && k_bf16 && v_bf16 && q_bf16 && out && workspace &&
+              ((uintptr_t)workspace) % 256 == 0 && std::isfinite(softmax_scale);
+  int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH], target[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs && fuse; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    len[i] = c->len[k];
+    bl[i] = c->body_len[k];
+    target[i] = std::max(bl[i], len[i] + 1 - W);
+    if ((long)len[i] + 1 > c->cfg.capacity) fuse = false;                 // reported by kvq_append
+    else if (c->cfg.kvarn && !c->calibrated[k]) fuse = false;             // calibration comes first
+    else if (len[i] + 1 - bl[i] > R) fuse = false;                        // the append would evict itself
+    else if (target[i] > len[i]) fuse = false;                            // would evict the new token
+    else if (target[i] > bl[i] && bl[i] / kvq::kTile != (target[i] - 1) / kvq::kTile) fuse = false;
+  }
+  if (!fuse) {
+    int32_t ones[KVQ_MAX_BATCH];
+    for (int i = 0; i < n_seqs; ++i) ones[i] = 1;
+    s = kvq_append_evict(c, layer, n_seqs, seq_ids, ones, k_bf16, v_bf16, stream);
+    return s != KVQ_OK ? s : kvq_decode_attn(c, layer, n_seqs, seq_ids, q_bf16, out, softmax_scale, workspace, ws_bytes,
+                                              stream);
+  }
+  int len_new[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) len_new[i] = len[i] + 1;
+  kvq::DecodeArgs a{};
+  a.g = geometry(c);
+  const SplitPlan p = plan_splits(c, n_seqs, len_new, target, a.seqs);
+  if (p.max_splits > kvq::kMaxSplits) return fail(KVQ_E_INVALID, "too many splits (%d)", p.max_splits);
+  const size_t need = (size_t)n_seqs * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  for (int i = 0; i < n_seqs; ++i) {
+    a.seqs[i].slab = slab_offset(c, layer, seq_ids[i]);
+    a.seqs[i].app_pos = len[i];
+    a.seqs[i].ev0 = bl[i];
+    a.seqs[i].ev1 = target[i];
+    // the last body split requantizes the evicted rows before it reads anything: it takes kStepHandicap
+    // fewer tiles than an even share (when that leaves it at least one)
+    const int nsp = a.seqs[i].n_body_splits;
+    const int tiles = (target[i] + kvq::kTile - 1) / kvq::kTile;
+    if (target[i] > bl[i] && nsp > 1) {
+      const int share = tiles / nsp;
+      if (share > kStepHandicap) a.seqs[i].last_tb = tiles - (share - kStepHandicap);
+    }
+  }
+  a.q = (const uint16_t*)q_bf16;
+  a.out = out;
+  a.partials = (float*)workspace;
+  a.k_in = (const uint16_t*)k_bf16;
+  a.v_in = (const uint16_t*)v_bf16;
+  a.step = 1;
+  a.n_seqs = n_seqs;
+  a.n_q_heads = c->cfg.n_q_heads;
+  a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  a.max_splits = p.max_splits;
+  a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
+  hipError_t e = timed(c, KVQ_KERNEL_DECODE, (hipStream_t)stream,
+                       [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_decode(a, p.total_wgs, (hipStream_t)stream, e0, e1); });
+  if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  for (int i = 0; i < n_seqs; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    c->len[k] = len_new[i];
+    c->body_len[k] = target[i];
+  }
+  int n_splits[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
+  return launch_combine_for(c, n_seqs, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
+}
+
 kvq_status kvq_sparse_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                   const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
                                   float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {

@@ -84,16 +84,26 @@ struct DecodeSeq {
   int len, body_len;
   int n_body_splits, n_ring_splits;
   int ring_tile0;    // first position tile of the ring range (body_len / 32)
+  // fused decode step (step != 0): the token appended at position app_pos (input row = sequence index; -1:
+  // none) is written into the ring by the work-group of the last ring split, the ring rows [ev0, ev1) that
+  // leave the window are requantized into the body by the work-group of the last body split, each before
+  // it reads those tiles
+  int app_pos, ev0, ev1;
+  int last_tb;       // > 0: first tile of the last body split (the others share the tiles before it)
 };
 struct DecodeArgs {
   Geometry g;
   const uint16_t* q;           // [n_seqs][Hq][D] bf16
   float* out;                  // [n_seqs][Hq][D]
   float* partials;             // [n_seqs][Hkv][max_splits][8 * (D + 2)]
+  const uint16_t* k_in;        // fused decode step: the appended K and V tokens [n_seqs][Hkv][D] bf16
+  const uint16_t* v_in;
+  int step;
   int n_seqs, n_q_heads, group, max_splits;
   float scale;                 // softmax scale
   DecodeSeq seqs[kMaxBatch];
 };
+
 
 // Gather decode over a list of positions of a row-layout cache (sparse decode), or over all positions
 // (dense decode of a row-layout cache: positions == nullptr, entry i is position i).

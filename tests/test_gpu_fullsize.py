@@ -7,6 +7,7 @@ whole context in fp64 (about a second per call at 65,536 positions)."""
 import numpy as np
 import pytest
 
+import oracle
 import workloads as W
 from tests.gpu_util import TOL, Pair, dev, max_err
 
@@ -44,13 +45,16 @@ def test_dense_decode_full_size(cfg_id):
     for st in range(max(1, min(2, wl.decode_steps))):
         k, v, q = step_inputs(wl, 0, st)
         if wl.decode_steps:   # the single-layer q8_0 workload decodes its prefill as is
-            p.gpu.append_evict(0, seqs, [1] * wl.batch, dev(k), dev(v))
+            # as bench.py runs a step: append, evict and decode in one call
+            got = p.gpu.decode_step(0, seqs, dev(k), dev(v), dev(q)).cpu().numpy()
             p.ora.append(0, seqs, [1] * wl.batch, k, v)
             p.ora.tail_evict(0, seqs)
             for seq in seqs:
                 p.lengths_match(0, seq)
             p.assert_slab_equal(0, 0)
-        got, want = p.decode(0, seqs, q)
+            want = oracle.decode_reference(p.ora, 0, seqs, q)
+        else:
+            got, want = p.decode(0, seqs, q)
         err = max_err(got, want)
         assert err <= TOL, f"{wl.name} step {st}: max abs error {err:.3e}"
         for _ in range(2):

@@ -15,6 +15,11 @@ from workloads import small_tokens, small_query, channel_scales
 pytestmark = pytest.mark.gpu
 
 
+def oracle_decode(p, layer, seq_ids, q):
+    import oracle
+    return oracle.decode_reference(p.ora, layer, seq_ids, q)
+
+
 def cfg(**kw):
     c = dict(n_layers=2, max_seqs=3, capacity=512, n_q_heads=16, n_kv_heads=2, head_dim=256, k_bits=6,
              v_bits=5, kvarn=0, tail_len=0, tail_slack=0, tail_dtype=0)
@@ -210,3 +215,37 @@ def test_append_evict_matches_append_then_evict(tail_dtype, kvarn):
     assert fused == (6 if tail_dtype else 0), fused   # the decode-style steps took the single launch
     got, want = p.decode(1, [0, 2], q)
     assert max_err(got, want) <= TOL
+
+
+@pytest.mark.parametrize("tail_dtype,kvarn,n_seqs", [(1, 0, 1), (2, 0, 2), (1, 1, 3), (2, 1, 1)])
+def test_decode_step_matches_append_evict_decode(tail_dtype, kvarn, n_seqs):
+    """kvq_decode_step (the append and evict written inside the decode launch) against the oracle doing append,
+    evict and decode: ring bytes, body bytes and outputs after every step, for sequences whose ring is below the
+    window (no requantization yet), just filling it, and in steady state."""
+    c = cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=6, v_bits=5, capacity=1024)
+    p = Pair(c)
+    rng_seed = 90 + tail_dtype + 2 * kvarn + 5 * n_seqs
+    k, v = small_tokens(rng_seed, 1200, 2, 256, scale=scales(7, "loguniform"))
+    seqs = list(range(n_seqs))
+    off = 0
+    # a prefill below and one above the window for the first sequence, shorter ones for the others
+    for i, n in zip(seqs, (150, 40, 63)):
+        p.append(1, [i], [n], k[off:off + n], v[off:off + n])
+        off += n
+    p.evict(1, seqs)
+    p.gpu.timing(True)
+    for step in range(6):
+        kk, vv = k[off:off + n_seqs], v[off:off + n_seqs]
+        off += n_seqs
+        q = small_query(rng_seed + step, n_seqs, 16, 256)
+        got = p.gpu.decode_step(1, seqs, dev(kk), dev(vv), dev(q)).cpu().numpy()
+        p.ora.append(1, seqs, [1] * n_seqs, kk, vv)
+        p.ora.tail_evict(1, seqs)
+        want = oracle_decode(p, 1, seqs, q)
+        for i in seqs:
+            p.lengths_match(1, i)
+            p.assert_slab_equal(1, i)
+        assert max_err(got, want) <= TOL, f"step {step}: {max_err(got, want):.3e}"
+    separate = p.gpu.timing_read("append")[1] + p.gpu.timing_read("append_evict")[1]
+    p.gpu.timing(False)
+    assert separate == 0, separate   # every step ran in the decode launch
