@@ -683,7 +683,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
 }
 
 // Tiles the work-group that requantizes a decode step's evicted rows gives up (about the time those writes take).
-constexpr int kStepHandicap = 4;
+constexpr int kStepHandicap = 8;
 
 kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* k_bf16,
                            const void* v_bf16, const void* q_bf16, float* out, float softmax_scale, void* workspace,
