@@ -712,7 +712,8 @@ __device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, co
 // ------------------------------------------------------------------ the split kernel
 
 struct QArgs {
-  const uint16_t* qrow;   // this lane's query head (bf16)
+  const uint16_t* qgroup; // the query heads of this KV head's group (bf16 [group][D]), a uniform address
+  int group;
   const uint16_t* sig;    // KVarN sigma of this KV head ([K,V][D] fp16)
   bool use_sigma, head_ok, lo_lane;
   float scale;
@@ -731,7 +732,10 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   TileRaw<NK, NV> cur, nxt;
   // Wave w prepares block w of the query operand. Its query (and KVarN sigma) loads go out before the
   // first tile's: issued behind the tile loads they would wait for the work-group's tile traffic.
-  const u32x4 qraw = *(const u32x4*)(qa.qrow + 32 * wave + 8 * gq);
+  // this lane's head row, computed here from the lane id (a per-lane pointer kept from the kernel's start
+  // would stay live through the other wave path's tile loop)
+  const int hh = lane & 7;
+  const u32x4 qraw = *(const u32x4*)(qa.qgroup + (hh < qa.group ? hh : 0) * 256 + 32 * wave + 8 * gq);
   u32x4 sraw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
   if (qa.use_sigma) sraw = *(const u32x4*)(qa.sig + 32 * wave + 8 * gq);
   KVQ_SB
@@ -926,7 +930,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   } else {
     const uint32_t lane_mask = lo_lane ? 0xFFFFFFFFu : 0u;
-    const QArgs qa{qrow, sig, use_sigma, head_ok, lo_lane, a.scale};
+    const QArgs qa{a.q + ((size_t)si * a.n_q_heads + (size_t)head * a.group) * D, a.group, sig, use_sigma, head_ok,
+                   lo_lane, a.scale};
     u32x4* sbuf = &s_scales[wave][0][0];
     if (!is_ring) {
       const uint8_t* kbase = slab + g.k_body + (size_t)head * (g.cap32 / kTile) * g.tile_k;
