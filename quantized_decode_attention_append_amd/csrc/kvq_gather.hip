@@ -238,17 +238,28 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const bool kvarn = g.kvarn != 0;
   const uint16_t* sig = (const uint16_t*)(slab + g.sigma) + (size_t)head * 2 * D;
 
-  // query of the group's heads (and times sigma_K for body rows), [channel][head] in LDS
-  for (int e = tid; e < D * G; e += 256) {
-    const int h = e / D, c = e % D;
-    float qv = 0.0f;
-    if (h < a.group) qv = bf16f(a.q[((size_t)si * a.n_q_heads + head * a.group + h) * D + c]);
-    s_q[0][c][h] = qv;
-    s_q[1][c][h] = kvarn ? qv * f16f(sig[c]) : qv;   // exact (8 + 11 bits)
+  // query of the group's heads (and times sigma_K for body rows), [channel][head] in LDS: thread (h, c0) reads
+  // 8 channels of head h with one 16-byte load (one round trip for the whole work-group)
+  {
+    const int h = tid >> 5, c0 = 8 * (tid & 31);
+    u32x4 qw = {0u, 0u, 0u, 0u};
+    if (h < a.group) qw = *(const u32x4*)(a.q + ((size_t)si * a.n_q_heads + head * a.group + h) * D + c0);
+    u32x4 sw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
+    if (kvarn) sw = *(const u32x4*)(sig + c0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float qv = bf16f((qw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      s_q[0][c0 + i][h] = qv;
+      s_q[1][c0 + i][h] = qv * f16f((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);   // exact (8 + 11 bits)
+    }
   }
   float sv[4];   // sigma_V of this lane's P.V channels
+  {
+    u32x2 vw = {0x3C003C00u, 0x3C003C00u};
+    if (kvarn) vw = *(const u32x2*)(sig + D + 4 * lane);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) sv[k] = kvarn ? f16f(sig[D + 4 * lane + k]) : 1.0f;
+    for (int k = 0; k < 4; ++k) sv[k] = f16f((vw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+  }
   __syncthreads();
 
   const int ib = (int)((long)split * S.n_list / S.n_splits);
