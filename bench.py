@@ -169,6 +169,48 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
             "tok_per_s_per_layer": round(steps * (ctx + steps / 2) / t_total, 1)}
 
 
+def graph_steps(torch, step, first: int, n: int, n_layers: int) -> float:
+    """Seconds per step with each step's launches (all layers) captured into one HIP graph beforehand.
+
+    Capturing runs no kernel but advances the cache's host state, so steps first .. first+n-1 are captured
+    in order and their graphs replayed in the same order: the device work is that of n ordinary steps, without
+    the per-launch host overhead."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+                step(first + i)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    log(f"graph: {n} steps of {n_layers} layers, {dt * 1e3:.4f} ms per step")
+    return dt
+
+
+def cold_calls(torch, cache, seqs, q, out, ws, n: int) -> dict:
+    """Decode call time with the cache's lines evicted from L2 and the 256 MB MALL first (a 512 MiB write
+    before every call), from the library's launch timing."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cache.timing(True)
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        cache.decode_attn(0, seqs, q, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t = {k: cache.timing_read(k) for k in ("decode", "combine")}
+    cache.timing(False)
+    del scratch
+    return {"kernel_us": {k: round(v[0] * 1e3 / v[1], 3) for k, v in t.items() if v[1]},
+            "how": "each decode call after a 512 MiB device write (L2 and MALL evicted)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,7 +232,8 @@ def main() -> int:
     from quantized_decode_attention_append_amd import kvq
 
     wl = W.workload(args.config)
-    total_steps = args.warmup + 2 * args.steps   # warmup, timed steps, then as many steps with kernel timing
+    # warmup, timed steps, as many steps with kernel timing, then as many captured as HIP graphs
+    total_steps = args.warmup + 3 * args.steps
     ctx = list(wl.contexts)
     cfg = wl.cache_config(capacity=((max(ctx) + total_steps + 8 + 31) // 32) * 32)
     L, B = wl.n_layers, wl.batch
@@ -295,6 +338,8 @@ def main() -> int:
     torch.cuda.synchronize()
     times = {k: cache.timing_read(k) for k in ("decode", "gather", "combine", "append", "evict", "append_evict")}
     cache.timing(False)
+    graph = graph_steps(torch, step, args.warmup + 2 * args.steps, args.steps, L)
+    cold = cold_calls(torch, cache, seqs, qin_d[0, 0], out[0], ws, args.steps) if (L == 1 and not appends) else None
 
     main_kernel = "gather" if (sparse or cfg.get("layout", 0) == 1) else "decode"
     ms, n = times[main_kernel]
@@ -338,6 +383,12 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": kname, "bytes_per_launch": int(bytes_per_launch)},
     }
+    gbytes = float(sum(nbytes)) / args.steps   # the graph steps read the same bytes per step (to a few rows)
+    res["graph"] = {"ms_per_step": round(graph * 1e3, 4), "value": round(gbytes / graph / 1e9, 2), "unit": "GB/s",
+                    "how": f"one HIP graph per step ({L} layers), all {args.steps} captured before timing, "
+                           "replayed back to back"}
+    if cold is not None:
+        res["cold"] = cold
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

@@ -3,66 +3,69 @@
 // over all positions of a row-layout cache (dense decode with KVQ_LAYOUT_ROWS, list = 0..len-1).
 //
 // Every listed position is one K row and one V row, so the bytes read are exactly budget x row bytes.
-// The work is small (a budget of 2048 positions is ~2 MB per layer) and latency-bound, so the kernel is
-// plain VALU arithmetic in fp32; no tile staging:
+// A budget of 2048 positions is ~2 MB per layer: the call is latency-bound, and what sets its time is the
+// length of one wave's instruction stream. So:
 //
-// * grid (split, KV head, sequence); a work-group of 4 waves owns a contiguous range of list entries and
+// * grid (split, KV head, sequence); a work-group of 8 waves owns a contiguous range of list entries and
 //   emits one partial (m, l, o) per query head of the group, merged by the same combine kernel as the
 //   dense path;
-// * a wave takes 16 list entries at a time. For QK, lane (p = lane & 15, j = lane >> 4) reads the pieces
-//   (j, b = 0..7) of entry p's K row (channels 32b + 8j + i, contiguous in the row) and forms the 8 heads'
-//   partial dot products with the query read from LDS; the 4 partial sums of a position are added by lane
-//   shuffles;
-// * online softmax in exp2 form (wave-wide max per head);
-// * for P.V, lane c owns channels 4c..4c+3 of all 8 heads; for each of the 16 positions the weights are
-//   broadcast with readlane and the lane decodes its 4 codes of that position's V row.
-// Rows in the tail ring (positions >= body_len) are read as q8_0 or bf16 rows; KVarN scales apply to body
-// rows only (K through the query, V per position).
+// * a wave takes 16 list entries at a time. Lane (j = lane >> 4, e = lane & 15) loads the pieces (j, b),
+//   b = 0..7, of entry e's K row (channels 32b + 8j + i, contiguous in the row): that is the B operand of
+//   a 16x16x32 MFMA with the entries as columns, so QK is one MFMA per K bit plane and block, with the
+//   codes as exact fp16 denormals and the query as A operand (rows 0-7: fp16 hi parts of the 8 heads of
+//   the group, rows 8-15: lo parts, exponent-shifted and weighted per plane), scaled per (entry, block)
+//   in fp32, the same scheme as the dense kernel;
+// * online softmax in exp2 form (maximum over the 16 entries by DPP row operations); the weights go
+//   through LDS to every lane;
+// * for P.V, lane c owns channels 4c..4c+3 of all 8 heads and decodes its 4 codes of each entry's V row.
+// Rows in the tail ring (positions >= body_len) are read as q8_0 rows (a second query operand without the
+// KVarN scale) or bf16 rows (bf16 MFMA); KVarN scales apply to body rows only (K through the query, V per
+// position).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "kvq_kernels.h"
+#include "kvq_mfma.h"
 
 namespace kvq {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kNegBig = -1.0e30f;
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kGroup = 16;    // list entries per wave step
-constexpr int kWaves = 4;
+constexpr int kGWaves = 8;    // waves per work-group
 
 __device__ inline float f16f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
 __device__ inline float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Compile-time plane description of an N-bit code (least significant plane first).
-template <int N> struct PL;
-template <> struct PL<2> { static constexpr int n = 1, w0 = 2, w1 = 0, w2 = 0, s1 = 0, s2 = 0; };
-template <> struct PL<3> { static constexpr int n = 2, w0 = 2, w1 = 1, w2 = 0, s1 = 2, s2 = 0; };
-template <> struct PL<4> { static constexpr int n = 1, w0 = 4, w1 = 0, w2 = 0, s1 = 0, s2 = 0; };
-template <> struct PL<5> { static constexpr int n = 2, w0 = 4, w1 = 1, w2 = 0, s1 = 4, s2 = 0; };
-template <> struct PL<6> { static constexpr int n = 2, w0 = 4, w1 = 2, w2 = 0, s1 = 4, s2 = 0; };
-template <> struct PL<7> { static constexpr int n = 3, w0 = 4, w1 = 2, w2 = 1, s1 = 4, s2 = 6; };
-template <> struct PL<8> { static constexpr int n = 1, w0 = 8, w1 = 0, w2 = 0, s1 = 0, s2 = 0; };
-
-// Element i of piece `piece` (index j*NB + b within a plane of width w) of a row plane, given the plane's
-// 32-bit words starting at `words` (the word holding the piece is words[piece * w / 4]).
+// Element i of piece `piece` of a row plane of width W < 8, given the 32-bit word holding the piece.
 template <int W>
 __device__ inline uint32_t piece_elem(uint32_t word, int piece, int i) {
-  if constexpr (W == 8) {
-    return (word >> (8 * (i & 3))) & 0xFFu;   // word = bytes 4*(i/4).. of the piece
-  } else {
-    const int slot = piece % (4 / W);
-    return (word >> (16 * (i & 1) + 4 * W * slot + W * (i >> 1))) & ((1u << W) - 1);
-  }
+  const int slot = piece % (4 / W);
+  return (word >> (16 * (i & 1) + 4 * W * slot + W * (i >> 1))) & ((1u << W) - 1);
 }
 
-// ---- QK side: the lane's 64 channels (pieces (j, b), b = 0..7) of one row
+// Maximum / sum over the 16 lanes of a row (DPP: swaps within quads, then rotations by 4 and 8).
+#define KVQ_DPP(x, c) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), c, 0xF, 0xF, false))
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, KVQ_DPP(x, 0xB1));    // quad_perm(1, 0, 3, 2)
+  x = fmaxf(x, KVQ_DPP(x, 0x4E));    // quad_perm(2, 3, 0, 1)
+  x = fmaxf(x, KVQ_DPP(x, 0x124));   // row_ror 4
+  x = fmaxf(x, KVQ_DPP(x, 0x128));   // row_ror 8
+  return x;
+}
+__device__ inline float row16_sum(float x) {
+  x += KVQ_DPP(x, 0xB1);
+  x += KVQ_DPP(x, 0x4E);
+  x += KVQ_DPP(x, 0x124);
+  x += KVQ_DPP(x, 0x128);
+  return x;
+}
+#undef KVQ_DPP
 
-// Raw words of the lane's part of one row. Body/q8 rows: per plane the run of NB pieces for lane group j,
-// then the 8 fp16 block scales. bf16 rows: 8 x 8 channels.
+// ---- K side: the lane's 64 channels (pieces (j, b), b = 0..7) of one row
+
+// Raw words of the lane's part of one row. qN_0 rows: per plane the run of 8 pieces of lane group j (plane 0
+// at w[0..], plane 1 at w[16..], plane 2 at w[24..]), then the row's 8 fp16 block scales at w[28..31].
+// bf16 rows: 8 x 8 channels at w[0..31].
 struct KRaw {
   uint32_t w[32];
 };
@@ -70,10 +73,10 @@ struct KRaw {
 template <int N>
 __device__ inline void load_k_qrow(KRaw& r, const uint8_t* row, int j) {
   constexpr int NB = 8;
-  using P = PL<N>;
-  // plane 0 run: NB * w0 bytes at j * NB * w0
-  constexpr int n0 = NB * P::w0 / 4, n1 = NB * P::w1 / 4, n2 = NB * P::w2 / 4;
-  const uint8_t* p0 = row + j * NB * P::w0;
+  using P = Planes<N>;
+  constexpr int w0 = P::w[0], w1 = P::w[1], w2 = P::w[2];
+  constexpr int n0 = NB * w0 / 4, n1 = NB * w1 / 4;
+  const uint8_t* p0 = row + j * NB * w0;
 #pragma unroll
   for (int k = 0; k < n0; k += (n0 >= 4 ? 4 : 2)) {
     if constexpr (n0 >= 4) {
@@ -85,7 +88,7 @@ __device__ inline void load_k_qrow(KRaw& r, const uint8_t* row, int j) {
     }
   }
   if constexpr (P::n >= 2) {
-    const uint8_t* p1 = row + 4 * NB * P::w0 + j * NB * P::w1;
+    const uint8_t* p1 = row + 4 * NB * w0 + j * NB * w1;
 #pragma unroll
     for (int k = 0; k < n1; k += (n1 >= 4 ? 4 : 2)) {
       if constexpr (n1 >= 4) {
@@ -98,33 +101,11 @@ __device__ inline void load_k_qrow(KRaw& r, const uint8_t* row, int j) {
     }
   }
   if constexpr (P::n >= 3) {
-    const uint8_t* p2 = row + 4 * NB * (P::w0 + P::w1) + j * NB * P::w2;
-    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p2);
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)(row + 4 * NB * (w0 + w1) + j * NB * w2));
     r.w[24] = v[0]; r.w[25] = v[1];
   }
   const u32x4 sc = __builtin_nontemporal_load((const u32x4*)(row + 4 * NB * N));
   r.w[28] = sc[0]; r.w[29] = sc[1]; r.w[30] = sc[2]; r.w[31] = sc[3];
-}
-
-// The 8 values of block b (channels 32b + 8j + i) of a qN_0 row part loaded by load_k_qrow.
-template <int N>
-__device__ inline void k_block_values(const KRaw& r, int j, int b, float* x) {
-  constexpr int NB = 8;
-  using P = PL<N>;
-  const float d = f16f(r.w[28 + (b >> 1)] >> (16 * (b & 1)));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t u;
-    if constexpr (N == 8) {
-      u = piece_elem<8>(r.w[2 * b + (i >> 2)], 0, i);
-    } else {
-      const int pc = j * NB + b;   // piece index in the plane; the lane's run starts at piece j * NB
-      u = piece_elem<P::w0>(r.w[(b * P::w0) / 4], pc, i);
-      if constexpr (P::n >= 2) u |= piece_elem<P::w1>(r.w[16 + (b * P::w1) / 4], pc, i) << P::s1;
-      if constexpr (P::n >= 3) u |= piece_elem<P::w2>(r.w[24 + (b * P::w2) / 4], pc, i) << P::s2;
-    }
-    x[i] = (float)((int)u - (1 << (N - 1))) * d;   // exact: integer code times an fp16 scale
-  }
 }
 
 __device__ inline void load_k_bf16(KRaw& r, const uint8_t* row, int j) {
@@ -135,38 +116,58 @@ __device__ inline void load_k_bf16(KRaw& r, const uint8_t* row, int j) {
   }
 }
 
-// Partial scores of the 8 heads over the lane's 64 channels of one qN_0 row (qt: query [channel][head]).
+// QK of block B over a qN_0 row part: the plane MFMAs (query operand of plane p at qb[p * 512 + B * 64 + lane])
+// plus the code-bias product, times the block scale d (0 for a lane whose row is not of this kind).
+template <int N, int B>
+__device__ inline void qk_block(const KRaw& kr, const half8* qb, half8 kbias, float d, floatx4& acc) {
+  const int lane = threadIdx.x & 63;
+  KPlanes<N> kp;
+  dn_piece<N, B>(&kr.w[0], &kr.w[16], &kr.w[24], kp);
+  const half8 q0 = qb[B * 64 + lane];
+  floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(q0, kbias, floatx4{0, 0, 0, 0}, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(q0, kp.a[0], c, 0, 0, 0);
+  if constexpr (Planes<N>::n >= 2) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[512 + B * 64 + lane], kp.a[1], c, 0, 0, 0);
+  if constexpr (Planes<N>::n >= 3) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[1024 + B * 64 + lane], kp.a[2], c, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = fmaf(d, c[r], acc[r]);
+}
+
+// -2^(N-1) * 2^(q_i - 24) per element: with the plane-0 query operand, minus the code bias 2^(N-1)
 template <int N>
-__device__ inline void qk_qrow(const KRaw& kr, int j, const float (*qt)[kPartialHeads], float* acc) {
+__device__ inline half8 k_bias() {
+  half8 kb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kb[i] = (_Float16)(-ldexpf(1.0f, N - 1 + dn_bitpos(Planes<N>::w[0], 0, i) - 24));
+  return kb;
+}
+
+template <int N>
+__device__ inline void qk_qrow(const KRaw& kr, const half8* qb, bool use, floatx4& acc) {
+  const half8 kb = k_bias<N>();
+  float d[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) d[b] = use ? f16f((kr.w[28 + (b >> 1)] >> (16 * (b & 1))) & 0xFFFFu) : 0.0f;
+  qk_block<N, 0>(kr, qb, kb, d[0], acc);
+  qk_block<N, 1>(kr, qb, kb, d[1], acc);
+  qk_block<N, 2>(kr, qb, kb, d[2], acc);
+  qk_block<N, 3>(kr, qb, kb, d[3], acc);
+  qk_block<N, 4>(kr, qb, kb, d[4], acc);
+  qk_block<N, 5>(kr, qb, kb, d[5], acc);
+  qk_block<N, 6>(kr, qb, kb, d[6], acc);
+  qk_block<N, 7>(kr, qb, kb, d[7], acc);
+}
+
+__device__ inline void qk_bf16(const KRaw& kr, const bf16x8* qb, bool use, floatx4& acc) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    float x[8];
-    k_block_values<N>(kr, j, b, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float* qc = qt[32 * b + 8 * j + i];
-#pragma unroll
-      for (int h = 0; h < kPartialHeads; ++h) acc[h] = fmaf(x[i], qc[h], acc[h]);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounds the live query values
+    u32x4 w = {kr.w[4 * b], kr.w[4 * b + 1], kr.w[4 * b + 2], kr.w[4 * b + 3]};
+    if (!use) w = u32x4{0u, 0u, 0u, 0u};   // another kind of row: its bytes need not be finite as bf16
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[b * 64 + lane], __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);
   }
 }
 
-__device__ inline void qk_bf16(const KRaw& kr, int j, const float (*qt)[kPartialHeads], float* acc) {
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = bf16f((kr.w[4 * b + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu);
-      const float* qc = qt[32 * b + 8 * j + i];
-#pragma unroll
-      for (int h = 0; h < kPartialHeads; ++h) acc[h] = fmaf(x, qc[h], acc[h]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// ---- P.V side: channels 4c..4c+3 of one V row
+// ---- V side: channels 4c..4c+3 of one row
 
 struct VRaw {
   uint32_t w[4];   // one word per plane (w <= 3 planes) + the block scale in w[3] (bf16: w[0..1])
@@ -175,18 +176,18 @@ struct VRaw {
 template <int N>
 __device__ inline void load_v_qrow(VRaw& r, const uint8_t* row, int c) {
   constexpr int NB = 8;
-  using P = PL<N>;
+  using P = Planes<N>;
+  constexpr int w0 = P::w[0], w1 = P::w[1], w2 = P::w[2];
   const int b = c >> 3, j = (c & 7) >> 1;
   const int pc = j * NB + b;
   if constexpr (N == 8) {
     r.w[0] = __builtin_nontemporal_load((const uint32_t*)(row + pc * 8 + 4 * (c & 1)));
   } else {
-    r.w[0] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * ((pc * P::w0) / 4)));
+    r.w[0] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * ((pc * w0) / 4)));
     if constexpr (P::n >= 2)
-      r.w[1] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * NB * P::w0 + 4 * ((pc * P::w1) / 4)));
+      r.w[1] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * NB * w0 + 4 * ((pc * w1) / 4)));
     if constexpr (P::n >= 3)
-      r.w[2] = __builtin_nontemporal_load(
-          (const uint32_t*)(row + 4 * NB * (P::w0 + P::w1) + 4 * ((pc * P::w2) / 4)));
+      r.w[2] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * NB * (w0 + w1) + 4 * ((pc * w2) / 4)));
   }
   r.w[3] = __builtin_nontemporal_load((const uint16_t*)(row + 4 * NB * N + 2 * b));
 }
@@ -194,7 +195,7 @@ __device__ inline void load_v_qrow(VRaw& r, const uint8_t* row, int c) {
 template <int N>
 __device__ inline void v_values(const VRaw& r, int c, float* v) {
   constexpr int NB = 8;
-  using P = PL<N>;
+  using P = Planes<N>;
   const int b = c >> 3, j = (c & 7) >> 1, i0 = 4 * (c & 1);
   const int pc = j * NB + b;
   const float d = f16f(r.w[3]);
@@ -204,22 +205,25 @@ __device__ inline void v_values(const VRaw& r, int c, float* v) {
     if constexpr (N == 8) {
       u = (r.w[0] >> (8 * k)) & 0xFFu;
     } else {
-      u = piece_elem<P::w0>(r.w[0], pc, i0 + k);
-      if constexpr (P::n >= 2) u |= piece_elem<P::w1>(r.w[1], pc, i0 + k) << P::s1;
-      if constexpr (P::n >= 3) u |= piece_elem<P::w2>(r.w[2], pc, i0 + k) << P::s2;
+      u = piece_elem<P::w[0]>(r.w[0], pc, i0 + k);
+      if constexpr (P::n >= 2) u |= piece_elem<P::w[1]>(r.w[1], pc, i0 + k) << P::sh[1];
+      if constexpr (P::n >= 3) u |= piece_elem<P::w[2]>(r.w[2], pc, i0 + k) << P::sh[2];
     }
-    v[k] = (float)((int)u - (1 << (N - 1))) * d;
+    v[k] = (float)((int)u - (1 << (N - 1))) * d;   // exact: integer code times an fp16 scale
   }
 }
 
 // ---- the kernel
 
 template <int NK, int NV>
-__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-  constexpr int D = 256, NB = 8, G = kPartialHeads;
-  __shared__ float s_q[2][D][G];               // [plain, times KVarN sigma_K][channel][head]
-  __shared__ float s_o[kWaves][G][D];
-  __shared__ float s_ml[kWaves][2][G];
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gather_kernel(GatherArgs a) {
+  constexpr int D = 256, G = kPartialHeads, NW = kGWaves;
+  __shared__ half8 s_qb[3 * 8 * 64];            // body query operand: [plane][block][lane]
+  __shared__ half8 s_qr[8 * 64];                // ring query operand (q8_0: fp16 weighted; bf16: bf16 q)
+  __shared__ float s_o[NW][G][D];
+  __shared__ float s_ml[NW][2][G];
+  __shared__ float s_p[NW][kGroup + 1][G];      // per wave: weights [entry][head], then the step's maxima
+  __shared__ float s_amax[NW][2];
 
   const Geometry& g = a.g;
   int rem = blockIdx.x, si = 0;
@@ -232,25 +236,77 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const GatherSeq S = a.seqs[si];
   const int head = rem / S.n_splits;
   const int split = rem % S.n_splits;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = g.ring_slots;
+  const int tail = g.tail_dtype;
   const uint8_t* slab = g.arena + S.slab;
   const bool kvarn = g.kvarn != 0;
   const uint16_t* sig = (const uint16_t*)(slab + g.sigma) + (size_t)head * 2 * D;
+  const int j = lane >> 4, e16 = lane & 15;
 
-  // query of the group's heads (and times sigma_K for body rows), [channel][head] in LDS: thread (h, c0) reads
-  // 8 channels of head h with one 16-byte load (one round trip for the whole work-group)
+  // ---- query operands: wave w builds block w (channels 32w + 8j + i) for row e16 of the A operand
+  int e = 0, er = 0;   // exponent shifts of the body and the q8_0 ring operands (the same in every lane)
   {
-    const int h = tid >> 5, c0 = 8 * (tid & 31);
-    u32x4 qw = {0u, 0u, 0u, 0u};
-    if (h < a.group) qw = *(const u32x4*)(a.q + ((size_t)si * a.n_q_heads + head * a.group + h) * D + c0);
+    const int hh = e16 & 7;
+    const bool lo_row = e16 >= 8, head_ok = hh < a.group;
+    const uint16_t* qrow = a.q + ((size_t)si * a.n_q_heads + head * a.group + (head_ok ? hh : 0)) * D + 32 * wave + 8 * j;
+    const u32x4 qw = *(const u32x4*)qrow;
     u32x4 sw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
-    if (kvarn) sw = *(const u32x4*)(sig + c0);
+    if (kvarn) sw = *(const u32x4*)(sig + 32 * wave + 8 * j);
+    float x[8], xr[8];
+    float am = 0.0f, amr = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float qv = bf16f((qw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      s_q[0][c0 + i][h] = qv;
-      s_q[1][c0 + i][h] = qv * f16f((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);   // exact (8 + 11 bits)
+      xr[i] = head_ok ? bf16f((qw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) : 0.0f;
+      x[i] = xr[i] * f16f((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);   // exact in fp32 (8 + 11 bits)
+      am = fmaxf(am, fabsf(x[i]));
+      amr = fmaxf(amr, fabsf(xr[i]));
+    }
+    if (tail == 1) {   // bf16 ring: the query itself in rows 0-7, zero lo rows
+      u32x4 b = lo_row || !head_ok ? u32x4{0u, 0u, 0u, 0u} : qw;
+      ((u32x4*)s_qr)[wave * 64 + lane] = b;
+    }
+    // one exponent shift per work-group and operand: |q| < 2^9 after it, so that the plane weights (up to
+    // 2^6) keep every operand in fp16 range
+    am = row16_max(wave_max_16_32(am));
+    amr = row16_max(wave_max_16_32(amr));
+    if (lane == 0) {
+      s_amax[wave][0] = am;
+      s_amax[wave][1] = amr;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      am = fmaxf(am, s_amax[w][0]);
+      amr = fmaxf(amr, s_amax[w][1]);
+    }
+    e = am > 0.0f ? ilogbf(am) - 8 : 0;
+    er = amr > 0.0f ? ilogbf(amr) - 8 : 0;
+    float part[8], partr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xs = ldexpf(x[i], -e);
+      const _Float16 h = (_Float16)xs;
+      part[i] = lo_row ? (float)(_Float16)(xs - (float)h) : (float)h;
+      const float xq = ldexpf(xr[i], -er);
+      const _Float16 hq = (_Float16)xq;
+      partr[i] = lo_row ? (float)(_Float16)(xq - (float)hq) : (float)hq;
+    }
+#pragma unroll
+    for (int p = 0; p < Planes<NK>::n; ++p) {
+      const int w = Planes<NK>::w[p];
+      const int slot = w == 8 ? 0 : wave % (4 / w);
+      half8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (_Float16)ldexpf(part[i], Planes<NK>::sh[p] - dn_bitpos(w, slot, i));   // exact
+      s_qb[p * 512 + wave * 64 + lane] = v;
+    }
+    if (tail == 2) {
+      half8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (_Float16)partr[i];   // 8-bit plane: every field at bit 0
+      s_qr[wave * 64 + lane] = v;
     }
   }
   float sv[4];   // sigma_V of this lane's P.V channels
@@ -261,39 +317,45 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     for (int k = 0; k < 4; ++k) sv[k] = f16f((vw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
   }
   __syncthreads();
+  const float qsc = a.scale * kLog2e;
+  const float qmul_b = qsc * ldexpf(1.0f, e + 24);   // body scores: C * d * 2^(e + 24)
+  const float qmul_r = tail == 2 ? qsc * ldexpf(1.0f, er + 24) : qsc;
 
   const int ib = (int)((long)split * S.n_list / S.n_splits);
   const int ie = (int)((long)(split + 1) * S.n_list / S.n_splits);
-  const int p16 = lane & 15, j = lane >> 4;
-  const float qmul = a.scale * kLog2e;
   const uint8_t* kbody = slab + g.k_body + (size_t)head * g.cap32 * g.row_k;
   const uint8_t* vbody = slab + g.v_body + (size_t)head * g.cap32 * g.row_v;
   const uint8_t* kring = slab + g.k_ring + (size_t)head * R * g.ring_row_k;
   const uint8_t* vring = slab + g.v_ring + (size_t)head * R * g.ring_row_v;
   const int32_t* plist = a.positions ? a.positions + (size_t)si * a.pos_stride : nullptr;
+  float (*sp)[G] = s_p[wave];
 
-  float m[G], l[G], o[G][4];
+  float m[G], o[G][4], m4[4], l4[4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegBig;
-    l[h] = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) o[h][k] = 0.0f;
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {   // the running maximum and sum of heads 4 (j & 1) + r (sum: lanes 0-31)
+    m4[r] = kNegBig;
+    l4[r] = 0.0f;
+  }
 
-  for (int g0 = ib + kGroup * wave; g0 < ie; g0 += kGroup * kWaves) {
-    // ---- this lane's list entry (p16) and its source
-    const int idx = g0 + p16;
+  for (int g0 = ib + kGroup * wave; g0 < ie; g0 += kGroup * NW) {
+    // ---- this lane's list entry (e16) and its source
+    const int idx = g0 + e16;
     int pos = -1;
     if (idx < ie) pos = plist ? plist[idx] : idx;
     const bool valid = pos >= 0 && pos < S.len;
     const bool body = valid && pos < S.body_len;
-    // ---- K part of the entry's row
+    const bool ring = valid && !body;
     KRaw kr;
     if (body) {
       load_k_qrow<NK>(kr, kbody + (size_t)pos * g.row_k, j);
-    } else if (valid) {
-      if (g.tail_dtype == 2) load_k_qrow<8>(kr, kring + (size_t)(pos % R) * g.ring_row_k, j);
+    } else if (ring) {
+      if (tail == 2) load_k_qrow<8>(kr, kring + (size_t)(pos % R) * g.ring_row_k, j);
       else load_k_bf16(kr, kring + (size_t)(pos % R) * g.ring_row_k, j);
     }
     // ---- V loads for the 16 entries (lane = channel group), issued before the QK arithmetic
@@ -308,7 +370,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
         if (pt < S.body_len) {
           bmask |= 1u << t;
           load_v_qrow<NV>(vr[t], vbody + (size_t)pt * g.row_v, lane);
-        } else if (g.tail_dtype == 2) {
+        } else if (tail == 2) {
           load_v_qrow<8>(vr[t], vring + (size_t)(pt % R) * g.ring_row_v, lane);
         } else {
           const u32x2 x = __builtin_nontemporal_load((const u32x2*)(vring + (size_t)(pt % R) * g.ring_row_v + 8 * lane));
@@ -317,31 +379,48 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
         }
       }
     }
-    // ---- scores: partial dot products over the lane's 64 channels, summed over the 4 lane groups
-    float acc[G];
+    if (!vmask) continue;
+    // ---- scores: lane (j, e16) ends with rows 4j..4j+3 of the 16 x 16 product (query rows x entries)
+    floatx4 accb = {0, 0, 0, 0}, accr = {0, 0, 0, 0};
+    if (bmask) qk_qrow<NK>(kr, s_qb, body, accb);
+    if (vmask & ~bmask) {
+      if (tail == 2) qk_qrow<8>(kr, s_qr, ring, accr);
+      else qk_bf16(kr, (const bf16x8*)s_qr, ring, accr);
+    }
+    float s[4], mx[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-    // (one path per row source, so that each path is straight-line code)
-    if (body) qk_qrow<NK>(kr, j, s_q[1], acc);
-    else if (valid && g.tail_dtype == 2) qk_qrow<8>(kr, j, s_q[0], acc);
-    else if (valid) qk_bf16(kr, j, s_q[0], acc);
-    float p[G];
+    for (int r = 0; r < 4; ++r) {
+      s[r] = sum_xor32(accb[r] * qmul_b + accr[r] * qmul_r);   // hi rows + lo rows: heads 4 (j & 1) + r
+      s[r] = valid ? s[r] : -INFINITY;
+      mx[r] = row16_max(s[r]);
+    }
+    // ---- online softmax: the step's maxima of all 8 heads to every lane through LDS
+    if (lane == 0 || lane == 16) *(floatx4*)&sp[kGroup][4 * j] = floatx4{mx[0], mx[1], mx[2], mx[3]};
+    __builtin_amdgcn_wave_barrier();
+    const floatx4 mlo = *(const floatx4*)&sp[kGroup][0], mhi = *(const floatx4*)&sp[kGroup][4];
+    float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float sc = acc[h] + __shfl_xor(acc[h], 16);
-      sc += __shfl_xor(sc, 32);
-      sc = valid ? sc * qmul : -INFINITY;
-      float mx = sc;
-#pragma unroll
-      for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
-      const float m_new = fmaxf(m[h], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
-      m[h] = m_new;
-      p[h] = __builtin_amdgcn_exp2f(sc - m_new);
-      l[h] = l[h] * alpha + (j == 0 ? p[h] : 0.0f);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[h][k] *= alpha;
+      const float mn = fmaxf(m[h], h < 4 ? mlo[h] : mhi[h - 4]);
+      alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
+      m[h] = mn;
     }
+    {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {   // the same maxima as m[4 (j & 1) + r], from this lane's own row
+        const float mn = fmaxf(m4[r], mx[r]);
+        p[r] = __builtin_amdgcn_exp2f(s[r] - mn);
+        l4[r] = l4[r] * __builtin_amdgcn_exp2f(m4[r] - mn) + p[r];
+        m4[r] = mn;
+      }
+      if (lane < 32) *(floatx4*)&sp[e16][4 * j] = floatx4{p[0], p[1], p[2], p[3]};
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[h][k] *= alpha[h];
+    __builtin_amdgcn_wave_barrier();
     // ---- P.V for the 16 entries
 #pragma unroll
     for (int t = 0; t < kGroup; ++t) {
@@ -351,7 +430,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
         v_values<NV>(vr[t], lane, v);
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] *= sv[k];
-      } else if (g.tail_dtype == 2) {
+      } else if (tail == 2) {
         v_values<8>(vr[t], lane, v);
       } else {
         v[0] = bf16f(vr[t].w[0] & 0xFFFFu);
@@ -359,55 +438,60 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
         v[2] = bf16f(vr[t].w[1] & 0xFFFFu);
         v[3] = bf16f(vr[t].w[1] >> 16);
       }
+      const floatx4 p0 = *(const floatx4*)&sp[t][0], p1 = *(const floatx4*)&sp[t][4];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float ph = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[h]), t));   // entry t
+        const float ph = h < 4 ? p0[h] : p1[h - 4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[h][k] = fmaf(ph, v[k], o[h][k]);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_wave_barrier();   // the next step's writes of sp come after these reads
   }
 
   // ---- wave partials to LDS, then the work-group merge
+  float lsum[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float ls = l[h];
+  for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lane < 32 ? l4[r] : 0.0f);
+  if (lane == 0 || lane == 16) {
 #pragma unroll
-    for (int o2 = 1; o2 < 64; o2 <<= 1) ls += __shfl_xor(ls, o2);
-    if (lane == 0) {
-      s_ml[wave][0][h] = m[h];
-      s_ml[wave][1][h] = ls;
-    }
+    for (int r = 0; r < 4; ++r) s_ml[wave][1][4 * j + r] = lsum[r];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_ml[wave][0][h] = m[h];
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int k = 0; k < 4; ++k) s_o[wave][h][4 * lane + k] = o[h][k];
-  }
   __syncthreads();
   float* part = a.partials + (((size_t)si * g.n_kv_heads + head) * a.max_splits + split) * (G * (D + 2));
-  const int c = tid;
+  const int c = tid & 255;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = tid >> 8; h < G; h += 2) {
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0][h]);
-    float L = 0.0f, O = 0.0f;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    float O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_ml[w][0][h] - M);
-      L += s_ml[w][1][h] * f;
-      O += s_o[w][h][c] * f;
-    }
+    for (int w = 0; w < NW; ++w) O += s_o[w][h][c] * __builtin_amdgcn_exp2f(s_ml[w][0][h] - M);
     part[2 * G + h * D + c] = O;
-    if (c == 0) {
-      part[h] = M;
-      part[G + h] = L;
-    }
+  }
+  if (tid < G) {
+    float M = kNegBig, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][tid]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += s_ml[w][1][tid] * __builtin_amdgcn_exp2f(s_ml[w][0][tid] - M);
+    part[tid] = M;
+    part[G + tid] = L;
   }
 }
 
 template <int NK, int NV>
 hipError_t launch_gather_t(const GatherArgs& a, int grid_x, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_k(gather_kernel<NK, NV>, dim3(grid_x), dim3(256), s, e0, e1, a);
+  return launch_k(gather_kernel<NK, NV>, dim3(grid_x), dim3(64 * kGWaves), s, e0, e1, a);
 }
 
 }  // namespace

@@ -228,11 +228,11 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
   return p;
 }
 
-// Gather decode: list entries per work-group are at least kGatherMin; about two work-groups per CU over all
-// (sequence, KV head) pairs.
-constexpr int kGatherMin = 64;
+// Gather decode: list entries per work-group are at least kGatherMin (one 16-entry step for each of its 8
+// waves); at most one work-group per CU over all (sequence, KV head) pairs.
+constexpr int kGatherMin = 128;
 int gather_budget_h(const kvq_cache* c) {
-  return std::max(1, std::min(2 * c->n_cu, kvq::kMaxSplits) / c->cfg.n_kv_heads);
+  return std::max(1, std::min(c->n_cu, kvq::kMaxSplits) / c->cfg.n_kv_heads);
 }
 int plan_gather(const kvq_cache* c, int n_seqs, const int* n_list, kvq::GatherSeq* out, int* total_wgs) {
   long total = 0;
