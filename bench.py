@@ -16,7 +16,10 @@ with their start and end (library launch timing, measured on a second run of the
 against 8 TB/s HBM3E. `traffic` is the HBM bytes per launch measured with
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by the copy-kernel calibration stored with them),
 used only while the kernel source still matches the one that was measured. `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload. Also reported: `graph` (the same steps with each step's
+launches captured into one HIP graph beforehand and replayed back to back), `cold` (single-layer workloads:
+decode time after a 512 MiB write has evicted L2 and the MALL) and `copy_ceiling_gbs` (a plain 1 GiB device
+copy, bytes read + written per second).
 """
 from __future__ import annotations
 
@@ -195,6 +198,24 @@ def graph_steps(torch, step, first: int, n: int, n_layers: int) -> float:
     return dt
 
 
+def copy_ceiling(torch, mib: int = 1024, reps: int = 5) -> float:
+    """Device-to-device copy rate (GB/s of bytes read + written) of a plain 1 GiB torch copy: the streaming
+    ceiling measured on this GPU, beside the 8 TB/s specification."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(reps):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    return 2.0 * (mib << 20) / best / 1e9
+
+
 def cold_calls(torch, cache, seqs, q, out, ws, n: int) -> dict:
     """Decode call time with the cache's lines evicted from L2 and the 256 MB MALL first (a 512 MiB write
     before every call), from the library's launch timing."""
@@ -304,6 +325,12 @@ def main() -> int:
                 cache.decode_step(layer, seqs, kin_d[st, layer], vin_d[st, layer], qin_d[st, layer], out=out[layer],
                                   workspace=ws)
                 continue
+            if sparse and appends and wl.tail_len == 0:   # append one token and attend: one call
+                if nbytes is not None:
+                    nbytes.append(sparse_call_bytes(cfg, wl.budget, B))
+                cache.sparse_decode_step(layer, seqs, kin_d[st, layer], vin_d[st, layer], qin_d[st, layer],
+                                         pin_d[st, layer], out=out[layer], workspace=ws)
+                continue
             if appends:   # append one token and requantize the one leaving the window: one launch
                 cache.append_evict(layer, seqs, ones, kin_d[st, layer], vin_d[st, layer])
             if sparse:
@@ -371,7 +398,7 @@ def main() -> int:
                    "k_bits": wl.k_bits, "v_bits": wl.v_bits, "kvarn": wl.kvarn, "tail": wl.tail_len,
                    "tail_dtype": ["none", "bf16", "q8_0"][wl.tail_dtype], "budget": wl.budget,
                    "layout": ["tiles", "rows"][cfg.get("layout", 0)],
-                   "step": ("per layer: append 1 token, sparse decode over the step's position list" if sparse
+                   "step": ("per layer: append 1 token, sparse decode over the step's position list (one call)" if sparse
                             else "per layer: append 1 token, evict 1 tail token, decode attention (one call)"
                             if fused else "per layer: append 1 token, evict 1 tail token, decode attention" if appends
                             else "per layer: decode attention")},
@@ -389,6 +416,7 @@ def main() -> int:
                            "replayed back to back"}
     if cold is not None:
         res["cold"] = cold
+    res["copy_ceiling_gbs"] = round(copy_ceiling(torch), 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

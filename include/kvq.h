@@ -171,6 +171,18 @@ kvq_status kvq_sparse_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seq
                                   const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
                                   float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
 
+/* One sparse decode step of every listed sequence: append one token each (k_bf16, v_bf16: device bf16
+ * [n_seqs][Hkv][D]), then sparse decode attention over positions (which index the cache after the append:
+ * the new token is at the old length), with the results of kvq_append (n_new = 1 each) followed by
+ * kvq_sparse_decode_attn. Without a tail ring and with no KVarN calibration pending, the new rows are
+ * quantized into the body inside the sparse decode launch (by the first work-group of each KV head and by
+ * every work-group whose list range holds the new position, before it reads any row; they write the same
+ * bytes); otherwise the calls run in turn. Arguments and errors as those calls. */
+kvq_status kvq_sparse_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                  const void* k_bf16, const void* v_bf16, const void* q_bf16,
+                                  const int32_t* positions, int32_t budget, float* out, float softmax_scale,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
 /* Kernel kinds for launch timing. */
 typedef enum {
   KVQ_KERNEL_DECODE = 0,   /* split kernel of dense decode (tile layout)                      */

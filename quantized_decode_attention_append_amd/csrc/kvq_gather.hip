@@ -26,12 +26,14 @@
 
 #include "kvq_kernels.h"
 #include "kvq_mfma.h"
+#include "kvq_write.h"
 
 namespace kvq {
 namespace {
 
 constexpr int kGroup = 16;    // list entries per wave step
-constexpr int kGWaves = 8;    // waves per work-group
+constexpr int kGWaves = kGatherWaves;
+constexpr int kImgRow = 288;   // bytes per LDS row image (a q8_0 row is 272)
 
 __device__ inline float f16f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
 __device__ inline float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -213,10 +215,126 @@ __device__ inline void v_values(const VRaw& r, int c, float* v) {
   }
 }
 
+// ---- one wave step: the sources of 16 list entries and their K and V loads
+
+struct StepRows {
+  int pos;                  // this lane's entry (e16), -1 past the range
+  bool valid, body;
+  uint32_t vmask, bmask;    // entries that are valid / body rows
+  KRaw kr;
+  VRaw vr[16];
+};
+
+struct RowSrc {
+  const uint8_t *kbody, *vbody, *kring, *vring;
+  const int32_t* plist;
+  int len, body_len, R, tail, row_k, row_v, ring_row_k, ring_row_v;
+};
+
+__device__ inline void load_pos(StepRows& st, const RowSrc& rs, int g0, int ie) {
+  const int idx = g0 + (threadIdx.x & 15);
+  int pos = -1;
+  if (idx < ie) pos = rs.plist ? rs.plist[idx] : idx;
+  st.pos = pos;
+}
+
+// (Rows go to local copies first and into st once at the end: stores to st made on some paths only would be
+// merged behind a select of their addresses, which keeps st out of registers.)
+template <int NK, int NV>
+__device__ inline void load_rows(StepRows& st, const RowSrc& rs) {
+  const int lane = threadIdx.x & 63, j = lane >> 4;
+  const int pos = st.pos;
+  const bool valid = pos >= 0 && pos < rs.len;
+  const bool body = valid && pos < rs.body_len;
+  KRaw kr = {};
+  if (body) {
+    load_k_qrow<NK>(kr, rs.kbody + (size_t)pos * rs.row_k, j);
+  } else if (valid) {
+    if (rs.tail == 2) load_k_qrow<8>(kr, rs.kring + (size_t)(pos % rs.R) * rs.ring_row_k, j);
+    else load_k_bf16(kr, rs.kring + (size_t)(pos % rs.R) * rs.ring_row_k, j);
+  }
+  // V rows of the 16 entries (lane = channel group)
+  uint32_t vmask = 0, bmask = 0;
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t) {
+    const int pt = __builtin_amdgcn_readlane(pos, t);
+    VRaw vr = {};
+    if (pt >= 0 && pt < rs.len) {
+      vmask |= 1u << t;
+      if (pt < rs.body_len) {
+        bmask |= 1u << t;
+        load_v_qrow<NV>(vr, rs.vbody + (size_t)pt * rs.row_v, lane);
+      } else if (rs.tail == 2) {
+        load_v_qrow<8>(vr, rs.vring + (size_t)(pt % rs.R) * rs.ring_row_v, lane);
+      } else {
+        const u32x2 x = __builtin_nontemporal_load((const u32x2*)(rs.vring + (size_t)(pt % rs.R) * rs.ring_row_v + 8 * lane));
+        vr.w[0] = x[0];
+        vr.w[1] = x[1];
+      }
+    }
+    st.vr[t] = vr;
+  }
+  st.kr = kr;
+  st.valid = valid;
+  st.body = body;
+  st.vmask = vmask;
+  st.bmask = bmask;
+}
+
+template <int NK>
+__device__ inline void image_k(StepRows& st, const uint8_t* img_k, int app) {
+  KRaw im;
+  load_k_qrow<NK>(im, img_k, (threadIdx.x & 63) >> 4);
+  const bool m = st.pos == app;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) st.kr.w[k] = m ? im.w[k] : st.kr.w[k];   // selects: no partial writes
+}
+template <int NV>
+__device__ inline void image_v(StepRows& st, const uint8_t* img_v, int app) {
+  VRaw im;
+  load_v_qrow<NV>(im, img_v, threadIdx.x & 63);
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t) {
+    const bool m = __builtin_amdgcn_readlane(st.pos, t) == app;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st.vr[t].w[k] = m ? im.w[k] : st.vr[t].w[k];
+  }
+}
+
+// The append of a fused sparse decode step (a cache without a ring): one token of this sequence and KV head
+// quantized into body row app_pos, K and V, as the body write of an append does it (thread c
+// owns channel c of K and V, or of K or V; a block's 32 values are the 32 lanes of a half-wave).
+// With img_k / img_v (zeroed LDS row images) the same bytes go there too.
+template <int NTHREADS>
+__device__ inline void sparse_step_write(const GatherArgs& a, const GatherSeq& S, int si, int head, uint8_t* img_k,
+                                         uint8_t* img_v) {
+  const Geometry& g = a.g;
+  constexpr int D = 256;
+  const int c = threadIdx.x & (D - 1);
+  uint8_t* slab = g.arena + S.slab;
+  const int p = S.app_pos;
+  for (int kv = threadIdx.x / D; kv < 2; kv += NTHREADS / D) {
+    const int nb = kv ? g.v_bits : g.k_bits;
+    const uint16_t* in = kv ? a.v_in : a.k_in;
+    float x = bf16_to_f32(in[((size_t)si * g.n_kv_heads + head) * D + c]);
+    if (g.kvarn) x = x / f16_to_f32(((const uint16_t*)(slab + g.sigma))[((size_t)head * 2 + kv) * D + c]);
+    uint16_t dq;
+    const uint32_t u = quant_lane(x, nb, &dq);
+    uint8_t* row = slab + (kv ? g.v_body : g.k_body) + ((size_t)head * g.cap32 + p) * (kv ? g.row_v : g.row_k);
+    or_code(row, nullptr, true, kv, nb, 0, c, u, D);   // the row was zeroed with its slab
+    if ((c % kBlock) == 0) ((uint16_t*)(row + 4 * (D / kBlock) * nb))[c / kBlock] = dq;
+    if (img_k) {
+      uint8_t* im = kv ? img_v : img_k;
+      or_code(im, nullptr, true, kv, nb, 0, c, u, D);
+      if ((c % kBlock) == 0) ((uint16_t*)(im + 4 * (D / kBlock) * nb))[c / kBlock] = dq;
+    }
+  }
+}
+
 // ---- the kernel
 
 template <int NK, int NV>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gather_kernel(GatherArgs a) {
+__global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kGWaves / 4, kGWaves / 4))) void gather_kernel(GatherArgs a) {
   constexpr int D = 256, G = kPartialHeads, NW = kGWaves;
   __shared__ half8 s_qb[3 * 8 * 64];            // body query operand: [plane][block][lane]
   __shared__ half8 s_qr[8 * 64];                // ring query operand (q8_0: fp16 weighted; bf16: bf16 q)
@@ -224,6 +342,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float s_ml[NW][2][G];
   __shared__ float s_p[NW][kGroup + 1][G];      // per wave: weights [entry][head], then the step's maxima
   __shared__ float s_amax[NW][2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_img[2 * kImgRow];   // fused step: K and V row images
 
   const Geometry& g = a.g;
   int rem = blockIdx.x, si = 0;
@@ -244,28 +363,51 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool kvarn = g.kvarn != 0;
   const uint16_t* sig = (const uint16_t*)(slab + g.sigma) + (size_t)head * 2 * D;
   const int j = lane >> 4, e16 = lane & 15;
+  const int ib = (int)((long)split * S.n_list / S.n_splits);
+  const int ie = (int)((long)(split + 1) * S.n_list / S.n_splits);
+  const RowSrc rs{slab + g.k_body + (size_t)head * g.cap32 * g.row_k,
+                  slab + g.v_body + (size_t)head * g.cap32 * g.row_v,
+                  slab + g.k_ring + (size_t)head * R * g.ring_row_k,
+                  slab + g.v_ring + (size_t)head * R * g.ring_row_v,
+                  a.positions ? a.positions + (size_t)si * a.pos_stride : nullptr,
+                  S.len, S.body_len, R, tail, g.row_k, g.row_v, g.ring_row_k, g.ring_row_v};
+  // ---- query operands: wave w builds blocks w + NW k (channels 32 b + 8j + i) for row e16 of the A operand
+  constexpr int BPW = 8 / NW;   // blocks per wave
+  const int hh = e16 & 7;
+  const bool lo_row = e16 >= 8, head_ok = hh < a.group;
+  int g0 = ib + kGroup * wave;
+  // fused append (a.step): the new position's rows are written by the first split of the KV head and by every
+  // work-group whose range lists the position; such a work-group also builds the rows in LDS and reads those
+  // entries from there (so no work-group waits for another's writes)
+  const int app = a.step ? S.app_pos : -1;
+  bool hit = false;
+  if (app >= 0) {
+    for (int idx = ib + tid; idx < ie; idx += 64 * NW) hit |= (rs.plist ? rs.plist[idx] : idx) == app;
+    for (int w = tid; w < 2 * kImgRow / 4; w += 64 * NW) ((uint32_t*)s_img)[w] = 0u;
+  }
 
-  // ---- query operands: wave w builds block w (channels 32w + 8j + i) for row e16 of the A operand
   int e = 0, er = 0;   // exponent shifts of the body and the q8_0 ring operands (the same in every lane)
   {
-    const int hh = e16 & 7;
-    const bool lo_row = e16 >= 8, head_ok = hh < a.group;
-    const uint16_t* qrow = a.q + ((size_t)si * a.n_q_heads + head * a.group + (head_ok ? hh : 0)) * D + 32 * wave + 8 * j;
-    const u32x4 qw = *(const u32x4*)qrow;
-    u32x4 sw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
-    if (kvarn) sw = *(const u32x4*)(sig + 32 * wave + 8 * j);
-    float x[8], xr[8];
+    float x[BPW][8], xr[BPW][8];
     float am = 0.0f, amr = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xr[i] = head_ok ? bf16f((qw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) : 0.0f;
-      x[i] = xr[i] * f16f((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);   // exact in fp32 (8 + 11 bits)
-      am = fmaxf(am, fabsf(x[i]));
-      amr = fmaxf(amr, fabsf(xr[i]));
-    }
-    if (tail == 1) {   // bf16 ring: the query itself in rows 0-7, zero lo rows
-      u32x4 b = lo_row || !head_ok ? u32x4{0u, 0u, 0u, 0u} : qw;
-      ((u32x4*)s_qr)[wave * 64 + lane] = b;
+    for (int k = 0; k < BPW; ++k) {
+      const int b = wave + NW * k;
+      const u32x4 qw = *(const u32x4*)(a.q + ((size_t)si * a.n_q_heads + head * a.group + (head_ok ? hh : 0)) * D +
+                                        32 * b + 8 * j);
+      u32x4 sw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
+      if (kvarn) sw = *(const u32x4*)(sig + 32 * b + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xr[k][i] = head_ok ? bf16f((qw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) : 0.0f;
+        x[k][i] = xr[k][i] * f16f((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);   // exact in fp32 (8 + 11 bits)
+        am = fmaxf(am, fabsf(x[k][i]));
+        amr = fmaxf(amr, fabsf(xr[k][i]));
+      }
+      if (tail == 1) {   // bf16 ring: the query itself in rows 0-7, zero lo rows
+        const u32x4 bq = lo_row || !head_ok ? u32x4{0u, 0u, 0u, 0u} : qw;
+        ((u32x4*)s_qr)[b * 64 + lane] = bq;
+      }
     }
     // one exponent shift per work-group and operand: |q| < 2^9 after it, so that the plane weights (up to
     // 2^6) keep every operand in fp16 range
@@ -275,7 +417,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s_amax[wave][0] = am;
       s_amax[wave][1] = amr;
     }
-    __syncthreads();
+    hit = __syncthreads_or(hit);   // (also publishes s_amax and the zeroed row images)
+    if (app >= 0 && (hit || split == 0))
+      sparse_step_write<64 * NW>(a, S, si, head, hit ? s_img : nullptr, hit ? s_img + kImgRow : nullptr);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       am = fmaxf(am, s_amax[w][0]);
@@ -283,30 +427,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     e = am > 0.0f ? ilogbf(am) - 8 : 0;
     er = amr > 0.0f ? ilogbf(amr) - 8 : 0;
-    float part[8], partr[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float xs = ldexpf(x[i], -e);
-      const _Float16 h = (_Float16)xs;
-      part[i] = lo_row ? (float)(_Float16)(xs - (float)h) : (float)h;
-      const float xq = ldexpf(xr[i], -er);
-      const _Float16 hq = (_Float16)xq;
-      partr[i] = lo_row ? (float)(_Float16)(xq - (float)hq) : (float)hq;
-    }
+    for (int k = 0; k < BPW; ++k) {
+      const int b = wave + NW * k;
+      float part[8], partr[8];
 #pragma unroll
-    for (int p = 0; p < Planes<NK>::n; ++p) {
-      const int w = Planes<NK>::w[p];
-      const int slot = w == 8 ? 0 : wave % (4 / w);
-      half8 v;
+      for (int i = 0; i < 8; ++i) {
+        const float xs = ldexpf(x[k][i], -e);
+        const _Float16 h = (_Float16)xs;
+        part[i] = lo_row ? (float)(_Float16)(xs - (float)h) : (float)h;
+        const float xq = ldexpf(xr[k][i], -er);
+        const _Float16 hq = (_Float16)xq;
+        partr[i] = lo_row ? (float)(_Float16)(xq - (float)hq) : (float)hq;
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (_Float16)ldexpf(part[i], Planes<NK>::sh[p] - dn_bitpos(w, slot, i));   // exact
-      s_qb[p * 512 + wave * 64 + lane] = v;
-    }
-    if (tail == 2) {
-      half8 v;
+      for (int p = 0; p < Planes<NK>::n; ++p) {
+        const int w = Planes<NK>::w[p];
+        const int slot = w == 8 ? 0 : b % (4 / w);
+        half8 v;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (_Float16)partr[i];   // 8-bit plane: every field at bit 0
-      s_qr[wave * 64 + lane] = v;
+        for (int i = 0; i < 8; ++i) v[i] = (_Float16)ldexpf(part[i], Planes<NK>::sh[p] - dn_bitpos(w, slot, i));   // exact
+        s_qb[p * 512 + b * 64 + lane] = v;
+      }
+      if (tail == 2) {
+        half8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (_Float16)partr[i];   // 8-bit plane: every field at bit 0
+        s_qr[b * 64 + lane] = v;
+      }
     }
   }
   float sv[4];   // sigma_V of this lane's P.V channels
@@ -321,13 +469,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float qmul_b = qsc * ldexpf(1.0f, e + 24);   // body scores: C * d * 2^(e + 24)
   const float qmul_r = tail == 2 ? qsc * ldexpf(1.0f, er + 24) : qsc;
 
-  const int ib = (int)((long)split * S.n_list / S.n_splits);
-  const int ie = (int)((long)(split + 1) * S.n_list / S.n_splits);
-  const uint8_t* kbody = slab + g.k_body + (size_t)head * g.cap32 * g.row_k;
-  const uint8_t* vbody = slab + g.v_body + (size_t)head * g.cap32 * g.row_v;
-  const uint8_t* kring = slab + g.k_ring + (size_t)head * R * g.ring_row_k;
-  const uint8_t* vring = slab + g.v_ring + (size_t)head * R * g.ring_row_v;
-  const int32_t* plist = a.positions ? a.positions + (size_t)si * a.pos_stride : nullptr;
   float (*sp)[G] = s_p[wave];
 
   float m[G], o[G][4], m4[4], l4[4];
@@ -343,42 +484,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     l4[r] = 0.0f;
   }
 
-  for (int g0 = ib + kGroup * wave; g0 < ie; g0 += kGroup * NW) {
-    // ---- this lane's list entry (e16) and its source
-    const int idx = g0 + e16;
-    int pos = -1;
-    if (idx < ie) pos = plist ? plist[idx] : idx;
-    const bool valid = pos >= 0 && pos < S.len;
-    const bool body = valid && pos < S.body_len;
-    const bool ring = valid && !body;
-    KRaw kr;
-    if (body) {
-      load_k_qrow<NK>(kr, kbody + (size_t)pos * g.row_k, j);
-    } else if (ring) {
-      if (tail == 2) load_k_qrow<8>(kr, kring + (size_t)(pos % R) * g.ring_row_k, j);
-      else load_k_bf16(kr, kring + (size_t)(pos % R) * g.ring_row_k, j);
-    }
-    // ---- V loads for the 16 entries (lane = channel group), issued before the QK arithmetic
-    VRaw vr[kGroup];
-    uint32_t vmask = 0, bmask = 0;
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-      const int pt = __builtin_amdgcn_readlane(pos, t);
-      const bool vt = pt >= 0 && pt < S.len;
-      if (vt) {
-        vmask |= 1u << t;
-        if (pt < S.body_len) {
-          bmask |= 1u << t;
-          load_v_qrow<NV>(vr[t], vbody + (size_t)pt * g.row_v, lane);
-        } else if (tail == 2) {
-          load_v_qrow<8>(vr[t], vring + (size_t)(pt % R) * g.ring_row_v, lane);
-        } else {
-          const u32x2 x = __builtin_nontemporal_load((const u32x2*)(vring + (size_t)(pt % R) * g.ring_row_v + 8 * lane));
-          vr[t].w[0] = x[0];
-          vr[t].w[1] = x[1];
-        }
-      }
-    }
+  for (; g0 < ie; g0 += kGroup * NW) {
+    StepRows st;
+    load_pos(st, rs, g0, ie);
+    load_rows<NK, NV>(st, rs);
+    if (hit) image_k<NK>(st, s_img, app);
+    const uint32_t vmask = st.vmask, bmask = st.bmask;
+    const bool valid = st.valid, body = st.body, ring = valid && !body;
+    const KRaw& kr = st.kr;
     if (!vmask) continue;
     // ---- scores: lane (j, e16) ends with rows 4j..4j+3 of the 16 x 16 product (query rows x entries)
     floatx4 accb = {0, 0, 0, 0}, accr = {0, 0, 0, 0};
@@ -387,6 +500,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (tail == 2) qk_qrow<8>(kr, s_qr, ring, accr);
       else qk_bf16(kr, (const bf16x8*)s_qr, ring, accr);
     }
+    if (hit) image_v<NV>(st, s_img + kImgRow, app);   // after QK: the V loads had that long to arrive
     float s[4], mx[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -421,29 +535,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[h][k] *= alpha[h];
     __builtin_amdgcn_wave_barrier();
-    // ---- P.V for the 16 entries
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-      if (!(vmask & (1u << t))) continue;
-      float v[4];
-      if (bmask & (1u << t)) {
-        v_values<NV>(vr[t], lane, v);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] *= sv[k];
-      } else if (tail == 2) {
-        v_values<8>(vr[t], lane, v);
-      } else {
-        v[0] = bf16f(vr[t].w[0] & 0xFFFFu);
-        v[1] = bf16f(vr[t].w[0] >> 16);
-        v[2] = bf16f(vr[t].w[1] & 0xFFFFu);
-        v[3] = bf16f(vr[t].w[1] >> 16);
-      }
+    // ---- P.V for the 16 entries (a step of body rows only is straight-line code: the weight reads of the
+    // next entries can be issued ahead of the arithmetic)
+    auto pv = [&](int t, const float* v) {
       const floatx4 p0 = *(const floatx4*)&sp[t][0], p1 = *(const floatx4*)&sp[t][4];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float ph = h < 4 ? p0[h] : p1[h - 4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[h][k] = fmaf(ph, v[k], o[h][k]);
+      }
+    };
+    if (bmask == 0xFFFFu) {
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        float v[4];
+        v_values<NV>(st.vr[t], lane, v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] *= sv[k];
+        pv(t, v);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        if (!(vmask & (1u << t))) continue;
+        float v[4];
+        const VRaw& vr = st.vr[t];
+        if (bmask & (1u << t)) {
+          v_values<NV>(vr, lane, v);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] *= sv[k];
+        } else if (tail == 2) {
+          v_values<8>(vr, lane, v);
+        } else {
+          v[0] = bf16f(vr.w[0] & 0xFFFFu);
+          v[1] = bf16f(vr.w[0] >> 16);
+          v[2] = bf16f(vr.w[1] & 0xFFFFu);
+          v[3] = bf16f(vr.w[1] >> 16);
+        }
+        pv(t, v);
       }
     }
     __builtin_amdgcn_wave_barrier();   // the next step's writes of sp come after these reads
@@ -467,9 +597,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int k = 0; k < 4; ++k) s_o[wave][h][4 * lane + k] = o[h][k];
   __syncthreads();
   float* part = a.partials + (((size_t)si * g.n_kv_heads + head) * a.max_splits + split) * (G * (D + 2));
-  const int c = tid & 255;
+  const int c = tid % D;
 #pragma unroll
-  for (int h = tid >> 8; h < G; h += 2) {
+  for (int h = tid / D; h < G; h += 64 * NW / D) {
     float M = kNegBig;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);

@@ -228,11 +228,11 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
   return p;
 }
 
-// Gather decode: list entries per work-group are at least kGatherMin (one 16-entry step for each of its 8
-// waves); at most one work-group per CU over all (sequence, KV head) pairs.
-constexpr int kGatherMin = 128;
+// Gather decode: list entries per work-group are at least kGatherMin (one 16-entry step for each of its
+// waves); up to two work-groups per CU over all (sequence, KV head) pairs.
+constexpr int kGatherMin = 16 * kvq::kGatherWaves;
 int gather_budget_h(const kvq_cache* c) {
-  return std::max(1, std::min(c->n_cu, kvq::kMaxSplits) / c->cfg.n_kv_heads);
+  return std::max(1, std::min(2 * c->n_cu, kvq::kMaxSplits) / c->cfg.n_kv_heads);
 }
 int plan_gather(const kvq_cache* c, int n_seqs, const int* n_list, kvq::GatherSeq* out, int* total_wgs) {
   long total = 0;
@@ -269,10 +269,12 @@ kvq_status launch_combine_for(kvq_cache* c, int n_seqs, const int* n_splits, int
 }
 
 // The gather path shared by sparse decode and dense decode of a row-layout cache. positions: device
-// [n_seqs][pos_stride] or nullptr (entry i = position i, n_list[i] = len).
+// [n_seqs][pos_stride] or nullptr (entry i = position i, n_list[i] = len). With k_in / v_in (a fused sparse
+// step of a cache without a ring) the launch first appends one token per sequence at its current length.
 kvq_status run_gather(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
                       const int32_t* positions, int pos_stride, const int* n_list, float* out, float softmax_scale,
-                      void* workspace, size_t ws_bytes, void* stream) {
+                      void* workspace, size_t ws_bytes, void* stream, const void* k_in = nullptr,
+                      const void* v_in = nullptr) {
   kvq::GatherArgs a{};
   a.g = geometry(c);
   int total_wgs = 0;
@@ -282,13 +284,18 @@ kvq_status run_gather(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
   int n_splits[KVQ_MAX_BATCH];
   for (int i = 0; i < n_seqs; ++i) {
     const int k = c->idx(layer, seq_ids[i]);
+    const int app = k_in ? 1 : 0;
     a.seqs[i].slab = slab_offset(c, layer, seq_ids[i]);
-    a.seqs[i].len = c->len[k];
-    a.seqs[i].body_len = c->body_len[k];
+    a.seqs[i].len = c->len[k] + app;
+    a.seqs[i].body_len = c->body_len[k] + app;
     a.seqs[i].n_list = n_list[i];
+    a.seqs[i].app_pos = app ? c->len[k] : -1;
     n_splits[i] = a.seqs[i].n_splits;
   }
   a.q = (const uint16_t*)q_bf16;
+  a.k_in = (const uint16_t*)k_in;
+  a.v_in = (const uint16_t*)v_in;
+  a.step = k_in ? 1 : 0;
   a.positions = positions;
   a.pos_stride = pos_stride;
   a.partials = (float*)workspace;
@@ -300,6 +307,13 @@ kvq_status run_gather(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
   hipError_t e = timed(c, KVQ_KERNEL_GATHER, (hipStream_t)stream,
                        [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_gather(a, total_wgs, (hipStream_t)stream, e0, e1); });
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  if (k_in) {
+    for (int i = 0; i < n_seqs; ++i) {
+      const int k = c->idx(layer, seq_ids[i]);
+      c->len[k] += 1;
+      c->body_len[k] = c->len[k];
+    }
+  }
   return launch_combine_for(c, n_seqs, n_splits, max_splits, out, workspace, (hipStream_t)stream);
 }
 
@@ -762,9 +776,10 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   return launch_combine_for(c, n_seqs, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
 }
 
-kvq_status kvq_sparse_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
-                                  const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
-                                  float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+// Host checks of a sparse decode call (before any work).
+static kvq_status check_sparse(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
+                               const int32_t* positions, int32_t budget, const float* out, float softmax_scale,
+                               const void* workspace) {
   kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != KVQ_OK) return s;
   if (c->cfg.layout != KVQ_LAYOUT_ROWS)
@@ -774,10 +789,44 @@ kvq_status kvq_sparse_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, c
   if (((uintptr_t)positions) % 4 != 0) return fail(KVQ_E_INVALID, "positions must be 4-byte aligned");
   if (budget < 1 || budget > (1 << 28)) return fail(KVQ_E_INVALID, "budget must be in [1, 2^28] (got %d)", budget);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
+  return KVQ_OK;
+}
+
+kvq_status kvq_sparse_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                  const void* q_bf16, const int32_t* positions, int32_t budget, float* out,
+                                  float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_sparse(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, out, softmax_scale, workspace);
+  if (s != KVQ_OK) return s;
   int n_list[KVQ_MAX_BATCH];
   for (int i = 0; i < n_seqs; ++i) n_list[i] = budget;
   return run_gather(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, n_list, out, softmax_scale, workspace,
                     ws_bytes, stream);
+}
+
+kvq_status kvq_sparse_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                  const void* k_bf16, const void* v_bf16, const void* q_bf16,
+                                  const int32_t* positions, int32_t budget, float* out, float softmax_scale,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_sparse(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, out, softmax_scale, workspace);
+  if (s != KVQ_OK) return s;
+  // one launch when the new rows go straight to the body (no ring) and are quantized with known scales
+  bool fuse = c->cfg.tail_len == 0 && k_bf16 && v_bf16;
+  for (int i = 0; i < n_seqs && fuse; ++i) {
+    const int k = c->idx(layer, seq_ids[i]);
+    if ((long)c->len[k] + 1 > c->cfg.capacity) fuse = false;               // reported by kvq_append
+    else if (c->cfg.kvarn && !c->calibrated[k]) fuse = false;             // calibration comes first
+  }
+  if (!fuse) {
+    int32_t ones[KVQ_MAX_BATCH];
+    for (int i = 0; i < n_seqs; ++i) ones[i] = 1;
+    s = kvq_append(c, layer, n_seqs, seq_ids, ones, k_bf16, v_bf16, stream);
+    return s != KVQ_OK ? s : kvq_sparse_decode_attn(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, out,
+                                                     softmax_scale, workspace, ws_bytes, stream);
+  }
+  int n_list[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) n_list[i] = budget;
+  return run_gather(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, n_list, out, softmax_scale, workspace,
+                    ws_bytes, stream, k_bf16, v_bf16);
 }
 
 }  // extern "C"

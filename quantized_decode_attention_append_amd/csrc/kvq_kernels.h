@@ -105,6 +105,8 @@ struct DecodeArgs {
 };
 
 
+constexpr int kGatherWaves = 8;    // waves per gather work-group (16 list entries per wave step)
+
 // Gather decode over a list of positions of a row-layout cache (sparse decode), or over all positions
 // (dense decode of a row-layout cache: positions == nullptr, entry i is position i).
 struct GatherSeq {
@@ -112,6 +114,7 @@ struct GatherSeq {
   int len, body_len;
   int n_list;        // list entries of this sequence (budget, or len)
   int n_splits;      // work-groups per KV head
+  int app_pos;       // fused sparse step: the body position written from input row (sequence index); -1: none
 };
 struct GatherArgs {
   Geometry g;
@@ -119,6 +122,9 @@ struct GatherArgs {
   const int32_t* positions;    // [n_seqs][pos_stride] or nullptr
   int pos_stride;
   float* partials;             // [n_seqs][Hkv][max_splits][8 * (D + 2)]
+  const uint16_t* k_in;        // fused sparse step: the appended K and V tokens [n_seqs][Hkv][D] bf16
+  const uint16_t* v_in;
+  int step;
   int n_seqs, n_q_heads, group, max_splits;
   float scale;
   GatherSeq seqs[kMaxBatch];

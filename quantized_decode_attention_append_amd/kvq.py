@@ -26,7 +26,7 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
 KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5}
 
 
@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "kvq_tail_evict": (I32, [P, I32, I32, IP, P]),
         "kvq_decode_attn": (I32, [P, I32, I32, IP, P, P, F, P, SZ, P]),
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
+        "kvq_sparse_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, I32, P, F, P, SZ, P]),
         "kvq_timing_enable": (I32, [P, I32]),
         "kvq_timing_read": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), IP]),
         "kvq_last_error": (ctypes.c_char_p, []),
@@ -261,6 +262,33 @@ class Cache:
         if workspace is None:
             workspace = self.workspace(n, budget)
         _check(_lib.kvq_sparse_decode_attn(self._h, layer, n, _ids(seq_ids), _dev(q, q.dtype, "q"),
+                                           _dev(positions, torch.int32, "positions"), budget,
+                                           _dev(out, torch.float32, "out"), float(softmax_scale),
+                                           _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                           ctypes.c_void_p(_stream(stream))))
+        return out
+
+    def sparse_decode_step(self, layer: int, seq_ids: Sequence[int], k: torch.Tensor, v: torch.Tensor,
+                           q: torch.Tensor, positions: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None):
+        """append() of one token per sequence, then sparse_decode_attn() (one launch without a tail ring).
+        k, v: bf16 [n_seqs, Hkv, D]; q: bf16 [n_seqs, Hq, D]; positions: int32 [n_seqs, budget] (after the
+        append: the new token is at the old length)."""
+        n = len(seq_ids)
+        for name, t in (("k", k), ("v", v)):
+            if t.numel() != n * self.hk * self.d or t.element_size() != 2:
+                raise ValueError(f"{name} must be bf16 [n_seqs, Hkv, D]")
+        if q.numel() != n * self.hq * self.d or q.element_size() != 2:
+            raise ValueError("q must be bf16 [n_seqs, Hq, D]")
+        if positions.dim() != 2 or positions.shape[0] != n:
+            raise ValueError("positions must be int32 [n_seqs, budget]")
+        budget = positions.shape[1]
+        if out is None:
+            out = torch.empty((n, self.hq, self.d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(n, budget)
+        _check(_lib.kvq_sparse_decode_step(self._h, layer, n, _ids(seq_ids), _dev(k, k.dtype, "k"),
+                                           _dev(v, v.dtype, "v"), _dev(q, q.dtype, "q"),
                                            _dev(positions, torch.int32, "positions"), budget,
                                            _dev(out, torch.float32, "out"), float(softmax_scale),
                                            _dev(workspace, torch.uint8, "workspace"), workspace.numel(),

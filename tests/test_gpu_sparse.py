@@ -143,3 +143,54 @@ def test_sparse_needs_the_row_layout():
     with pytest.raises(kvq.KvqError) as e:
         p.gpu.sparse_decode_attn(0, [0], dev(small_query(0, 1, 16, 256)), pos)
     assert e.value.status == kvq.KVQ_E_INVALID
+
+
+@pytest.mark.parametrize("nk,nv,kvarn,tail_dtype,n_seqs", [(8, 8, 0, 0, 1), (6, 5, 1, 0, 2), (3, 7, 0, 0, 3),
+                                                          (4, 4, 0, 1, 1), (8, 8, 1, 0, 1)])
+def test_sparse_decode_step_matches_append_then_sparse(nk, nv, kvarn, tail_dtype, n_seqs):
+    """kvq_sparse_decode_step against the oracle doing the append and then sparse decode: body bytes and
+    outputs after every step. Without a ring (and calibrated KVarN scales) the new rows are written inside the
+    gather launch, also by work-groups whose range lists the new position (the list holds it at varying
+    places, or not at all); with a ring, or before KVarN calibration, the calls run in turn."""
+    c = cfg(k_bits=nk, v_bits=nv, kvarn=kvarn, tail_dtype=tail_dtype, tail_len=64 if tail_dtype else 0,
+            tail_slack=32 if tail_dtype else 0, capacity=1024)
+    p = Pair(c)
+    k, v = small_tokens(700 + nk * 10 + nv + kvarn, 900, 2, 256, scale=outlier_scale())
+    seqs = list(range(n_seqs))
+    off = 0
+    for i, n in zip(seqs, (300, 150, 125)):
+        p.append(0, [i], [n], k[off:off + n], v[off:off + n])
+        off += n
+    rng = np.random.default_rng(nk + 10 * nv + 100 * kvarn)
+    p.gpu.timing(True)
+    for step in range(5):
+        kk, vv = k[off:off + n_seqs], v[off:off + n_seqs]
+        off += n_seqs
+        lens = [p.gpu.lengths(0, i)[0] + 1 for i in seqs]
+        budget = 120   # two list ranges per KV head: the new position falls in either, or in none
+        pos = []
+        for i, n in enumerate(lens):
+            recent = np.arange(n - 16, n)
+            rest = rng.choice(n - 16, size=budget - 16, replace=False)
+            lst = np.concatenate([rest, recent]) if step % 2 else np.concatenate([recent, rest])
+            if step == 3 and i == 0:
+                lst = rest[:budget]   # the new position not listed: still appended
+                lst = np.concatenate([lst, rng.choice(n - 16, size=budget - len(lst), replace=False)])
+            pos.append(lst)
+        pos = np.stack(pos).astype(np.int32)
+        q = small_query(50 + step, n_seqs, 16, 256)
+        import torch
+        got = p.gpu.sparse_decode_step(0, seqs, dev(kk), dev(vv), dev(q), torch.from_numpy(pos).to("cuda")).cpu().numpy()
+        p.ora.append(0, seqs, [1] * n_seqs, kk, vv)
+        import oracle
+        want = oracle.sparse_reference(p.ora, 0, seqs, q, pos)
+        for i in seqs:
+            p.lengths_match(0, i)
+            p.assert_slab_equal(0, i)
+        assert max_err(got, want) <= TOL, f"step {step}: {max_err(got, want):.3e}"
+    appends = p.gpu.timing_read("append")[1]
+    p.gpu.timing(False)
+    if tail_dtype == 0:
+        assert appends == 0, appends   # every step's append ran in the gather launch
+    else:
+        assert appends > 0
