@@ -64,7 +64,9 @@ def test_decode_step_graph(tail_dtype, kvarn):
         assert max_err(e_got, oracle.decode_reference(p.ora, 1, seqs, q2)) <= TOL
 
 
-def test_sparse_step_graph():
+@pytest.mark.parametrize("fused", [False, True])
+def test_sparse_step_graph(fused):
+    """Append + sparse decode, as two calls or as kvq_sparse_decode_step (the append inside the gather launch)."""
     import torch
     p = Pair(cfg(k_bits=8, v_bits=8, layout=1))
     k, v = small_tokens(310, 600, 2, 256)
@@ -78,8 +80,11 @@ def test_sparse_step_graph():
     ws = p.gpu.workspace(1, 256)
 
     def step():
-        p.gpu.append(0, [0], [1], kk, vv)
-        p.gpu.sparse_decode_attn(0, [0], qd, posd, out=out, workspace=ws)
+        if fused:
+            p.gpu.sparse_decode_step(0, [0], kk, vv, qd, posd, out=out, workspace=ws)
+        else:
+            p.gpu.append(0, [0], [1], kk, vv)
+            p.gpu.sparse_decode_attn(0, [0], qd, posd, out=out, workspace=ws)
 
     g = capture(torch, step)
     p.ora.append(0, [0], [1], k[500:501], v[500:501])
