@@ -41,7 +41,10 @@ typedef enum {
 typedef enum {
   KVQ_TAIL_NONE = 0,    /* no precision tail: every token goes straight to the qN_0 body          */
   KVQ_TAIL_BF16 = 1,    /* newest tail_len tokens kept in bf16 (BeeLlama page, precision tail)     */
-  KVQ_TAIL_Q8_0 = 2     /* newest tail_len tokens kept as q8_0 (Qwen3.8-27B page, 8-bit ring)      */
+  KVQ_TAIL_Q8_0 = 2,    /* newest tail_len tokens kept as q8_0 (Qwen3.8-27B page, 8-bit ring)      */
+  KVQ_TAIL_F16 = 3      /* newest tail_len tokens kept in f16 (BeeLlama page, precision tail: BF16 or
+                         * F16): the bf16 input rounded to IEEE binary16, nearest even; magnitudes
+                         * above 65504 become infinite (the caller keeps K, V in f16 range)       */
 } kvq_tail_dtype;
 
 typedef enum {

@@ -4,8 +4,11 @@ Test infrastructure only. Follows, step by step:
 
 * qN_0 body with separate K and V widths (KVarN benchmark page, K/V pair table;
   "Hard numbers on Qwen3.8-27B's KV cache" page, K 6-bit / V 5-bit setting D).
-* Precision tail: the newest W tokens are kept in bf16, the rest quantized as usual
-  (BeeLlama.cpp v0.4.1 page, KV cache precision tail paragraph).
+* Precision tail: the newest W tokens are kept in bf16 or f16, the rest quantized as
+  usual (BeeLlama.cpp v0.4.1 page, KV cache precision tail paragraph and feature list).
+  Reading for f16: the bf16 input is converted to IEEE binary16 with round to nearest
+  even (exact for every bf16 value of magnitude in [2^-14, 65504]; smaller ones round to
+  f16 subnormals, larger ones overflow to infinity).
 * 8-bit recent ring: the newest 2,048 positions sit in an 8-bit ring; below the
   window the output equals a q8_0 cache (Qwen3.8-27B page, KV low-bit section).
   Reading: ring rows are q8_0 blocks; eviction requantizes the dequantized q8_0
@@ -31,12 +34,22 @@ from .layout import (pack_k_rows, pack_k_tiles, pack_bf16_k_tiles, pack_v_tiles,
                      slab_layout, TILE)
 from .quant import quantize_blocks, kvarn_sigma, normalize, dequantize_blocks
 
-TAIL_NONE, TAIL_BF16, TAIL_Q8 = 0, 1, 2
+TAIL_NONE, TAIL_BF16, TAIL_Q8, TAIL_F16 = 0, 1, 2, 3
+_TAIL_16 = (TAIL_BF16, TAIL_F16)   # rings of 16-bit values
 LAYOUT_TILES, LAYOUT_ROWS = 0, 1
 
 
 def _bf16_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _f16_bits(x32):
+    """IEEE binary16 bit patterns of fp32 values (round to nearest even)."""
+    return np.asarray(x32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _f16_f32(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
 
 
 class _SeqState:
@@ -53,7 +66,7 @@ class _SeqState:
         self.vu = np.zeros((cap32, hk, d), dtype=np.uint8)
         self.vd = np.zeros((cap32, hk, nb), dtype=np.float16)
         r = lay["ring_slots"]
-        if cfg["tail_len"] > 0 and cfg["tail_dtype"] == TAIL_BF16:
+        if cfg["tail_len"] > 0 and cfg["tail_dtype"] in _TAIL_16:
             self.rk = np.zeros((r, hk, d), dtype=np.uint16)
             self.rv = np.zeros((r, hk, d), dtype=np.uint16)
         elif cfg["tail_len"] > 0:
@@ -86,6 +99,8 @@ class OracleCache:
         """fp32 ring representation r(x) of K and V at ring slots: [n, Hkv, D] each."""
         if self.tail == TAIL_BF16:
             return _bf16_f32(s.rk[slots]), _bf16_f32(s.rv[slots])
+        if self.tail == TAIL_F16:
+            return _f16_f32(s.rk[slots]), _f16_f32(s.rv[slots])
         k = dequantize_blocks(s.rku[slots], s.rkd[slots], 8).astype(np.float32)   # exact c * d16
         v = dequantize_blocks(s.rvu[slots], s.rvd[slots], 8).astype(np.float32)
         return k, v
@@ -94,6 +109,8 @@ class OracleCache:
         """r(x) for fresh inputs (what the ring would store, read back as fp32)."""
         k = _bf16_f32(k_bits)
         v = _bf16_f32(v_bits)
+        if self.tail == TAIL_F16:
+            k, v = _f16_f32(_f16_bits(k)), _f16_f32(_f16_bits(v))
         if self.tail == TAIL_Q8:
             ku, kd = quantize_blocks(k, 8)
             vu, vd = quantize_blocks(v, 8)
@@ -118,6 +135,9 @@ class OracleCache:
         if self.tail == TAIL_BF16:
             s.rk[slots] = k_bits
             s.rv[slots] = v_bits
+        elif self.tail == TAIL_F16:
+            s.rk[slots] = _f16_bits(_bf16_f32(k_bits))
+            s.rv[slots] = _f16_bits(_bf16_f32(v_bits))
         else:
             s.rku[slots], s.rkd[slots] = quantize_blocks(_bf16_f32(k_bits), 8)
             s.rvu[slots], s.rvd[slots] = quantize_blocks(_bf16_f32(v_bits), 8)
@@ -221,7 +241,7 @@ class OracleCache:
             return pack_k_tiles(s.ku[lo:hi, head].reshape(-1, TILE, d), s.kd[lo:hi, head].reshape(-1, TILE, d // 32), kb)
         if region == "k_ring" and not self.rows:
             assert lo % TILE == 0 and hi % TILE == 0
-            if self.tail == TAIL_BF16:
+            if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return pack_bf16_k_tiles(s.rk[lo:hi, head].reshape(-1, TILE, d))
             return pack_k_tiles(s.rku[lo:hi, head].reshape(-1, TILE, d), s.rkd[lo:hi, head].reshape(-1, TILE, d // 32), 8)
         if region == "k_body":
@@ -229,7 +249,7 @@ class OracleCache:
         if region == "v_body" and self.rows:
             return pack_k_rows(s.vu[lo:hi, head], s.vd[lo:hi, head], vb)
         if region == "v_ring" and self.rows:
-            if self.tail == TAIL_BF16:
+            if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return np.ascontiguousarray(s.rv[lo:hi, head]).view(np.uint8)
             return pack_k_rows(s.rvu[lo:hi, head], s.rvd[lo:hi, head], 8)
         if region == "v_body":
@@ -238,12 +258,12 @@ class OracleCache:
             d = s.vd[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"] // 32)
             return pack_v_tiles(u, d, vb)
         if region == "k_ring":
-            if self.tail == TAIL_BF16:
+            if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return np.ascontiguousarray(s.rk[lo:hi, head]).view(np.uint8)
             return pack_k_rows(s.rku[lo:hi, head], s.rkd[lo:hi, head], 8)
         if region == "v_ring":
             assert lo % TILE == 0 and hi % TILE == 0
-            if self.tail == TAIL_BF16:
+            if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return pack_bf16_v_tiles(s.rv[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"]))
             u = s.rvu[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"])
             d = s.rvd[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"] // 32)

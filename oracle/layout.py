@@ -318,7 +318,7 @@ def slab_layout(cfg: dict) -> dict:
     rk = row_bytes(cfg["k_bits"], d)
     rv = row_bytes(cfg["v_bits"], d)
     r = ring_slots(cfg)
-    if cfg["tail_len"] > 0 and cfg["tail_dtype"] == 1:
+    if cfg["tail_len"] > 0 and cfg["tail_dtype"] in (1, 3):   # bf16 or f16 values
         ring_rk = ring_rv = 2 * d
     elif cfg["tail_len"] > 0 and cfg["tail_dtype"] == 2:
         ring_rk = ring_rv = row_bytes(8, d)

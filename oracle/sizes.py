@@ -16,7 +16,7 @@ def kv_token_bytes(n_bits_k: int, n_bits_v: int, n_kv_heads: int, head_dim: int)
 
 
 def ring_token_bytes(tail_dtype: int, n_kv_heads: int, head_dim: int) -> int:
-    if tail_dtype == 1:
+    if tail_dtype in (1, 3):   # bf16 or f16 values: 2 bytes each
         return n_kv_heads * 2 * head_dim * 2
     if tail_dtype == 2:
         return n_kv_heads * 2 * row_bytes(8, head_dim)

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
 __global__ __launch_bounds__(512) void step_write_kernel(StepArgs a) {
   const int x = blockIdx.x;
   if (x < a.ring_wgs) {
-    if (a.ring.g.tail_dtype == 1) bf16_ring_write_wg(a.ring, x, blockIdx.y);
+    if (a.ring.g.tail_dtype != 2) bf16_ring_write_wg(a.ring, x, blockIdx.y);   // bf16 or f16 values
     else body_write_wg(a.ring, x, blockIdx.y);
   } else {
     body_write_wg(a.body, x - a.ring_wgs, blockIdx.y);

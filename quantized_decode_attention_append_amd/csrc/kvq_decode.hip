@@ -458,6 +458,53 @@ __device__ inline void tile_bf16(WaveState& st, const bf16x8* qb, float qmul, co
   }
 }
 
+// One 32-position tile of the f16 tail ring: as tile_bf16 with fp16 MFMA. The query B operand holds fp16 hi
+// parts in columns 0-7 and lo parts in columns 8-15 (the bf16 query is not always exact in fp16), so a score
+// is the sum of columns h and h + 8 (one DPP rotation by 8 within the 16-lane row).
+__device__ inline void tile_f16(WaveState& st, const half8* qb, float qmul, const uint8_t* kt,
+                                const uint8_t* vt, int tile, int lo, int hi, bool lo_lane) {
+  constexpr int NT = 16;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  float sc[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    half8 kk[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) kk[b] = __builtin_nontemporal_load((const half8*)(kt + ((s * 8 + b) * 64 + lane) * 16));
+    floatx4 c = {0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk[b], qb[b * 64 + lane], c, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[s][r] = c[r] + dpp_ror8(c[r]);   // hi column + lo column
+  }
+  float x[8], p[8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pos = tile * kTile + 16 * s + 4 * g + r;
+      x[4 * s + r] = (pos >= lo && pos < hi) ? sc[s][r] * qmul : -INFINITY;
+    }
+  softmax_update(st, x, p);
+  half8 a;
+  const float kf = lo_lane ? 1.0f : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 h = (_Float16)p[i];
+    a[i] = (_Float16)fmaf(-kf, (float)h, p[i]);
+  }
+#pragma unroll
+  for (int n0 = 0; n0 < NT; n0 += 4) {
+    half8 vv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vv[k] = __builtin_nontemporal_load((const half8*)(vt + (n0 + k) * 1024 + lane * 16));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      st.o[n0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, vv[k], st.o[n0 + k], 0, 0, 0);
+  }
+}
+
 // ------------------------------------------------------------------ the split kernel
 
 struct QArgs {
@@ -560,7 +607,7 @@ __device__ inline void step_writes(const DecodeArgs& a, const DecodeSeq& S, int 
   if (is_ring && split == n_splits - 1 && S.app_pos >= 0) {
     const StepWriteView w{a.g, a.k_in, a.v_in, 1, 1,
                           {WriteItem{S.slab, S.app_pos, S.app_pos + 1, S.app_pos, si, S.app_pos / kTile, 0}}};
-    if (a.g.tail_dtype == 1) bf16_ring_write_wg(w, 0, head);
+    if (a.g.tail_dtype != 2) bf16_ring_write_wg(w, 0, head);   // bf16 or f16 values
     else body_write_wg(w, 0, head);
   } else if (!is_ring && split == S.n_body_splits - 1 && S.ev1 > S.ev0) {
     const StepWriteView w{a.g, a.k_in, a.v_in, 0, 1,
@@ -659,23 +706,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int n = 0; n < NT; ++n) st.o[n] = floatx4{0, 0, 0, 0};
 
   // channels of this lane's B operand: 32b + 8*gq + i
-  if (is_ring && tail == 1) {
-    bf16x8* qb = (bf16x8*)s_qb;
+  if (is_ring && (tail == 1 || tail == 3)) {
+    // B operands of QK: bf16 ring: the bf16 query, columns 8-15 repeating heads 0-7 so the lo-part lanes see
+    // the same scores; f16 ring: fp16 hi parts in columns 0-7, lo parts in columns 8-15
+    u32x4* qb = (u32x4*)s_qb;
     if (wave == 0) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        // columns 8-15 repeat heads 0-7 so the lo-part lanes see the same scores
-        bf16x8 v = *(const bf16x8*)(qrow + 32 * b + 8 * gq);
-        if (!head_ok) v = bf16x8{};
-        qb[b * 64 + lane] = v;
+        u32x4 w = *(const u32x4*)(qrow + 32 * b + 8 * gq);
+        if (tail == 3) {
+          half8 v;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float q = __uint_as_float((w[i >> 1] >> (16 * (i & 1))) << 16);
+            const _Float16 h = (_Float16)q;
+            v[i] = lo_lane ? (_Float16)(q - (float)h) : h;
+          }
+          w = __builtin_bit_cast(u32x4, v);
+        }
+        if (!head_ok) w = u32x4{0u, 0u, 0u, 0u};
+        qb[b * 64 + lane] = w;
       }
     }
     __syncthreads();
     const float qmul = a.scale * kLog2e;
     for (int t = wb; t < we; t = grab_tile(&s_next)) {
       const size_t rt = (size_t)head * (R / kTile) + ((t * kTile) % R) / kTile;
-      tile_bf16(st, qb, qmul, slab + g.k_ring + rt * g.ring_tile_k, slab + g.v_ring + rt * g.ring_tile_v, t, lo, hi,
-                lo_lane);
+      const uint8_t* kt = slab + g.k_ring + rt * g.ring_tile_k;
+      const uint8_t* vt = slab + g.v_ring + rt * g.ring_tile_v;
+      if (tail == 3) tile_f16(st, (const half8*)qb, qmul, kt, vt, t, lo, hi, lo_lane);
+      else tile_bf16(st, (const bf16x8*)qb, qmul, kt, vt, t, lo, hi, lo_lane);
     }
   } else {
     const uint32_t lane_mask = lo_lane ? 0xFFFFFFFFu : 0u;

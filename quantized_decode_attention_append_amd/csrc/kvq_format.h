@@ -102,7 +102,7 @@ struct SlabLayout {
   int cap32, row_k, row_v, ring_row_k, ring_row_v, ring_slots;
 };
 
-// tail_dtype: 0 none, 1 bf16, 2 q8_0.
+// tail_dtype: 0 none, 1 bf16, 2 q8_0, 3 f16.
 KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_bits, int v_bits,
                               int kvarn, int tail_len, int tail_slack, int tail_dtype) {
   SlabLayout L{};
@@ -110,7 +110,7 @@ KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_
   L.row_k = row_bytes(k_bits, head_dim);
   L.row_v = row_bytes(v_bits, head_dim);
   L.ring_slots = tail_len > 0 ? tail_len + tail_slack : 0;
-  if (tail_len > 0 && tail_dtype == 1) {
+  if (tail_len > 0 && (tail_dtype == 1 || tail_dtype == 3)) {   // 16-bit values
     L.ring_row_k = L.ring_row_v = 2 * head_dim;
   } else if (tail_len > 0 && tail_dtype == 2) {
     L.ring_row_k = L.ring_row_v = row_bytes(8, head_dim);

@@ -19,7 +19,7 @@
 //   through LDS to every lane;
 // * for P.V, lane c owns channels 4c..4c+3 of all 8 heads and decodes its 4 codes of each entry's V row.
 // Rows in the tail ring (positions >= body_len) are read as q8_0 rows (a second query operand without the
-// KVarN scale) or bf16 rows (bf16 MFMA); KVarN scales apply to body rows only (K through the query, V per
+// KVarN scale), f16 rows (fp16 MFMA on the values with that operand) or bf16 rows (bf16 MFMA); KVarN scales apply to body rows only (K through the query, V per
 // position).
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -157,6 +157,17 @@ __device__ inline void qk_qrow(const KRaw& kr, const half8* qb, bool use, floatx
   qk_block<N, 5>(kr, qb, kb, d[5], acc);
   qk_block<N, 6>(kr, qb, kb, d[6], acc);
   qk_block<N, 7>(kr, qb, kb, d[7], acc);
+}
+
+// f16 ring rows: the fp16 values themselves against the shifted fp16 hi / lo query rows.
+__device__ inline void qk_f16(const KRaw& kr, const half8* qb, bool use, floatx4& acc) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    u32x4 w = {kr.w[4 * b], kr.w[4 * b + 1], kr.w[4 * b + 2], kr.w[4 * b + 3]};
+    if (!use) w = u32x4{0u, 0u, 0u, 0u};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[b * 64 + lane], __builtin_bit_cast(half8, w), acc, 0, 0, 0);
+  }
 }
 
 __device__ inline void qk_bf16(const KRaw& kr, const bf16x8* qb, bool use, floatx4& acc) {
@@ -449,7 +460,7 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
         for (int i = 0; i < 8; ++i) v[i] = (_Float16)ldexpf(part[i], Planes<NK>::sh[p] - dn_bitpos(w, slot, i));   // exact
         s_qb[p * 512 + b * 64 + lane] = v;
       }
-      if (tail == 2) {
+      if (tail == 2 || tail == 3) {   // q8_0 or f16 ring: the shifted query as fp16 hi / lo rows
         half8 v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (_Float16)partr[i];   // 8-bit plane: every field at bit 0
@@ -467,7 +478,7 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
   __syncthreads();
   const float qsc = a.scale * kLog2e;
   const float qmul_b = qsc * ldexpf(1.0f, e + 24);   // body scores: C * d * 2^(e + 24)
-  const float qmul_r = tail == 2 ? qsc * ldexpf(1.0f, er + 24) : qsc;
+  const float qmul_r = tail == 2 ? qsc * ldexpf(1.0f, er + 24) : tail == 3 ? qsc * ldexpf(1.0f, er) : qsc;
 
   float (*sp)[G] = s_p[wave];
 
@@ -498,6 +509,7 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
     if (bmask) qk_qrow<NK>(kr, s_qb, body, accb);
     if (vmask & ~bmask) {
       if (tail == 2) qk_qrow<8>(kr, s_qr, ring, accr);
+      else if (tail == 3) qk_f16(kr, s_qr, ring, accr);
       else qk_bf16(kr, (const bf16x8*)s_qr, ring, accr);
     }
     if (hit) image_v<NV>(st, s_img + kImgRow, app);   // after QK: the V loads had that long to arrive
@@ -567,6 +579,11 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
           for (int k = 0; k < 4; ++k) v[k] *= sv[k];
         } else if (tail == 2) {
           v_values<8>(vr, lane, v);
+        } else if (tail == 3) {
+          v[0] = f16f(vr.w[0] & 0xFFFFu);
+          v[1] = f16f(vr.w[0] >> 16);
+          v[2] = f16f(vr.w[1] & 0xFFFFu);
+          v[3] = f16f(vr.w[1] >> 16);
         } else {
           v[0] = bf16f(vr.w[0] & 0xFFFFu);
           v[1] = bf16f(vr.w[0] >> 16);

@@ -110,8 +110,8 @@ kvq_status validate(const kvq_config* c) {
   if (c->layout != KVQ_LAYOUT_TILES && c->layout != KVQ_LAYOUT_ROWS)
     return fail(KVQ_E_INVALID, "layout must be KVQ_LAYOUT_TILES or KVQ_LAYOUT_ROWS (got %d)", c->layout);
   if (c->tail_len > 0) {
-    if (c->tail_dtype != KVQ_TAIL_BF16 && c->tail_dtype != KVQ_TAIL_Q8_0)
-      return fail(KVQ_E_INVALID, "tail_dtype must be KVQ_TAIL_BF16 or KVQ_TAIL_Q8_0 when tail_len > 0");
+    if (c->tail_dtype != KVQ_TAIL_BF16 && c->tail_dtype != KVQ_TAIL_Q8_0 && c->tail_dtype != KVQ_TAIL_F16)
+      return fail(KVQ_E_INVALID, "tail_dtype must be KVQ_TAIL_BF16, KVQ_TAIL_Q8_0 or KVQ_TAIL_F16 when tail_len > 0");
     const long r = (long)c->tail_len + c->tail_slack;
     if (r % kvq::kTile != 0) return fail(KVQ_E_INVALID, "tail_len + tail_slack must be a multiple of 32 (got %ld)", r);
     if (r > (1 << 24)) return fail(KVQ_E_INVALID, "tail_len + tail_slack too large");
@@ -184,7 +184,7 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
   const int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
   // Cost of a tile in a work-group's time: a qN_0 tile (body or q8_0 ring) is decode- and MFMA-bound, a bf16
   // ring tile carries 2.7x the bytes of a K6/V5 tile with little decode and no prefetch: it counts double.
-  const double ring_w = c->cfg.tail_dtype == KVQ_TAIL_BF16 ? 2.0 : 1.0;
+  const double ring_w = c->cfg.tail_dtype == KVQ_TAIL_Q8_0 ? 1.0 : 2.0;
   int tiles[2 * KVQ_MAX_BATCH], nwg[2 * KVQ_MAX_BATCH];
   double wt[2 * KVQ_MAX_BATCH];
   double total = 0;
@@ -545,7 +545,7 @@ kvq_status kvq_append(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
   }
   if (ring_wgs) {
     e = timed(c, KVQ_KERNEL_APPEND, st, [&](hipEvent_t e0, hipEvent_t e1) {
-      return (c->cfg.tail_dtype == KVQ_TAIL_BF16) ? kvq::launch_bf16_ring_write(ring, ring_wgs, st, e0, e1)
+      return (c->cfg.tail_dtype != KVQ_TAIL_Q8_0) ? kvq::launch_bf16_ring_write(ring, ring_wgs, st, e0, e1)
                                                   : kvq::launch_body_write(ring, ring_wgs, st, e0, e1);
     });
     if (e != hipSuccess) return hip_fail(e, "ring write launch");

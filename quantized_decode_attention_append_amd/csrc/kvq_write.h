@@ -17,6 +17,10 @@ namespace {
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 __device__ inline float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+// IEEE binary16 bits of a bf16 value (round to nearest even; overflow to infinity): the f16 tail's stored form
+__device__ inline uint16_t bf16_to_f16_bits(uint16_t b) {
+  return __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(b));
+}
 
 // ------------------------------------------------------------------------------ body write
 //
@@ -52,8 +56,9 @@ __device__ inline uint32_t quant_lane(float x, int n_bits, uint16_t* d16_bits) {
   return (uint32_t)((int)c + off);
 }
 
-// fp32 ring representation r(x) of one value: the bf16 value itself, or its q8_0 round trip.
+// fp32 ring representation r(x) of one value: the bf16 value itself, its f16 rounding, or its q8_0 round trip.
 __device__ inline float ring_rep(float x, int tail_dtype) {
+  if (tail_dtype == 3) return (float)(_Float16)x;
   if (tail_dtype != 2) return x;
   uint16_t d;
   const uint32_t u = quant_lane(x, 8, &d);
@@ -74,15 +79,17 @@ __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int k
   const int j = (c % kBlock) / 8;
   const int klane = 16 * j + (t % 16);   // K tile lane of (slot, channel)
   const size_t rt = (size_t)head * (R / kTile) + slot / kTile;   // ring tile (tile layout)
-  if (g.tail_dtype == 1) {
+  if (g.tail_dtype == 1 || g.tail_dtype == 3) {   // 16-bit values: bf16 or f16
+    const bool f16 = g.tail_dtype == 3;
+    auto cv = [&](uint16_t bits) { return f16 ? f16_to_f32(bits) : bf16_to_f32(bits); };
     if (g.layout == 1)
-      return bf16_to_f32(((const uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c]);
+      return cv(((const uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c]);
     if (kv == 0) {
       const uint16_t* kt = (const uint16_t*)(slab + g.k_ring + rt * g.ring_tile_k);
-      return bf16_to_f32(kt[(((t / 16) * NB + b) * 64 + klane) * 8 + (c % 8)]);
+      return cv(kt[(((t / 16) * NB + b) * 64 + klane) * 8 + (c % 8)]);
     }
     const uint8_t* tile = slab + g.v_ring + rt * g.ring_tile_v;
-    return bf16_to_f32(*((const uint16_t*)(tile + (size_t)(c / 16) * 64 * 16 + lane * 16) + e));
+    return cv(*((const uint16_t*)(tile + (size_t)(c / 16) * 64 * 16 + lane * 16) + e));
   }
   if (g.layout == 1) {
     const uint8_t* row = slab + (kv ? g.v_ring : g.k_ring) + ((size_t)head * R + slot) * g.ring_row_k;
@@ -361,7 +368,8 @@ __device__ inline void body_write_wg(const A& a, int wg, int head) {
 
 // ------------------------------------------------------------------------------ bf16 ring write
 
-// One work-group of 512 threads per (position tile, KV head): thread (kv, c) copies channel c.
+// One work-group of 512 threads per (position tile, KV head): thread (kv, c) copies channel c (bf16 tail) or
+// rounds it to f16 (f16 tail).
 template <class A>
 __device__ inline void bf16_ring_write_wg(const A& a, int wg, int head) {
   const Geometry& g = a.g;
@@ -379,7 +387,8 @@ __device__ inline void bf16_ring_write_wg(const A& a, int wg, int head) {
   const uint16_t* in = kv ? a.v_in : a.k_in;
   for (int t = t0; t < t1; ++t) {
     const int p = tile * kTile + t;
-    const uint16_t v = in[((size_t)(w.src_row + p - w.len_old) * g.n_kv_heads + head) * D + c];
+    uint16_t v = in[((size_t)(w.src_row + p - w.len_old) * g.n_kv_heads + head) * D + c];
+    if (g.tail_dtype == 3) v = bf16_to_f16_bits(v);   // f16 tail
     const int slot = p % R;
     if (g.layout == 1) {
       ((uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c] = v;

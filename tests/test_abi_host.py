@@ -48,7 +48,7 @@ def _random_cfgs(n=60):
                    capacity=int(rng.integers(1, 300000)), n_kv_heads=hk, n_q_heads=hk * int(rng.integers(1, 9)),
                    k_bits=int(rng.integers(2, 9)), v_bits=int(rng.integers(2, 9)), kvarn=int(rng.integers(0, 2)),
                    tail_len=w, tail_slack=int(rng.choice([0, 32, 512])) if w else 0,
-                   tail_dtype=int(rng.integers(1, 3)))
+                   tail_dtype=int(rng.integers(1, 4)))
 
 
 def test_cache_bytes_and_regions_match_oracle():
@@ -75,7 +75,7 @@ def test_kv_mib_table_through_the_library():
 @pytest.mark.parametrize("bad", [
     dict(n_layers=0), dict(max_seqs=0), dict(capacity=0), dict(n_q_heads=15), dict(n_q_heads=32),
     dict(head_dim=100), dict(k_bits=1), dict(v_bits=9), dict(kvarn=2), dict(tail_len=-1),
-    dict(tail_len=64, tail_slack=31), dict(tail_len=64, tail_dtype=0), dict(tail_len=64, tail_dtype=3),
+    dict(tail_len=64, tail_slack=31), dict(tail_len=64, tail_dtype=0), dict(tail_len=64, tail_dtype=4),
 ])
 def test_validation_rejects(bad):
     from quantized_decode_attention_append_amd import kvq

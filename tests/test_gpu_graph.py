@@ -33,7 +33,7 @@ def capture(torch, fn):
     return g
 
 
-@pytest.mark.parametrize("tail_dtype,kvarn", [(1, 0), (2, 1)])
+@pytest.mark.parametrize("tail_dtype,kvarn", [(1, 0), (2, 1), (3, 0)])
 def test_decode_step_graph(tail_dtype, kvarn):
     import torch
     p = Pair(cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn))

@@ -53,7 +53,7 @@ def test_body_bytes_and_decode_no_tail(nk, nv):
     assert max_err(got, want) <= TOL
 
 
-@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("tail_dtype", [1, 2, 3])
 @pytest.mark.parametrize("kvarn", [0, 1])
 def test_tail_ring_bytes_evict_and_decode(tail_dtype, kvarn):
     c = cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=6, v_bits=5)
@@ -95,9 +95,10 @@ def test_decode_short_and_ragged(length):
     assert max_err(got, want) <= TOL
 
 
-@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("tail_dtype", [1, 2, 3])
 def test_ring_only_equals_lossless_or_q8(tail_dtype):
-    # context below the window: a bf16 tail is lossless, an 8-bit ring behaves as q8_0 (pages' special cases)
+    # context below the window: a bf16 tail is lossless, an 8-bit ring behaves as q8_0 (pages' special cases),
+    # an f16 tail holds the binary16 values
     p = Pair(cfg(tail_len=256, tail_slack=32, tail_dtype=tail_dtype))
     k, v = small_tokens(11, 200, 2, 256, scale=scales(2, "loguniform"))
     p.append(0, [0], [200], k, v)
@@ -181,7 +182,7 @@ def test_workspace_reused_across_calls_and_allocations():
 
 
 
-@pytest.mark.parametrize("tail_dtype,kvarn", [(1, 0), (2, 0), (1, 1), (0, 0)])
+@pytest.mark.parametrize("tail_dtype,kvarn", [(1, 0), (2, 0), (1, 1), (0, 0), (3, 0)])
 def test_append_evict_matches_append_then_evict(tail_dtype, kvarn):
     """kvq_append_evict against the oracle doing the two calls: decode steps (one launch), a batch with an
     empty sequence, a chunk that evicts its own rows and the first (calibrating) append (two launches)."""
@@ -217,7 +218,7 @@ def test_append_evict_matches_append_then_evict(tail_dtype, kvarn):
     assert max_err(got, want) <= TOL
 
 
-@pytest.mark.parametrize("tail_dtype,kvarn,n_seqs", [(1, 0, 1), (2, 0, 2), (1, 1, 3), (2, 1, 1)])
+@pytest.mark.parametrize("tail_dtype,kvarn,n_seqs", [(1, 0, 1), (2, 0, 2), (1, 1, 3), (2, 1, 1), (3, 1, 2)])
 def test_decode_step_matches_append_evict_decode(tail_dtype, kvarn, n_seqs):
     """kvq_decode_step (the append and evict written inside the decode launch) against the oracle doing append,
     evict and decode: ring bytes, body bytes and outputs after every step, for sequences whose ring is below the

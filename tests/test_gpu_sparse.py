@@ -47,7 +47,7 @@ def test_rows_bytes_dense_and_sparse(nk, nv):
     assert max_err(got, want) <= TOL
 
 
-@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("tail_dtype", [1, 2, 3])
 @pytest.mark.parametrize("kvarn", [0, 1])
 def test_rows_tail_ring_evict_dense_and_sparse(tail_dtype, kvarn):
     c = cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=6, v_bits=5)
@@ -146,7 +146,7 @@ def test_sparse_needs_the_row_layout():
 
 
 @pytest.mark.parametrize("nk,nv,kvarn,tail_dtype,n_seqs", [(8, 8, 0, 0, 1), (6, 5, 1, 0, 2), (3, 7, 0, 0, 3),
-                                                          (4, 4, 0, 1, 1), (8, 8, 1, 0, 1)])
+                                                          (4, 4, 0, 1, 1), (8, 8, 1, 0, 1), (6, 5, 0, 3, 2)])
 def test_sparse_decode_step_matches_append_then_sparse(nk, nv, kvarn, tail_dtype, n_seqs):
     """kvq_sparse_decode_step against the oracle doing the append and then sparse decode: body bytes and
     outputs after every step. Without a ring (and calibrated KVarN scales) the new rows are written inside the

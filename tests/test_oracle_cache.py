@@ -50,7 +50,7 @@ def test_q8_ring_below_window_equals_q8_body():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("tail_dtype", [1, 2, 3])
 @pytest.mark.parametrize("kvarn", [0, 1])
 def test_chunk_invariance(tail_dtype, kvarn):
     c = cfg(tail_dtype=tail_dtype, kvarn=kvarn, tail_len=64, tail_slack=32)
@@ -87,7 +87,7 @@ def test_append_evicts_only_on_overflow_and_evict_drains_to_window():
     assert o.lengths(0, 0) == (400, 400 - 96)
 
 
-@pytest.mark.parametrize("tail_dtype", [1, 2])
+@pytest.mark.parametrize("tail_dtype", [1, 2, 3])
 def test_evicted_rows_are_requantized_ring_values(tail_dtype):
     c = cfg(tail_len=64, tail_slack=32, tail_dtype=tail_dtype)
     k, v = small_tokens(5, 200, 2, 256)
@@ -98,6 +98,8 @@ def test_evicted_rows_are_requantized_ring_values(tail_dtype):
     if tail_dtype == 2:
         u8, d8 = quant.quantize_blocks(kx, 8)
         kx = quant.dequantize_blocks(u8, d8, 8).astype(np.float32)
+    if tail_dtype == 3:   # the f16 value (numpy's IEEE binary16 conversion, round to nearest even)
+        kx = kx.astype(np.float16).astype(np.float32)
     u, d = quant.quantize_blocks(kx, 6)
     assert np.array_equal(s.ku[:136], u) and np.array_equal(s.kd[:136].view(np.uint16), d.view(np.uint16))
 
@@ -160,3 +162,47 @@ def test_sequences_are_independent():
     b = _append_all(c, k[100:], v[100:], [50], seq=0)
     assert np.array_equal(o.dequantized(0, 1)[0], a.dequantized(0, 1)[0])
     assert np.array_equal(o.dequantized(0, 0)[1], b.dequantized(0, 0)[1])
+
+
+# bf16 input bits -> IEEE binary16 bits, worked out from the two formats' definitions (1 sign, 8 / 5 exponent
+# bits with bias 127 / 15, 7 / 10 mantissa bits; f16 subnormals are multiples of 2^-24; ties to even)
+F16_CASES = [
+    (0x3F80, 0x3C00),   # 1.0
+    (0xC020, 0xC100),   # -2.5 = -1.25 * 2^1: exponent 16, mantissa 256
+    (0x477F, 0x7BF8),   # 65280 = 1.9921875 * 2^15: exponent 30, mantissa 1016
+    (0x4780, 0x7C00),   # 65536: above the largest f16 (65504) -> +infinity
+    (0x3580, 0x0010),   # 2^-20 = 16 * 2^-24: subnormal
+    (0x3300, 0x0000),   # 2^-25: half of 2^-24, tie -> even (zero)
+    (0x33C0, 0x0002),   # 1.5 * 2^-24: tie between 1 and 2 ulps -> even (2)
+    (0x3340, 0x0001),   # 0.75 * 2^-24 -> 1 ulp
+]
+
+
+def test_f16_tail_stores_ieee_binary16_of_the_input():
+    """F16 precision tail (BeeLlama.cpp v0.4.1 page: recent tokens kept in BF16 or F16): the ring holds the
+    binary16 rounding of each bf16 input value."""
+    c = cfg(tail_len=64, tail_slack=32, tail_dtype=3)
+    k = np.zeros((len(F16_CASES), 2, 256), dtype=np.uint16)
+    v = np.zeros_like(k)
+    for i, (b, _) in enumerate(F16_CASES):
+        k[i, :, 3 * i] = b
+        v[i, 1, 7] = b
+    o = _append_all(c, k, v, [len(F16_CASES)])
+    s = o.st(0, 0)
+    for i, (_, want) in enumerate(F16_CASES):
+        assert s.rk[i, 0, 3 * i] == want and s.rk[i, 1, 3 * i] == want, (hex(F16_CASES[i][0]), hex(s.rk[i, 0, 3 * i]))
+        assert s.rv[i, 1, 7] == want
+
+
+def test_f16_tail_below_window_holds_the_rounded_inputs():
+    """Below the window nothing is quantized: the f16 cache holds exactly the binary16 values of the inputs
+    (numpy's IEEE conversion), including inputs in the f16 subnormal range, where the rounding shows."""
+    c = cfg(tail_len=128, tail_slack=32, tail_dtype=3)
+    k, v = small_tokens(8, 100, 2, 256, scale=np.full((2, 2, 256), 4.0, dtype=np.float32))
+    k[:, 0, 0] = 0x3581   # 2^-20 * (1 + 2^-7) = 16.125 * 2^-24 -> 16 * 2^-24 in f16
+    o = _append_all(c, k, v, [60, 40])
+    kk, vv = o.dequantized(0, 0)
+    k16 = bf16_to_f32(k).astype(np.float16).astype(np.float64)
+    v16 = bf16_to_f32(v).astype(np.float16).astype(np.float64)
+    assert np.array_equal(kk, k16) and np.array_equal(vv, v16)
+    assert np.all(kk[:, 0, 0] == 16 * 2.0 ** -24)
