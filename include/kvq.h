@@ -158,7 +158,8 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
  * the results of kvq_append_evict (n_new = 1 each) followed by kvq_decode_attn. With the tile layout and a
  * ring, when the step is a ring write plus the requantization of rows that were in the ring before the call
  * (every step after the prefill), the writes are done inside the decode launch by the work-groups that read
- * those tiles, before they read them; otherwise the calls run in turn. Arguments and errors as those calls. */
+ * those tiles, before they read them; otherwise the calls run in turn. Arguments and errors as those calls;
+ * the workspace size (kvq_workspace_bytes for the lengths after the append) is checked before any write. */
 kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                            const void* k_bf16, const void* v_bf16, const void* q_bf16, float* out,
                            float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
@@ -180,7 +181,8 @@ kvq_status kvq_sparse_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seq
  * kvq_sparse_decode_attn. Without a tail ring and with no KVarN calibration pending, the new rows are
  * quantized into the body inside the sparse decode launch (by the first work-group of each KV head and by
  * every work-group whose list range holds the new position, before it reads any row; they write the same
- * bytes); otherwise the calls run in turn. Arguments and errors as those calls. */
+ * bytes); otherwise the calls run in turn. Arguments and errors as those calls; the workspace size
+ * (kvq_workspace_bytes(cache, n_seqs, budget)) is checked before any write. */
 kvq_status kvq_sparse_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                   const void* k_bf16, const void* v_bf16, const void* q_bf16,
                                   const int32_t* positions, int32_t budget, float* out, float softmax_scale,

@@ -704,6 +704,12 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
                            size_t ws_bytes, void* stream) {
   kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
   if (s != KVQ_OK) return s;
+  {   // the documented workspace size, checked before anything is appended
+    int max_len = 1;
+    for (int i = 0; i < n_seqs; ++i) max_len = std::max(max_len, c->len[c->idx(layer, seq_ids[i])] + 1);
+    const size_t ws_need = kvq_workspace_bytes(c, n_seqs, max_len);
+    if (!workspace || ws_bytes < ws_need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, ws_need);
+  }
   const int W = c->cfg.tail_len;
   const int R = c->lay.ring_slots;
   // One launch when every sequence's step is a ring write plus the requantization of at most the rows of one
@@ -809,6 +815,9 @@ kvq_status kvq_sparse_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, c
                                   void* workspace, size_t ws_bytes, void* stream) {
   kvq_status s = check_sparse(c, layer, n_seqs, seq_ids, q_bf16, positions, budget, out, softmax_scale, workspace);
   if (s != KVQ_OK) return s;
+  // the documented workspace size, checked before anything is appended
+  const size_t ws_need = kvq_workspace_bytes(c, n_seqs, budget);
+  if (ws_bytes < ws_need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, ws_need);
   // one launch when the new rows go straight to the body (no ring) and are quantized with known scales
   bool fuse = c->cfg.tail_len == 0 && k_bf16 && v_bf16;
   for (int i = 0; i < n_seqs && fuse; ++i) {

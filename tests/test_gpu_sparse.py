@@ -143,6 +143,32 @@ def test_sparse_needs_the_row_layout():
     with pytest.raises(kvq.KvqError) as e:
         p.gpu.sparse_decode_attn(0, [0], dev(small_query(0, 1, 16, 256)), pos)
     assert e.value.status == kvq.KVQ_E_INVALID
+    # the fused step checks the same before it appends anything
+    with pytest.raises(kvq.KvqError) as e:
+        p.gpu.sparse_decode_step(0, [0], dev(k[:1]), dev(v[:1]), dev(small_query(0, 1, 16, 256)), pos)
+    assert e.value.status == kvq.KVQ_E_INVALID
+    assert p.gpu.lengths(0, 0) == (64, 64)
+
+
+def test_sparse_decode_step_errors_leave_the_cache_unchanged():
+    from quantized_decode_attention_append_amd import kvq
+    import torch
+    p = Pair(cfg(capacity=64))
+    k, v = small_tokens(3, 65, 2, 256)
+    p.append(0, [0], [64], k[:64], v[:64])
+    q = dev(small_query(1, 1, 16, 256))
+    pos = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:   # full: the append is refused
+        p.gpu.sparse_decode_step(0, [0], dev(k[64:]), dev(v[64:]), q, pos)
+    assert e.value.status == kvq.KVQ_E_CAPACITY
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    p2 = Pair(cfg())
+    p2.append(0, [0], [64], k[:64], v[:64])
+    with pytest.raises(kvq.KvqError) as e:   # workspace too small: reported before the launch
+        p2.gpu.sparse_decode_step(0, [0], dev(k[64:]), dev(v[64:]), q, pos, workspace=ws)
+    assert e.value.status == kvq.KVQ_E_SIZE
+    assert p.gpu.lengths(0, 0) == (64, 64) and p2.gpu.lengths(0, 0) == (64, 64)
+    p2.assert_slab_equal(0, 0)
 
 
 @pytest.mark.parametrize("nk,nv,kvarn,tail_dtype,n_seqs", [(8, 8, 0, 0, 1), (6, 5, 1, 0, 2), (3, 7, 0, 0, 3),
