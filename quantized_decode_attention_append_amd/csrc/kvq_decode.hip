@@ -1,9 +1,9 @@
 // Decode attention over the quantized cache: split-K flash decode with MFMA for the GQA group.
 //
-// Decode is bandwidth-bound: every step streams the whole cache of a full-attention layer (offload page,
-// "decode is a bandwidth problem"), so the kernel is built around one pass over HBM per call:
+// Decode is bandwidth-bound: every step streams the whole cache of a full-attention layer (offload page, on
+// the bytes a decode step reads), so the kernel is built around one pass over HBM per call:
 //
-// * grid (split, KV head, sequence); a work-group of 4 waves owns a contiguous range of 32-position tiles
+// * grid (split, KV head, sequence); a work-group of 8 waves (two per SIMD) owns a contiguous range of 32-position tiles
 //   of either the qN_0 body or the tail ring (two KV paths per layer, Qwen3.8-27B page) and emits one
 //   partial (m, l, o) per query head of the group;
 // * each wave streams its tiles with 128-bit loads straight into registers: K rows are laid out so that
@@ -157,9 +157,6 @@ __device__ inline void load_tile_v(TileRaw<NK, NV>& t, const uint8_t* kt, int kb
 }
 
 #define KVQ_SB __builtin_amdgcn_sched_barrier(0);
-#ifndef TRACE_QLOADED
-#define TRACE_QLOADED
-#endif
 
 __device__ inline float lo_h(uint32_t w) { return (float)as_h2(w)[0]; }
 __device__ inline float hi_h(uint32_t w) { return (float)as_h2(w)[1]; }
@@ -549,7 +546,6 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  TRACE_QLOADED
   amax = wave_max_16_32(amax);
   if (lane < 16) s_amax[wave * 16 + lane] = amax;
   __syncthreads();
