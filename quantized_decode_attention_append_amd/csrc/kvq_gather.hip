@@ -250,14 +250,16 @@ __device__ inline void load_pos(StepRows& st, const RowSrc& rs, int g0, int ie) 
 }
 
 // (Rows go to local copies first and into st once at the end: stores to st made on some paths only would be
-// merged behind a select of their addresses, which keeps st out of registers.)
+// merged behind a select of their addresses, which keeps st out of registers. Entries with no row keep
+// undefined words: their scale is zero (body and q8_0 chains), their bf16 / f16 operand is zeroed, and P.V
+// skips them.)
 template <int NK, int NV>
 __device__ inline void load_rows(StepRows& st, const RowSrc& rs) {
   const int lane = threadIdx.x & 63, j = lane >> 4;
   const int pos = st.pos;
   const bool valid = pos >= 0 && pos < rs.len;
   const bool body = valid && pos < rs.body_len;
-  KRaw kr = {};
+  KRaw kr;   // (no zero fill: merging it with the loads would wait for them here)
   if (body) {
     load_k_qrow<NK>(kr, rs.kbody + (size_t)pos * rs.row_k, j);
   } else if (valid) {
@@ -269,7 +271,7 @@ __device__ inline void load_rows(StepRows& st, const RowSrc& rs) {
 #pragma unroll
   for (int t = 0; t < kGroup; ++t) {
     const int pt = __builtin_amdgcn_readlane(pos, t);
-    VRaw vr = {};
+    VRaw vr;
     if (pt >= 0 && pt < rs.len) {
       vmask |= 1u << t;
       if (pt < rs.body_len) {
@@ -428,7 +430,8 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
       s_amax[wave][0] = am;
       s_amax[wave][1] = amr;
     }
-    hit = __syncthreads_or(hit);   // (also publishes s_amax and the zeroed row images)
+    if (app >= 0) hit = __syncthreads_or(hit);   // (also publishes s_amax and the zeroed row images)
+    else __syncthreads();
     if (app >= 0 && (hit || split == 0))
       sparse_step_write<64 * NW>(a, S, si, head, hit ? s_img : nullptr, hit ? s_img + kImgRow : nullptr);
 #pragma unroll
