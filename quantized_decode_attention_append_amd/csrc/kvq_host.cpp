@@ -172,6 +172,7 @@ int tiles_of(int p0, int p1) { return p1 > p0 ? (p1 - 1) / kvq::kTile - p0 / kvq
 // work-group per CU: each (sequence, body|ring) segment gets a share of the CU budget proportional to
 // its tiles (at least one), leftover work-groups go to the segments with the most tiles per work-group.
 constexpr int kMaxWgBudget = 1024;
+constexpr int kMinTilesPerWg = 4;
 constexpr size_t kPartialFloats(int d) { return (size_t)kvq::kPartialHeads * (d + 2); }
 
 struct SplitPlan {
@@ -181,7 +182,7 @@ struct SplitPlan {
 
 SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out) {
   const int hk = c->cfg.n_kv_heads;
-  const int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
+  int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
   // Cost of a tile in a work-group's time: a qN_0 tile (body or q8_0 ring) is decode- and MFMA-bound, a bf16
   // ring tile carries 2.7x the bytes of a K6/V5 tile with little decode and no prefetch: it counts double.
   const double ring_w = c->cfg.tail_dtype == KVQ_TAIL_Q8_0 ? 1.0 : 2.0;
@@ -196,6 +197,9 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
     wt[2 * i + 1] = ring_w * tiles[2 * i + 1];
     total += wt[2 * i] + wt[2 * i + 1];
   }
+  // short contexts: at least ~kMinTilesPerWg tiles of cost per work-group (fewer, fuller work-groups and fewer
+  // partials to merge; measured on the 4k single-layer workload)
+  budget_h = std::min(budget_h, std::max(1, (int)(total / kMinTilesPerWg)));
   int used = 0;
   for (int k = 0; k < 2 * n_seqs; ++k) {
     nwg[k] = tiles[k] ? std::max(1, (int)(budget_h * wt[k] / std::max(total, 1.0))) : 0;
