@@ -76,9 +76,16 @@ def sparse_call_bytes(cfg: dict, budget: int, n_seqs: int) -> int:
     return n_seqs * budget * hk * (row_bytes(cfg["k_bits"], d) + row_bytes(cfg["v_bits"], d))
 
 
+SHARED_HEADERS = ("kvq_kernels.h", "kvq_mfma.h", "kvq_write.h", "kvq_format.h")
+
+
 def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of a kernel source together with the device headers every kernel source includes."""
+    h = hashlib.sha256()
+    for p in (path, *(os.path.join(os.path.dirname(path), n) for n in SHARED_HEADERS)):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str, kernel: str, src: str):

@@ -6,7 +6,7 @@
 // A budget of 2048 positions is ~2 MB per layer: the call is latency-bound, and what sets its time is the
 // length of one wave's instruction stream. So:
 //
-// * grid (split, KV head, sequence); a work-group of 8 waves owns a contiguous range of list entries and
+// * grid (split, KV head, sequence); a work-group of 4 waves (one per SIMD) owns a contiguous range of list entries and
 //   emits one partial (m, l, o) per query head of the group, merged by the same combine kernel as the
 //   dense path;
 // * a wave takes 16 list entries at a time. Lane (j = lane >> 4, e = lane & 15) loads the pieces (j, b),

@@ -105,7 +105,7 @@ struct DecodeArgs {
 };
 
 
-constexpr int kGatherWaves = 8;    // waves per gather work-group (16 list entries per wave step)
+constexpr int kGatherWaves = 4;    // waves per gather work-group (16 list entries per wave step)
 
 // Gather decode over a list of positions of a row-layout cache (sparse decode), or over all positions
 // (dense decode of a row-layout cache: positions == nullptr, entry i is position i).
