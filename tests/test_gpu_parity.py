@@ -250,3 +250,36 @@ def test_decode_step_matches_append_evict_decode(tail_dtype, kvarn, n_seqs):
     separate = p.gpu.timing_read("append")[1] + p.gpu.timing_read("append_evict")[1]
     p.gpu.timing(False)
     assert separate == 0, separate   # every step ran in the decode launch
+
+
+def test_largest_batch_of_64_sequences():
+    """A call over the largest batch (64 sequences, ragged lengths 1..130): one append, evict, decode, and decode
+    steps (more sequences than one fused step launch takes: the step falls back to its separate calls)."""
+    import oracle
+    c = cfg(max_seqs=64, capacity=256, tail_len=32, tail_slack=32, tail_dtype=1, k_bits=4, v_bits=3, n_layers=1)
+    p = Pair(c)
+    rng = np.random.default_rng(64)
+    lens = [int(x) for x in rng.integers(1, 131, size=64)]
+    k, v = small_tokens(640, sum(lens) + 64 * 3, 2, 256)
+    seqs = list(range(64))
+    p.append(0, seqs, lens, k[:sum(lens)], v[:sum(lens)])
+    p.evict(0, seqs)
+    for s in (0, 17, 63):
+        p.lengths_match(0, s)
+        p.assert_slab_equal(0, s)
+    q = small_query(64, 64, 16, 256)
+    got, want = p.decode(0, seqs, q)
+    assert max_err(got, want) <= TOL
+    off = sum(lens)
+    for st in range(2):
+        kk, vv = k[off:off + 64], v[off:off + 64]
+        off += 64
+        q = small_query(65 + st, 64, 16, 256)
+        got = p.gpu.decode_step(0, seqs, dev(kk), dev(vv), dev(q)).cpu().numpy()
+        p.ora.append(0, seqs, [1] * 64, kk, vv)
+        p.ora.tail_evict(0, seqs)
+        want = oracle.decode_reference(p.ora, 0, seqs, q)
+        assert max_err(got, want) <= TOL, st
+        for s in (5, 40, 63):
+            p.lengths_match(0, s)
+            p.assert_slab_equal(0, s)

@@ -220,3 +220,28 @@ def test_sparse_decode_step_matches_append_then_sparse(nk, nv, kvarn, tail_dtype
         assert appends == 0, appends   # every step's append ran in the gather launch
     else:
         assert appends > 0
+
+
+def test_sparse_largest_batch_and_fused_step():
+    """64 sequences in one sparse call and one fused sparse step (the new rows written in the gather launch)."""
+    import oracle
+    import torch
+    p = Pair(cfg(max_seqs=64, capacity=256, n_layers=1, k_bits=5, v_bits=6))
+    rng = np.random.default_rng(640)
+    lens = [int(x) for x in rng.integers(40, 200, size=64)]
+    k, v = small_tokens(641, sum(lens) + 64, 2, 256)
+    seqs = list(range(64))
+    p.append(0, seqs, lens, k[:sum(lens)], v[:sum(lens)])
+    q = small_query(66, 64, 16, 256)
+    pos = np.stack([rng.choice(n, size=32, replace=False) for n in lens]).astype(np.int32)
+    got, want = p.sparse(0, seqs, q, pos)
+    assert max_err(got, want) <= TOL
+    kk, vv = k[sum(lens):], v[sum(lens):]
+    pos = np.stack([np.concatenate([[n], rng.choice(n, size=31, replace=False)]) for n in lens]).astype(np.int32)
+    got = p.gpu.sparse_decode_step(0, seqs, dev(kk), dev(vv), dev(q), torch.from_numpy(pos).to("cuda")).cpu().numpy()
+    p.ora.append(0, seqs, [1] * 64, kk, vv)
+    want = oracle.sparse_reference(p.ora, 0, seqs, q, pos)
+    assert max_err(got, want) <= TOL
+    for s in (0, 31, 63):
+        p.lengths_match(0, s)
+        p.assert_slab_equal(0, s)
