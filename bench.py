@@ -159,7 +159,7 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
         k, v = W.kv_tokens(wl.cfg, 0, 0, s, min(W.CHUNK, ctx - s))
         o.append(0, [0], [k.shape[0]], k, v)
     o.tail_evict(0, [0])
-    t_total, nbytes, steps = 0.0, 0, 0
+    t_total, t_write, nbytes, steps = 0.0, 0.0, 0, 0
     with limit:
         while t_total < budget_s and steps < max(wl.decode_steps, 1):
             q = W.query(wl.cfg, 0, 0, steps)[None]
@@ -168,6 +168,7 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
                 k, v = W.decode_token(wl.cfg, 0, 0, steps)
                 o.append(0, [0], [1], k, v)
                 o.tail_evict(0, [0])
+            t_write += time.perf_counter() - t0
             oracle.decode_reference(o, 0, [0], q)
             t_total += time.perf_counter() - t0
             ln, bl = o.lengths(0, 0)
@@ -176,7 +177,8 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"layer 0 of the workload at context {ctx}: {steps} decode steps (append 1, evict, "
                       f"fp64 attention over the dequantized cache), {t_total:.1f} s, one BLAS thread",
-            "tok_per_s_per_layer": round(steps * (ctx + steps / 2) / t_total, 1)}
+            "tok_per_s_per_layer": round(steps * (ctx + steps / 2) / t_total, 1),
+            "append_evict_ms_per_step": round(t_write * 1e3 / max(steps, 1), 3)}
 
 
 def graph_steps(torch, step, first: int, n: int, n_layers: int) -> float:
