@@ -283,3 +283,34 @@ def test_largest_batch_of_64_sequences():
         for s in (5, 40, 63):
             p.lengths_match(0, s)
             p.assert_slab_equal(0, s)
+
+
+def test_seq_reset_reuses_a_slab_like_a_fresh_sequence():
+    """kvq_seq_reset: the sequence's slab is zeroed and its lengths and KVarN calibration forgotten (the oracle's
+    fresh state); a new token stream then recalibrates and matches a fresh oracle sequence byte for byte; other
+    sequences and layers are untouched."""
+    c = cfg(kvarn=1, tail_len=64, tail_slack=32, tail_dtype=1, k_bits=5, v_bits=4)
+    p = Pair(c)
+    k, v = small_tokens(90, 240, 2, 256, scale=scales(3, "student"))
+    k2, v2 = small_tokens(91, 150, 2, 256, scale=scales(4, "loguniform"))
+    p.append(0, [0, 1], [150, 90], k, v)
+    p.append(1, [0], [60], k[:60], v[:60])
+    p.evict(0, [0, 1])
+    p.gpu.seq_reset(0, [0])
+    p.ora.state.pop((0, 0), None)
+    assert p.gpu.lengths(0, 0) == (0, 0)
+    for layer, seq in ((0, 0), (0, 1), (1, 0)):
+        p.assert_slab_equal(layer, seq)
+    p.append(0, [0], [120], k2[:120], v2[:120])
+    p.evict(0, [0])
+    p.lengths_match(0, 0)
+    p.assert_slab_equal(0, 0)
+    got, want = p.decode(0, [0, 1], small_query(12, 2, 16, 256))
+    assert max_err(got, want) <= TOL
+    # every layer at once
+    p.gpu.seq_reset(-1, [0])
+    for layer in (0, 1):
+        p.ora.state.pop((layer, 0), None)
+        assert p.gpu.lengths(layer, 0) == (0, 0)
+        p.assert_slab_equal(layer, 0)
+    p.assert_slab_equal(0, 1)
