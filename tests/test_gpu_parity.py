@@ -314,3 +314,29 @@ def test_seq_reset_reuses_a_slab_like_a_fresh_sequence():
         assert p.gpu.lengths(layer, 0) == (0, 0)
         p.assert_slab_equal(layer, 0)
     p.assert_slab_equal(0, 1)
+
+
+@pytest.mark.parametrize("tail_dtype", [1, 2, 3])
+def test_decode_steps_across_ring_wraparound(tail_dtype):
+    """Many fused decode steps on a small ring (R = 64 slots): ring slots wrap around several times, the row
+    leaving the window and the appended row sit in every slot position, and the body grows tile by tile."""
+    import oracle
+    c = cfg(tail_len=32, tail_slack=32, tail_dtype=tail_dtype, k_bits=6, v_bits=5, capacity=512, n_layers=1)
+    p = Pair(c)
+    k, v = small_tokens(120 + tail_dtype, 300, 2, 256, scale=scales(6, "loguniform"))
+    p.append(0, [0, 1], [40, 7], k[:47], v[:47])
+    p.evict(0, [0, 1])
+    off = 47
+    for step in range(150):
+        kk, vv = k[off:off + 2], v[off:off + 2]
+        off = 47 + (off - 47 + 2) % 250   # reuse the token pool
+        q = small_query(300 + step, 2, 16, 256)
+        got = p.gpu.decode_step(0, [0, 1], dev(kk), dev(vv), dev(q)).cpu().numpy()
+        p.ora.append(0, [0, 1], [1, 1], kk, vv)
+        p.ora.tail_evict(0, [0, 1])
+        if step % 25 == 24 or step < 3:
+            want = oracle.decode_reference(p.ora, 0, [0, 1], q)
+            assert max_err(got, want) <= TOL, step
+            for s in (0, 1):
+                p.lengths_match(0, s)
+                p.assert_slab_equal(0, s)
