@@ -245,3 +245,31 @@ def test_sparse_largest_batch_and_fused_step():
     for s in (0, 31, 63):
         p.lengths_match(0, s)
         p.assert_slab_equal(0, s)
+
+
+def test_many_fused_sparse_steps():
+    """100 fused sparse steps (the appended row written inside the gather launch each time), lists of newest +
+    drawn positions of varying budget placement; bytes and outputs checked along the way."""
+    import oracle
+    import torch
+    p = Pair(cfg(k_bits=6, v_bits=4, capacity=512, n_layers=1, max_seqs=2, kvarn=1))
+    k, v = small_tokens(777, 400, 2, 256, scale=outlier_scale())
+    p.append(0, [0, 1], [100, 33], k[:133], v[:133])
+    rng = np.random.default_rng(777)
+    off = 133
+    for step in range(100):
+        kk, vv = k[off:off + 2], v[off:off + 2]
+        off += 2
+        lens = [p.gpu.lengths(0, s)[0] + 1 for s in (0, 1)]
+        budget = 24
+        pos = np.stack([np.concatenate([np.arange(n - 8, n), rng.choice(n - 8, size=budget - 8, replace=False)])
+                        [rng.permutation(budget)] for n in lens]).astype(np.int32)
+        q = small_query(900 + step, 2, 16, 256)
+        got = p.gpu.sparse_decode_step(0, [0, 1], dev(kk), dev(vv), dev(q), torch.from_numpy(pos).to("cuda")).cpu().numpy()
+        p.ora.append(0, [0, 1], [1, 1], kk, vv)
+        if step % 20 == 19 or step < 2:
+            want = oracle.sparse_reference(p.ora, 0, [0, 1], q, pos)
+            assert max_err(got, want) <= TOL, step
+            for s in (0, 1):
+                p.lengths_match(0, s)
+                p.assert_slab_equal(0, s)
