@@ -273,3 +273,35 @@ def test_many_fused_sparse_steps():
             for s in (0, 1):
                 p.lengths_match(0, s)
                 p.assert_slab_equal(0, s)
+
+
+def test_long_lists_take_several_steps_per_wave():
+    """Lists long enough that every wave takes several 16-entry steps (the split count is capped by the
+    work-group budget): dense decode of a 40,000-position row-layout cache with a q8_0 ring, and a fused
+    sparse step over a 30,000-entry list that holds the new position near its end."""
+    import oracle
+    import torch
+    c = cfg(k_bits=6, v_bits=5, capacity=40960, n_layers=1, max_seqs=1, tail_len=64, tail_slack=64, tail_dtype=2)
+    p = Pair(c)
+    n = 40000
+    for s0 in range(0, n, 8000):
+        k, v = small_tokens(900 + s0 // 8000, 8000, 2, 256)
+        p.append(0, [0], [8000], k, v)
+    p.evict(0, [0])
+    p.lengths_match(0, 0)
+    q = small_query(77, 1, 16, 256)
+    got, want = p.decode(0, [0], q)
+    assert max_err(got, want) <= TOL
+    c2 = cfg(k_bits=8, v_bits=8, capacity=40960, n_layers=1, max_seqs=1)
+    p2 = Pair(c2)
+    k, v = small_tokens(950, 32001, 2, 256)
+    p2.append(0, [0], [32000], k[:32000], v[:32000])
+    rng = np.random.default_rng(951)
+    pos = rng.choice(32000, size=30000, replace=False).astype(np.int32)
+    pos[-5] = 32000   # the appended position
+    got = p2.gpu.sparse_decode_step(0, [0], dev(k[32000:]), dev(v[32000:]), dev(q),
+                                    torch.from_numpy(pos[None].copy()).to("cuda")).cpu().numpy()
+    p2.ora.append(0, [0], [1], k[32000:], v[32000:])
+    want = oracle.sparse_reference(p2.ora, 0, [0], q, pos[None])
+    assert max_err(got, want) <= TOL
+    p2.lengths_match(0, 0)
