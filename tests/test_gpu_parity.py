@@ -340,3 +340,40 @@ def test_decode_steps_across_ring_wraparound(tail_dtype):
             for s in (0, 1):
                 p.lengths_match(0, s)
                 p.assert_slab_equal(0, s)
+
+
+@pytest.mark.parametrize("hk,hq", [(1, 4), (4, 32), (8, 8), (3, 21)])
+def test_kv_head_counts(hk, hq):
+    """Other numbers of KV heads (and groups of 1 to 8 query heads): bytes, decode and a fused decode step in
+    the tile layout; bytes and sparse decode, plain and fused, in the row layout."""
+    import oracle
+    import torch
+    c = cfg(n_kv_heads=hk, n_q_heads=hq, tail_len=64, tail_slack=32, tail_dtype=1, k_bits=6, v_bits=5)
+    p = Pair(c)
+    k, v = small_tokens(200 + hk, 300, hk, 256)
+    p.append(0, [0, 1], [180, 60], k[:240], v[:240])
+    p.evict(0, [0, 1])
+    for s in (0, 1):
+        p.assert_slab_equal(0, s)
+    q = small_query(hk, 2, hq, 256)
+    got, want = p.decode(0, [0, 1], q)
+    assert max_err(got, want) <= TOL
+    got = p.gpu.decode_step(0, [0, 1], dev(k[240:242]), dev(v[240:242]), dev(q)).cpu().numpy()
+    p.ora.append(0, [0, 1], [1, 1], k[240:242], v[240:242])
+    p.ora.tail_evict(0, [0, 1])
+    assert max_err(got, oracle.decode_reference(p.ora, 0, [0, 1], q)) <= TOL
+    for s in (0, 1):
+        p.assert_slab_equal(0, s)
+    r = Pair(cfg(n_kv_heads=hk, n_q_heads=hq, k_bits=8, v_bits=8, layout=1))
+    r.append(0, [0], [200], k[:200], v[:200])
+    r.assert_slab_equal(0, 0)
+    rng = np.random.default_rng(hk)
+    pos = rng.choice(200, size=70, replace=False).astype(np.int32)[None]
+    got, want = r.sparse(0, [0], q[:1], pos)
+    assert max_err(got, want) <= TOL
+    pos2 = np.concatenate([[200], rng.choice(200, size=69, replace=False)]).astype(np.int32)[None]
+    got = r.gpu.sparse_decode_step(0, [0], dev(k[200:201]), dev(v[200:201]), dev(q[:1]),
+                                   torch.from_numpy(pos2).to("cuda")).cpu().numpy()
+    r.ora.append(0, [0], [1], k[200:201], v[200:201])
+    assert max_err(got, oracle.sparse_reference(r.ora, 0, [0], q[:1], pos2)) <= TOL
+    r.assert_slab_equal(0, 0)
