@@ -377,3 +377,42 @@ def test_kv_head_counts(hk, hq):
     r.ora.append(0, [0], [1], k[200:201], v[200:201])
     assert max_err(got, oracle.sparse_reference(r.ora, 0, [0], q[:1], pos2)) <= TOL
     r.assert_slab_equal(0, 0)
+
+
+RING_WIDTHS = [(2, 5, 1, 0), (3, 7, 2, 1), (4, 2, 3, 0), (5, 8, 1, 1), (6, 3, 2, 0), (7, 6, 3, 1), (8, 4, 1, 1)]
+
+
+@pytest.mark.parametrize("nk,nv,tail_dtype,kvarn", RING_WIDTHS)
+def test_ring_requantized_into_every_body_width(nk, nv, tail_dtype, kvarn):
+    """Ring rows leaving the window are requantized into bodies of every K and V width (each of 2..8 bits once
+    on each side, over all three ring kinds, with and without KVarN): after a prefill past the window, through
+    fused decode steps, and through a separate append of a chunk larger than the window followed by an evict."""
+    c = cfg(tail_len=32, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=nk, v_bits=nv, capacity=512)
+    p = Pair(c)
+    seed = 300 + 10 * nk + nv
+    k, v = small_tokens(seed, 300, 2, 256, scale=scales(nk, "student" if kvarn else "loguniform"))
+    seqs = [0, 2]
+    p.append(0, seqs, [100, 45], k[:145], v[:145])
+    p.evict(0, seqs)
+    off = 145
+    for i in seqs:
+        p.lengths_match(0, i)
+        p.assert_slab_equal(0, i)
+    for step in range(4):
+        kk, vv = k[off:off + 2], v[off:off + 2]
+        off += 2
+        q = small_query(seed + step, 2, 16, 256)
+        got = p.gpu.decode_step(0, seqs, dev(kk), dev(vv), dev(q)).cpu().numpy()
+        p.ora.append(0, seqs, [1, 1], kk, vv)
+        p.ora.tail_evict(0, seqs)
+        want = oracle_decode(p, 0, seqs, q)
+        for i in seqs:
+            p.lengths_match(0, i)
+            p.assert_slab_equal(0, i)
+        assert max_err(got, want) <= TOL, f"step {step}: {max_err(got, want):.3e}"
+    p.append(0, [2], [70], k[off:off + 70], v[off:off + 70])
+    p.evict(0, [2])
+    p.lengths_match(0, 2)
+    p.assert_slab_equal(0, 2)
+    got, want = p.decode(0, seqs, small_query(seed + 9, 2, 16, 256))
+    assert max_err(got, want) <= TOL
