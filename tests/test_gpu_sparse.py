@@ -305,3 +305,28 @@ def test_long_lists_take_several_steps_per_wave():
     want = oracle.sparse_reference(p2.ora, 0, [0], q, pos[None])
     assert max_err(got, want) <= TOL
     p2.lengths_match(0, 0)
+
+
+@pytest.mark.parametrize("nk,nv,tail_dtype,kvarn", [(2, 5, 1, 0), (3, 7, 2, 1), (4, 2, 3, 0), (5, 8, 1, 1),
+                                                    (6, 3, 2, 0), (7, 6, 3, 1), (8, 4, 1, 1)])
+def test_rows_ring_requantized_into_every_body_width(nk, nv, tail_dtype, kvarn):
+    """Row layout: ring rows leaving the window are requantized into body rows of every K and V width (each of
+    2..8 bits once on each side, over all three ring kinds, with and without KVarN); dense decode through the
+    gather and sparse lists that mix body and ring rows agree with the oracle after every step."""
+    p = Pair(cfg(tail_len=32, tail_slack=32, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=nk, v_bits=nv))
+    k, v = small_tokens(700 + 10 * nk + nv, 300, 2, 256, scale=outlier_scale())
+    rng = np.random.default_rng(nk * 11 + nv)
+    off = 0
+    for n, ev in ((20, False), (60, True), (1, True), (1, True), (70, False), (2, True)):
+        p.append(0, [2], [n], k[off:off + n], v[off:off + n])
+        off += n
+        if ev:
+            p.evict(0, [2])
+        p.lengths_match(0, 2)
+        p.assert_slab_equal(0, 2)
+        q = small_query(off, 1, 16, 256)
+        got, want = p.decode(0, [2], q)
+        assert max_err(got, want) <= TOL, (n, ev)
+        pos = rng.choice(off, size=min(off, 45), replace=False)[None]
+        got, want = p.sparse(0, [2], q, pos)
+        assert max_err(got, want) <= TOL, (n, ev)
