@@ -34,5 +34,5 @@ from .layout import (planes, cache_bytes, slab_layout, pack_k_rows, pack_v_tiles
                      pack_bf16_v_tiles, unpack_k_rows, unpack_v_tiles, pack_k_tiles, unpack_k_tiles,
                      pack_bf16_k_tiles, unpack_bf16_k_tiles)
 from .cache import OracleCache  # noqa: F401
-from .attention import attend, decode_reference, sparse_reference  # noqa: F401
+from .attention import attend, decode_reference, sparse_reference, multi_query_reference  # noqa: F401
 from .sizes import decode_bytes, sparse_bytes, row_bytes  # noqa: F401

@@ -68,3 +68,23 @@ def sparse_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, positions: 
         k, v = cache.dequantized(layer, sid, pos)
         out.append(attend(_q64(q_bits[i]), k, v, sc))
     return np.stack(out)
+
+
+def multi_query_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, scale=None) -> np.ndarray:
+    """Decode of T = 1 + k queries per sequence at once, as in verifying k drafted tokens (Qwen3.8-27B page,
+    decode-speed paragraph: the engine drafts up to 7 tokens per step with MTP heads). q_bits [n_seqs, T, Hq, D]
+    bf16 bits -> out [n_seqs, T, Hq, D] fp64.
+
+    Reading (the pages do not spell out the verification step): the T tokens are the last T positions already in
+    the cache; query t sits at position len - T + t and, causally, attends to positions 0 .. len - T + t."""
+    sc = _scale(cache, scale)
+    n_q = q_bits.shape[1]
+    out = np.zeros(q_bits.shape, dtype=np.float64)
+    for i, sid in enumerate(seq_ids):
+        n, _ = cache.lengths(layer, sid)
+        if n < n_q:
+            raise ValueError(f"sequence {sid} holds {n} positions, fewer than {n_q} queries")
+        for t in range(n_q):
+            k, v = cache.dequantized(layer, sid, np.arange(n - n_q + t + 1))
+            out[i, t] = attend(_q64(q_bits[i, t]), k, v, sc)
+    return out

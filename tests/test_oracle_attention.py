@@ -4,7 +4,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import OracleCache, attend, decode_reference, sparse_reference
+from oracle import OracleCache, attend, decode_reference, sparse_reference, multi_query_reference
 from workloads import small_tokens, small_query
 
 
@@ -102,3 +102,58 @@ def test_default_scale_is_inverse_sqrt_dim():
     o, *_ = _cache()
     q = small_query(3, 1, 16, 256)
     np.testing.assert_array_equal(decode_reference(o, 0, [0], q, 0.0), decode_reference(o, 0, [0], q, 1 / 16))
+
+
+def _mq(seed, n_seqs, n_q):
+    return small_query(seed, n_seqs * n_q, 16, 256).reshape(n_seqs, n_q, 16, 256)
+
+
+def test_multi_query_of_one_is_dense_decode():
+    o, *_ = _cache()
+    q = _mq(7, 1, 1)
+    np.testing.assert_array_equal(multi_query_reference(o, 0, [0], q)[:, 0], decode_reference(o, 0, [0], q[:, 0]))
+
+
+def test_multi_query_equals_dense_decode_of_each_prefix():
+    """Without a ring the cached codes of a prefix do not depend on what follows: query t of T equals dense decode
+    over a fresh cache that holds only the first len - T + t + 1 tokens."""
+    o, k, v, c = _cache(tail_len=0)
+    q = _mq(8, 1, 5)
+    got = multi_query_reference(o, 0, [0], q)
+    for t in range(5):
+        n_t = 300 - 5 + t + 1
+        prefix = OracleCache(c)
+        prefix.append(0, [0], [n_t], k[:n_t], v[:n_t])
+        np.testing.assert_allclose(got[0, t], decode_reference(prefix, 0, [0], q[:, t])[0], atol=1e-12, rtol=0)
+
+
+def test_multi_query_masked_softmax_brute_force():
+    """The causal reading as a mask over all cached positions (masked scores at -inf), summed with math.fsum, on a
+    cache that mixes body rows and bf16 ring rows."""
+    c = dict(n_layers=1, max_seqs=1, capacity=128, n_q_heads=4, n_kv_heads=2, head_dim=256,
+             k_bits=4, v_bits=3, kvarn=0, tail_len=32, tail_slack=32, tail_dtype=1)
+    k, v = small_tokens(12, 45, 2, 256)
+    o = OracleCache(c)
+    o.append(0, [0], [45], k, v)
+    o.tail_evict(0, [0])
+    n_q = 3
+    q = small_query(9, n_q, 4, 256).reshape(1, n_q, 4, 256)
+    got = multi_query_reference(o, 0, [0], q)
+    kd, vd = o.dequantized(0, 0, np.arange(45))
+    qf = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for t in range(n_q):
+        for h in range(4):
+            g = h // 2
+            s = [math.fsum(float(qf[0, t, h, i]) * float(kd[j, g, i]) for i in range(256)) / 16.0
+                 if j <= 45 - n_q + t else -math.inf for j in range(45)]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            den = math.fsum(w)
+            want = [math.fsum(w[j] * float(vd[j, g, i]) for j in range(45)) / den for i in range(256)]
+            np.testing.assert_allclose(got[0, t, h], want, atol=1e-12, rtol=0)
+
+
+def test_multi_query_needs_as_many_positions_as_queries():
+    o, *_ = _cache(n=3)
+    with pytest.raises(ValueError):
+        multi_query_reference(o, 0, [0], _mq(1, 1, 4))
