@@ -57,6 +57,9 @@ typedef enum {
 /* Maximum number of sequences one call may name. */
 #define KVQ_MAX_BATCH 64
 
+/* Maximum queries per sequence of kvq_decode_attn_multi: the token being verified plus up to 7 drafts. */
+#define KVQ_MAX_QUERIES 8
+
 /* Cache configuration. K and V bit widths are chosen separately (KVarN benchmark page, K/V pairs). */
 typedef struct {
   int32_t n_layers;     /* layers held by the arena                                        */
@@ -163,6 +166,21 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
 kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                            const void* k_bf16, const void* v_bf16, const void* q_bf16, float* out,
                            float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
+
+/* Dense decode of T = n_queries queries per sequence in one call, as when the last accepted token and up
+ * to 7 drafted ones are verified together (Qwen3.8-27B page, decode-speed paragraph: the engine drafts up to
+ * 7 tokens per step with MTP heads). The T tokens must already be in the cache (appended as usual); query t
+ * (0 <= t < T) of sequence i sits at position len - T + t and attends causally to positions
+ * [0, len - T + t]: out[i][t][h][:] as kvq_decode_attn over that prefix (body rows before body_len, ring rows
+ * after). q_bf16: device bf16 [n_seqs][T][Hq][D]; out: device fp32 [n_seqs][T][Hq][D]; workspace:
+ * kvq_workspace_bytes(cache, n_seqs * T, max len) bytes. The cache is not changed: dropping rejected drafts
+ * is the caller's (a cache without them is rebuilt by appending the accepted tokens). Each (sequence, query)
+ * pair runs as one sequence of the dense decode launch over the same cache rows.
+ * Errors: KVQ_E_INVALID if T is outside [1, KVQ_MAX_QUERIES] or n_seqs * T > KVQ_MAX_BATCH; KVQ_E_STATE if
+ * a sequence holds fewer than T positions; others as kvq_decode_attn. */
+kvq_status kvq_decode_attn_multi(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                 int32_t n_queries, const void* q_bf16, float* out, float softmax_scale,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* Sparse decode attention over an indexer budget (offload page, QSA: the layer reads only the
  * main-KV rows at the positions the indexer chose, so the budget, not the context, bounds the bytes).

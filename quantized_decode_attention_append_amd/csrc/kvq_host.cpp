@@ -660,34 +660,27 @@ kvq_status kvq_append_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const i
   return KVQ_OK;
 }
 
-kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
-                           float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
-  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
-  if (s != KVQ_OK) return s;
-  if (!q_bf16 || !out || !workspace) return fail(KVQ_E_INVALID, "q/out/workspace is NULL");
-  if (((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
-  if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
-  int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH];
-  for (int i = 0; i < n_seqs; ++i) {
-    const int k = c->idx(layer, seq_ids[i]);
-    len[i] = c->len[k];
-    bl[i] = c->body_len[k];
-    if (len[i] < 1) return fail(KVQ_E_STATE, "seq %d of layer %d is empty", seq_ids[i], layer);
-  }
+namespace {
+
+// Dense decode of n entries, entry i reading sequence ids[i] over positions [0, len[i]) (its body range
+// [0, min(body_len, len[i])) and the ring rows after it): the query and output rows follow the entries.
+kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, const int* len, const void* q_bf16,
+                      float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
   if (c->cfg.layout == KVQ_LAYOUT_ROWS)
-    return run_gather(c, layer, n_seqs, seq_ids, q_bf16, nullptr, 0, len, out, softmax_scale, workspace, ws_bytes,
-                      stream);
+    return run_gather(c, layer, n, ids, q_bf16, nullptr, 0, len, out, softmax_scale, workspace, ws_bytes, stream);
+  int bl[KVQ_MAX_BATCH];
+  for (int i = 0; i < n; ++i) bl[i] = std::min(c->body_len[c->idx(layer, ids[i])], len[i]);
   kvq::DecodeArgs a{};
   a.g = geometry(c);
-  const SplitPlan p = plan_splits(c, n_seqs, len, bl, a.seqs);
+  const SplitPlan p = plan_splits(c, n, len, bl, a.seqs);
   if (p.max_splits > kvq::kMaxSplits) return fail(KVQ_E_INVALID, "too many splits (%d)", p.max_splits);
-  const size_t need = (size_t)n_seqs * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
+  const size_t need = (size_t)n * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-  for (int i = 0; i < n_seqs; ++i) a.seqs[i].slab = slab_offset(c, layer, seq_ids[i]);
+  for (int i = 0; i < n; ++i) a.seqs[i].slab = slab_offset(c, layer, ids[i]);
   a.q = (const uint16_t*)q_bf16;
   a.out = out;
   a.partials = (float*)workspace;
-  a.n_seqs = n_seqs;
+  a.n_seqs = n;
   a.n_q_heads = c->cfg.n_q_heads;
   a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
   a.max_splits = p.max_splits;
@@ -696,8 +689,56 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
                        [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_decode(a, p.total_wgs, (hipStream_t)stream, e0, e1); });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   int n_splits[KVQ_MAX_BATCH];
-  for (int i = 0; i < n_seqs; ++i) n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
-  return launch_combine_for(c, n_seqs, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
+  for (int i = 0; i < n; ++i) n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
+  return launch_combine_for(c, n, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
+}
+
+kvq_status check_decode_args(const void* q_bf16, const float* out, const void* workspace, float softmax_scale) {
+  if (!q_bf16 || !out || !workspace) return fail(KVQ_E_INVALID, "q/out/workspace is NULL");
+  if (((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
+                           float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  s = check_decode_args(q_bf16, out, workspace, softmax_scale);
+  if (s != KVQ_OK) return s;
+  int len[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) {
+    len[i] = c->len[c->idx(layer, seq_ids[i])];
+    if (len[i] < 1) return fail(KVQ_E_STATE, "seq %d of layer %d is empty", seq_ids[i], layer);
+  }
+  return run_decode(c, layer, n_seqs, seq_ids, len, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
+}
+
+kvq_status kvq_decode_attn_multi(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                 int32_t n_queries, const void* q_bf16, float* out, float softmax_scale,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (n_queries < 1 || n_queries > KVQ_MAX_QUERIES)
+    return fail(KVQ_E_INVALID, "n_queries must be in [1, %d] (got %d)", KVQ_MAX_QUERIES, n_queries);
+  if (n_seqs * n_queries > KVQ_MAX_BATCH)
+    return fail(KVQ_E_INVALID, "n_seqs * n_queries must be at most %d (got %d)", KVQ_MAX_BATCH, n_seqs * n_queries);
+  s = check_decode_args(q_bf16, out, workspace, softmax_scale);
+  if (s != KVQ_OK) return s;
+  int ids[KVQ_MAX_BATCH], len[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) {
+    const int n = c->len[c->idx(layer, seq_ids[i])];
+    if (n < n_queries)
+      return fail(KVQ_E_STATE, "seq %d of layer %d holds %d positions, fewer than %d queries", seq_ids[i], layer, n,
+                  n_queries);
+    for (int t = 0; t < n_queries; ++t) {   // query t of the sequence sits at position n - n_queries + t
+      ids[i * n_queries + t] = seq_ids[i];
+      len[i * n_queries + t] = n - n_queries + t + 1;
+    }
+  }
+  return run_decode(c, layer, n_seqs * n_queries, ids, len, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
 }
 
 // Tiles the work-group that requantizes a decode step's evicted rows gives up (about the time those writes take).

@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_E_INVALID, KVQ_E_CAPACITY, KVQ_E_SIZE, KVQ_E_HIP, KVQ_E_STATE = 0, -1, -2, -3, -4, -5
+KVQ_MAX_BATCH, KVQ_MAX_QUERIES = 64, 8
 TAIL_NONE, TAIL_BF16, TAIL_Q8_0 = 0, 1, 2
 LAYOUT_TILES, LAYOUT_ROWS = 0, 1
 REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab": 5}
@@ -26,7 +27,7 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
 KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5}
 
 
@@ -61,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "kvq_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, F, P, SZ, P]),
         "kvq_tail_evict": (I32, [P, I32, I32, IP, P]),
         "kvq_decode_attn": (I32, [P, I32, I32, IP, P, P, F, P, SZ, P]),
+        "kvq_decode_attn_multi": (I32, [P, I32, I32, IP, I32, P, P, F, P, SZ, P]),
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
         "kvq_sparse_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, I32, P, F, P, SZ, P]),
         "kvq_timing_enable": (I32, [P, I32]),
@@ -224,6 +226,25 @@ class Cache:
                                     _dev(out, torch.float32, "out"), float(softmax_scale),
                                     _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                     ctypes.c_void_p(_stream(stream))))
+        return out
+
+    def decode_attn_multi(self, layer: int, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None):
+        """Decode of the last T cached positions of each sequence at once, causal among them (verification of
+        drafted tokens). q: bf16 [n_seqs, T, Hq, D]; returns fp32 [n_seqs, T, Hq, D]."""
+        n = len(seq_ids)
+        if q.dim() != 4 or q.shape[0] != n or q.shape[2] != self.hq or q.shape[3] != self.d or q.element_size() != 2:
+            raise ValueError("q must be bf16 [n_seqs, T, Hq, D]")
+        t = q.shape[1]
+        if out is None:
+            out = torch.empty((n, t, self.hq, self.d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            max_len = max(self.lengths(layer, s)[0] for s in seq_ids)
+            workspace = self.workspace(max(1, min(n * t, KVQ_MAX_BATCH)), max(1, max_len))
+        _check(_lib.kvq_decode_attn_multi(self._h, layer, n, _ids(seq_ids), t, _dev(q, q.dtype, "q"),
+                                          _dev(out, torch.float32, "out"), float(softmax_scale),
+                                          _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                          ctypes.c_void_p(_stream(stream))))
         return out
 
     def decode_step(self, layer: int, seq_ids: Sequence[int], k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,

@@ -1,0 +1,108 @@
+"""GPU parity of multi-query decode (the last T cached positions of a sequence decoded at once, causal among
+them, as when drafted tokens are verified) through the C ABI, against the oracle's fp64 result over the same
+dequantized values: within 2e-3 absolute, on both layouts, every ring kind, KVarN, and queries that straddle
+the body/ring boundary."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import Pair, TOL, dev, max_err
+from workloads import small_tokens, small_query
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg(**kw):
+    c = dict(n_layers=2, max_seqs=3, capacity=1024, n_q_heads=16, n_kv_heads=2, head_dim=256, k_bits=6,
+             v_bits=5, kvarn=0, tail_len=0, tail_slack=0, tail_dtype=0, layout=0)
+    c.update(kw)
+    return c
+
+
+def mq(seed, n_seqs, n_q, hq=16):
+    return small_query(seed, n_seqs * n_q, hq, 256).reshape(n_seqs, n_q, hq, 256)
+
+
+def run_multi(p, layer, seq_ids, q):
+    got = p.gpu.decode_attn_multi(layer, seq_ids, dev(q).view(*q.shape)).cpu().numpy()
+    want = oracle.multi_query_reference(p.ora, layer, seq_ids, q)
+    return got, want
+
+
+@pytest.mark.parametrize("layout,tail_dtype,kvarn,n_q", [
+    (0, 0, 0, 1), (0, 0, 0, 8), (0, 1, 0, 5), (0, 2, 1, 8), (0, 3, 0, 2), (0, 1, 1, 8),
+    (1, 0, 0, 8), (1, 1, 0, 5), (1, 2, 1, 2), (1, 3, 1, 8)])
+def test_multi_query_matches_oracle(layout, tail_dtype, kvarn, n_q):
+    tail = dict(tail_len=64, tail_slack=32, tail_dtype=tail_dtype) if tail_dtype else {}
+    p = Pair(cfg(layout=layout, kvarn=kvarn, **tail))
+    seed = 40 * layout + 10 * tail_dtype + 3 * kvarn + n_q
+    k, v = small_tokens(seed, 800, 2, 256)
+    p.append(1, [0, 2], [300, 170], k[:470], v[:470])
+    p.evict(1, [0, 2])
+    # the drafts arrive as one more chunk (ring rows when there is a ring)
+    p.append(1, [0, 2], [n_q, n_q], k[470:470 + 2 * n_q], v[470:470 + 2 * n_q])
+    for s in (0, 2):
+        p.lengths_match(1, s)
+    got, want = run_multi(p, 1, [0, 2], mq(seed, 2, n_q))
+    assert max_err(got, want) <= TOL, max_err(got, want)
+
+
+def test_multi_query_of_one_equals_decode_attn_bit_for_bit():
+    p = Pair(cfg(tail_len=64, tail_slack=32, tail_dtype=1))
+    k, v = small_tokens(3, 400, 2, 256)
+    p.append(0, [1], [333], k[:333], v[:333])
+    p.evict(0, [1])
+    q = mq(5, 1, 1)
+    multi = p.gpu.decode_attn_multi(0, [1], dev(q).view(*q.shape)).cpu().numpy()
+    single = p.gpu.decode_attn(0, [1], dev(q[:, 0])).cpu().numpy()
+    np.testing.assert_array_equal(multi[:, 0], single)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_queries_straddle_the_body_and_ring(layout):
+    """A window of 4 and 8 queries: after an evict the first drafts sit in the body, the last in the ring."""
+    p = Pair(cfg(layout=layout, tail_len=4, tail_slack=28, tail_dtype=1, k_bits=4, v_bits=4))
+    k, v = small_tokens(17, 300, 2, 256)
+    p.append(0, [0], [200], k[:200], v[:200])
+    p.append(0, [0], [8], k[200:208], v[200:208])
+    p.evict(0, [0])
+    n, body = p.gpu.lengths(0, 0)
+    assert n - 8 < body < n, (n, body)
+    got, want = run_multi(p, 0, [0], mq(18, 1, 8))
+    assert max_err(got, want) <= TOL
+
+
+def test_largest_batch_of_entries_and_a_long_context():
+    """8 sequences x 8 queries (64 entries in one launch, ragged lengths), then one sequence of 8k positions."""
+    p = Pair(cfg(max_seqs=8, capacity=8192, n_layers=1, tail_len=32, tail_slack=32, tail_dtype=2))
+    rng = np.random.default_rng(23)
+    lens = [int(x) for x in rng.integers(8, 200, size=8)]
+    k, v = small_tokens(24, sum(lens), 2, 256)
+    p.append(0, list(range(8)), lens, k, v)
+    p.evict(0, list(range(8)))
+    got, want = run_multi(p, 0, list(range(8)), mq(25, 8, 8))
+    assert max_err(got, want) <= TOL
+    p = Pair(cfg(max_seqs=1, capacity=8192, n_layers=1, tail_len=32, tail_slack=32, tail_dtype=2))
+    k, v = small_tokens(26, 8000, 2, 256)
+    p.append(0, [0], [8000], k, v)
+    p.evict(0, [0])
+    got, want = run_multi(p, 0, [0], mq(27, 1, 4))
+    assert max_err(got, want) <= TOL
+
+
+def test_multi_query_errors():
+    from quantized_decode_attention_append_amd import kvq
+    p = Pair(cfg(max_seqs=9, n_layers=1))
+    k, v = small_tokens(1, 40, 2, 256)
+    p.append(0, [0, 1], [5, 35], k, v)
+    for n_q in (0, 9):
+        q = dev(mq(1, 1, max(n_q, 1))).view(1, max(n_q, 1), 16, 256)
+        with pytest.raises(kvq.KvqError) as e:
+            p.gpu.decode_attn_multi(0, [1], q[:, :n_q] if n_q == 0 else q)
+        assert e.value.status == kvq.KVQ_E_INVALID
+    with pytest.raises(kvq.KvqError) as e:        # 9 sequences x 8 queries > 64 entries
+        p.gpu.decode_attn_multi(0, list(range(9)), dev(mq(2, 9, 8)).view(9, 8, 16, 256))
+    assert e.value.status == kvq.KVQ_E_INVALID
+    with pytest.raises(kvq.KvqError) as e:        # 5 positions, 6 queries
+        p.gpu.decode_attn_multi(0, [0, 1], dev(mq(3, 2, 6)).view(2, 6, 16, 256))
+    assert e.value.status == kvq.KVQ_E_STATE
