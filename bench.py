@@ -19,7 +19,8 @@ used only while the kernel source still matches the one that was measured. `cpu_
 oracle timed on a bounded sample of the same workload. Also reported: `graph` (the same steps with each step's
 launches captured into one HIP graph beforehand and replayed back to back), `cold` (single-layer workloads:
 decode time after a 512 MiB write has evicted L2 and the MALL) and `copy_ceiling_gbs` (a plain 1 GiB device
-copy, bytes read + written per second).
+copy, bytes read + written per second). With --verify-queries T, `multi_query` times multi-query decode of the
+last T positions of every sequence (verification of T - 1 drafted tokens) over every layer.
 """
 from __future__ import annotations
 
@@ -53,7 +54,7 @@ def row_bytes(n_bits: int, d: int) -> int:
 def ring_row_bytes(cfg: dict) -> int:
     if cfg["tail_len"] == 0:
         return 0
-    return 2 * cfg["head_dim"] if cfg["tail_dtype"] == 1 else row_bytes(8, cfg["head_dim"])
+    return 2 * cfg["head_dim"] if cfg["tail_dtype"] in (1, 3) else row_bytes(8, cfg["head_dim"])   # bf16 / f16, or q8_0
 
 
 def decode_call_bytes(cfg: dict, lens, bodies) -> int:
@@ -241,6 +242,47 @@ def cold_calls(torch, cache, seqs, q, out, ws, n: int) -> dict:
             "how": "each decode call after a 512 MiB device write (L2 and MALL evicted)"}
 
 
+def multi_query_leg(torch, cache, cfg, L, seqs, qin, n_q, reps, dev):
+    """Multi-query decode (the last n_q cached positions of every sequence, causal among them) over every layer,
+    reps times: wall time per pass over the layers, the split kernel's dispatch-stamped average, and that kernel's
+    rate in unique cache bytes (each row counted once, however many queries read it)."""
+    B = len(seqs)
+    hq, d = qin.shape[-2], qin.shape[-1]
+    qm = [torch.from_numpy(np.ascontiguousarray(qin[np.arange(n_q) % qin.shape[0], layer].transpose(1, 0, 2, 3))
+                           .view(np.int16)).to(dev) for layer in range(L)]
+    lens = [cache.lengths(0, s) for s in seqs]
+    ws = cache.workspace(min(B * n_q, 64), max(x[0] for x in lens))
+    out = torch.empty((B, n_q, hq, d), dtype=torch.float32, device=dev)
+
+    def run():
+        for layer in range(L):
+            cache.decode_attn_multi(layer, seqs, qm[layer], out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kind = "gather" if cfg.get("layout", 0) == 1 else "decode"
+    cache.timing(True)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms, n = cache.timing_read(kind)
+    cms, cn = cache.timing_read("combine")
+    cache.timing(False)
+    unique = decode_call_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens])
+    k_us = ms * 1e3 / max(n, 1)
+    log(f"multi-query decode, {n_q} queries per sequence: {k_us:.2f} us per {kind} launch")
+    return {"queries": n_q, "ms_per_pass": round(elapsed * 1e3 / reps, 4), "kernel": kind,
+            "kernel_us": round(k_us, 3), "combine_us": round(cms * 1e3 / max(cn, 1), 3),
+            "unique_bytes_per_call": int(unique),
+            "unique_GBs": round(unique / (k_us * 1e-6) / 1e9, 2),
+            "frac": round(unique / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +292,9 @@ def main() -> int:
                     help="1: q8_0 4k single layer; 2: K6/V5 + bf16 tail, 64k, 16 layers (default); 3: KVarN "
                          "K4/V4, 8 streams; 4: K6/V5 + q8_0 ring, 262k; 5: sparse q8_0, budget 2048 of 262k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify-queries", type=int, default=0,
+                    help="also time multi-query decode of the last T positions per sequence (T = 1 + drafts, <= 8) "
+                         "on dense workloads, reported as the line's multi_query object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
@@ -377,6 +422,9 @@ def main() -> int:
     graph = graph_steps(torch, step, args.warmup + 2 * args.steps, args.steps, L)
     cold = cold_calls(torch, cache, seqs, qin_d[0, 0], out[0], ws, args.steps) if (L == 1 and not appends) else None
 
+    multi = None
+    if args.verify_queries and not sparse:
+        multi = multi_query_leg(torch, cache, cfg, L, seqs, qin, args.verify_queries, args.steps, dev)
     main_kernel = "gather" if (sparse or cfg.get("layout", 0) == 1) else "decode"
     ms, n = times[main_kernel]
     avg_s = ms / 1e3 / max(n, 1)
@@ -419,6 +467,8 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": kname, "bytes_per_launch": int(bytes_per_launch)},
     }
+    if multi is not None:
+        res["multi_query"] = multi
     gbytes = float(sum(nbytes)) / args.steps   # the graph steps read the same bytes per step (to a few rows)
     res["graph"] = {"ms_per_step": round(graph * 1e3, 4), "value": round(gbytes / graph / 1e9, 2), "unit": "GB/s",
                     "how": f"one HIP graph per step ({L} layers), all {args.steps} captured before timing, "
