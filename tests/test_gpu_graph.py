@@ -99,3 +99,33 @@ def test_sparse_step_graph(fused):
         p.assert_slab_equal(0, 0)
         e_got, e_want = p.sparse(0, [0], small_query(313 + rep, 1, 16, 256), pos[None])
         assert max_err(e_got, e_want) <= TOL
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_multi_query_graph(layout):
+    """kvq_decode_attn_multi captured and replayed (8 queries on each of two sequences), eager single-query
+    decode on the same stream and workspace between the replays; every replay matches the eager call bit for bit
+    and the oracle within the tolerance."""
+    import torch
+    p = Pair(cfg(tail_len=64, tail_slack=32, tail_dtype=1, layout=layout))
+    k, v = small_tokens(320 + layout, 500, 2, 256)
+    seqs = [0, 1]
+    p.append(0, seqs, [260, 90], k[:350], v[:350])
+    p.evict(0, seqs)
+    p.append(0, seqs, [8, 8], k[350:366], v[350:366])
+    qn = small_query(321, 16, 16, 256).reshape(2, 8, 16, 256)
+    q = dev(qn).view(2, 8, 16, 256)
+    out = torch.zeros((2, 8, 16, 256), dtype=torch.float32, device="cuda")
+    ws = p.gpu.workspace(16, 400)
+    eager = p.gpu.decode_attn_multi(0, seqs, q, out=torch.empty_like(out), workspace=ws).cpu().numpy()
+    want = oracle.multi_query_reference(p.ora, 0, seqs, qn)
+    assert max_err(eager, want) <= TOL
+    g = capture(torch, lambda: p.gpu.decode_attn_multi(0, seqs, q, out=out, workspace=ws))
+    q1 = small_query(322, 2, 16, 256)
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), eager, err_msg=f"replay {rep}")
+        e_got = p.gpu.decode_attn(0, seqs, dev(q1), workspace=ws).cpu().numpy()
+        assert max_err(e_got, oracle.decode_reference(p.ora, 0, seqs, q1)) <= TOL
