@@ -175,7 +175,8 @@ kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
  * after). q_bf16: device bf16 [n_seqs][T][Hq][D]; out: device fp32 [n_seqs][T][Hq][D]; workspace:
  * kvq_workspace_bytes(cache, n_seqs * T, max len) bytes. The cache is not changed: dropping rejected drafts
  * is the caller's (a cache without them is rebuilt by appending the accepted tokens). Each (sequence, query)
- * pair runs as one sequence of the dense decode launch over the same cache rows.
+ * pair runs as one entry of the dense decode launch (of the gather launch for KVQ_LAYOUT_ROWS) over the
+ * same cache rows.
  * Errors: KVQ_E_INVALID if T is outside [1, KVQ_MAX_QUERIES] or n_seqs * T > KVQ_MAX_BATCH; KVQ_E_STATE if
  * a sequence holds fewer than T positions; others as kvq_decode_attn. */
 kvq_status kvq_decode_attn_multi(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
