@@ -173,6 +173,9 @@ int tiles_of(int p0, int p1) { return p1 > p0 ? (p1 - 1) / kvq::kTile - p0 / kvq
 // its tiles (at least one), leftover work-groups go to the segments with the most tiles per work-group.
 constexpr int kMaxWgBudget = 1024;
 constexpr int kMinTilesPerWg = 4;
+// Ring work-groups per sequence that multi-query decode plans outside the per-head budget (at most).
+constexpr int kRingExtra = 2;
+
 constexpr size_t kPartialFloats(int d) { return (size_t)kvq::kPartialHeads * (d + 2); }
 
 struct SplitPlan {
@@ -180,7 +183,11 @@ struct SplitPlan {
   int total_wgs;
 };
 
-SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out) {
+// allow_ring_extra: when the sequences are many against the per-head budget (as the entries of multi-query
+// decode can be), their short ring segments get work-groups on top of the budget instead of taking most of it
+// from the body segments.
+SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out,
+                      bool allow_ring_extra = false) {
   const int hk = c->cfg.n_kv_heads;
   int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
   // Cost of a tile in a work-group's time: a qN_0 tile (body or q8_0 ring) is decode- and MFMA-bound, a bf16
@@ -200,9 +207,20 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
   // short contexts: at least ~kMinTilesPerWg tiles of cost per work-group (fewer, fuller work-groups and fewer
   // partials to merge; measured on the 4k single-layer workload)
   budget_h = std::min(budget_h, std::max(1, (int)(total / kMinTilesPerWg)));
+  const bool ring_extra = allow_ring_extra && 4 * n_seqs > budget_h;
+  double shared = total;   // the cost that shares the budget
+  if (ring_extra) {
+    shared = 0;
+    for (int i = 0; i < n_seqs; ++i) shared += wt[2 * i];
+  }
+  const double per_wg = std::max(shared / budget_h, 1.0);
   int used = 0;
   for (int k = 0; k < 2 * n_seqs; ++k) {
-    nwg[k] = tiles[k] ? std::max(1, (int)(budget_h * wt[k] / std::max(total, 1.0))) : 0;
+    if (ring_extra && (k & 1)) {   // outside the budget: about one body work-group's cost each, at most kRingExtra
+      nwg[k] = tiles[k] ? std::min({tiles[k], kRingExtra, std::max(1, (int)(wt[k] / per_wg + 0.5))}) : 0;
+      continue;
+    }
+    nwg[k] = tiles[k] ? std::max(1, (int)(budget_h * wt[k] / std::max(shared, 1.0))) : 0;
     nwg[k] = std::min(nwg[k], tiles[k]);
     used += nwg[k];
   }
@@ -210,7 +228,7 @@ SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int*
     int best = -1;
     double best_r = 0.0;
     for (int k = 0; k < 2 * n_seqs; ++k)
-      if (nwg[k] && nwg[k] < tiles[k] && wt[k] / nwg[k] > best_r) {
+      if (!(ring_extra && (k & 1)) && nwg[k] && nwg[k] < tiles[k] && wt[k] / nwg[k] > best_r) {
         best_r = wt[k] / nwg[k];
         best = k;
       }
@@ -449,7 +467,7 @@ size_t kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) 
   // splits per (sequence, KV head) never exceed the tiles of a sequence (+1 for the body/ring boundary
   // tile) nor the per-head work-group budget
   const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 1;
-  long splits = std::min<long>(tiles, std::max(1, std::min(c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads));
+  long splits = std::min<long>(tiles, std::max(1, std::min(c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads) + kRingExtra);
   // the gather path (sparse decode, and dense decode of a row-layout cache)
   const long gsplits = std::min<long>((max_len + kGatherMin - 1) / kGatherMin, gather_budget_h(c));
   splits = std::max(splits, std::max(1L, gsplits));
@@ -665,14 +683,15 @@ namespace {
 // Dense decode of n entries, entry i reading sequence ids[i] over positions [0, len[i]) (its body range
 // [0, min(body_len, len[i])) and the ring rows after it): the query and output rows follow the entries.
 kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, const int* len, const void* q_bf16,
-                      float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+                      float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream,
+                      bool ring_extra = false) {
   if (c->cfg.layout == KVQ_LAYOUT_ROWS)
     return run_gather(c, layer, n, ids, q_bf16, nullptr, 0, len, out, softmax_scale, workspace, ws_bytes, stream);
   int bl[KVQ_MAX_BATCH];
   for (int i = 0; i < n; ++i) bl[i] = std::min(c->body_len[c->idx(layer, ids[i])], len[i]);
   kvq::DecodeArgs a{};
   a.g = geometry(c);
-  const SplitPlan p = plan_splits(c, n, len, bl, a.seqs);
+  const SplitPlan p = plan_splits(c, n, len, bl, a.seqs, ring_extra);
   if (p.max_splits > kvq::kMaxSplits) return fail(KVQ_E_INVALID, "too many splits (%d)", p.max_splits);
   const size_t need = (size_t)n * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -738,7 +757,10 @@ kvq_status kvq_decode_attn_multi(kvq_cache* c, int32_t layer, int32_t n_seqs, co
       len[i * n_queries + t] = n - n_queries + t + 1;
     }
   }
-  return run_decode(c, layer, n_seqs * n_queries, ids, len, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
+  // with several queries per sequence the many short ring segments get work-groups outside the budget; one query
+  // per sequence plans (and computes) exactly as kvq_decode_attn
+  return run_decode(c, layer, n_seqs * n_queries, ids, len, q_bf16, out, softmax_scale, workspace, ws_bytes, stream,
+                    n_queries > 1);
 }
 
 // Tiles the work-group that requantizes a decode step's evicted rows gives up (about the time those writes take).
