@@ -197,6 +197,17 @@ class OracleCache:
                 continue
             self._evict_to(s, max(s.body_len, s.len - self.W))
 
+    def truncate(self, layer: int, seq_ids, new_lens):
+        """Drop the newest positions of each sequence down to new_lens[i], which must lie in [body_len, len]: only
+        rows still in the ring can be dropped (drafted tokens a verification step rejected; Qwen3.8-27B page,
+        decode-speed paragraph on MTP drafting). The dropped ring rows stay in their slots until later appends
+        write those slots again; KVarN calibration is kept."""
+        for sid, n in zip(seq_ids, new_lens):
+            s = self.st(layer, sid)
+            if not s.body_len <= int(n) <= s.len:
+                raise ValueError(f"truncate to {n} outside [body_len {s.body_len}, len {s.len}]")
+            s.len = int(n)
+
     # ------------------------------------------------------------------ reading
     def lengths(self, layer: int, seq: int):
         s = self.st(layer, seq)

@@ -206,3 +206,52 @@ def test_f16_tail_below_window_holds_the_rounded_inputs():
     v16 = bf16_to_f32(v).astype(np.float16).astype(np.float64)
     assert np.array_equal(kk, k16) and np.array_equal(vv, v16)
     assert np.all(kk[:, 0, 0] == 16 * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("tail_dtype,kvarn", [(1, 0), (2, 1), (3, 0)])
+def test_truncate_then_append_equals_never_appending_the_dropped(tail_dtype, kvarn):
+    """Rolling back rejected drafts: append drafts, truncate, append the accepted tokens, step on; every length,
+    dequantized value and attention output equals a cache that only ever saw the accepted tokens."""
+    import oracle
+    from workloads import small_query
+    c = dict(n_layers=1, max_seqs=1, capacity=512, n_q_heads=4, n_kv_heads=2, head_dim=256, k_bits=5,
+             v_bits=3, kvarn=kvarn, tail_len=16, tail_slack=16, tail_dtype=tail_dtype)
+    k, v = small_tokens(40 + tail_dtype, 300, 2, 256)
+    a, b = OracleCache(c), OracleCache(c)
+    a.append(0, [0], [100], k[:100], v[:100])
+    b.append(0, [0], [100], k[:100], v[:100])
+    a.tail_evict(0, [0])
+    b.tail_evict(0, [0])
+    off = 100
+    for drafts, accepted in ((7, 3), (4, 0), (7, 7), (2, 1)):
+        a.append(0, [0], [drafts], k[200:200 + drafts], v[200:200 + drafts])   # drafts that will be rejected
+        n, _ = a.lengths(0, 0)
+        a.truncate(0, [0], [n - drafts])
+        a.append(0, [0], [accepted], k[off:off + accepted], v[off:off + accepted])
+        b.append(0, [0], [accepted], k[off:off + accepted], v[off:off + accepted])
+        off += accepted
+        a.tail_evict(0, [0])
+        b.tail_evict(0, [0])
+        assert a.lengths(0, 0) == b.lengths(0, 0)
+        ka, va = a.dequantized(0, 0)
+        kb, vb = b.dequantized(0, 0)
+        np.testing.assert_array_equal(ka, kb)
+        np.testing.assert_array_equal(va, vb)
+        q = small_query(off, 1, 4, 256)
+        np.testing.assert_array_equal(oracle.decode_reference(a, 0, [0], q), oracle.decode_reference(b, 0, [0], q))
+
+
+def test_truncate_keeps_to_the_ring():
+    c = dict(n_layers=1, max_seqs=1, capacity=256, n_q_heads=4, n_kv_heads=2, head_dim=256, k_bits=4,
+             v_bits=4, kvarn=0, tail_len=16, tail_slack=16, tail_dtype=1)
+    k, v = small_tokens(3, 60, 2, 256)
+    o = OracleCache(c)
+    o.append(0, [0], [60], k, v)
+    o.tail_evict(0, [0])
+    n, body = o.lengths(0, 0)
+    with pytest.raises(ValueError):
+        o.truncate(0, [0], [body - 1])
+    with pytest.raises(ValueError):
+        o.truncate(0, [0], [n + 1])
+    o.truncate(0, [0], [body])
+    assert o.lengths(0, 0) == (body, body)
