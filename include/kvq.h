@@ -111,6 +111,17 @@ void kvq_cache_destroy(kvq_cache* cache);
 kvq_status kvq_seq_reset(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                          void* stream);
 
+/* Drop the newest positions of each listed sequence of a layer down to new_len[i] (host int32[n_seqs]), as
+ * after a verification step that rejected drafted tokens (Qwen3.8-27B page, decode-speed paragraph on MTP
+ * drafting): only rows still in the ring can be dropped, so body_len <= new_len[i] <= len (keep drafts in the
+ * ring: tail_len at least the number of drafts, and evict after the verification, not before). The dropped ring
+ * rows need no clearing (later appends write their slots again); KVarN calibration is kept. Host state only:
+ * ordered before every later launch on any stream.
+ * Errors: KVQ_E_INVALID if new_len[i] is outside [0, len]; KVQ_E_STATE if it is below body_len. No sequence is
+ * changed when an error is returned. */
+kvq_status kvq_seq_truncate(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                            const int32_t* new_len);
+
 /* Host-side lengths of a (layer, seq): positions held (len) and positions in the qN_0 body. */
 kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t seq, int32_t* len,
                            int32_t* body_len);

@@ -436,6 +436,24 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_arena, size_t arena_b
 
 void kvq_cache_destroy(kvq_cache* cache) { delete cache; }
 
+kvq_status kvq_seq_truncate(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                            const int32_t* new_len) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (!new_len) return fail(KVQ_E_INVALID, "new_len is NULL");
+  for (int i = 0; i < n_seqs; ++i) {   // every sequence is checked before any is changed
+    const int k = c->idx(layer, seq_ids[i]);
+    if (new_len[i] < 0 || new_len[i] > c->len[k])
+      return fail(KVQ_E_INVALID, "seq %d: new length %d outside [0, %d]", seq_ids[i], new_len[i], c->len[k]);
+    if (new_len[i] < c->body_len[k])
+      return fail(KVQ_E_STATE, "seq %d: new length %d would drop body rows (body_len %d)", seq_ids[i], new_len[i],
+                  c->body_len[k]);
+  }
+  // ring writes read-modify-write their slot, so the dropped rows need no clearing
+  for (int i = 0; i < n_seqs; ++i) c->len[c->idx(layer, seq_ids[i])] = new_len[i];
+  return KVQ_OK;
+}
+
 kvq_status kvq_seq_reset(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, void* stream) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
   if (layer < -1 || layer >= c->cfg.n_layers) return fail(KVQ_E_INVALID, "layer %d out of range", layer);

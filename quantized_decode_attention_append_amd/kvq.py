@@ -26,7 +26,7 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
            "kvarn", "tail_len", "tail_slack", "tail_dtype", "layout")
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
-           "kvq_seq_reset", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
+           "kvq_seq_reset", "kvq_seq_truncate", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
            "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
 KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5}
 
@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "kvq_cache_init": (I32, [CP, P, SZ, P, ctypes.POINTER(P)]),
         "kvq_cache_destroy": (None, [P]),
         "kvq_seq_reset": (I32, [P, I32, I32, IP, P]),
+        "kvq_seq_truncate": (I32, [P, I32, I32, IP, IP]),
         "kvq_seq_lengths": (I32, [P, I32, I32, IP, IP]),
         "kvq_workspace_bytes": (SZ, [P, I32, I32]),
         "kvq_append": (I32, [P, I32, I32, IP, IP, P, P, P]),
@@ -161,6 +162,12 @@ class Cache:
 
     def seq_reset(self, layer: int, seq_ids: Sequence[int], stream=None):
         _check(_lib.kvq_seq_reset(self._h, layer, len(seq_ids), _ids(seq_ids), ctypes.c_void_p(_stream(stream))))
+
+    def seq_truncate(self, layer: int, seq_ids: Sequence[int], new_lens: Sequence[int]):
+        """Drop the newest positions (still in the ring) of each sequence down to new_lens[i]."""
+        if len(new_lens) != len(seq_ids):
+            raise ValueError("one new length per sequence")
+        _check(_lib.kvq_seq_truncate(self._h, layer, len(seq_ids), _ids(seq_ids), _ids(new_lens)))
 
     def workspace_bytes(self, n_seqs: int, max_len: int) -> int:
         return int(_lib.kvq_workspace_bytes(self._h, n_seqs, max_len))

@@ -106,3 +106,52 @@ def test_multi_query_errors():
     with pytest.raises(kvq.KvqError) as e:        # 5 positions, 6 queries
         p.gpu.decode_attn_multi(0, [0, 1], dev(mq(3, 2, 6)).view(2, 6, 16, 256))
     assert e.value.status == kvq.KVQ_E_STATE
+
+
+@pytest.mark.parametrize("layout,tail_dtype,kvarn", [(0, 1, 0), (0, 2, 1), (0, 3, 0), (1, 1, 1), (1, 2, 0)])
+def test_verify_and_roll_back_drafts(layout, tail_dtype, kvarn):
+    """The draft-verification loop: append 1 + k tokens, decode them together, drop the rejected drafts with
+    kvq_seq_truncate, then a fused decode step; slabs byte-exact and outputs within the tolerance every round."""
+    p = Pair(cfg(layout=layout, tail_len=16, tail_slack=16, tail_dtype=tail_dtype, kvarn=kvarn, k_bits=5, v_bits=3))
+    seed = 500 + 10 * layout + tail_dtype + 3 * kvarn
+    k, v = small_tokens(seed, 600, 2, 256)
+    seqs = [0, 1]
+    p.append(0, seqs, [120, 45], k[:165], v[:165])
+    p.evict(0, seqs)
+    off = 165
+    for rnd, (n_q, keep) in enumerate(((8, (3, 8)), (5, (1, 5)), (8, (8, 2)), (2, (2, 1)))):
+        p.append(0, seqs, [n_q, n_q], k[off:off + 2 * n_q], v[off:off + 2 * n_q])
+        off += 2 * n_q
+        got, want = run_multi(p, 0, seqs, mq(seed + rnd, 2, n_q))
+        assert max_err(got, want) <= TOL, (rnd, max_err(got, want))
+        new = [p.gpu.lengths(0, s)[0] - n_q + keep[i] for i, s in enumerate(seqs)]
+        p.gpu.seq_truncate(0, seqs, new)
+        p.ora.truncate(0, seqs, new)
+        q = small_query(seed + 50 + rnd, 2, 16, 256)
+        if layout == 0:
+            got = p.gpu.decode_step(0, seqs, dev(k[off:off + 2]), dev(v[off:off + 2]), dev(q)).cpu().numpy()
+            p.ora.append(0, seqs, [1, 1], k[off:off + 2], v[off:off + 2])
+            p.ora.tail_evict(0, seqs)
+            want = oracle.decode_reference(p.ora, 0, seqs, q)
+            off += 2
+        else:
+            p.evict(0, seqs)
+            got, want = p.decode(0, seqs, q)
+        assert max_err(got, want) <= TOL, (rnd, max_err(got, want))
+        for s in seqs:
+            p.lengths_match(0, s)
+            p.assert_slab_equal(0, s)
+
+
+def test_truncate_errors_leave_the_cache_unchanged():
+    from quantized_decode_attention_append_amd import kvq
+    p = Pair(cfg(tail_len=16, tail_slack=16, tail_dtype=1))
+    k, v = small_tokens(2, 100, 2, 256)
+    p.append(0, [0, 1], [60, 30], k[:90], v[:90])
+    p.evict(0, [0, 1])
+    before = [p.gpu.lengths(0, s) for s in (0, 1)]
+    for new, status in (([59, 31], kvq.KVQ_E_INVALID), ([40, 20], kvq.KVQ_E_STATE), ([-1, 30], kvq.KVQ_E_INVALID)):
+        with pytest.raises(kvq.KvqError) as e:
+            p.gpu.seq_truncate(0, [0, 1], new)
+        assert e.value.status == status
+        assert [p.gpu.lengths(0, s) for s in (0, 1)] == before
