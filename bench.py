@@ -5,22 +5,25 @@ per layer, append one token per sequence (tail-ring write), evict the oldest tai
 into the qN_0 body) and run decode attention over the whole cache; sparse workloads append and then
 run sparse decode over the step's position list.
 
-Default workload: 16 layers, batch 1, context 65,536, 16 query / 2 KV heads x 256, K 6-bit / V 5-bit
-body with a 2,048-token bf16 precision tail, 64 decode steps (synthetic Gaussian K/V with per-channel
-standard deviations log-uniform in [0.1, 10]).
+Default workload (the largest single-GPU one): 16 layers, batch 1, context 262,144, 16 query / 2 KV heads
+x 256, K 6-bit / V 5-bit body with a 2,048-position 8-bit (q8_0) recent-token ring, a decode step at full
+length (synthetic Gaussian K/V with 4 outlier K channels x20). --config 1..5 selects the other workloads.
 
-Prints one JSON line. `value` is the effective KV GB/s of decode attention over the whole step
-(algorithmic KV bytes read by the decode calls / step time). `roofline` is the decode kernel's rate:
-algorithmic bytes per launch / average kernel time, from HIP events that the kernel dispatches stamp
+Prints one JSON line. `value` is the effective GB/s of decode attention over the whole step (algorithmic
+bytes of the decode calls / step time; a call's algorithmic bytes are the K and V rows it attends, the KVarN
+scales, the bf16 query rows it reads and the fp32 output rows it writes). `roofline` is the decode kernel's
+rate: algorithmic bytes per launch / average kernel time, from HIP events that the kernel dispatches stamp
 with their start and end (library launch timing, measured on a second run of the same number of steps),
-against 8 TB/s HBM3E. `traffic` is the HBM bytes per launch measured with
-rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by the copy-kernel calibration stored with them),
-used only while the kernel source still matches the one that was measured. `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same workload. Also reported: `graph` (the same steps with each step's
-launches captured into one HIP graph beforehand and replayed back to back), `cold` (single-layer workloads:
-decode time after a 512 MiB write has evicted L2 and the MALL) and `copy_ceiling_gbs` (a plain 1 GiB device
-copy, bytes read + written per second). With --verify-queries T, `multi_query` times multi-query decode of the
-last T positions of every sequence (verification of T - 1 drafted tokens) over every layer.
+against 8 TB/s HBM3E. `traffic` is the HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+counters (scaled by the copy-kernel calibration stored with them), used only while the kernel source still
+matches the one that was measured. `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload, one layer per worker process over the host's cores (measured before the GPU is touched). Also
+reported: `graph` (the same steps with each step's launches captured into one HIP graph beforehand and
+replayed back to back), `cold` (single-layer workloads: decode time after a 512 MiB write has evicted L2 and
+the MALL), `copy_ceiling_gbs` (a plain 1 GiB device copy, bytes read + written per second) and
+`read_ceiling` (a plain read-only pass over 1 GiB, and over the decode call's own byte count, by the
+streaming-read probe). With --verify-queries T, `multi_query` times multi-query decode of the last T
+positions of every sequence (verification of T - 1 drafted tokens) over every layer.
 """
 from __future__ import annotations
 
@@ -57,9 +60,9 @@ def ring_row_bytes(cfg: dict) -> int:
     return 2 * cfg["head_dim"] if cfg["tail_dtype"] in (1, 3) else row_bytes(8, cfg["head_dim"])   # bf16 / f16, or q8_0
 
 
-def decode_call_bytes(cfg: dict, lens, bodies) -> int:
-    """Algorithmic KV bytes of one dense decode call: every attended body row and ring row, K and V,
-    plus the KVarN scales."""
+def decode_kv_bytes(cfg: dict, lens, bodies) -> int:
+    """Cache bytes of one dense decode call: every attended body row and ring row, K and V, plus the KVarN
+    scales of each sequence."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
     body = hk * (row_bytes(cfg["k_bits"], d) + row_bytes(cfg["v_bits"], d))
     ring = hk * 2 * ring_row_bytes(cfg)
@@ -71,10 +74,25 @@ def decode_call_bytes(cfg: dict, lens, bodies) -> int:
     return total
 
 
-def sparse_call_bytes(cfg: dict, budget: int, n_seqs: int) -> int:
-    """Algorithmic KV bytes of one sparse decode call over a body-only cache: budget K and V rows."""
+def query_out_bytes(cfg: dict, n: int) -> int:
+    """bf16 query rows read and fp32 output rows written for n query vectors."""
+    return n * cfg["n_q_heads"] * cfg["head_dim"] * (2 + 4)
+
+
+def decode_call_bytes(cfg: dict, lens, bodies) -> int:
+    """Algorithmic bytes of one dense decode call (one query per sequence)."""
+    return decode_kv_bytes(cfg, lens, bodies) + query_out_bytes(cfg, len(lens))
+
+
+def sparse_kv_bytes(cfg: dict, budget: int, n_seqs: int) -> int:
+    """Cache bytes of one sparse decode call over a body-only cache: budget K and V rows per sequence."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
     return n_seqs * budget * hk * (row_bytes(cfg["k_bits"], d) + row_bytes(cfg["v_bits"], d))
+
+
+def sparse_call_bytes(cfg: dict, budget: int, n_seqs: int) -> int:
+    """Algorithmic bytes of one sparse decode call over a body-only cache."""
+    return sparse_kv_bytes(cfg, budget, n_seqs) + query_out_bytes(cfg, n_seqs)
 
 
 SHARED_HEADERS = ("kvq_kernels.h", "kvq_mfma.h", "kvq_write.h", "kvq_format.h")
@@ -108,78 +126,171 @@ def measured_traffic(workload: str, kernel: str, src: str):
     return None
 
 
-def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
-    """The oracle (plain NumPy, fp64 attention) on layer 0 of the workload, one BLAS thread."""
+# ---------------------------------------------------------------------------------------------- CPU baseline
+
+def _blas_one_thread():
     import contextlib
     try:
         from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(limits=1)
+        return threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limit = contextlib.nullcontext()
+        return contextlib.nullcontext()
+
+
+def _oracle_dense_layer(job) -> dict:
+    """One worker of the CPU baseline: layer `layer` of a dense workload in the oracle (one BLAS thread). The
+    prefill appends are timed as the oracle's append rate; then decode steps as the GPU runs them (append one
+    token per sequence, evict, fp64 attention over the dequantized cache) until `budget_s` of step time or the
+    workload's steps are done."""
+    cfg_id, layer, budget_s = job
     import oracle
     import workloads as W
-    cfg1 = dict(wl.cache_config(), n_layers=1, max_seqs=1)
-    ctx = wl.contexts[0]
-    if wl.budget:
-        # body-only rows depend on their own token only: a cache holding just the step's listed tokens
-        # attends over the same rows as the full cache
-        t_total, nbytes, steps = 0.0, 0, 0
-        with limit:
-            while t_total < budget_s and steps < wl.decode_steps:
-                n = ctx + steps + 1
-                pos = W.sparse_positions(wl.cfg, 0, 0, steps, n, wl.budget, wl.recent)
-                k = np.zeros((wl.budget, wl.n_kv_heads, wl.head_dim), dtype=np.uint16)
-                v = np.zeros_like(k)
-                chunks = {}
-                for i, p in enumerate(pos):
-                    p = int(p)
-                    if p >= ctx:
-                        kk, vv = W.decode_token(wl.cfg, 0, 0, p - ctx)
-                        k[i], v[i] = kk[0], vv[0]
-                    else:
-                        c0 = (p // W.CHUNK) * W.CHUNK
-                        if c0 not in chunks:
-                            chunks[c0] = W.kv_tokens(wl.cfg, 0, 0, c0, min(W.CHUNK, ctx - c0))
-                        k[i], v[i] = chunks[c0][0][p - c0], chunks[c0][1][p - c0]
-                q = W.query(wl.cfg, 0, 0, steps)[None]
-                cfg_s = dict(cfg1, capacity=wl.budget)
+    wl = W.workload(cfg_id)
+    seqs = list(range(wl.batch))
+    cfg1 = dict(wl.cache_config(), n_layers=1)
+    with _blas_one_thread():
+        o = oracle.OracleCache(cfg1)
+        t_app, n_app = 0.0, 0
+        for seq, n in enumerate(wl.contexts):
+            for s0 in range(0, n, W.CHUNK):
+                k, v = W.kv_tokens(wl.cfg, layer, seq, s0, min(W.CHUNK, n - s0))
                 t0 = time.perf_counter()
-                o = oracle.OracleCache(cfg_s)
-                o.append(0, [0], [wl.budget], k, v)
-                oracle.decode_reference(o, 0, [0], q)
-                t_total += time.perf_counter() - t0
-                nbytes += sparse_call_bytes(cfg1, wl.budget, 1)
-                steps += 1
-        return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"layer 0: {steps} sparse decode steps over {wl.budget} listed positions (quantize the "
-                          f"listed tokens, fp64 attention), {t_total:.1f} s, one BLAS thread",
-                "tok_per_s_per_layer": round(steps * wl.budget / t_total, 1)}
-    log(f"cpu baseline: oracle prefill of {ctx} tokens (not timed)")
-    o = oracle.OracleCache(cfg1)
-    for s in range(0, ctx, W.CHUNK):
-        k, v = W.kv_tokens(wl.cfg, 0, 0, s, min(W.CHUNK, ctx - s))
-        o.append(0, [0], [k.shape[0]], k, v)
-    o.tail_evict(0, [0])
-    t_total, t_write, nbytes, steps = 0.0, 0.0, 0, 0
-    with limit:
-        while t_total < budget_s and steps < max(wl.decode_steps, 1):
-            q = W.query(wl.cfg, 0, 0, steps)[None]
+                o.append(0, [seq], [k.shape[0]], k, v)
+                t_app += time.perf_counter() - t0
+                n_app += k.shape[0]
+        t0 = time.perf_counter()
+        o.tail_evict(0, seqs)
+        t_app += time.perf_counter() - t0
+        t_write, t_total, nbytes, steps, attended = 0.0, 0.0, 0, 0, 0
+        while steps < max(wl.decode_steps, 1) and (steps == 0 or t_total < budget_s):
+            q = np.stack([W.query(wl.cfg, layer, s, steps) for s in seqs])
+            toks = [W.decode_token(wl.cfg, layer, s, steps) for s in seqs] if wl.decode_steps else []
             t0 = time.perf_counter()
-            if wl.decode_steps:
-                k, v = W.decode_token(wl.cfg, 0, 0, steps)
-                o.append(0, [0], [1], k, v)
-                o.tail_evict(0, [0])
-            t_write += time.perf_counter() - t0
+            if toks:
+                o.append(0, seqs, [1] * len(seqs), np.concatenate([t[0] for t in toks]),
+                         np.concatenate([t[1] for t in toks]))
+                o.tail_evict(0, seqs)
+            t1 = time.perf_counter()
+            oracle.decode_reference(o, 0, seqs, q)
+            t2 = time.perf_counter()
+            t_write += t1 - t0
+            t_total += t2 - t0
+            lens = [o.lengths(0, s) for s in seqs]
+            nbytes += decode_call_bytes(cfg1, [x[0] for x in lens], [x[1] for x in lens])
+            attended += sum(x[0] for x in lens)
+            steps += 1
+    return {"layer": layer, "steps": steps, "seconds": t_total, "write_seconds": t_write, "bytes": nbytes,
+            "attended": attended, "append_seconds": t_app, "appended": n_app}
+
+
+def _oracle_sparse_layer(job) -> dict:
+    """One worker of the CPU baseline on the sparse workload: body-only rows depend on their own token only, so
+    a cache holding just the step's listed tokens attends over the same rows as the full cache; each step
+    quantizes the listed tokens (timed as append) and runs fp64 attention over them."""
+    cfg_id, layer, budget_s = job
+    import oracle
+    import workloads as W
+    wl = W.workload(cfg_id)
+    ctx = wl.contexts[0]
+    cfg1 = dict(wl.cache_config(), n_layers=1, max_seqs=1, capacity=wl.budget)
+    t_total, t_app, nbytes, steps = 0.0, 0.0, 0, 0
+    with _blas_one_thread():
+        while steps < wl.decode_steps and (steps == 0 or t_total < budget_s):
+            n = ctx + steps + 1
+            pos = W.sparse_positions(wl.cfg, layer, 0, steps, n, wl.budget, wl.recent)
+            k = np.zeros((wl.budget, wl.n_kv_heads, wl.head_dim), dtype=np.uint16)
+            v = np.zeros_like(k)
+            chunks = {}
+            for i, p in enumerate(pos):
+                p = int(p)
+                if p >= ctx:
+                    kk, vv = W.decode_token(wl.cfg, layer, 0, p - ctx)
+                    k[i], v[i] = kk[0], vv[0]
+                else:
+                    c0 = (p // W.CHUNK) * W.CHUNK
+                    if c0 not in chunks:
+                        chunks[c0] = W.kv_tokens(wl.cfg, layer, 0, c0, min(W.CHUNK, ctx - c0))
+                    k[i], v[i] = chunks[c0][0][p - c0], chunks[c0][1][p - c0]
+            q = W.query(wl.cfg, layer, 0, steps)[None]
+            t0 = time.perf_counter()
+            o = oracle.OracleCache(cfg1)
+            o.append(0, [0], [wl.budget], k, v)
+            t1 = time.perf_counter()
             oracle.decode_reference(o, 0, [0], q)
             t_total += time.perf_counter() - t0
-            ln, bl = o.lengths(0, 0)
-            nbytes += decode_call_bytes(cfg1, [ln], [bl])
+            t_app += t1 - t0
+            nbytes += sparse_call_bytes(cfg1, wl.budget, 1)
             steps += 1
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of the workload at context {ctx}: {steps} decode steps (append 1, evict, "
-                      f"fp64 attention over the dequantized cache), {t_total:.1f} s, one BLAS thread",
-            "tok_per_s_per_layer": round(steps * (ctx + steps / 2) / t_total, 1),
-            "append_evict_ms_per_step": round(t_write * 1e3 / max(steps, 1), 3)}
+    return {"layer": layer, "steps": steps, "seconds": t_total, "write_seconds": t_app, "bytes": nbytes,
+            "attended": steps * wl.budget, "append_seconds": t_app, "appended": steps * wl.budget}
+
+
+def _single_core_cfg1(budget_s: float = 4.0) -> dict:
+    """The oracle's decode of the 4k single-layer q8_0 workload on one core (one BLAS thread)."""
+    import oracle
+    import workloads as W
+    wl = W.workload(1)
+    cfg1 = wl.cache_config()
+    with _blas_one_thread():
+        o = oracle.OracleCache(cfg1)
+        k, v = W.kv_tokens(wl.cfg, 0, 0, 0, wl.contexts[0])
+        t0 = time.perf_counter()
+        o.append(0, [0], [k.shape[0]], k, v)
+        t_app = time.perf_counter() - t0
+        q = W.query(wl.cfg, 0, 0, 0)[None]
+        t_total, calls = 0.0, 0
+        while calls == 0 or t_total < budget_s:
+            t0 = time.perf_counter()
+            oracle.decode_reference(o, 0, [0], q)
+            t_total += time.perf_counter() - t0
+            calls += 1
+    nb = decode_call_bytes(cfg1, [wl.contexts[0]], [wl.contexts[0]])
+    return {"value": round(nb * calls / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "ms_per_call": round(t_total * 1e3 / calls, 2),
+            "append_tok_per_s": round(k.shape[0] / t_app, 1),
+            "sample": f"q8_0 single layer, context 4096: {calls} decode calls (fp64 attention), one core"}
+
+
+def cpu_pool_size() -> int:
+    """Worker processes of the CPU baseline: the host's cores, at most 16 (the CPU share of one GPU on the
+    measurement boxes)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n, os.cpu_count() or 1))
+
+
+def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
+    """The oracle (plain NumPy, fp64 attention) timed on the host's cores: one worker process per layer (up to
+    the pool size), each with one BLAS thread, running the workload's decode steps on its layer for a bounded
+    time. Aggregate rate = bytes of all workers / the longest worker's step time (they run at the same time).
+    Run before the GPU is initialized (the workers are started with 'spawn')."""
+    import multiprocessing as mp
+    P = cpu_pool_size()
+    layers = list(range(min(wl.n_layers, P)))
+    fn = _oracle_sparse_layer if wl.budget else _oracle_dense_layer
+    log(f"cpu baseline: oracle on layers 0..{layers[-1]} in {len(layers)} worker processes")
+    t0 = time.time()
+    with mp.get_context("spawn").Pool(len(layers)) as pool:
+        res = pool.map(fn, [(wl.cfg, layer, budget_s) for layer in layers])
+    wall = time.time() - t0
+    longest = max(r["seconds"] for r in res)
+    nbytes = sum(r["bytes"] for r in res)
+    attended = sum(r["attended"] for r in res)
+    steps = sum(r["steps"] for r in res)
+    single = _single_core_cfg1()
+    log(f"cpu baseline done in {wall:.1f} s")
+    return {"value": round(nbytes / longest / 1e9, 4), "unit": "GB/s", "cores": len(layers), "kind": "oracle",
+            "sample": f"layers 0..{layers[-1]} of the workload, one worker process per layer with one BLAS thread "
+                      f"({len(layers)} of {os.cpu_count()} host cores): {steps} layer-steps in all "
+                      f"({'quantize the listed tokens, fp64 attention' if wl.budget else 'append 1, evict, fp64 attention over the dequantized cache'}), "
+                      f"longest worker {longest:.1f} s of step time",
+            "tok_per_s_per_layer": round(attended / longest / len(layers), 1),
+            "append_evict_ms_per_step": round(1e3 * sum(r["write_seconds"] for r in res) / max(steps, 1), 3),
+            "append_tok_per_s_per_core": round(sum(r["appended"] for r in res)
+                                               / max(sum(r["append_seconds"] for r in res), 1e-9), 1),
+            "single_core_cfg1": single}
 
 
 def graph_steps(torch, step, first: int, n: int, n_layers: int) -> float:
@@ -224,6 +335,66 @@ def copy_ceiling(torch, mib: int = 1024, reps: int = 5) -> float:
         best = min(best, e0.elapsed_time(e1) / 1e3)
     del src, dst
     return 2.0 * (mib << 20) / best / 1e9
+
+
+def read_ceiling(torch, call_bytes: int, mib: int = 1024) -> dict:
+    """Read-only streaming rate of this GPU, by the probe library (a plain pass of 16-byte loads XOR-reduced to
+    one word per work-group): the best over launch shapes of one pass over 1 GiB, and the best time of a pass over
+    `call_bytes` (the decode call's algorithmic bytes), both with the buffer cold in L2 and the 256 MB MALL (the
+    1 GiB pass exceeds them; the call-sized passes rotate over 5 regions of the buffer)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_decode_attention_append_amd", "libkvq_probe.so"))
+    lib.kvq_probe_read.restype = ctypes.c_int
+    lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = mib << 20
+    call16 = (call_bytes + 15) // 16 * 16
+    region = (call16 + 4095) // 4096 * 4096
+    buf = torch.zeros(max(nbytes, 5 * region), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(off, size, shape):
+        grid, block, unroll, nt = shape
+        rc = lib.kvq_probe_read(ctypes.c_void_p(buf.data_ptr() + off), size, ctypes.c_void_p(sink.data_ptr()),
+                                grid, block, unroll, nt, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"read probe launch failed ({rc})")
+
+    def timed(off, size, shape, reps):
+        best = float("inf")
+        for r in range(reps):
+            o = off[r % len(off)] if isinstance(off, list) else off
+            e0.record()
+            run(o, size, shape)
+            e1.record()
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 1e3)
+        return best
+
+    shapes = [(g * n_cu, b, u, nt) for g in (1, 2, 4, 8) for b in (256, 512, 1024) for u in (2, 4, 8) for nt in (0, 1)
+              if g * b <= 2048]
+    res = []
+    for sh in shapes:
+        run(0, nbytes, sh)
+        res.append((nbytes / timed(0, nbytes, sh, 3) / 1e9, sh))
+    res.sort(reverse=True)
+    offs = [i * region for i in range(5)]
+    call = []
+    for gbs, sh in res[:6]:
+        t = timed(offs, call16, sh, 10)
+        call.append((t, sh))
+    call.sort()
+    del buf, sink
+    best = res[0]
+    return {"gbs_1gib": round(best[0], 1), "shape_1gib": {"grid": best[1][0], "block": best[1][1],
+                                                          "unroll": best[1][2], "nontemporal": best[1][3]},
+            "call_bytes": int(call16), "call_us": round(call[0][0] * 1e6, 2),
+            "call_gbs": round(call16 / call[0][0] / 1e9, 1),
+            "how": "plain read-only pass (16-byte loads), best over launch shapes; the call-sized pass is timed "
+                   "with HIP events on the launch stream, cold in L2 and MALL"}
 
 
 def cold_calls(torch, cache, seqs, q, out, ws, n: int) -> dict:
@@ -273,7 +444,7 @@ def multi_query_leg(torch, cache, cfg, L, seqs, qin, n_q, reps, dev):
     ms, n = cache.timing_read(kind)
     cms, cn = cache.timing_read("combine")
     cache.timing(False)
-    unique = decode_call_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens])
+    unique = decode_kv_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens]) + query_out_bytes(cfg, B * n_q)
     k_us = ms * 1e3 / max(n, 1)
     log(f"multi-query decode, {n_q} queries per sequence: {k_us:.2f} us per {kind} launch")
     return {"queries": n_q, "ms_per_pass": round(elapsed * 1e3 / reps, 4), "kernel": kind,
@@ -288,9 +459,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="1: q8_0 4k single layer; 2: K6/V5 + bf16 tail, 64k, 16 layers (default); 3: KVarN "
-                         "K4/V4, 8 streams; 4: K6/V5 + q8_0 ring, 262k; 5: sparse q8_0, budget 2048 of 262k")
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="1: q8_0 4k single layer; 2: K6/V5 + bf16 tail, 64k, 16 layers; 3: KVarN K4/V4, 8 streams; "
+                         "4: K6/V5 + q8_0 ring, 262k, 16 layers (default: the largest single-GPU workload); "
+                         "5: sparse q8_0, budget 2048 of 262k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verify-queries", type=int, default=0,
                     help="also time multi-query decode of the last T positions per sequence (T = 1 + drafts, <= 8) "
@@ -302,11 +474,14 @@ def main() -> int:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
-    import torch
     import workloads as W
+    wl = W.workload(args.config)
+    # the CPU baseline first: its worker processes start before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+
+    import torch
     from quantized_decode_attention_append_amd import kvq
 
-    wl = W.workload(args.config)
     # warmup, timed steps, as many steps with kernel timing, then as many captured as HIP graphs
     total_steps = args.warmup + 3 * args.steps
     ctx = list(wl.contexts)
@@ -320,18 +495,30 @@ def main() -> int:
     cache = kvq.Cache(cfg)
 
     # ---- prefill (set-up, not timed): 4096-token chunks per (layer, sequence), then drain the ring to W
+    # the seeded chunks are drawn by a thread pool (numpy's generator releases the GIL), one layer ahead of the
+    # appends
+    from concurrent.futures import ThreadPoolExecutor
+    gen = ThreadPoolExecutor(max_workers=cpu_pool_size())
+
+    def submit_layer(layer):
+        return [(seq, gen.submit(W.kv_tokens, wl.cfg, layer, seq, s, min(W.CHUNK, ctx[seq] - s)))
+                for seq in range(B) for s in range(0, ctx[seq], W.CHUNK)]
+
     t0 = time.time()
+    pending = submit_layer(0)
     for layer in range(L):
-        for seq in range(B):
-            n = ctx[seq]
-            for s in range(0, n, W.CHUNK):
-                k, v = W.kv_tokens(wl.cfg, layer, seq, s, min(W.CHUNK, n - s))
-                cache.append(layer, [seq], [k.shape[0]], torch.from_numpy(k.view(np.int16)).to(dev),
-                             torch.from_numpy(v.view(np.int16)).to(dev))
+        chunks = pending
+        pending = submit_layer(layer + 1) if layer + 1 < L else []
+        for seq, fut in chunks:
+            k, v = fut.result()
+            cache.append(layer, [seq], [k.shape[0]], torch.from_numpy(k.view(np.int16)).to(dev),
+                         torch.from_numpy(v.view(np.int16)).to(dev))
+        del chunks
         cache.tail_evict(layer, list(range(B)))
         if layer % 4 == 3 or layer == L - 1:
             torch.cuda.synchronize()
             log(f"prefill layers 0..{layer} done ({time.time() - t0:.1f} s)")
+    gen.shutdown()
 
     # ---- step inputs resident in HBM before timing
     kin = np.zeros((total_steps, L, B, wl.n_kv_heads, wl.head_dim), dtype=np.uint16)
@@ -453,7 +640,7 @@ def main() -> int:
         "config": {"workload": wl.name, "layers": L, "batch": B, "context": ctx if B > 1 else ctx[0],
                    "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
                    "k_bits": wl.k_bits, "v_bits": wl.v_bits, "kvarn": wl.kvarn, "tail": wl.tail_len,
-                   "tail_dtype": ["none", "bf16", "q8_0"][wl.tail_dtype], "budget": wl.budget,
+                   "tail_dtype": ["none", "bf16", "q8_0", "f16"][wl.tail_dtype], "budget": wl.budget,
                    "layout": ["tiles", "rows"][cfg.get("layout", 0)],
                    "step": ("per layer: append 1 token, sparse decode over the step's position list (one call)" if sparse
                             else "per layer: append 1 token, evict 1 tail token, decode attention (one call)"
@@ -476,8 +663,10 @@ def main() -> int:
     if cold is not None:
         res["cold"] = cold
     res["copy_ceiling_gbs"] = round(copy_ceiling(torch), 1)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl)
+    if not sparse:
+        res["read_ceiling"] = read_ceiling(torch, int(bytes_per_launch))
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
     return 0
 

@@ -184,8 +184,9 @@ kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
  * (0 <= t < T) of sequence i sits at position len - T + t and attends causally to positions
  * [0, len - T + t]: out[i][t][h][:] as kvq_decode_attn over that prefix (body rows before body_len, ring rows
  * after). q_bf16: device bf16 [n_seqs][T][Hq][D]; out: device fp32 [n_seqs][T][Hq][D]; workspace:
- * kvq_workspace_bytes(cache, n_seqs * T, max len) bytes. The cache is not changed: dropping rejected drafts
- * is the caller's (a cache without them is rebuilt by appending the accepted tokens). Each (sequence, query)
+ * kvq_workspace_bytes(cache, n_seqs * T, max len) bytes. The cache is not changed; rejected drafts are
+ * dropped afterwards with kvq_seq_truncate, which requires them to still be ring rows: tail_len >= T - 1, and
+ * any kvq_tail_evict (or fused step) comes after the verification, not before it. Each (sequence, query)
  * pair runs as one entry of the dense decode launch (of the gather launch for KVQ_LAYOUT_ROWS) over the
  * same cache rows.
  * Errors: KVQ_E_INVALID if T is outside [1, KVQ_MAX_QUERIES] or n_seqs * T > KVQ_MAX_BATCH; KVQ_E_STATE if

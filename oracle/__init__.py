@@ -23,7 +23,10 @@ What it computes, and where the pages fix it (pages cited by title and passage):
 * ``attention`` - exact softmax attention over the dequantized values in fp64,
                   dense over all positions and sparse over an indexer budget of
                   positions (offload page, QSA paragraph).
-* ``sizes``     - algorithmic bytes read per decode call.
+* ``indexer``   - the QSA indexer: pooled index keys, their scores against an
+                  index query and the choice of a budget of positions (offload
+                  page, QSA paragraph).
+* ``sizes``     - algorithmic bytes of a decode call (rows read, query read, output written).
 
 Where the pages are silent the functions state the reading they take. The quantizer emulates fp32 arithmetic exactly (numpy
 float32 operations are IEEE round-to-nearest-even, with no contraction), and
@@ -34,5 +37,7 @@ from .layout import (planes, cache_bytes, slab_layout, pack_k_rows, pack_v_tiles
                      pack_bf16_v_tiles, unpack_k_rows, unpack_v_tiles, pack_k_tiles, unpack_k_tiles,
                      pack_bf16_k_tiles, unpack_bf16_k_tiles)
 from .cache import OracleCache  # noqa: F401
+from . import indexer  # noqa: F401
 from .attention import attend, decode_reference, sparse_reference, multi_query_reference  # noqa: F401
-from .sizes import decode_bytes, sparse_bytes, row_bytes  # noqa: F401
+from .sizes import (decode_bytes, decode_kv_bytes, query_out_bytes, sparse_bytes, sparse_kv_bytes,  # noqa: F401
+                    row_bytes, kv_token_bytes, ring_token_bytes)

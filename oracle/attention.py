@@ -84,7 +84,8 @@ def multi_query_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, scale=
         n, _ = cache.lengths(layer, sid)
         if n < n_q:
             raise ValueError(f"sequence {sid} holds {n} positions, fewer than {n_q} queries")
+        k, v = cache.dequantized(layer, sid)              # positions 0 .. n-1
         for t in range(n_q):
-            k, v = cache.dequantized(layer, sid, np.arange(n - n_q + t + 1))
-            out[i, t] = attend(_q64(q_bits[i, t]), k, v, sc)
+            end = n - n_q + t + 1                         # query t attends to positions [0, end)
+            out[i, t] = attend(_q64(q_bits[i, t]), k[:end], v[:end], sc)
     return out

@@ -33,6 +33,7 @@ import numpy as np
 from .layout import (pack_k_rows, pack_k_tiles, pack_bf16_k_tiles, pack_v_tiles, pack_bf16_v_tiles,
                      slab_layout, TILE)
 from .quant import quantize_blocks, kvarn_sigma, normalize, dequantize_blocks
+from . import indexer
 
 TAIL_NONE, TAIL_BF16, TAIL_Q8, TAIL_F16 = 0, 1, 2, 3
 _TAIL_16 = (TAIL_BF16, TAIL_F16)   # rings of 16-bit values
@@ -65,6 +66,8 @@ class _SeqState:
         self.kd = np.zeros((cap32, hk, nb), dtype=np.float16)
         self.vu = np.zeros((cap32, hk, d), dtype=np.uint8)
         self.vd = np.zeros((cap32, hk, nb), dtype=np.float16)
+        if cfg.get("index_dim", 0):
+            self.ikey = np.zeros((cap32, indexer.POOLED), dtype=np.uint16)   # pooled index keys, bf16 bits
         r = lay["ring_slots"]
         if cfg["tail_len"] > 0 and cfg["tail_dtype"] in _TAIL_16:
             self.rk = np.zeros((r, hk, d), dtype=np.uint16)
@@ -208,6 +211,31 @@ class OracleCache:
                 raise ValueError(f"truncate to {n} outside [body_len {s.body_len}, len {s.len}]")
             s.len = int(n)
 
+    # ------------------------------------------------------------------ the indexer (offload page, QSA)
+    def index_write(self, layer: int, seq_ids, n_new, key_bits: np.ndarray):
+        """Pool and store the indexer keys of the newest n_new[i] positions of each sequence (already appended):
+        key_bits bf16 [sum(n_new), index_dim], sequences in order."""
+        ratio = self.cfg["index_pool"]
+        off = 0
+        for sid, n in zip(seq_ids, n_new):
+            n = int(n)
+            s = self.st(layer, sid)
+            if n > s.len:
+                raise ValueError(f"sequence {sid} holds {s.len} positions, fewer than {n} keys")
+            if n:
+                s.ikey[s.len - n:s.len] = indexer.pool_keys(key_bits[off:off + n], ratio)
+            off += n
+
+    def index_select(self, layer: int, seq_ids, query_bits: np.ndarray, budget: int, n_recent: int = 0):
+        """Positions chosen by the indexer for each sequence: int32 [n_seqs, budget] (ascending, -1 padded)."""
+        out = []
+        for i, sid in enumerate(seq_ids):
+            s = self.st(layer, sid)
+            m = max(s.len - n_recent, 0)
+            sc = indexer.scores(query_bits[i], s.ikey[:m])
+            out.append(indexer.select(sc, s.len, budget, n_recent))
+        return np.stack(out)
+
     # ------------------------------------------------------------------ reading
     def lengths(self, layer: int, seq: int):
         s = self.st(layer, seq)
@@ -281,6 +309,8 @@ class OracleCache:
             return pack_v_tiles(u, d, 8)
         if region == "sigma":
             return np.ascontiguousarray(s.sigma[head]).view(np.uint8).reshape(-1)
+        if region == "index":
+            return np.ascontiguousarray(s.ikey[lo:hi]).view(np.uint8).reshape(-1)
         raise ValueError(region)
 
     def slab_image(self, layer: int, seq: int) -> np.ndarray:
@@ -301,4 +331,7 @@ class OracleCache:
             per = size // hk
             for h in range(hk):
                 img[off + h * per: off + (h + 1) * per] = self.region_bytes(layer, seq, "sigma", h, 0, 0)
+        off, size = lay["index"]
+        if size:
+            img[off:off + size] = self.region_bytes(layer, seq, "index", 0, 0, cap32)
         return img

@@ -50,7 +50,9 @@ one V row. The region sizes equal those of the tile layout.
 Arena: slabs of [layer][sequence]; each slab holds, in order and 256-byte
 aligned: K body [head][capacity32/32][tile], V body [head][capacity32/32][tile],
 K ring [head][R/32][tile], V ring [head][R/32][tile] (row layout: [head][.][row]
-for K, and for V as well), KVarN sigma [head][K,V][D] fp16.
+for K, and for V as well), KVarN sigma [head][K,V][D] fp16, and (when the cache
+carries an indexer) the pooled index keys [capacity32][32] bf16, 64 bytes per
+position (offload page: 1 x (128 / 4) x 2 bytes per token and layer).
 capacity32 is the capacity rounded up to 32; R = W + S (ring slots).
 """
 from __future__ import annotations
@@ -330,10 +332,11 @@ def slab_layout(cfg: dict) -> dict:
         "k_ring": hk * r * ring_rk,
         "v_ring": hk * r * ring_rv,
         "sigma": hk * 2 * d * 2 if cfg["kvarn"] else 0,
+        "index": cap32 * 64 if cfg.get("index_dim", 0) else 0,
     }
     off = 0
     lay = {}
-    for name in ("k_body", "v_body", "k_ring", "v_ring", "sigma"):
+    for name in ("k_body", "v_body", "k_ring", "v_ring", "sigma", "index"):
         off = _round_up(off, 256)
         lay[name] = (off, sizes[name])
         off += sizes[name]

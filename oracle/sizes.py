@@ -3,7 +3,14 @@
 The offload page counts the bytes a step reads: a bf16 QSA row is 2 KV heads x
 256 x (K and V) x 2 bytes = 2,048 bytes per token per layer, so a budget of 2,048
 positions reads 4 MiB per layer (offload page, byte arithmetic and QSA paragraph).
-The same count applies to a quantized cache with the row size of its format.
+The same count applies to a quantized cache with the row size of its format
+(BeeLlama.cpp v0.4.1 page, KV MiB column: N bits per value plus one fp16 scale per
+32 values).
+
+A call's algorithmic bytes are the rows it must read (every attended position's K
+and V row of each KV head, from the body or the ring), the KVarN scales of each
+sequence, the bf16 query rows it reads and the fp32 output rows it writes; the
+split partials and any repeated read are not counted.
 """
 from __future__ import annotations
 
@@ -16,6 +23,7 @@ def kv_token_bytes(n_bits_k: int, n_bits_v: int, n_kv_heads: int, head_dim: int)
 
 
 def ring_token_bytes(tail_dtype: int, n_kv_heads: int, head_dim: int) -> int:
+    """Bytes of one ring token in one layer: bf16 or f16 values (tail dtypes 1 and 3), or q8_0 rows (2)."""
     if tail_dtype in (1, 3):   # bf16 or f16 values: 2 bytes each
         return n_kv_heads * 2 * head_dim * 2
     if tail_dtype == 2:
@@ -23,11 +31,11 @@ def ring_token_bytes(tail_dtype: int, n_kv_heads: int, head_dim: int) -> int:
     return 0
 
 
-def decode_bytes(cfg: dict, lengths, body_lengths) -> int:
-    """KV bytes one dense decode call reads: body rows + ring rows (+ KVarN sigma)."""
+def decode_kv_bytes(cfg: dict, lengths, body_lengths) -> int:
+    """Cache bytes one dense decode call reads: body rows + ring rows (+ the KVarN scales per sequence)."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
     body = kv_token_bytes(cfg["k_bits"], cfg["v_bits"], hk, d)
-    ring = ring_token_bytes(cfg["tail_dtype"], hk, d)
+    ring = ring_token_bytes(cfg["tail_dtype"] if cfg["tail_len"] > 0 else 0, hk, d)
     total = 0
     for ln, bl in zip(lengths, body_lengths):
         total += bl * body + (ln - bl) * ring
@@ -36,10 +44,26 @@ def decode_bytes(cfg: dict, lengths, body_lengths) -> int:
     return total
 
 
-def sparse_bytes(cfg: dict, n_body: int, n_ring: int) -> int:
+def query_out_bytes(cfg: dict, n_queries: int) -> int:
+    """bf16 query rows read and fp32 output rows written by a call over n_queries query vectors."""
+    return n_queries * cfg["n_q_heads"] * cfg["head_dim"] * (2 + 4)
+
+
+def decode_bytes(cfg: dict, lengths, body_lengths) -> int:
+    """Algorithmic bytes of one dense decode call (one query per sequence)."""
+    return decode_kv_bytes(cfg, lengths, body_lengths) + query_out_bytes(cfg, len(lengths))
+
+
+def sparse_kv_bytes(cfg: dict, n_body: int, n_ring: int) -> int:
+    """Cache bytes of a sparse read of n_body body positions and n_ring ring positions."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
     return (n_body * kv_token_bytes(cfg["k_bits"], cfg["v_bits"], hk, d)
-            + n_ring * ring_token_bytes(cfg["tail_dtype"], hk, d))
+            + n_ring * ring_token_bytes(cfg["tail_dtype"] if cfg.get("tail_len", 0) > 0 else 0, hk, d))
+
+
+def sparse_bytes(cfg: dict, n_body: int, n_ring: int) -> int:
+    """Cache bytes of a sparse read (kept as the name the pins use)."""
+    return sparse_kv_bytes(cfg, n_body, n_ring)
 
 
 def bf16_token_bytes(n_kv_heads: int, head_dim: int) -> int:

@@ -1,4 +1,5 @@
-"""Build libkvq.so (the HIP library behind include/kvq.h) in-tree for gfx950.
+"""Build libkvq.so (the HIP library behind include/kvq.h) in-tree for gfx950, and libkvq_probe.so (the
+streaming-read probe the benchmark measures the HBM read ceiling with; not part of the cache's ABI).
 
 Each translation unit is compiled by hipcc in parallel, then linked into a shared library that sits
 next to this file. Flags:
@@ -17,6 +18,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 BUILD = os.path.join(HERE, "_build")
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -29,6 +31,7 @@ UNITS = [
     ("kvq_decode.hip", ["-ffp-contract=fast"]),
     ("kvq_gather.hip", ["-ffp-contract=fast"]),
 ]
+PROBE_UNITS = [("kvq_probe.hip", [])]
 
 
 def _hipcc() -> str:
@@ -47,18 +50,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(UNITS)) as ex:
-        objs = list(ex.map(lambda u: _compile(*u), UNITS))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    units = UNITS + PROBE_UNITS
+    with cf.ThreadPoolExecutor(max_workers=len(units)) as ex:
+        objs = list(ex.map(lambda u: _compile(*u), units))
+    _link(objs[:len(UNITS)], LIB)
+    _link(objs[len(UNITS):], PROBE_LIB)
     if verbose:
-        print(f"[kvq] built {LIB}", file=sys.stderr)
+        print(f"[kvq] built {LIB} and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 

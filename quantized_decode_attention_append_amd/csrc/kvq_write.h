@@ -3,8 +3,10 @@
 // of a fused decode step. Quantization follows the symmetric qN_0 block format of the BeeLlama page (32
 // values, one fp16 scale, no offset): d = amax / qmax in IEEE fp32, fp16 round-to-nearest-even saturating at
 // 65504, codes rne(x / d16) clamped to [-qmax, qmax], stored biased by 2^(N-1). Every file that includes this
-// is built with correctly rounded fp32 division, and the code below has no product that could be fused with
-// an addition, so the codes are bit-identical to a plain IEEE evaluation.
+// is built with correctly rounded fp32 division, and every function below that does floating-point arithmetic
+// turns contraction off for its own body (#pragma clang fp contract(off)), whatever the including file's
+// -ffp-contract: no product is ever fused with an addition, so the codes are bit-identical to a plain IEEE
+// evaluation in the kernels of the fused steps as well.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +41,7 @@ __device__ inline float block_amax(float v) {
 // Quantize one value of a block (all 32 lanes of the block call this together). Returns the biased code;
 // *d16_bits receives the block's fp16 scale.
 __device__ inline uint32_t quant_lane(float x, int n_bits, uint16_t* d16_bits) {
+#pragma clang fp contract(off)
   const float amax = block_amax(fabsf(x));
   const float qmax = (float)((1 << (n_bits - 1)) - 1);
   float d = amax / qmax;                        // correctly rounded (see build flags)
@@ -58,6 +61,7 @@ __device__ inline uint32_t quant_lane(float x, int n_bits, uint16_t* d16_bits) {
 
 // fp32 ring representation r(x) of one value: the bf16 value itself, its f16 rounding, or its q8_0 round trip.
 __device__ inline float ring_rep(float x, int tail_dtype) {
+#pragma clang fp contract(off)
   if (tail_dtype == 3) return (float)(_Float16)x;
   if (tail_dtype != 2) return x;
   uint16_t d;
@@ -67,6 +71,7 @@ __device__ inline float ring_rep(float x, int tail_dtype) {
 
 // Value of channel c of position p (kv: 0 K, 1 V) read back from the ring, as fp32.
 __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int kv, int head, int p, int c) {
+#pragma clang fp contract(off)
   const int D = g.head_dim;
   const int NB = D / kBlock;
   const int NT = D / 16;
@@ -158,6 +163,7 @@ constexpr int kDirectPositions = 4;
 // (the kernel argument itself, so that the item list is read in place).
 template <class A>
 __device__ inline void body_write_wg(const A& a, int wg, int head) {
+#pragma clang fp contract(off)
   __shared__ uint8_t codes[2][kTile][256];     // [K,V][tile position][channel]
   const Geometry& g = a.g;
   int it = 0;

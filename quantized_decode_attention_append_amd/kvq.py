@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_E_INVALID, KVQ_E_CAPACITY, KVQ_E_SIZE, KVQ_E_HIP, KVQ_E_STATE = 0, -1, -2, -3, -4, -5
 KVQ_MAX_BATCH, KVQ_MAX_QUERIES = 64, 8
-TAIL_NONE, TAIL_BF16, TAIL_Q8_0 = 0, 1, 2
+TAIL_NONE, TAIL_BF16, TAIL_Q8_0, TAIL_F16 = 0, 1, 2, 3
 LAYOUT_TILES, LAYOUT_ROWS = 0, 1
 REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab": 5}
 MAX_BATCH = 64

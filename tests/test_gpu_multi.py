@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads as W
 from tests.gpu_util import Pair, TOL, dev, max_err
 from workloads import small_tokens, small_query
 
@@ -155,3 +156,59 @@ def test_truncate_errors_leave_the_cache_unchanged():
             p.gpu.seq_truncate(0, [0, 1], new)
         assert e.value.status == status
         assert [p.gpu.lengths(0, s) for s in (0, 1)] == before
+
+
+def _drafts(wl, layer, seq, n_q):
+    """n_q decode-step tokens of a workload, appended as one chunk (the token being verified and its drafts)."""
+    ks, vs = zip(*[W.decode_token(wl.cfg, layer, seq, st) for st in range(n_q)])
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def _workload_queries(wl, layer, n_seqs, n_q):
+    return np.stack([np.stack([W.query(wl.cfg, layer, s, st) for st in range(n_q)]) for s in range(n_seqs)])
+
+
+def test_multi_query_at_the_64k_workload_size():
+    """T = 8 over layer 0 of the K6/V5 + bf16 tail workload at 65,536 positions, the size bench.py
+    --config 2 --verify-queries 8 times."""
+    from tests.test_gpu_fullsize import prefill_all
+    wl = W.workload(2)
+    p = Pair(dict(wl.cache_config(), n_layers=1))
+    prefill_all(p, wl, 0)
+    k, v = _drafts(wl, 0, 0, 8)
+    p.append(0, [0], [8], k, v)
+    got, want = run_multi(p, 0, [0], _workload_queries(wl, 0, 1, 8))
+    assert max_err(got, want) <= TOL, max_err(got, want)
+
+
+def test_multi_query_64_entries_at_the_eight_stream_workload_size():
+    """8 streams x 8 queries (64 entries: ring segments planned outside the per-head budget) over layer 0 of the
+    KVarN K4/V4 + bf16 tail workload at its full contexts (16k-64k), the size bench.py --config 3
+    --verify-queries 8 times."""
+    from tests.test_gpu_fullsize import prefill_all
+    wl = W.workload(3)
+    p = Pair(dict(wl.cache_config(), n_layers=1))
+    prefill_all(p, wl, 0)
+    seqs = list(range(wl.batch))
+    for s in seqs:
+        k, v = _drafts(wl, 0, s, 8)
+        p.append(0, [s], [8], k, v)
+    got, want = run_multi(p, 0, seqs, _workload_queries(wl, 0, wl.batch, 8))
+    assert max_err(got, want) <= TOL, max_err(got, want)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_multi_query_64_entries_with_bodies_of_thousands(layout):
+    """8 sequences x 8 queries with bodies of 2k-8k positions, KVarN K4/V4 and a 1,024-position bf16 tail: the
+    plan that gives the ring segments work-groups outside the per-head budget, with long body segments."""
+    p = Pair(cfg(n_layers=1, max_seqs=8, capacity=8192 + 64, layout=layout, kvarn=1, k_bits=4, v_bits=4,
+                 tail_len=1024, tail_slack=512, tail_dtype=1))
+    rng = np.random.default_rng(31 + layout)
+    lens = [int(x) for x in rng.integers(2048, 8192, size=8)]
+    k, v = small_tokens(32 + layout, sum(lens) + 64, 2, 256,
+                        scale=np.abs(np.random.default_rng(33).standard_t(3, size=(2, 2, 256))) + 0.05)
+    p.append(0, list(range(8)), lens, k[:sum(lens)], v[:sum(lens)])
+    p.evict(0, list(range(8)))
+    p.append(0, list(range(8)), [8] * 8, k[sum(lens):], v[sum(lens):])
+    got, want = run_multi(p, 0, list(range(8)), mq(34 + layout, 8, 8))
+    assert max_err(got, want) <= TOL, max_err(got, want)
