@@ -167,6 +167,19 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
                            const void* q_bf16, float* out, float softmax_scale, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* kvq_decode_attn without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The split partials go to the
+ * library's static scratch: 16 MiB of device memory per GPU, held from the first kvq_cache_init on that GPU
+ * until the process ends; results are those of kvq_decode_attn. Every call on one GPU uses the same scratch,
+ * so calls that may overlap on one GPU (other streams, other threads, other caches) race and must be
+ * serialized by the caller; the scratch needs no initial contents (each call writes every partial it reads).
+ * Arguments and errors as kvq_decode_attn; KVQ_E_SIZE if the call's partials exceed the scratch: they take
+ * n_seqs x n_kv_heads x (the most splits planned for one of the sequences) records of 8 x (head_dim + 2) fp32,
+ * at most 2,032 records at head_dim 256 (one sequence of any length fits; a call for which
+ * kvq_workspace_bytes(cache, n_seqs, max len) <= 16 MiB always fits). */
+kvq_status kvq_decode_attn_noalloc(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                   const void* q_bf16, float* out, float softmax_scale, void* stream);
+
 /* One decode step of every listed sequence: append one token each (k_bf16, v_bf16: device bf16
  * [n_seqs][Hkv][D]) and requantize the ring rows that leave the window, then dense decode attention, with
  * the results of kvq_append_evict (n_new = 1 each) followed by kvq_decode_attn. With the tile layout and a

@@ -30,6 +30,7 @@ UNITS = [
     ("kvq_append.hip", ["-ffp-contract=off"]),
     ("kvq_decode.hip", ["-ffp-contract=fast"]),
     ("kvq_gather.hip", ["-ffp-contract=fast"]),
+    ("kvq_scratch.hip", ["-ffp-contract=off"]),
 ]
 PROBE_UNITS = [("kvq_probe.hip", [])]
 

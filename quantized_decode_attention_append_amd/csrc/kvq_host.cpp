@@ -32,6 +32,7 @@ struct kvq_cache {
   std::vector<int32_t> len, body_len;
   std::vector<uint8_t> calibrated;
   int n_cu = 256;            // compute units of the device (split planning)
+  int device = 0;            // device current at kvq_cache_init (the arena's device)
   int idx(int layer, int seq) const { return layer * cfg.max_seqs + seq; }
   ~kvq_cache() {
     for (auto& t : times) {
@@ -425,6 +426,12 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* dev_arena, size_t arena_b
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
     c->n_cu = ncu;
+  c->device = dev;
+  {   // set-up of the static scratch on this device (kvq_decode_attn_noalloc); a failure here is reported by
+      // that entry point, which looks the address up again
+    void* p = nullptr;
+    (void)kvq::scratch_device_ptr(dev, &p);
+  }
   hipError_t e = kvq::launch_fill_zero(dev_arena, need, (hipStream_t)stream);
   if (e != hipSuccess) {
     delete c;
@@ -751,6 +758,27 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
     if (len[i] < 1) return fail(KVQ_E_STATE, "seq %d of layer %d is empty", seq_ids[i], layer);
   }
   return run_decode(c, layer, n_seqs, seq_ids, len, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
+}
+
+kvq_status kvq_decode_attn_noalloc(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                   const void* q_bf16, float* out, float softmax_scale, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (!q_bf16 || !out) return fail(KVQ_E_INVALID, "q/out is NULL");
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
+  int len[KVQ_MAX_BATCH];
+  for (int i = 0; i < n_seqs; ++i) {
+    len[i] = c->len[c->idx(layer, seq_ids[i])];
+    if (len[i] < 1) return fail(KVQ_E_STATE, "seq %d of layer %d is empty", seq_ids[i], layer);
+  }
+  void* scratch = nullptr;
+  const hipError_t e = kvq::scratch_device_ptr(c->device, &scratch);
+  if (e != hipSuccess) return hip_fail(e, "address of the static scratch");
+  s = run_decode(c, layer, n_seqs, seq_ids, len, q_bf16, out, softmax_scale, scratch, kvq::kScratchBytes, stream);
+  if (s == KVQ_E_SIZE)
+    return fail(KVQ_E_SIZE, "kvq_decode_attn_noalloc: the call's split partials exceed the static scratch of %zu bytes "
+                "(%s); use kvq_decode_attn with a workspace", kvq::kScratchBytes, g_err.c_str());
+  return s;
 }
 
 kvq_status kvq_decode_attn_multi(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,

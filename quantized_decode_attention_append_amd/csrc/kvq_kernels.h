@@ -154,6 +154,12 @@ hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s, hipEven
                          hipEvent_t e1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
+// The library's static scratch buffer (kvq_scratch.hip): kScratchBytes of device memory per GPU, for the
+// entry points that take no workspace. scratch_device_ptr returns its device address on `device` (looked up
+// once per device with that device current; later calls return the stored address).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_device_ptr(int device, void** ptr);
+
 // Plain or timed launch of a kernel with one by-value argument block.
 template <typename K, typename A>
 inline hipError_t launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const A& a) {

@@ -27,7 +27,7 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_truncate", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
 KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5}
 
 
@@ -63,6 +63,7 @@ def _load() -> ctypes.CDLL:
         "kvq_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, F, P, SZ, P]),
         "kvq_tail_evict": (I32, [P, I32, I32, IP, P]),
         "kvq_decode_attn": (I32, [P, I32, I32, IP, P, P, F, P, SZ, P]),
+        "kvq_decode_attn_noalloc": (I32, [P, I32, I32, IP, P, P, F, P]),
         "kvq_decode_attn_multi": (I32, [P, I32, I32, IP, I32, P, P, F, P, SZ, P]),
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
         "kvq_sparse_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, I32, P, F, P, SZ, P]),
@@ -233,6 +234,20 @@ class Cache:
                                     _dev(out, torch.float32, "out"), float(softmax_scale),
                                     _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                     ctypes.c_void_p(_stream(stream))))
+        return out
+
+    def decode_attn_noalloc(self, layer: int, seq_ids: Sequence[int], q: torch.Tensor, out: torch.Tensor,
+                            softmax_scale: float = 0.0, stream=None):
+        """decode_attn() with the split partials in the library's static scratch (no workspace): for callers that
+        cannot allocate. out must be given (fp32 [n_seqs, Hq, D]); calls on one GPU must not overlap."""
+        n = len(seq_ids)
+        if q.numel() != n * self.hq * self.d or q.element_size() != 2:
+            raise ValueError("q must be bf16 [n_seqs, Hq, D]")
+        if out.numel() != n * self.hq * self.d:
+            raise ValueError("out must be fp32 [n_seqs, Hq, D]")
+        _check(_lib.kvq_decode_attn_noalloc(self._h, layer, n, _ids(seq_ids), _dev(q, q.dtype, "q"),
+                                            _dev(out, torch.float32, "out"), float(softmax_scale),
+                                            ctypes.c_void_p(_stream(stream))))
         return out
 
     def decode_attn_multi(self, layer: int, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
