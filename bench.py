@@ -454,6 +454,67 @@ def multi_query_leg(torch, cache, cfg, L, seqs, qin, n_q, reps, dev):
             "frac": round(unique / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def indexer_leg(torch, cache, cfg, wl, L, seqs, first_step, n_steps, ws, dev):
+    """Sparse steps whose positions the QSA indexer chooses: per layer, append one token, write its index key,
+    choose the budget (the `recent` newest forced, the rest by score) and run sparse decode over the choice.
+    Reports the step time and the indexer's and the gather kernel's dispatch-stamped times."""
+    import workloads as W
+    B = len(seqs)
+    steps = list(range(first_step, first_step + 2 * n_steps))
+    kin, vin, ikin, iq, qin = {}, {}, {}, {}, {}
+    for st in steps:
+        for layer in range(L):
+            ks, vs, iks, iqs, qs = [], [], [], [], []
+            for s in seqs:
+                k, v = W.decode_token(wl.cfg, layer, s, st)
+                ks.append(k)
+                vs.append(v)
+                iks.append(W.index_keys(wl.cfg, layer, s, 0, 1, chunk_id=W.DECODE_BASE + st))
+                iqs.append(W.index_query(wl.cfg, layer, s, st))
+                qs.append(W.query(wl.cfg, layer, s, st))
+            key = (st, layer)
+            kin[key] = torch.from_numpy(np.concatenate(ks).view(np.int16)).to(dev)
+            vin[key] = torch.from_numpy(np.concatenate(vs).view(np.int16)).to(dev)
+            ikin[key] = torch.from_numpy(np.concatenate(iks).view(np.int16)).to(dev)
+            iq[key] = torch.from_numpy(np.stack(iqs).view(np.int16)).to(dev)
+            qin[key] = torch.from_numpy(np.stack(qs).view(np.int16)).to(dev)
+    max_len = max(cache.lengths(0, s)[0] for s in seqs) + len(steps) + 1
+    iws = torch.empty(max(cache.index_workspace_bytes(B, max_len), 256), dtype=torch.uint8, device=dev)
+    pos = torch.empty((L, B, wl.budget), dtype=torch.int32, device=dev)
+    out = torch.empty((L, B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    ones = [1] * B
+
+    def step(st):
+        for layer in range(L):
+            key = (st, layer)
+            cache.append(layer, seqs, ones, kin[key], vin[key])
+            cache.index_write(layer, seqs, ones, ikin[key])
+            cache.index_select(layer, seqs, iq[key], wl.budget, wl.recent, out=pos[layer], workspace=iws)
+            cache.sparse_decode_attn(layer, seqs, qin[key], pos[layer], out=out[layer], workspace=ws)
+
+    step(steps[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in steps[1:n_steps]:
+        step(st)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(n_steps - 1, 1)
+    cache.timing(True)
+    for st in steps[n_steps:]:
+        step(st)
+    torch.cuda.synchronize()
+    t = {k: cache.timing_read(k) for k in ("index", "gather", "combine", "append")}
+    cache.timing(False)
+    us = {k: round(v[0] * 1e3 / v[1], 3) for k, v in t.items() if v[1]}
+    log(f"indexer steps: {dt * 1e3:.4f} ms per step")
+    index_bytes = sum(cache.lengths(0, s)[0] for s in seqs) * 64
+    return {"ms_per_step": round(dt * 1e3, 4), "kernel_us": us, "launches": {k: v[1] for k, v in t.items() if v[1]},
+            "index_key_bytes_per_layer": int(index_bytes),
+            "how": f"per layer: append 1 token, write its pooled index key, index select {wl.budget} positions "
+                   f"({wl.recent} newest forced), sparse decode over them; 'index' spans the select's scoring and "
+                   f"picking launches, 'append' covers the row and index key writes"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +528,10 @@ def main() -> int:
     ap.add_argument("--verify-queries", type=int, default=0,
                     help="also time multi-query decode of the last T positions per sequence (T = 1 + drafts, <= 8) "
                          "on dense workloads, reported as the line's multi_query object")
+    ap.add_argument("--indexer", action="store_true",
+                    help="sparse workload: also time steps whose positions the QSA indexer chooses (append, index key "
+                         "write, index select of the budget with the newest `recent` forced, sparse decode), reported "
+                         "as the line's indexer object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
@@ -485,7 +550,11 @@ def main() -> int:
     # warmup, timed steps, as many steps with kernel timing, then as many captured as HIP graphs
     total_steps = args.warmup + 3 * args.steps
     ctx = list(wl.contexts)
-    cfg = wl.cache_config(capacity=((max(ctx) + total_steps + 8 + 31) // 32) * 32)
+    use_index = bool(args.indexer and wl.budget)
+    index_steps = args.steps if use_index else 0
+    cfg = wl.cache_config(capacity=((max(ctx) + total_steps + 2 * index_steps + 8 + 31) // 32) * 32)
+    if use_index:   # offload page: indexer_head_dim 128, compress ratio 4
+        cfg.update(index_dim=128, index_pool=4)
     L, B = wl.n_layers, wl.batch
     sparse = wl.budget > 0
     appends = wl.decode_steps > 0
@@ -500,9 +569,13 @@ def main() -> int:
     from concurrent.futures import ThreadPoolExecutor
     gen = ThreadPoolExecutor(max_workers=cpu_pool_size())
 
+    def chunk(layer, seq, s):
+        n = min(W.CHUNK, ctx[seq] - s)
+        k, v = W.kv_tokens(wl.cfg, layer, seq, s, n)
+        return k, v, (W.index_keys(wl.cfg, layer, seq, s, n) if use_index else None)
+
     def submit_layer(layer):
-        return [(seq, gen.submit(W.kv_tokens, wl.cfg, layer, seq, s, min(W.CHUNK, ctx[seq] - s)))
-                for seq in range(B) for s in range(0, ctx[seq], W.CHUNK)]
+        return [(seq, gen.submit(chunk, layer, seq, s)) for seq in range(B) for s in range(0, ctx[seq], W.CHUNK)]
 
     t0 = time.time()
     pending = submit_layer(0)
@@ -510,9 +583,11 @@ def main() -> int:
         chunks = pending
         pending = submit_layer(layer + 1) if layer + 1 < L else []
         for seq, fut in chunks:
-            k, v = fut.result()
+            k, v, ik = fut.result()
             cache.append(layer, [seq], [k.shape[0]], torch.from_numpy(k.view(np.int16)).to(dev),
                          torch.from_numpy(v.view(np.int16)).to(dev))
+            if ik is not None:
+                cache.index_write(layer, [seq], [k.shape[0]], torch.from_numpy(ik.view(np.int16)).to(dev))
         del chunks
         cache.tail_evict(layer, list(range(B)))
         if layer % 4 == 3 or layer == L - 1:
@@ -609,6 +684,7 @@ def main() -> int:
     graph = graph_steps(torch, step, args.warmup + 2 * args.steps, args.steps, L)
     cold = cold_calls(torch, cache, seqs, qin_d[0, 0], out[0], ws, args.steps) if (L == 1 and not appends) else None
 
+    indexed = indexer_leg(torch, cache, cfg, wl, L, seqs, total_steps, index_steps, ws, dev) if use_index else None
     multi = None
     if args.verify_queries and not sparse:
         multi = multi_query_leg(torch, cache, cfg, L, seqs, qin, args.verify_queries, args.steps, dev)
@@ -656,6 +732,8 @@ def main() -> int:
     }
     if multi is not None:
         res["multi_query"] = multi
+    if indexed is not None:
+        res["indexer"] = indexed
     gbytes = float(sum(nbytes)) / args.steps   # the graph steps read the same bytes per step (to a few rows)
     res["graph"] = {"ms_per_step": round(graph * 1e3, 4), "value": round(gbytes / graph / 1e9, 2), "unit": "GB/s",
                     "how": f"one HIP graph per step ({L} layers), all {args.steps} captured before timing, "

@@ -75,13 +75,16 @@ typedef struct {
   int32_t tail_slack;   /* S: extra ring slots; ring capacity R = W + S must be a multiple of 32 */
   int32_t tail_dtype;   /* kvq_tail_dtype (ignored when tail_len == 0)                          */
   int32_t layout;       /* kvq_layout: placement of V rows (both layouts have the same size)       */
+  int32_t index_dim;    /* 0: no indexer; else the QSA indexer head dim, whose keys are pooled to 32 values
+                           (offload page: indexer_head_dim 128, compress ratio 4): index_dim = 32 x index_pool */
+  int32_t index_pool;   /* pooling ratio of the index keys: 1, 2, 4, 8 or 16 (ignored when index_dim == 0)  */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache;
 
 /* Regions of one (layer, sequence) slab, for kvq_region(). */
 enum { KVQ_REGION_K_BODY = 0, KVQ_REGION_V_BODY = 1, KVQ_REGION_K_RING = 2, KVQ_REGION_V_RING = 3,
-       KVQ_REGION_SIGMA = 4, KVQ_REGION_SLAB = 5 };
+       KVQ_REGION_SIGMA = 4, KVQ_REGION_SLAB = 5, KVQ_REGION_INDEX = 6 };
 
 /* Validate a configuration (host only). */
 kvq_status kvq_config_validate(const kvq_config* cfg);
@@ -232,15 +235,49 @@ kvq_status kvq_sparse_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seq
                                   const int32_t* positions, int32_t budget, float* out, float softmax_scale,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- The QSA indexer (offload page, QSA paragraph: a cheap indexer runs over keys pooled to
+ * indexer_head_dim / indexer_compress_ratio = 128 / 4 = 32 values, picks at most indexer_budget = 2,048
+ * positions, and the layer reads only the main-KV rows there; what stays resident is the pooled key, 1 x (128/4)
+ * x 2 = 64 bytes per token and layer). A cache with index_dim > 0 holds one pooled key per position. */
+
+/* Pool and store the indexer keys of the newest n_new[i] positions of each listed sequence (call it after the
+ * kvq_append that added them). key_bf16: device bf16 [sum n_new][index_dim], sequences packed in call order.
+ * Each group of index_pool consecutive values becomes their mean (fp32 sum in order, times 1 / index_pool),
+ * rounded to bf16 (nearest even).
+ * Errors: KVQ_E_INVALID if the cache has no indexer (index_dim == 0); KVQ_E_STATE if n_new[i] exceeds the
+ * sequence's length. */
+kvq_status kvq_index_write(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                           const int32_t* n_new, const void* key_bf16, void* stream);
+
+/* Workspace bytes kvq_index_select needs for n_seqs sequences of at most max_len positions. */
+size_t kvq_index_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t max_len);
+
+/* Choose `budget` positions per sequence for sparse decode: the newest n_recent positions, then, of the older
+ * positions, those whose pooled key scores highest against the sequence's index query (equal scores: the lower
+ * position first). The score of position t is the sum over i = 0..31 of q_i * k_ti, each product exact in fp32
+ * and the sum taken in fp32 in channel order, so the choice is reproducible bit for bit. A sequence with no more
+ * than `budget` positions has all of them chosen.
+ * query_bf16: device bf16 [n_seqs][32]. positions: device int32 [n_seqs][budget], written in ascending order,
+ * padded with -1 (entries kvq_sparse_decode_attn skips) when a sequence holds fewer than budget positions.
+ * workspace: device, kvq_index_workspace_bytes(cache, n_seqs, max len) bytes, 256-byte aligned, no initial
+ * contents needed. Three kernel launches.
+ * Errors: KVQ_E_INVALID if the cache has no indexer, budget < 1 or n_recent is outside [0, budget];
+ * KVQ_E_SIZE if the workspace is too small. */
+kvq_status kvq_index_select(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                            const void* query_bf16, int32_t budget, int32_t n_recent, int32_t* positions,
+                            void* workspace, size_t ws_bytes, void* stream);
+
 /* Kernel kinds for launch timing. */
 typedef enum {
   KVQ_KERNEL_DECODE = 0,   /* split kernel of dense decode (tile layout)                      */
   KVQ_KERNEL_GATHER = 1,   /* gather kernel of sparse decode / dense decode of a row layout     */
   KVQ_KERNEL_COMBINE = 2,  /* merge of the split partials                                      */
-  KVQ_KERNEL_APPEND = 3,   /* append kernels (calibration, body and ring writes)               */
+  KVQ_KERNEL_APPEND = 3,   /* append kernels (calibration, body and ring writes, index key writes) */
   KVQ_KERNEL_EVICT = 4,    /* tail-evict requantization                                         */
   KVQ_KERNEL_APPEND_EVICT = 5, /* fused append + evict of kvq_append_evict                        */
-  KVQ_KERNEL_COUNT = 6
+  KVQ_KERNEL_INDEX = 6,    /* kvq_index_select, from the start of its scoring launch to the end of its
+                              picking launch                                                          */
+  KVQ_KERNEL_COUNT = 7
 } kvq_kernel;
 
 /* Launch timing, for measuring kernels against the memory roofline. While enabled, every launch the

@@ -31,6 +31,7 @@ UNITS = [
     ("kvq_decode.hip", ["-ffp-contract=fast"]),
     ("kvq_gather.hip", ["-ffp-contract=fast"]),
     ("kvq_scratch.hip", ["-ffp-contract=off"]),
+    ("kvq_index.hip", ["-ffp-contract=off"]),
 ]
 PROBE_UNITS = [("kvq_probe.hip", [])]
 
@@ -42,8 +43,19 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the kvq HIP library cannot be built")
 
 
-def _compile(src: str, extra) -> str:
+def _up_to_date(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return False
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
+    deps.append(os.path.join(os.path.dirname(HERE), "include", "kvq.h"))
+    return all(os.path.getmtime(d) <= t for d in deps)
+
+
+def _compile(src: str, extra, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if incremental and _up_to_date(src, obj):
+        return obj
     cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -60,11 +72,12 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every unit (incremental=True: only units older than their source or a header) and link."""
     os.makedirs(BUILD, exist_ok=True)
     units = UNITS + PROBE_UNITS
     with cf.ThreadPoolExecutor(max_workers=len(units)) as ex:
-        objs = list(ex.map(lambda u: _compile(*u), units))
+        objs = list(ex.map(lambda u: _compile(*u, incremental=incremental), units))
     _link(objs[:len(UNITS)], LIB)
     _link(objs[len(UNITS):], PROBE_LIB)
     if verbose:
@@ -73,4 +86,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv)

@@ -51,7 +51,10 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
   }
 }
 
-__global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) { body_write_wg(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(512) void body_write_kernel(WriteArgs a) {
+  __shared__ WriteCodes codes;
+  body_write_wg(a, blockIdx.x, blockIdx.y, codes);
+}
 
 __global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
   bf16_ring_write_wg(a, blockIdx.x, blockIdx.y);
@@ -61,12 +64,13 @@ __global__ __launch_bounds__(512) void bf16_ring_write_kernel(WriteArgs a) {
 // ring, the rest requantize ring rows that were already there into the body. The two touch disjoint bytes
 // (the host only fuses calls whose evicted positions precede the appended ones and fit the ring together).
 __global__ __launch_bounds__(512) void step_write_kernel(StepArgs a) {
+  __shared__ WriteCodes codes;
   const int x = blockIdx.x;
   if (x < a.ring_wgs) {
     if (a.ring.g.tail_dtype != 2) bf16_ring_write_wg(a.ring, x, blockIdx.y);   // bf16 or f16 values
-    else body_write_wg(a.ring, x, blockIdx.y);
+    else body_write_wg(a.ring, x, blockIdx.y, codes);
   } else {
-    body_write_wg(a.body, x - a.ring_wgs, blockIdx.y);
+    body_write_wg(a.body, x - a.ring_wgs, blockIdx.y, codes);
   }
 }
 

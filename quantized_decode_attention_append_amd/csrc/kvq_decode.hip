@@ -24,6 +24,11 @@
 #include "kvq_mfma.h"
 #include "kvq_write.h"
 
+// Waves per SIMD the decode kernel is compiled for: one 8-wave work-group per CU, up to 256 VGPRs a wave.
+#ifndef KVQ_DECODE_WAVES_PER_EU
+#define KVQ_DECODE_WAVES_PER_EU 2
+#endif
+
 namespace kvq {
 namespace {
 
@@ -598,17 +603,18 @@ struct StepWriteView {
 // The writes of a fused decode step that fall to this work-group, done by all its threads before any of them
 // reads the cache: the last ring split writes the appended token into the ring, the last body split
 // requantizes the ring rows leaving the window into the body (the tiles they land in belong to that split).
-__device__ inline void step_writes(const DecodeArgs& a, const DecodeSeq& S, int si, int head, int split, bool is_ring) {
+__device__ inline void step_writes(const DecodeArgs& a, const DecodeSeq& S, int si, int head, int split, bool is_ring,
+                                   WriteCodes& codes) {
   const int n_splits = S.n_body_splits + S.n_ring_splits;
   if (is_ring && split == n_splits - 1 && S.app_pos >= 0) {
     const StepWriteView w{a.g, a.k_in, a.v_in, 1, 1,
                           {WriteItem{S.slab, S.app_pos, S.app_pos + 1, S.app_pos, si, S.app_pos / kTile, 0}}};
     if (a.g.tail_dtype != 2) bf16_ring_write_wg(w, 0, head);   // bf16 or f16 values
-    else body_write_wg(w, 0, head);
+    else body_write_wg(w, 0, head, codes);
   } else if (!is_ring && split == S.n_body_splits - 1 && S.ev1 > S.ev0) {
     const StepWriteView w{a.g, a.k_in, a.v_in, 0, 1,
                           {WriteItem{S.slab, S.ev0, S.ev1, S.len, 0, S.ev0 / kTile, 0}}};
-    body_write_wg(w, 0, head);
+    body_write_wg(w, 0, head, codes);
   } else {
     return;
   }
@@ -622,12 +628,19 @@ __device__ inline void step_writes(const DecodeArgs& a, const DecodeSeq& S, int 
 // a SIMD do not get equal issue slots, so a static share would leave one of them finishing late); the
 // waves' partial results are merged in LDS into one partial record.
 template <int NK, int NV>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KVQ_DECODE_WAVES_PER_EU, KVQ_DECODE_WAVES_PER_EU)))
+void decode_kernel(DecodeArgs a) {
   constexpr int D = 256, NB = 8, NT = 16, NW = 8;
-  __shared__ float s_o[NW][kPartialHeads][D];
+  // One 64 KiB LDS region serves three phases in turn, each ended by a work-group barrier: the codes of a fused
+  // step's writes; then the QK B operands (24 KiB) and the waves' tile scales (16 KiB); then the waves' partial
+  // outputs (64 KiB). Two work-groups fit one CU.
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kPartialHeads * NW * D * 4];
+  static_assert(sizeof(WriteCodes) <= sizeof(s_lds), "codes");
+  static_assert(kQbHalf8 * sizeof(half8) + NW * 2 * 64 * sizeof(u32x4) <= sizeof(s_lds), "operands and scales");
+  float (*s_o)[kPartialHeads][D] = (float (*)[kPartialHeads][D])s_lds;
+  half8* s_qb = (half8*)s_lds;                                                     // QK B operands
+  u32x4 (*s_scales)[2][64] = (u32x4 (*)[2][64])(s_lds + kQbHalf8 * sizeof(half8));   // per wave, double-buffered
   __shared__ float s_ml[NW][2][kPartialHeads];
-  __shared__ u32x4 s_scales[NW][2][64];   // per wave, double-buffered tile scales
-  __shared__ half8 s_qb[kQbHalf8];         // QK B operands (per plane, block and lane)
   __shared__ int s_next;                   // next unclaimed tile of this split
   __shared__ float s_amax[8 * 16];         // per wave: |q| maximum of each head over the wave's block
 
@@ -646,7 +659,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int head = rem / n_splits;
   const int split = rem % n_splits;
   const bool is_ring = split >= S.n_body_splits;
-  if (a.step) step_writes(a, S, si, head, split, is_ring);
+  if (a.step) step_writes(a, S, si, head, split, is_ring, *(WriteCodes*)s_lds);
   const int tail = g.tail_dtype;
   const int R = g.ring_slots;
   const uint8_t* slab = g.arena + S.slab;

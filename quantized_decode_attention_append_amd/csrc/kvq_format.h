@@ -28,7 +28,8 @@
 //   one of V. Region sizes are the same in both layouts.
 // * Arena: [layer][seq] slabs; a slab holds (256-byte aligned) K body [head][cap32/32][tile],
 //   V body [head][cap32/32][tile], K ring [head][R/32][tile], V ring [head][R/32][tile] (row layout:
-//   [head][positions][row] for K and V), KVarN sigma [head][K,V][D] fp16.
+//   [head][positions][row] for K and V), KVarN sigma [head][K,V][D] fp16, and for a cache with an indexer the
+//   pooled index keys [cap32][32] bf16 (64 bytes per position: offload page, 1 x (128 / 4) x 2 bytes).
 #pragma once
 
 #include <stddef.h>
@@ -46,6 +47,7 @@ namespace kvq {
 
 constexpr int kTile = 32;        // positions per V tile
 constexpr int kBlock = 32;       // values per quantization block
+constexpr int kIndexWidth = 32;  // pooled index key values per position (indexer head dim / pooling ratio)
 
 // Planes of an N-bit code: count, widths and shifts (least significant plane first).
 KVQ_HD int plane_count(int n) { return (n == 7) ? 3 : (n == 3 || n == 5 || n == 6) ? 2 : 1; }
@@ -96,15 +98,15 @@ KVQ_HD int vtile_lane_byte(int lane, int b, int nt, int w) {
 }
 
 struct SlabLayout {
-  size_t k_body, v_body, k_ring, v_ring, sigma;          // region offsets within a slab
-  size_t k_body_sz, v_body_sz, k_ring_sz, v_ring_sz, sigma_sz;
+  size_t k_body, v_body, k_ring, v_ring, sigma, index;   // region offsets within a slab
+  size_t k_body_sz, v_body_sz, k_ring_sz, v_ring_sz, sigma_sz, index_sz;
   size_t slab;                                           // slab bytes (256-aligned)
   int cap32, row_k, row_v, ring_row_k, ring_row_v, ring_slots;
 };
 
-// tail_dtype: 0 none, 1 bf16, 2 q8_0, 3 f16.
+// tail_dtype: 0 none, 1 bf16, 2 q8_0, 3 f16. index: 0 none, else the cache holds pooled index keys.
 KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_bits, int v_bits,
-                              int kvarn, int tail_len, int tail_slack, int tail_dtype) {
+                              int kvarn, int tail_len, int tail_slack, int tail_dtype, int index) {
   SlabLayout L{};
   L.cap32 = (int)round_up((size_t)capacity, kTile);
   L.row_k = row_bytes(k_bits, head_dim);
@@ -121,12 +123,14 @@ KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_
   L.k_ring_sz = hk * L.ring_slots * L.ring_row_k;
   L.v_ring_sz = hk * L.ring_slots * L.ring_row_v;
   L.sigma_sz = kvarn ? hk * 2 * head_dim * 2 : 0;
+  L.index_sz = index ? (size_t)L.cap32 * kIndexWidth * 2 : 0;
   size_t off = 0;
   L.k_body = off; off = round_up(off + L.k_body_sz, 256);
   L.v_body = off; off = round_up(off + L.v_body_sz, 256);
   L.k_ring = off; off = round_up(off + L.k_ring_sz, 256);
   L.v_ring = off; off = round_up(off + L.v_ring_sz, 256);
   L.sigma = off; off = round_up(off + L.sigma_sz, 256);
+  L.index = off; off = round_up(off + L.index_sz, 256);
   L.slab = off;
   return L;
 }

@@ -88,7 +88,7 @@ hipError_t timed(kvq_cache* c, int kind, hipStream_t stream, F launch) {
 
 SlabLayout layout_of(const kvq_config& c) {
   return kvq::slab_layout(c.capacity, c.n_kv_heads, c.head_dim, c.k_bits, c.v_bits, c.kvarn, c.tail_len,
-                          c.tail_slack, c.tail_dtype);
+                          c.tail_slack, c.tail_dtype, c.index_dim > 0 ? 1 : 0);
 }
 
 kvq_status validate(const kvq_config* c) {
@@ -110,6 +110,13 @@ kvq_status validate(const kvq_config* c) {
   if (c->tail_len < 0 || c->tail_slack < 0) return fail(KVQ_E_INVALID, "tail_len and tail_slack must be >= 0");
   if (c->layout != KVQ_LAYOUT_TILES && c->layout != KVQ_LAYOUT_ROWS)
     return fail(KVQ_E_INVALID, "layout must be KVQ_LAYOUT_TILES or KVQ_LAYOUT_ROWS (got %d)", c->layout);
+  if (c->index_dim != 0) {
+    const int p = c->index_pool;
+    if (p != 1 && p != 2 && p != 4 && p != 8 && p != 16)
+      return fail(KVQ_E_INVALID, "index_pool must be 1, 2, 4, 8 or 16 (got %d)", p);
+    if (c->index_dim != kvq::kIndexWidth * p)
+      return fail(KVQ_E_INVALID, "index_dim must be 32 x index_pool (got %d with pool %d)", c->index_dim, p);
+  }
   if (c->tail_len > 0) {
     if (c->tail_dtype != KVQ_TAIL_BF16 && c->tail_dtype != KVQ_TAIL_Q8_0 && c->tail_dtype != KVQ_TAIL_F16)
       return fail(KVQ_E_INVALID, "tail_dtype must be KVQ_TAIL_BF16, KVQ_TAIL_Q8_0 or KVQ_TAIL_F16 when tail_len > 0");
@@ -129,6 +136,7 @@ kvq::Geometry geometry(const kvq_cache* c) {
   g.k_ring = c->lay.k_ring;
   g.v_ring = c->lay.v_ring;
   g.sigma = c->lay.sigma;
+  g.index = c->lay.index;
   g.cap32 = c->lay.cap32;
   g.row_k = c->lay.row_k;
   g.row_v = c->lay.row_v;
@@ -173,6 +181,12 @@ int tiles_of(int p0, int p1) { return p1 > p0 ? (p1 - 1) / kvq::kTile - p0 / kvq
 // work-group per CU: each (sequence, body|ring) segment gets a share of the CU budget proportional to
 // its tiles (at least one), leftover work-groups go to the segments with the most tiles per work-group.
 constexpr int kMaxWgBudget = 1024;
+// Decode work-groups planned per CU: two 8-wave work-groups are co-resident on a CU (64 KiB of LDS and at most
+// 128 VGPRs each), so the plan fills both slots.
+#ifndef KVQ_DECODE_WGS_PER_CU
+#define KVQ_DECODE_WGS_PER_CU 1
+#endif
+constexpr int kDecodeWgsPerCu = KVQ_DECODE_WGS_PER_CU;
 constexpr int kMinTilesPerWg = 4;
 // Ring work-groups per sequence that multi-query decode plans outside the per-head budget (at most).
 constexpr int kRingExtra = 2;
@@ -190,7 +204,7 @@ struct SplitPlan {
 SplitPlan plan_splits(const kvq_cache* c, int n_seqs, const int* len, const int* body_len, kvq::DecodeSeq* out,
                       bool allow_ring_extra = false) {
   const int hk = c->cfg.n_kv_heads;
-  int budget_h = std::max(1, std::min(c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
+  int budget_h = std::max(1, std::min(kDecodeWgsPerCu * c->n_cu, kMaxWgBudget) / hk);   // work-groups per KV head
   // Cost of a tile in a work-group's time: a qN_0 tile (body or q8_0 ring) is decode- and MFMA-bound, a bf16
   // ring tile carries 2.7x the bytes of a K6/V5 tile with little decode and no prefetch: it counts double.
   const double ring_w = c->cfg.tail_dtype == KVQ_TAIL_Q8_0 ? 1.0 : 2.0;
@@ -397,6 +411,7 @@ kvq_status kvq_region(const kvq_config* cfg, int32_t layer, int32_t seq, int32_t
     case KVQ_REGION_V_RING: *offset = base + L.v_ring; *bytes = L.v_ring_sz; break;
     case KVQ_REGION_SIGMA: *offset = base + L.sigma; *bytes = L.sigma_sz; break;
     case KVQ_REGION_SLAB: *offset = base; *bytes = L.slab; break;
+    case KVQ_REGION_INDEX: *offset = base + L.index; *bytes = L.index_sz; break;
     default: return fail(KVQ_E_INVALID, "unknown region %d", region);
   }
   return KVQ_OK;
@@ -492,7 +507,8 @@ size_t kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) 
   // splits per (sequence, KV head) never exceed the tiles of a sequence (+1 for the body/ring boundary
   // tile) nor the per-head work-group budget
   const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 1;
-  long splits = std::min<long>(tiles, std::max(1, std::min(c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads) + kRingExtra);
+  long splits = std::min<long>(
+      tiles, std::max(1, std::min(kDecodeWgsPerCu * c->n_cu, kMaxWgBudget) / c->cfg.n_kv_heads) + kRingExtra);
   // the gather path (sparse decode, and dense decode of a row-layout cache)
   const long gsplits = std::min<long>((max_len + kGatherMin - 1) / kGatherMin, gather_budget_h(c));
   splits = std::max(splits, std::max(1L, gsplits));
@@ -893,6 +909,89 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   int n_splits[KVQ_MAX_BATCH];
   for (int i = 0; i < n_seqs; ++i) n_splits[i] = a.seqs[i].n_body_splits + a.seqs[i].n_ring_splits;
   return launch_combine_for(c, n_seqs, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------------------------------ indexer
+
+kvq_status kvq_index_write(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                           const void* key_bf16, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (c->cfg.index_dim == 0) return fail(KVQ_E_INVALID, "the cache has no indexer (index_dim = 0)");
+  if (!n_new) return fail(KVQ_E_INVALID, "n_new is NULL");
+  kvq::IndexWriteArgs a{};
+  a.g = geometry(c);
+  a.key_in = (const uint16_t*)key_bf16;
+  a.pool = c->cfg.index_pool;
+  int total = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int len = c->len[c->idx(layer, seq_ids[i])];
+    if (n_new[i] < 0) return fail(KVQ_E_INVALID, "n_new[%d] is negative", i);
+    if (n_new[i] > len)
+      return fail(KVQ_E_STATE, "seq %d holds %d positions, fewer than %d index keys", seq_ids[i], len, n_new[i]);
+    if (n_new[i] == 0) continue;
+    a.items[a.n_items++] = kvq::IndexWriteItem{slab_offset(c, layer, seq_ids[i]), len - n_new[i], n_new[i], total, total};
+    total += n_new[i];
+  }
+  if (total == 0) return KVQ_OK;
+  if (!key_bf16) return fail(KVQ_E_INVALID, "key input is NULL");
+  hipError_t e = timed(c, KVQ_KERNEL_APPEND, (hipStream_t)stream, [&](hipEvent_t e0, hipEvent_t e1) {
+    return kvq::launch_index_write(a, total, (hipStream_t)stream, e0, e1);
+  });
+  if (e != hipSuccess) return hip_fail(e, "index write launch");
+  return KVQ_OK;
+}
+
+namespace {
+int index_wgs(int m) { return std::max(1, (m + kvq::kIndexChunk - 1) / kvq::kIndexChunk); }
+}  // namespace
+
+size_t kvq_index_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) {
+  if (!c || n_seqs < 1 || max_len < 0) return 0;
+  return (size_t)n_seqs * kvq::index_ws_seq_bytes(index_wgs(max_len));
+}
+
+kvq_status kvq_index_select(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                            const void* query_bf16, int32_t budget, int32_t n_recent, int32_t* positions,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (c->cfg.index_dim == 0) return fail(KVQ_E_INVALID, "the cache has no indexer (index_dim = 0)");
+  if (!query_bf16 || !positions || !workspace) return fail(KVQ_E_INVALID, "query/positions/workspace is NULL");
+  if (((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
+  if (((uintptr_t)positions) % 4 != 0) return fail(KVQ_E_INVALID, "positions must be 4-byte aligned");
+  if (budget < 1 || budget > (1 << 28)) return fail(KVQ_E_INVALID, "budget must be in [1, 2^28] (got %d)", budget);
+  if (n_recent < 0 || n_recent > budget)
+    return fail(KVQ_E_INVALID, "n_recent must be in [0, budget] (got %d, budget %d)", n_recent, budget);
+  kvq::IndexArgs a{};
+  a.g = geometry(c);
+  a.q = (const uint16_t*)query_bf16;
+  a.out = positions;
+  a.ws = (uint8_t*)workspace;
+  a.budget = budget;
+  a.n_seqs = n_seqs;
+  size_t off = 0;
+  int wgs = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int len = c->len[c->idx(layer, seq_ids[i])];
+    const int recent = std::min(n_recent, len);
+    kvq::IndexSeq& S = a.seqs[i];
+    S.slab = slab_offset(c, layer, seq_ids[i]);
+    S.ws_off = off;
+    S.len = len;
+    S.m = len - recent;
+    S.k = budget - recent;
+    S.n_wgs = index_wgs(S.m);
+    S.wg_begin = wgs;
+    wgs += S.n_wgs;
+    off += kvq::index_ws_seq_bytes(S.n_wgs);
+  }
+  if (ws_bytes < off) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, off);
+  hipError_t e = timed(c, KVQ_KERNEL_INDEX, (hipStream_t)stream, [&](hipEvent_t e0, hipEvent_t e1) {
+    return kvq::launch_index_select(a, wgs, (hipStream_t)stream, e0, e1);
+  });
+  if (e != hipSuccess) return hip_fail(e, "index select launch");
+  return KVQ_OK;
 }
 
 // Host checks of a sparse decode call (before any work).

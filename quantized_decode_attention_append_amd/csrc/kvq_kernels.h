@@ -18,7 +18,7 @@ constexpr int kMaxSplits = 1024;   // split partials per (sequence, KV head)
 struct Geometry {
   uint8_t* arena;
   size_t slab_bytes;
-  size_t k_body, v_body, k_ring, v_ring, sigma;   // region offsets within a slab
+  size_t k_body, v_body, k_ring, v_ring, sigma, index;   // region offsets within a slab
   int cap32, row_k, row_v, tile_k, tile_v, ring_row_k, ring_row_v, ring_tile_k, ring_tile_v, ring_slots;
   int n_kv_heads, head_dim, k_bits, v_bits, kvarn, tail_dtype;
   int layout;                                      // 0: V tiles, 1: V rows
@@ -137,6 +137,51 @@ struct CombineArgs {
   int n_splits[kMaxBatch];
 };
 
+// ---------------------------------------------------------------- indexer (QSA)
+
+// Pooled index keys of the newest n positions of each item's sequence: positions p0 .. p0 + n - 1 from input
+// rows row0 .. row0 + n - 1 ([row][32 * pool] bf16); `begin` is the item's first position number over all items.
+struct IndexWriteItem {
+  size_t slab;
+  int p0, n, row0, begin;
+};
+struct IndexWriteArgs {
+  Geometry g;
+  const uint16_t* key_in;
+  int pool;
+  int n_items;
+  IndexWriteItem items[kMaxBatch];
+};
+
+// Selection of a budget of positions per sequence: the first m = len - recent positions are scored, k of them
+// chosen, then the `recent` newest appended. Work-groups of kIndexChunk positions; ws_off: the sequence's part of the
+// workspace (histogram, control words, keys, bitmap, candidates).
+struct IndexSeq {
+  size_t slab;
+  size_t ws_off;
+  int len, m, k;
+  int n_wgs, wg_begin;
+};
+struct IndexArgs {
+  Geometry g;
+  const uint16_t* q;        // [n_seqs][32] bf16 index queries
+  int32_t* out;             // [n_seqs][budget]
+  uint8_t* ws;
+  int budget;
+  int n_seqs;
+  IndexSeq seqs[kMaxBatch];
+};
+constexpr int kIndexChunk = 1024;      // positions per work-group of the selection kernels
+constexpr int kIndexHistCopies = 4;    // copies of a sequence's 16,384-bin score histogram
+
+// Workspace bytes of one sequence's selection with `n_wgs` work-groups: histogram copies, 16 control words,
+// keys, bitmap, candidates.
+inline size_t index_ws_seq_bytes(int n_wgs) {
+  const size_t words = (size_t)kIndexHistCopies * (1 << 14) + 16 + (size_t)n_wgs * kIndexChunk +
+                       (size_t)n_wgs * (kIndexChunk / 32);
+  return round_up(words * 4 + (size_t)n_wgs * kIndexChunk * 8, 256);
+}
+
 // Launch wrappers (return the launch status). With non-null events e0 / e1 the launch records the kernel's
 // start and end time in them (hipExtLaunchKernel: timestamps of the dispatch itself).
 hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s, hipEvent_t e0 = nullptr,
@@ -153,6 +198,11 @@ hipError_t launch_decode(const DecodeArgs& a, int grid_x, hipStream_t s, hipEven
 hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s, hipEvent_t e0 = nullptr,
                          hipEvent_t e1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+hipError_t launch_index_write(const IndexWriteArgs& a, int n_positions, hipStream_t s, hipEvent_t e0 = nullptr,
+                              hipEvent_t e1 = nullptr);
+// The three selection launches; e0 / e1 bracket the scoring and picking launches.
+hipError_t launch_index_select(const IndexArgs& a, int total_wgs, hipStream_t s, hipEvent_t e0 = nullptr,
+                               hipEvent_t e1 = nullptr);
 
 // The library's static scratch buffer (kvq_scratch.hip): kScratchBytes of device memory per GPU, for the
 // entry points that take no workspace. scratch_device_ptr returns its device address on `device` (looked up

@@ -158,13 +158,15 @@ __device__ inline void or_code(uint8_t* row, uint8_t* tile, bool rows, int kv, i
 // A work-group with at most this many positions ORs its codes straight into the body (no LDS staging).
 constexpr int kDirectPositions = 4;
 
+// LDS staging of one tile's codes: [K,V][tile position][channel].
+typedef uint8_t WriteCodes[2][kTile][256];
+
 // One work-group of 512 threads per (position tile, KV head): thread (kv, c) quantizes channel c of K (kv = 0)
 // or V (kv = 1) for every position of the tile that the call writes. A: WriteArgs, or one role of StepArgs
-// (the kernel argument itself, so that the item list is read in place).
+// (the kernel argument itself, so that the item list is read in place). codes: the caller's LDS buffer.
 template <class A>
-__device__ inline void body_write_wg(const A& a, int wg, int head) {
+__device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& codes) {
 #pragma clang fp contract(off)
-  __shared__ uint8_t codes[2][kTile][256];     // [K,V][tile position][channel]
   const Geometry& g = a.g;
   int it = 0;
   while (it + 1 < a.n_items && a.items[it + 1].wg_begin <= wg) ++it;

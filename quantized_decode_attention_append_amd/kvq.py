@@ -19,16 +19,19 @@ KVQ_OK, KVQ_E_INVALID, KVQ_E_CAPACITY, KVQ_E_SIZE, KVQ_E_HIP, KVQ_E_STATE = 0, -
 KVQ_MAX_BATCH, KVQ_MAX_QUERIES = 64, 8
 TAIL_NONE, TAIL_BF16, TAIL_Q8_0, TAIL_F16 = 0, 1, 2, 3
 LAYOUT_TILES, LAYOUT_ROWS = 0, 1
-REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab": 5}
+REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab": 5, "index": 6}
 MAX_BATCH = 64
 
 _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits",
-           "kvarn", "tail_len", "tail_slack", "tail_dtype", "layout")
+           "kvarn", "tail_len", "tail_slack", "tail_dtype", "layout", "index_dim", "index_pool")
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_truncate", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
-KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5}
+           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_index_write", "kvq_index_workspace_bytes", "kvq_index_select", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5, "index": 6}
+
+
+_OPTIONAL = ("layout", "index_dim", "index_pool")
 
 
 class Config(ctypes.Structure):
@@ -67,6 +70,9 @@ def _load() -> ctypes.CDLL:
         "kvq_decode_attn_multi": (I32, [P, I32, I32, IP, I32, P, P, F, P, SZ, P]),
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
         "kvq_sparse_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, I32, P, F, P, SZ, P]),
+        "kvq_index_write": (I32, [P, I32, I32, IP, IP, P, P]),
+        "kvq_index_workspace_bytes": (SZ, [P, I32, I32]),
+        "kvq_index_select": (I32, [P, I32, I32, IP, P, I32, I32, P, P, SZ, P]),
         "kvq_timing_enable": (I32, [P, I32]),
         "kvq_timing_read": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), IP]),
         "kvq_last_error": (ctypes.c_char_p, []),
@@ -87,8 +93,8 @@ def _check(status: int):
 
 
 def make_config(cfg: Dict[str, int]) -> Config:
-    """kvq_config from a dict; "layout" defaults to LAYOUT_TILES."""
-    return Config(*[int(cfg.get(f, 0) if f == "layout" else cfg[f]) for f in _FIELDS])
+    """kvq_config from a dict; "layout" defaults to LAYOUT_TILES, "index_dim" / "index_pool" to 0 (no indexer)."""
+    return Config(*[int(cfg.get(f, 0) if f in _OPTIONAL else cfg[f]) for f in _FIELDS])
 
 
 def config_validate(cfg: Dict[str, int]) -> None:
@@ -336,4 +342,42 @@ class Cache:
                                            _dev(out, torch.float32, "out"), float(softmax_scale),
                                            _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                            ctypes.c_void_p(_stream(stream))))
+        return out
+
+    # ---------------------------------------------------------------- the QSA indexer
+    def index_write(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], keys: torch.Tensor, stream=None):
+        """Pool and store the indexer keys of the newest n_new[i] positions of each sequence (after append()).
+        keys: bf16 (or 16-bit bit patterns) [sum(n_new), index_dim] on the device."""
+        total = int(sum(int(n) for n in n_new))
+        dim = self.cfg.get("index_dim", 0)
+        if total and dim and (keys.numel() != total * dim or keys.element_size() != 2):
+            raise ValueError(f"keys must be 16-bit [{total}, {dim}]")   # (a cache without an indexer: the library says so)
+        kp = _dev(keys, keys.dtype, "keys") if total else ctypes.c_void_p(0)
+        nn = (ctypes.c_int32 * len(n_new))(*[int(n) for n in n_new])
+        _check(_lib.kvq_index_write(self._h, layer, len(seq_ids), _ids(seq_ids), nn, kp,
+                                    ctypes.c_void_p(_stream(stream))))
+
+    def index_workspace_bytes(self, n_seqs: int, max_len: int) -> int:
+        return int(_lib.kvq_index_workspace_bytes(self._h, n_seqs, max_len))
+
+    def index_select(self, layer: int, seq_ids: Sequence[int], query: torch.Tensor, budget: int, n_recent: int = 0,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+        """Positions chosen by the indexer: int32 [n_seqs, budget] (ascending, -1 padded). query: bf16 [n_seqs, 32]."""
+        n = len(seq_ids)
+        if query.numel() != n * 32 or query.element_size() != 2:
+            raise ValueError("query must be bf16 [n_seqs, 32]")
+        if out is None:
+            out = torch.empty((n, budget), dtype=torch.int32, device=query.device)
+        if workspace is None:
+            max_len = max(self.lengths(layer, s)[0] for s in seq_ids)
+            need = max(self.index_workspace_bytes(n, max_len), 256)
+            ws = getattr(self, "_iws", None)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+                self._iws = ws
+            workspace = ws
+        _check(_lib.kvq_index_select(self._h, layer, n, _ids(seq_ids), _dev(query, query.dtype, "query"), int(budget),
+                                     int(n_recent), _dev(out, torch.int32, "out"),
+                                     _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                     ctypes.c_void_p(_stream(stream))))
         return out

@@ -44,7 +44,8 @@ def _random_cfgs(n=60):
     for _ in range(n):
         hk = int(rng.choice([1, 2, 4, 8]))
         w = int(rng.choice([0, 32, 1024, 2048]))
-        yield _cfg(n_layers=int(rng.integers(1, 17)), max_seqs=int(rng.integers(1, 9)),
+        pool = int(rng.choice([0, 1, 2, 4, 8, 16]))
+        yield _cfg(index_dim=32 * pool, index_pool=pool, n_layers=int(rng.integers(1, 17)), max_seqs=int(rng.integers(1, 9)),
                    capacity=int(rng.integers(1, 300000)), n_kv_heads=hk, n_q_heads=hk * int(rng.integers(1, 9)),
                    k_bits=int(rng.integers(2, 9)), v_bits=int(rng.integers(2, 9)), kvarn=int(rng.integers(0, 2)),
                    tail_len=w, tail_slack=int(rng.choice([0, 32, 512])) if w else 0,
@@ -58,7 +59,7 @@ def test_cache_bytes_and_regions_match_oracle():
         lay = slab_layout(c)
         for layer, seq in ((0, 0), (c["n_layers"] - 1, c["max_seqs"] - 1)):
             base = (layer * c["max_seqs"] + seq) * lay["slab"]
-            for name in ("k_body", "v_body", "k_ring", "v_ring", "sigma"):
+            for name in ("k_body", "v_body", "k_ring", "v_ring", "sigma", "index"):
                 off, size = kvq.region(c, layer, seq, name)
                 assert (off, size) == (base + lay[name][0], lay[name][1]), (c, name)
             assert kvq.region(c, layer, seq, "slab") == (base, lay["slab"])
@@ -76,6 +77,7 @@ def test_kv_mib_table_through_the_library():
     dict(n_layers=0), dict(max_seqs=0), dict(capacity=0), dict(n_q_heads=15), dict(n_q_heads=32),
     dict(head_dim=100), dict(k_bits=1), dict(v_bits=9), dict(kvarn=2), dict(tail_len=-1),
     dict(tail_len=64, tail_slack=31), dict(tail_len=64, tail_dtype=0), dict(tail_len=64, tail_dtype=4),
+    dict(index_dim=128, index_pool=3), dict(index_dim=96, index_pool=4), dict(index_dim=128, index_pool=0),
 ])
 def test_validation_rejects(bad):
     from quantized_decode_attention_append_amd import kvq

@@ -22,7 +22,7 @@ import numpy as np
 
 CHUNK = 4096            # prefill chunk length (tokens)
 DECODE_BASE = 1 << 20   # chunk ids >= this are decode-step tokens
-KIND_K, KIND_V, KIND_Q, KIND_SCALE, KIND_POS, KIND_LEN, KIND_OUTLIER = range(7)
+KIND_K, KIND_V, KIND_Q, KIND_SCALE, KIND_POS, KIND_LEN, KIND_OUTLIER, KIND_IKEY, KIND_IQ = range(9)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -191,3 +191,20 @@ def small_tokens(seed: int, n: int, n_kv_heads: int, head_dim: int, scale=None, 
 def small_query(seed: int, n_seqs: int, n_q_heads: int, head_dim: int, std: float = 1.0) -> np.ndarray:
     r = _rng(2000 + seed, 0, 0, 0, KIND_Q)
     return bf16_bits(std * r.standard_normal((n_seqs, n_q_heads, head_dim), dtype=np.float32))
+
+
+def index_keys(cfg: int, layer: int, seq: int, start: int, n: int, dim: int = 128,
+               chunk_id: Optional[int] = None) -> np.ndarray:
+    """Indexer keys (the model's indexer projection, not on the pages: N(0, 1) stand-ins) of tokens
+    [start, start + n) of one (layer, seq): bf16 bits [n, dim], drawn per prefill chunk like kv_tokens."""
+    if chunk_id is None:
+        assert start % CHUNK == 0 and n <= CHUNK, (start, n)
+        chunk_id = start // CHUNK
+    r = _rng(cfg, layer, seq, chunk_id, KIND_IKEY)
+    return bf16_bits(r.standard_normal((n, dim), dtype=np.float32))
+
+
+def index_query(cfg: int, layer: int, seq: int, step: int, width: int = 32) -> np.ndarray:
+    """Index query of a decode step in the pooled width: bf16 bits [width], N(0, 1)."""
+    r = _rng(cfg, layer, seq, DECODE_BASE + step, KIND_IQ)
+    return bf16_bits(r.standard_normal(width, dtype=np.float32))
