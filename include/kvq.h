@@ -202,14 +202,35 @@ kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
  * after). q_bf16: device bf16 [n_seqs][T][Hq][D]; out: device fp32 [n_seqs][T][Hq][D]; workspace:
  * kvq_workspace_bytes(cache, n_seqs * T, max len) bytes. The cache is not changed; rejected drafts are
  * dropped afterwards with kvq_seq_truncate, which requires them to still be ring rows: tail_len >= T - 1, and
- * any kvq_tail_evict (or fused step) comes after the verification, not before it. Each (sequence, query)
- * pair runs as one entry of the dense decode launch (of the gather launch for KVQ_LAYOUT_ROWS) over the
- * same cache rows.
+ * any kvq_tail_evict (or fused step) comes after the verification, not before it. With KVQ_LAYOUT_TILES
+ * and T >= 2 one multi-query launch reads and decodes every tile of a sequence once for all T queries (a
+ * work-group of 8 waves, one query per wave, over a range of the tiles, the decoded operands shared through
+ * LDS); T = 1 runs exactly as kvq_decode_attn; with KVQ_LAYOUT_ROWS each (sequence, query) pair is an entry
+ * of the gather launch.
  * Errors: KVQ_E_INVALID if T is outside [1, KVQ_MAX_QUERIES] or n_seqs * T > KVQ_MAX_BATCH; KVQ_E_STATE if
  * a sequence holds fewer than T positions; others as kvq_decode_attn. */
 kvq_status kvq_decode_attn_multi(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                  int32_t n_queries, const void* q_bf16, float* out, float softmax_scale,
                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Chunked prefill: append n_new[i] tokens to each listed sequence (exactly as kvq_append, which quantizes them
+ * into the ring and body) and compute causal attention for their queries over the cache as it then stands: the
+ * query of new token j of sequence i sits at position p = len_i + j (len_i: the length before the call) and
+ * attends to positions [0, p] through the stored representation of every position, the chunk's own tokens
+ * included (the KVarN benchmark page and the Qwen3.8-27B page measure prompt processing per cache type).
+ * k_bf16, v_bf16: device bf16 [sum n_new][Hkv][D]; q_bf16: device bf16 [sum n_new][Hq][D]; out: device fp32
+ * [sum n_new][Hq][D]; all packed in call order. Queries run in blocks of 8 through the multi-query kernel, each
+ * tile read and decoded once per block. workspace: kvq_prefill_workspace_bytes(cache, n_seqs, max n_new, max
+ * length after the call) bytes, 256-byte aligned (NULL allowed when that size is 256).
+ * Errors: as kvq_append; KVQ_E_INVALID for a KVQ_LAYOUT_ROWS cache; KVQ_E_SIZE if the workspace is too small
+ * (checked before anything is appended). */
+kvq_status kvq_prefill_attn(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                            const int32_t* n_new, const void* k_bf16, const void* v_bf16, const void* q_bf16,
+                            float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes kvq_prefill_attn needs for n_seqs sequences of at most max_new new tokens and max_len positions
+ * after the call (at least 256; 0 for invalid arguments). */
+size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t max_new, int32_t max_len);
 
 /* Sparse decode attention over an indexer budget (offload page, QSA: the layer reads only the
  * main-KV rows at the positions the indexer chose, so the budget, not the context, bounds the bytes).
@@ -260,7 +281,7 @@ size_t kvq_index_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t
  * query_bf16: device bf16 [n_seqs][32]. positions: device int32 [n_seqs][budget], written in ascending order,
  * padded with -1 (entries kvq_sparse_decode_attn skips) when a sequence holds fewer than budget positions.
  * workspace: device, kvq_index_workspace_bytes(cache, n_seqs, max len) bytes, 256-byte aligned, no initial
- * contents needed. Three kernel launches.
+ * contents needed. Five kernel launches.
  * Errors: KVQ_E_INVALID if the cache has no indexer, budget < 1 or n_recent is outside [0, budget];
  * KVQ_E_SIZE if the workspace is too small. */
 kvq_status kvq_index_select(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
@@ -277,7 +298,8 @@ typedef enum {
   KVQ_KERNEL_APPEND_EVICT = 5, /* fused append + evict of kvq_append_evict                        */
   KVQ_KERNEL_INDEX = 6,    /* kvq_index_select, from the start of its scoring launch to the end of its
                               picking launch                                                          */
-  KVQ_KERNEL_COUNT = 7
+  KVQ_KERNEL_MQ = 7,       /* multi-query kernel (kvq_decode_attn_multi with T >= 2, kvq_prefill_attn) */
+  KVQ_KERNEL_COUNT = 8
 } kvq_kernel;
 
 /* Launch timing, for measuring kernels against the memory roofline. While enabled, every launch the

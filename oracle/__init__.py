@@ -38,6 +38,6 @@ from .layout import (planes, cache_bytes, slab_layout, pack_k_rows, pack_v_tiles
                      pack_bf16_k_tiles, unpack_bf16_k_tiles)
 from .cache import OracleCache  # noqa: F401
 from . import indexer  # noqa: F401
-from .attention import attend, decode_reference, sparse_reference, multi_query_reference  # noqa: F401
+from .attention import attend, decode_reference, sparse_reference, multi_query_reference, prefill_reference  # noqa: F401
 from .sizes import (decode_bytes, decode_kv_bytes, query_out_bytes, sparse_bytes, sparse_kv_bytes,  # noqa: F401
                     row_bytes, kv_token_bytes, ring_token_bytes)

@@ -89,3 +89,32 @@ def multi_query_reference(cache, layer: int, seq_ids, q_bits: np.ndarray, scale=
             end = n - n_q + t + 1                         # query t attends to positions [0, end)
             out[i, t] = attend(_q64(q_bits[i, t]), k[:end], v[:end], sc)
     return out
+
+
+def prefill_reference(cache, layer: int, seq_ids, n_new, q_bits: np.ndarray, rows=None, scale=None) -> np.ndarray:
+    """Attention of the queries of a prefill chunk that has just been appended (the KVarN benchmark page and the
+    Qwen3.8-27B page measure prompt processing per cache type). q_bits [sum n_new, Hq, D] bf16 bits, sequences
+    packed in call order -> out [len(rows), Hq, D] fp64 for the packed rows ``rows`` (all rows by default).
+
+    Reading (the pages give prefill timings only): the query of new token j of sequence i sits at position
+    len_i - n_i + j (len_i: the length after the append) and attends causally to positions 0 .. len_i - n_i + j
+    through the cache as it stands after the append, i.e. through the stored representation of every position,
+    the chunk's own included."""
+    sc = _scale(cache, scale)
+    n_new = [int(x) for x in n_new]
+    total = sum(n_new)
+    rows = np.arange(total) if rows is None else np.asarray(rows, dtype=np.int64)
+    owner = np.repeat(np.arange(len(seq_ids)), n_new)            # packed row -> index into seq_ids
+    first = np.concatenate([[0], np.cumsum(n_new)])[:-1]
+    out = np.zeros((len(rows),) + q_bits.shape[1:], dtype=np.float64)
+    kv = {}
+    for r_i, row in enumerate(rows):
+        i = int(owner[row])
+        sid = seq_ids[i]
+        if sid not in kv:
+            kv[sid] = cache.dequantized(layer, sid)
+        k, v = kv[sid]
+        n, _ = cache.lengths(layer, sid)
+        end = n - n_new[i] + (row - first[i]) + 1                 # attends to positions [0, end)
+        out[r_i] = attend(_q64(q_bits[row]), k[:end], v[:end], sc)
+    return out

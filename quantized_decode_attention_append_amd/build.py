@@ -32,6 +32,7 @@ UNITS = [
     ("kvq_gather.hip", ["-ffp-contract=fast"]),
     ("kvq_scratch.hip", ["-ffp-contract=off"]),
     ("kvq_index.hip", ["-ffp-contract=off"]),
+    ("kvq_mq.hip", ["-ffp-contract=fast"]),
 ]
 PROBE_UNITS = [("kvq_probe.hip", [])]
 

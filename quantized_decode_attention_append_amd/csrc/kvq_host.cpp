@@ -753,6 +753,102 @@ kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, co
   return launch_combine_for(c, n, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
 }
 
+// ---- multi-query attention (kvq_decode_attn_multi for T >= 2, kvq_prefill_attn): queries in blocks of 8, each
+// (block, KV head) split so that the launch has about one work-group per CU. Without KVarN a split covers any range
+// of the block's tile list (body tiles, then ring tiles), so with one split per block the kernel writes the
+// outputs itself; with KVarN the body and ring tiles go to separate splits (the body's V values carry sigma_V).
+constexpr int kMqBlock = 8;
+
+// body length of a sequence after kvq_append of n tokens (the rule kvq_append applies)
+int body_len_after(const kvq_cache* c, int layer, int seq, int n) {
+  const int k = c->idx(layer, seq);
+  if (c->cfg.tail_len == 0) return c->len[k] + n;
+  return std::max(c->body_len[k], c->len[k] + n - c->lay.ring_slots);
+}
+
+long mq_budget(const kvq_cache* c) { return std::min(kDecodeWgsPerCu * c->n_cu, kMaxWgBudget); }
+
+struct MqPlan {
+  int total_wgs = 0, max_splits = 1, rows = 0;
+  bool partials = false;
+};
+
+MqPlan plan_mq(const kvq_cache* c, int n, const int* len, const int* body_len, const int* q0, const int* nq,
+               kvq::MqSeq* out) {
+  const int hk = c->cfg.n_kv_heads;
+  long blocks = 0;
+  for (int i = 0; i < n; ++i) blocks += (nq[i] + kMqBlock - 1) / kMqBlock;
+  const long entries = std::max(1L, blocks * hk);
+  // at most the dense decode's per-head budget per entry (so kvq_workspace_bytes(cache, n_seqs * T, len) covers
+  // kvq_decode_attn_multi), and rows x splits <= 8 x budget / Hkv (kvq_prefill_workspace_bytes)
+  const int per_entry = (int)std::max(1L, mq_budget(c) / entries);
+  MqPlan p;
+  for (int i = 0; i < n; ++i) {
+    kvq::MqSeq& S = out[i];
+    S.len = len[i];
+    S.body_len = body_len[i];
+    S.q0 = q0[i];
+    S.nq = nq[i];
+    S.row0 = p.rows;
+    const int end = q0[i] + nq[i];
+    const int bt = (std::min(body_len[i], end) + kvq::kTile - 1) / kvq::kTile;
+    const int rt = end > body_len[i] ? (end + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
+    int ns = std::min(per_entry, std::max(1, bt + rt));
+    int nr = 0;
+    if (c->cfg.kvarn && rt > 0) {   // separate body and ring splits
+      ns = std::max(ns, bt > 0 ? 2 : 1);
+      nr = bt > 0 ? std::max(1, std::min(ns - 1, (int)((long)ns * rt / (bt + rt)))) : ns;
+    }
+    S.n_splits = ns;
+    S.n_ring_splits = nr;
+    S.wg_begin = p.total_wgs;
+    p.total_wgs += ((nq[i] + kMqBlock - 1) / kMqBlock) * hk * ns;
+    p.max_splits = std::max(p.max_splits, ns);
+    p.partials = p.partials || ns > 1;
+    p.rows += nq[i];
+  }
+  return p;
+}
+
+size_t mq_partials_bytes(const kvq_cache* c, const MqPlan& p) {
+  return p.partials ? (size_t)p.rows * c->cfg.n_kv_heads * p.max_splits * kPartialFloats(c->cfg.head_dim) * sizeof(float)
+                    : 0;
+}
+
+kvq_status run_mq(kvq_cache* c, int layer, int n, const int32_t* ids, const int* q0, const int* nq, const void* q_bf16,
+                  float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  kvq::MqArgs a{};
+  a.g = geometry(c);
+  int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH];
+  for (int i = 0; i < n; ++i) {
+    const int k = c->idx(layer, ids[i]);
+    len[i] = c->len[k];
+    bl[i] = c->body_len[k];
+  }
+  const MqPlan p = plan_mq(c, n, len, bl, q0, nq, a.seqs);
+  const size_t need = mq_partials_bytes(c, p);
+  if (need && (!workspace || ws_bytes < need)) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  for (int i = 0; i < n; ++i) a.seqs[i].slab = slab_offset(c, layer, ids[i]);
+  a.q = (const uint16_t*)q_bf16;
+  a.out = out;
+  a.partials = (float*)workspace;
+  a.n_seqs = n;
+  a.n_q_heads = c->cfg.n_q_heads;
+  a.group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  a.max_splits = p.max_splits;
+  a.scale = softmax_scale > 0 ? softmax_scale : 1.0f / std::sqrt((float)c->cfg.head_dim);
+  if (p.total_wgs == 0) return KVQ_OK;
+  hipError_t e = timed(c, KVQ_KERNEL_MQ, (hipStream_t)stream,
+                       [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_mq(a, p.total_wgs, (hipStream_t)stream, e0, e1); });
+  if (e != hipSuccess) return hip_fail(e, "multi-query launch");
+  if (p.partials) {
+    e = timed(c, KVQ_KERNEL_COMBINE, (hipStream_t)stream,
+              [&](hipEvent_t e0, hipEvent_t e1) { return kvq::launch_mq_combine(a, p.rows, (hipStream_t)stream, e0, e1); });
+    if (e != hipSuccess) return hip_fail(e, "multi-query merge launch");
+  }
+  return KVQ_OK;
+}
+
 kvq_status check_decode_args(const void* q_bf16, const float* out, const void* workspace, float softmax_scale) {
   if (!q_bf16 || !out || !workspace) return fail(KVQ_E_INVALID, "q/out/workspace is NULL");
   if (((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
@@ -819,10 +915,68 @@ kvq_status kvq_decode_attn_multi(kvq_cache* c, int32_t layer, int32_t n_seqs, co
       len[i * n_queries + t] = n - n_queries + t + 1;
     }
   }
-  // with several queries per sequence the many short ring segments get work-groups outside the budget; one query
-  // per sequence plans (and computes) exactly as kvq_decode_attn
+  if (n_queries > 1 && c->cfg.layout == KVQ_LAYOUT_TILES) {
+    // the multi-query kernel: each tile read and decoded once for the T queries of a sequence
+    int q0[KVQ_MAX_BATCH], nq[KVQ_MAX_BATCH];
+    for (int i = 0; i < n_seqs; ++i) {
+      q0[i] = c->len[c->idx(layer, seq_ids[i])] - n_queries;
+      nq[i] = n_queries;
+    }
+    return run_mq(c, layer, n_seqs, seq_ids, q0, nq, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
+  }
+  // one query per sequence plans (and computes) exactly as kvq_decode_attn; a row-layout cache runs every
+  // (sequence, query) pair as an entry of the gather launch
   return run_decode(c, layer, n_seqs * n_queries, ids, len, q_bf16, out, softmax_scale, workspace, ws_bytes, stream,
                     n_queries > 1);
+}
+
+size_t kvq_prefill_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_new, int32_t max_len) {
+  if (!c || n_seqs < 1 || n_seqs > KVQ_MAX_BATCH || max_new < 1 || max_len < 1) return 0;
+  // partial records = rows x KV heads x the largest split count. A block holds at most 8 rows and gets at most
+  // budget / entries splits (entries >= blocks x Hkv), so rows x splits <= 8 x budget / Hkv; a KVarN block with
+  // body and ring tiles takes at least 2 splits; no block takes more splits than its tiles.
+  const long rows = (long)n_seqs * std::min(max_new, max_len);
+  const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 1;
+  const long cap = std::max(2L, std::min(tiles, mq_budget(c) / c->cfg.n_kv_heads));
+  const long records = std::min(rows * cap, std::max(2 * rows, kMqBlock * mq_budget(c) / c->cfg.n_kv_heads));
+  return std::max<size_t>((size_t)records * c->cfg.n_kv_heads * kPartialFloats(c->cfg.head_dim) * sizeof(float), 256);
+}
+
+kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                            const void* k_bf16, const void* v_bf16, const void* q_bf16, float* out, float softmax_scale,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status s = check_seqs(c, layer, n_seqs, seq_ids);
+  if (s != KVQ_OK) return s;
+  if (c->cfg.layout != KVQ_LAYOUT_TILES)
+    return fail(KVQ_E_INVALID, "prefill attention reads the tile layout (the cache uses KVQ_LAYOUT_ROWS)");
+  if (!n_new) return fail(KVQ_E_INVALID, "n_new is NULL");
+  if (!q_bf16 || !out) return fail(KVQ_E_INVALID, "q/out is NULL");
+  if (workspace && ((uintptr_t)workspace) % 256 != 0) return fail(KVQ_E_INVALID, "workspace must be 256-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_E_INVALID, "softmax_scale is not finite");
+  int q0[KVQ_MAX_BATCH], nq[KVQ_MAX_BATCH], max_new = 0, max_len = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (n_new[i] < 0) return fail(KVQ_E_INVALID, "n_new[%d] is negative", i);
+    const int k = c->idx(layer, seq_ids[i]);
+    q0[i] = c->len[k];
+    nq[i] = n_new[i];
+    max_new = std::max(max_new, n_new[i]);
+    max_len = std::max(max_len, c->len[k] + n_new[i]);
+  }
+  if (max_new == 0) return KVQ_OK;
+  {   // the workspace this call's plan needs, checked before the append changes anything
+    int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH];
+    for (int i = 0; i < n_seqs; ++i) {
+      len[i] = q0[i] + nq[i];
+      bl[i] = body_len_after(c, layer, seq_ids[i], nq[i]);
+    }
+    kvq::MqSeq seqs[KVQ_MAX_BATCH];
+    const size_t need = mq_partials_bytes(c, plan_mq(c, n_seqs, len, bl, q0, nq, seqs));
+    if (need && (!workspace || ws_bytes < need))
+      return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  }
+  s = kvq_append(c, layer, n_seqs, seq_ids, n_new, k_bf16, v_bf16, stream);
+  if (s != KVQ_OK) return s;
+  return run_mq(c, layer, n_seqs, seq_ids, q0, nq, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
 }
 
 // Tiles the work-group that requantizes a decode step's evicted rows gives up (about the time those writes take).

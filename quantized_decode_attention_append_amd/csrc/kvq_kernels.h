@@ -182,6 +182,30 @@ inline size_t index_ws_seq_bytes(int n_wgs) {
   return round_up(words * 4 + (size_t)n_wgs * kIndexChunk * 8, 256);
 }
 
+// ---------------------------------------------------------------- multi-query attention (draft verification,
+// chunked prefill)
+
+// Queries of one sequence: positions q0 .. q0 + nq - 1 (q0 + nq <= len), rows row0 .. row0 + nq - 1 of q / out;
+// query p attends to positions [0, p]. Blocks of 8 consecutive queries, each block and KV head split n_splits ways:
+// with n_ring_splits == 0 the splits share the block's whole tile list (body tiles, then ring tiles), else
+// n_splits - n_ring_splits body splits and n_ring_splits ring splits.
+struct MqSeq {
+  size_t slab;
+  int len, body_len;
+  int q0, nq, row0;
+  int n_splits, n_ring_splits;
+  int wg_begin;
+};
+struct MqArgs {
+  Geometry g;
+  const uint16_t* q;        // [rows][Hq][D] bf16
+  float* out;               // [rows][Hq][D]
+  float* partials;          // [rows][Hkv][max_splits][8 (D + 2)] (used when n_splits > 1)
+  int n_seqs, n_q_heads, group, max_splits;
+  float scale;
+  MqSeq seqs[kMaxBatch];
+};
+
 // Launch wrappers (return the launch status). With non-null events e0 / e1 the launch records the kernel's
 // start and end time in them (hipExtLaunchKernel: timestamps of the dispatch itself).
 hipError_t launch_calibrate(const CalibArgs& a, int n_items, hipStream_t s, hipEvent_t e0 = nullptr,
@@ -200,7 +224,10 @@ hipError_t launch_gather(const GatherArgs& a, int grid_x, hipStream_t s, hipEven
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_index_write(const IndexWriteArgs& a, int n_positions, hipStream_t s, hipEvent_t e0 = nullptr,
                               hipEvent_t e1 = nullptr);
-// The three selection launches; e0 / e1 bracket the scoring and picking launches.
+hipError_t launch_mq(const MqArgs& a, int grid_x, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+hipError_t launch_mq_combine(const MqArgs& a, int rows, hipStream_t s, hipEvent_t e0 = nullptr,
+                             hipEvent_t e1 = nullptr);
+// The selection launches; e0 / e1 bracket the scoring and finishing launches.
 hipError_t launch_index_select(const IndexArgs& a, int total_wgs, hipStream_t s, hipEvent_t e0 = nullptr,
                                hipEvent_t e1 = nullptr);
 

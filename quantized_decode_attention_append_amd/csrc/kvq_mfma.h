@@ -262,5 +262,55 @@ __device__ inline float wave_max_16_32(float x) { return max_xor32(max_xor16(x))
 // other lines and sustain a much higher read rate on gfx950 than ordinary loads.
 __device__ inline u32x4 ldnt(const uint8_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 
+
+// ------------------------------------------------------------------ per-wave attention state
+
+struct WaveState {
+  floatx4 o[16];   // C[row = 4g + r][col = d16] per n-tile: rows 0-7 hi heads, 8-15 lo heads
+  float m;         // running max (exp2 domain) of this lane's head
+  float l;         // running sum of p over this lane's positions
+};
+
+__device__ inline float lo_h(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ inline float hi_h(uint32_t w) { return (float)as_h2(w)[1]; }
+
+// Online-softmax update for this lane's 8 scores x[] (exp2 domain, -inf for masked positions); returns p[].
+// The scores are exponentiated against a reference max that moves only when some score of the wave exceeds it
+// by more than kLazy: until then p <= 2^kLazy, well inside the range of the fp32 accumulators and of the fp16 /
+// bf16 P.V operands, and the accumulators need no rescale (the split merge uses whatever reference a partial
+// carries).
+constexpr float kLazy = 8.0f;
+
+__device__ inline void softmax_update(WaveState& st, const float* x, float* p) {
+  float tmax = kNegBig;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+  tmax = wave_max_16_32(tmax);
+  if (__builtin_amdgcn_ballot_w64(tmax > st.m + kLazy)) {
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+    // The accumulator rows of lane (g, m16) are rows 4g..4g+3 of the P.V tile, i.e. heads 4g..4g+3 (hi parts for
+    // g < 2, lo parts for g >= 2), not the lane's own score column m16: take those heads' factors from the lanes
+    // of this 16-lane row that hold columns 4g..4g+3.
+    const int lane = threadIdx.x & 63;
+    const int src = (lane & 48) + ((lane >> 4) << 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((src + r) << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+      for (int n = 0; n < 16; ++n) st.o[n][r] *= ar;
+    }
+  }
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(x[i] - st.m);
+    psum += p[i];
+  }
+  st.l += psum;
+}
+
 }  // namespace
 }  // namespace kvq

@@ -27,8 +27,8 @@ _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_truncate", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
-           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_index_write", "kvq_index_workspace_bytes", "kvq_index_select", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
-KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5, "index": 6}
+           "kvq_append_evict", "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_multi", "kvq_decode_step", "kvq_sparse_decode_attn", "kvq_sparse_decode_step", "kvq_index_write", "kvq_index_workspace_bytes", "kvq_index_select", "kvq_prefill_attn", "kvq_prefill_workspace_bytes", "kvq_timing_enable", "kvq_timing_read", "kvq_last_error")
+KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5, "index": 6, "mq": 7}
 
 
 _OPTIONAL = ("layout", "index_dim", "index_pool")
@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
         "kvq_sparse_decode_attn": (I32, [P, I32, I32, IP, P, P, I32, P, F, P, SZ, P]),
         "kvq_sparse_decode_step": (I32, [P, I32, I32, IP, P, P, P, P, I32, P, F, P, SZ, P]),
         "kvq_index_write": (I32, [P, I32, I32, IP, IP, P, P]),
+        "kvq_prefill_attn": (I32, [P, I32, I32, IP, IP, P, P, P, P, F, P, SZ, P]),
+        "kvq_prefill_workspace_bytes": (SZ, [P, I32, I32, I32]),
         "kvq_index_workspace_bytes": (SZ, [P, I32, I32]),
         "kvq_index_select": (I32, [P, I32, I32, IP, P, I32, I32, P, P, SZ, P]),
         "kvq_timing_enable": (I32, [P, I32]),
@@ -379,5 +381,40 @@ class Cache:
         _check(_lib.kvq_index_select(self._h, layer, n, _ids(seq_ids), _dev(query, query.dtype, "query"), int(budget),
                                      int(n_recent), _dev(out, torch.int32, "out"),
                                      _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                     ctypes.c_void_p(_stream(stream))))
+        return out
+
+    # ---------------------------------------------------------------- chunked prefill
+    def prefill_workspace_bytes(self, n_seqs: int, max_new: int, max_len: int) -> int:
+        return int(_lib.kvq_prefill_workspace_bytes(self._h, n_seqs, max_new, max_len))
+
+    def prefill_attn(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor, v: torch.Tensor,
+                     q: torch.Tensor, out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+        """append() of n_new[i] tokens per sequence, then causal attention of their queries over the cache as it
+        then stands. k, v: bf16 [sum(n_new), Hkv, D]; q: bf16 [sum(n_new), Hq, D]; returns fp32 [sum(n_new), Hq, D]."""
+        total = int(sum(int(n) for n in n_new))
+        for name, t in (("k", k), ("v", v)):
+            if t.numel() != total * self.hk * self.d or t.element_size() != 2:
+                raise ValueError(f"{name} must be bf16 [{total}, Hkv, D]")
+        if q.numel() != total * self.hq * self.d or q.element_size() != 2:
+            raise ValueError("q must be bf16 [sum(n_new), Hq, D]")
+        if out is None:
+            out = torch.empty((total, self.hq, self.d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            max_new = max(1, max(int(x) for x in n_new))
+            max_len = max(1, max(self.lengths(layer, s)[0] + int(x) for s, x in zip(seq_ids, n_new)))
+            need = max(self.prefill_workspace_bytes(len(seq_ids), max_new, max_len), 256)
+            ws = getattr(self, "_pws", None)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+                self._pws = ws
+            workspace = ws
+        if total == 0:
+            return out
+        nn = (ctypes.c_int32 * len(n_new))(*[int(x) for x in n_new])
+        _check(_lib.kvq_prefill_attn(self._h, layer, len(seq_ids), _ids(seq_ids), nn, _dev(k, k.dtype, "k"),
+                                     _dev(v, v.dtype, "v"), _dev(q, q.dtype, "q"), _dev(out, torch.float32, "out"),
+                                     float(softmax_scale), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                      ctypes.c_void_p(_stream(stream))))
         return out

@@ -157,3 +157,70 @@ def test_multi_query_needs_as_many_positions_as_queries():
     o, *_ = _cache(n=3)
     with pytest.raises(ValueError):
         multi_query_reference(o, 0, [0], _mq(1, 1, 4))
+
+
+# ---- chunked prefill: the query of new token j attends causally to the cache as it stands after the append
+
+def _bf16_of(x):
+    from workloads import bf16_bits
+    return bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_prefill_with_zero_keys_is_the_running_mean_of_values():
+    """Closed form: with all keys zero every score is equal, so the query at position p returns the mean of the
+    stored V over positions 0..p. With a bf16 ring wider than the context V is stored exactly, so the mean is of
+    the inputs themselves; two sequences with ragged chunks (one of them empty) check the packed row order."""
+    from oracle import prefill_reference
+    c = dict(n_layers=1, max_seqs=3, capacity=256, n_q_heads=4, n_kv_heads=2, head_dim=256,
+             k_bits=4, v_bits=4, kvarn=0, tail_len=200, tail_slack=32, tail_dtype=1)
+    o = OracleCache(c)
+    rng = np.random.default_rng(5)
+    vals = {0: [], 2: []}
+    for n_new in ([13, 0], [7, 20], [1, 3]):
+        total = sum(n_new)
+        k = _bf16_of(np.zeros((total, 2, 256)))
+        v = _bf16_of(rng.standard_normal((total, 2, 256)))
+        q = small_query(int(total), total, 4, 256)
+        o.append(0, [0, 2], n_new, k, v)
+        got = prefill_reference(o, 0, [0, 2], n_new, q)
+        row = 0
+        for i, sid in enumerate((0, 2)):
+            vf = (v[row:row + n_new[i]].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            for j in range(n_new[i]):
+                vals[sid].append(vf[j])
+                hist = np.stack(vals[sid])                    # positions 0 .. p of this sequence
+                want = hist.mean(axis=0)                      # [Hkv, D]
+                for h in range(4):
+                    np.testing.assert_allclose(got[row + j, h], want[h // 2], atol=1e-12, rtol=0)
+            row += n_new[i]
+
+
+def test_prefill_rows_equal_dense_decode_of_fresh_prefix_caches():
+    """Without a ring the stored codes of a prefix do not depend on what follows: row j of a chunk equals dense
+    decode over a fresh cache holding only positions 0..p (p its position), appended in the same chunks."""
+    from oracle import prefill_reference
+    c = dict(n_layers=1, max_seqs=1, capacity=512, n_q_heads=16, n_kv_heads=2, head_dim=256,
+             k_bits=5, v_bits=3, kvarn=0, tail_len=0, tail_slack=0, tail_dtype=0)
+    k, v = small_tokens(41, 140, 2, 256)
+    q = small_query(42, 140, 16, 256)
+    o = OracleCache(c)
+    o.append(0, [0], [100], k[:100], v[:100])
+    o.append(0, [0], [40], k[100:], v[100:])
+    rows = [0, 17, 39]
+    got = prefill_reference(o, 0, [0], [40], q[100:], rows=rows)
+    for r_i, j in enumerate(rows):
+        p = 100 + j
+        fresh = OracleCache(c)
+        fresh.append(0, [0], [100], k[:100], v[:100])
+        fresh.append(0, [0], [j + 1], k[100:p + 1], v[100:p + 1])
+        want = decode_reference(fresh, 0, [0], q[100 + j][None])[0]
+        np.testing.assert_allclose(got[r_i], want, atol=1e-12, rtol=0)
+
+
+def test_prefill_last_row_is_dense_decode_of_the_whole_cache():
+    from oracle import prefill_reference
+    o, *_ = _cache()
+    n, _ = o.lengths(0, 0)
+    q = small_query(3, 4, 16, 256)
+    got = prefill_reference(o, 0, [0], [4], q, rows=[3])
+    np.testing.assert_array_equal(got[0], decode_reference(o, 0, [0], q[3][None])[0])

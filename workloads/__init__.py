@@ -166,6 +166,15 @@ def query(cfg: int, layer: int, seq: int, step: int, n_q_heads: int = 16, head_d
     return bf16_bits(r.standard_normal((n_q_heads, head_dim), dtype=np.float32))
 
 
+def prefill_queries(cfg: int, layer: int, seq: int, start: int, n: int, n_q_heads: int = 16,
+                    head_dim: int = 256) -> np.ndarray:
+    """Queries of prefill tokens [start, start + n) of one (layer, seq): bf16 bits [n, Hq, D], N(0, 1), drawn
+    per 4096-token chunk like kv_tokens (``start`` chunk-aligned)."""
+    assert start % CHUNK == 0 and n <= CHUNK, (start, n)
+    r = _rng(cfg, layer, seq, start // CHUNK, KIND_Q)
+    return bf16_bits(r.standard_normal((n, n_q_heads, head_dim), dtype=np.float32))
+
+
 def sparse_positions(cfg: int, layer: int, seq: int, step: int, length: int, budget: int,
                      recent: int) -> np.ndarray:
     """Budget of distinct positions in [0, length): the newest ``recent`` plus uniform draws
