@@ -23,7 +23,9 @@ replayed back to back), `cold` (single-layer workloads: decode time after a 512 
 the MALL), `copy_ceiling_gbs` (a plain 1 GiB device copy, bytes read + written per second) and
 `read_ceiling` (a plain read-only pass over 1 GiB, and over the decode call's own byte count, by the
 streaming-read probe). With --verify-queries T, `multi_query` times multi-query decode of the last T
-positions of every sequence (verification of T - 1 drafted tokens) over every layer.
+positions of every sequence (verification of T - 1 drafted tokens) over every layer. With --prefill, `prefill`
+times chunked prefill attention (append + causal attention of each 4096-token chunk) of layer 0 of the first
+sequence over its whole context.
 """
 from __future__ import annotations
 
@@ -436,7 +438,7 @@ def multi_query_leg(torch, cache, cfg, L, seqs, qin, n_q, reps, dev):
         run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kind = "gather" if cfg.get("layout", 0) == 1 else "decode"
+    kind = "gather" if cfg.get("layout", 0) == 1 else ("mq" if n_q > 1 else "decode")
     cache.timing(True)
     for _ in range(reps):
         run()
@@ -452,6 +454,62 @@ def multi_query_leg(torch, cache, cfg, L, seqs, qin, n_q, reps, dev):
             "unique_bytes_per_call": int(unique),
             "unique_GBs": round(unique / (k_us * 1e-6) / 1e9, 2),
             "frac": round(unique / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def prefill_leg(torch, kvq, W, wl, cfg, dev, reps: int = 2) -> dict:
+    """Chunked prefill of layer 0 of the workload's first sequence through kvq_prefill_attn: 4096-token chunks,
+    each appended and then attended causally by its own queries over the cache as it then stands. The chunk
+    inputs (K, V, queries) are generated and copied to HBM first; the sequence is reset between passes. Reports
+    prompt tokens per second (wall clock over the whole context), the multi-query and append kernels'
+    dispatch-stamped totals, and the attention rate in useful FLOP/s (QK and PV: 4 x Hq x D per query and
+    attended position) against the fp16 dense MFMA peak."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = wl.contexts[0]
+    pcfg = dict(cfg, n_layers=1, max_seqs=1, capacity=((n + 31) // 32) * 32)
+    pcfg.pop("index_dim", None)
+    pcfg.pop("index_pool", None)
+    cache = kvq.Cache(pcfg)
+    starts = list(range(0, n, W.CHUNK))
+
+    def gen(s):
+        m = min(W.CHUNK, n - s)
+        k, v = W.kv_tokens(wl.cfg, 0, 0, s, m)
+        q = W.prefill_queries(wl.cfg, 0, 0, s, m, wl.n_q_heads, wl.head_dim)
+        return [torch.from_numpy(x.view(np.int16)).to(dev) for x in (k, v, q)]
+
+    with ThreadPoolExecutor(max_workers=cpu_pool_size()) as ex:
+        inputs = list(ex.map(gen, starts))
+    out = torch.empty((W.CHUNK, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(cache.prefill_workspace_bytes(1, W.CHUNK, n), 256), dtype=torch.uint8, device=dev)
+
+    def run():
+        cache.seq_reset(0, [0])
+        for s, (k, v, q) in zip(starts, inputs):
+            m = k.shape[0]
+            cache.prefill_attn(0, [0], [m], k, v, q, out=out[:m], workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    cache.timing(True)
+    run()
+    torch.cuda.synchronize()
+    kt = {k: cache.timing_read(k) for k in ("mq", "combine", "append")}
+    cache.timing(False)
+    pairs = n * (n + 1) // 2                      # (query, attended position) pairs of the causal prefill
+    flops = 4.0 * wl.n_q_heads * wl.head_dim * pairs
+    mq_s = kt["mq"][0] / 1e3
+    log(f"prefill of {n} tokens (layer 0): {wall * 1e3:.1f} ms, multi-query kernels {mq_s * 1e3:.1f} ms")
+    del inputs, cache
+    return {"tokens": n, "chunk": W.CHUNK, "ms": round(wall * 1e3, 3), "tok_per_s": round(n / wall, 1),
+            "kernel_ms": {k: round(v[0], 3) for k, v in kt.items()},
+            "launches": {k: v[1] for k, v in kt.items()},
+            "attn_useful_TFLOPs": round(flops / mq_s / 1e12, 2),
+            "frac_fp16_mfma_peak": round(flops / mq_s / 1e12 / 2500.0, 4)}
 
 
 def indexer_leg(torch, cache, cfg, wl, L, seqs, first_step, n_steps, ws, dev):
@@ -532,6 +590,10 @@ def main() -> int:
                     help="sparse workload: also time steps whose positions the QSA indexer chooses (append, index key "
                          "write, index select of the budget with the newest `recent` forced, sparse decode), reported "
                          "as the line's indexer object")
+    ap.add_argument("--prefill", action="store_true",
+                    help="dense workloads: also time chunked prefill attention of layer 0 of the first sequence over "
+                         "its whole context (append + causal attention of each 4096-token chunk), reported as the "
+                         "line's prefill object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
@@ -688,6 +750,9 @@ def main() -> int:
     multi = None
     if args.verify_queries and not sparse:
         multi = multi_query_leg(torch, cache, cfg, L, seqs, qin, args.verify_queries, args.steps, dev)
+    pre = None
+    if args.prefill and not sparse and cfg.get("layout", 0) == 0:
+        pre = prefill_leg(torch, kvq, W, wl, cfg, dev)
     main_kernel = "gather" if (sparse or cfg.get("layout", 0) == 1) else "decode"
     ms, n = times[main_kernel]
     avg_s = ms / 1e3 / max(n, 1)
@@ -734,6 +799,8 @@ def main() -> int:
         res["multi_query"] = multi
     if indexed is not None:
         res["indexer"] = indexed
+    if pre is not None:
+        res["prefill"] = pre
     gbytes = float(sum(nbytes)) / args.steps   # the graph steps read the same bytes per step (to a few rows)
     res["graph"] = {"ms_per_step": round(graph * 1e3, 4), "value": round(gbytes / graph / 1e9, 2), "unit": "GB/s",
                     "how": f"one HIP graph per step ({L} layers), all {args.steps} captured before timing, "

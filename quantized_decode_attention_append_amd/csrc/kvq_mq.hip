@@ -7,12 +7,13 @@
 // A work-group of 8 waves takes one query block of one KV head over a range of the block's prefix tiles (the
 // qN_0 body tiles, then the ring tiles). Per 32-position tile:
 // * the work-group loads the raw tile once (every thread one to four 16-byte pieces, one tile ahead in
-//   registers) and decodes it cooperatively into MFMA operands in LDS: K codes and V codes as exact fp16
-//   integers (the "1024 + value" form), in the operand order of the decode kernel, plus the tile's fp16 scales;
-//   bf16 / f16 ring tiles are stored in that order already and are copied as they are;
+//   registers) and decodes it cooperatively into MFMA operands in LDS, in the operand order of the decode
+//   kernel: K codes as exact fp16 integers (the "1024 + value" form) with the tile's fp16 K scales, and each V
+//   code times its block scale as an fp16 pair, the rounded product and the (exact) remainder; bf16 / f16 ring
+//   tiles are stored in that order already and are copied as they are;
 // * wave w then computes query w of the block on its own: QK on MFMA (8 heads of the group as hi / lo fp16
 //   columns of the exponent-shifted query), the per-(position, block) K scale in fp32, its own causal mask,
-//   online softmax, and P.V on MFMA with A = P * dv split into hi / lo fp16 rows.
+//   online softmax, and P.V on MFMA with A = P split into hi / lo fp16 rows, against both V parts.
 // The operands are double-buffered, so a tile costs two work-group barriers. Each wave writes its query's
 // partial (max, sum, output) record; with one split per block it writes the normalized output instead.
 #include <hip/hip_runtime.h>
@@ -29,9 +30,9 @@ constexpr int kRawChunks = 2 * 32 * 272 / 16;   // 16-byte pieces of the largest
 
 struct MqOps {                 // one tile's MFMA operands in LDS
   u32x4 k[2 * 8 * 64];         // K operands [subtile][block][lane]: 8 codes (or 16-bit values) per lane
-  u32x4 v[16 * 64];            // V operands [n-tile][lane]
+  u32x4 v[16 * 64];            // V operands [n-tile][lane]: code x scale, fp16 rounded (or 16-bit values)
+  u32x4 vl[16 * 64];           // V operands, the remainders: code x scale - v, fp16 (exact)
   uint16_t ks[8 * 32];         // K scales [block][position]
-  uint16_t vs[8 * 32];         // V scales [block][position]
 };
 
 enum { kKindQ = 0, kKindQ8Ring = 1, kKindBf16Ring = 2, kKindF16Ring = 3 };
@@ -102,21 +103,39 @@ __device__ inline void decode_k_tile(const uint8_t* raw, MqOps& ops, uint32_t ma
   }
 }
 
-// V operands of one tile: thread t decodes n-tiles 2(t / 64) and 2(t / 64) + 1 of lane t % 64.
+// A V piece (8 exact fp16 codes, positions in operand order) times the scales of its positions: the fp16
+// rounded products and their remainders (each remainder exact: a product of an 8-bit code and an fp16 scale
+// has at most 19 significant bits).
+__device__ inline void scale_v_piece(half8 c, const uint32_t* dv, u32x4& hi, u32x4& lo) {
+  const u32x4 r = __builtin_bit_cast(u32x4, c);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const half2v h = as_h2(r[k]) * as_h2(dv[k]);
+    hi[k] = as_u(h);
+    lo[k] = as_u(__builtin_elementwise_fma(as_h2(r[k]), as_h2(dv[k]), -h));
+  }
+}
+
+// V operands of one tile: thread t decodes n-tiles 2(t / 64) and 2(t / 64) + 1 (block t / 64) of lane t % 64;
+// vscale: the tile's V scales [block][position].
 template <int N>
-__device__ inline void decode_v_tile(const uint8_t* raw, MqOps& ops, uint32_t magic) {
+__device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, MqOps& ops, uint32_t magic) {
   constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
   const int t = threadIdx.x;
-  const int lane = t & 63, np = t >> 6;
+  const int lane = t & 63, np = t >> 6, g = lane >> 4;
   uint32_t r0[4 * w0], r1[w1 ? 4 * w1 : 1], r2[w2 ? 4 * w2 : 1];
   raw_v_run<w0>(raw, 0, lane, r0);
   if constexpr (w1 > 0) raw_v_run<w1>(raw, 1024 * w0, lane, r1);
   if constexpr (w2 > 0) raw_v_run<w2>(raw, 1024 * (w0 + w1), lane, r2);
-  u32x4* dst = ops.v + 2 * np * 64 + lane;
+  // the scales of operand rows 8g..8g+7: positions 4g..4g+3 and 16+4g..16+4g+3 of block np
+  const u32x2 d0 = *(const u32x2*)(vscale + 2 * (np * 32 + 4 * g));
+  const u32x2 d1 = *(const u32x2*)(vscale + 2 * (np * 32 + 16 + 4 * g));
+  const uint32_t dv[4] = {d0[0], d0[1], d1[0], d1[1]};
+  const int o = 2 * np * 64 + lane;
 #define KVQ_VP(P)                                                                                        \
   case P:                                                                                                \
-    dst[0] = __builtin_bit_cast(u32x4, decode_run_piece<N, 2 * P>(r0, r1, r2, magic));                   \
-    dst[64] = __builtin_bit_cast(u32x4, decode_run_piece<N, 2 * P + 1>(r0, r1, r2, magic));              \
+    scale_v_piece(decode_run_piece<N, 2 * P>(r0, r1, r2, magic), dv, ops.v[o], ops.vl[o]);                \
+    scale_v_piece(decode_run_piece<N, 2 * P + 1>(r0, r1, r2, magic), dv, ops.v[o + 64], ops.vl[o + 64]);  \
     break;
   switch (np) { KVQ_VP(0) KVQ_VP(1) KVQ_VP(2) KVQ_VP(3) KVQ_VP(4) KVQ_VP(5) KVQ_VP(6) default: KVQ_VP(7) }
 #undef KVQ_VP
@@ -153,31 +172,23 @@ __device__ inline void mq_qk_q(const MqOps& ops, const half8* qop, float qmul, f
     for (int r = 0; r < 4; ++r) x[4 * s + r] = (sc[s][r] + dpp_ror8(sc[s][r])) * qmul;
 }
 
-// P.V of a qN_0 (or q8_0 ring) tile: for block B, A = P * dv16 as fp16 hi (lane_mask = 0) or lo parts.
-__device__ inline void mq_pv_q(WaveState& st, const MqOps& ops, const float* p, uint32_t lane_mask) {
+// P.V of a qN_0 (or q8_0 ring) tile: A = P as fp16 hi (rows 0-7) and lo (rows 8-15) parts, against the scaled
+// V values and their remainders, so the four partial products sum to P x code x scale.
+__device__ inline void mq_pv_q(WaveState& st, const MqOps& ops, const float* p, bool lo_lane) {
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  float pm[8];
+  const float kf = lo_lane ? 1.0f : 0.0f;
+  half8 a;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pm[i] = __uint_as_float(__float_as_uint(p[i]) & lane_mask);
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 h = (_Float16)p[i];
+    a[i] = (_Float16)fmaf(-kf, (float)h, p[i]);
+  }
 #pragma unroll
-  for (int B = 0; B < 8; ++B) {
-    const u32x2 d0 = *(const u32x2*)(ops.vs + B * 32 + 4 * g);
-    const u32x2 d1 = *(const u32x2*)(ops.vs + B * 32 + 16 + 4 * g);
-    const uint32_t dw[4] = {d0[0], d0[1], d1[0], d1[1]};
-    half8 a;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const half2v d = as_h2(dw[j]);
-      const _Float16 h0 = (_Float16)fmaf(pm[2 * j], (float)d[0], 0.0f);
-      const _Float16 h1 = (_Float16)fmaf(pm[2 * j + 1], (float)d[1], 0.0f);
-      a[2 * j] = (_Float16)fmaf(p[2 * j], (float)d[0], -(float)h0);
-      a[2 * j + 1] = (_Float16)fmaf(p[2 * j + 1], (float)d[1], -(float)h1);
-    }
-    st.o[2 * B] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, ops.v[(2 * B) * 64 + lane]),
-                                                         st.o[2 * B], 0, 0, 0);
-    st.o[2 * B + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-        a, __builtin_bit_cast(half8, ops.v[(2 * B + 1) * 64 + lane]), st.o[2 * B + 1], 0, 0, 0);
+  for (int n = 0; n < 16; ++n) {
+    st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, ops.v[n * 64 + lane]), st.o[n], 0, 0,
+                                                     0);
+    st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, ops.vl[n * 64 + lane]), st.o[n], 0,
+                                                     0, 0);
   }
 }
 
@@ -403,7 +414,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   st.l = 0.0f;
 #pragma unroll
   for (int n = 0; n < 16; ++n) st.o[n] = floatx4{0, 0, 0, 0};
-  const uint32_t lane_mask = lo_lane ? 0xFFFFFFFFu : 0u;
   uint32_t magic = kMagic;
   asm volatile("" : "+v"(magic));
 
@@ -441,15 +451,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     if (!raw16) {
       const uint8_t* raw = (const uint8_t*)s_raw;
+      const uint8_t* vscale = raw + r.kbytes + r.vbytes - 512;   // the V tile's last 512 bytes
       if (r.kind == kKindQ) {
         decode_k_tile<NK>(raw, ops, magic);
-        decode_v_tile<NV>(raw + r.kbytes, ops, magic);
+        decode_v_tile<NV>(raw + r.kbytes, vscale, ops, magic);
       } else {
         decode_k_tile<8>(raw, ops, magic);
-        decode_v_tile<8>(raw + r.kbytes, ops, magic);
+        decode_v_tile<8>(raw + r.kbytes, vscale, ops, magic);
       }
-      if (tid < 32) ((u32x4*)ops.ks)[tid] = s_raw[nk - 32 + tid];              // the tiles' last 512 bytes
-      else if (tid < 64) ((u32x4*)ops.vs)[tid - 32] = s_raw[nk + nv - 64 + tid];
+      if (tid < 32) ((u32x4*)ops.ks)[tid] = s_raw[nk - 32 + tid];              // the K tile's last 512 bytes
       __syncthreads();
     }
     // this wave's query over the tile: positions [lo, hi) of the tile's segment, causally up to qpos
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (pos < lo || pos >= hi) x[4 * s + rr] = -INFINITY;
           }
         softmax_update(st, x, p);
-        if (body || r.kind == kKindQ8Ring) mq_pv_q(st, ops, p, lane_mask);
+        if (body || r.kind == kKindQ8Ring) mq_pv_q(st, ops, p, lo_lane);
         else if (r.kind == kKindF16Ring) mq_pv_16<true>(st, ops, p, lo_lane);
         else mq_pv_16<false>(st, ops, p, lo_lane);
       }
