@@ -68,8 +68,8 @@ typedef struct {
   int32_t n_q_heads;    /* query heads; n_q_heads / n_kv_heads <= 8                           */
   int32_t n_kv_heads;   /* KV heads                                                          */
   int32_t head_dim;     /* 256 (the layout also covers 128; kernels are built for 256)       */
-  int32_t k_bits;       /* 2..8: qN_0 width of the K body                                     */
-  int32_t v_bits;       /* 2..8: qN_0 width of the V body                                     */
+  int32_t k_bits;       /* 2..8: code width of the K body (qN_0, or qN_1 with k_min)           */
+  int32_t v_bits;       /* 2..8: code width of the V body (qN_0, or qN_1 with v_min)           */
   int32_t kvarn;        /* 0/1: per-channel variance normalization before block quantization */
   int32_t tail_len;     /* W: newest tokens kept in the tail ring (0 = no ring)                */
   int32_t tail_slack;   /* S: extra ring slots; ring capacity R = W + S must be a multiple of 32 */
@@ -78,6 +78,10 @@ typedef struct {
   int32_t index_dim;    /* 0: no indexer; else the QSA indexer head dim, whose keys are pooled to 32 values
                            (offload page: indexer_head_dim 128, compress ratio 4): index_dim = 32 x index_pool */
   int32_t index_pool;   /* pooling ratio of the index keys: 1, 2, 4, 8 or 16 (ignored when index_dim == 0)  */
+  int32_t k_min;        /* 0: K body qN_0 (one fp16 scale per 32 values); 1: qN_1, a scale and an fp16 minimum
+                           per 32 values, value = scale x code + minimum with codes 0..2^N-1 (BeeLlama page,
+                           q2_1 .. q6_1; KVarN benchmark page, q5_1 and q8_0-q5_1). Needs KVQ_LAYOUT_TILES.   */
+  int32_t v_min;        /* 0/1: the same for the V body                                                    */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache;
@@ -90,7 +94,7 @@ enum { KVQ_REGION_K_BODY = 0, KVQ_REGION_V_BODY = 1, KVQ_REGION_K_RING = 2, KVQ_
 kvq_status kvq_config_validate(const kvq_config* cfg);
 
 /* Exact arena size in bytes for cfg (0 if cfg is invalid). The body costs N bits per value plus one
- * fp16 scale per 32 values; a tail ring costs R slots of bf16 or q8_0 rows; KVarN adds D fp16 scales
+ * fp16 scale (qN_1: and one fp16 minimum) per 32 values; a tail ring costs R slots of bf16 or q8_0 rows; KVarN adds D fp16 scales
  * per (layer, sequence, KV head, K/V). At 16 layers x 4 KV heads x 256 x 65,536 positions this gives the
  * BeeLlama page's KV MiB column for q4_0..q8_0 at tail 0 / 1024 / 2048. */
 size_t kvq_cache_bytes(const kvq_config* cfg);

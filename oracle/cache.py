@@ -1,9 +1,11 @@
-"""Cache state machine: qN_0 body, precision tail / 8-bit ring, requantization (oracle).
+"""Cache state machine: qN_0 or qN_1 body, precision tail / 8-bit ring, requantization (oracle).
 
 Test infrastructure only. Follows, step by step:
 
 * qN_0 body with separate K and V widths (KVarN benchmark page, K/V pair table;
-  "Hard numbers on Qwen3.8-27B's KV cache" page, K 6-bit / V 5-bit setting D).
+  "Hard numbers on Qwen3.8-27B's KV cache" page, K 6-bit / V 5-bit setting D); either
+  side may instead be qN_1, a scale and a minimum per block (BeeLlama.cpp v0.4.1 page,
+  q2_1 .. q6_1; KVarN benchmark page, the q8_0-q5_1 pair). The 8-bit ring stays q8_0.
 * Precision tail: the newest W tokens are kept in bf16 or f16, the rest quantized as
   usual (BeeLlama.cpp v0.4.1 page, KV cache precision tail paragraph and feature list).
   Reading for f16: the bf16 input is converted to IEEE binary16 with round to nearest
@@ -32,7 +34,7 @@ import numpy as np
 
 from .layout import (pack_k_rows, pack_k_tiles, pack_bf16_k_tiles, pack_v_tiles, pack_bf16_v_tiles,
                      slab_layout, TILE)
-from .quant import quantize_blocks, kvarn_sigma, normalize, dequantize_blocks
+from .quant import quantize_blocks, quantize_blocks_min, kvarn_sigma, normalize, dequantize_blocks, dequantize_blocks_min
 from . import indexer
 
 TAIL_NONE, TAIL_BF16, TAIL_Q8, TAIL_F16 = 0, 1, 2, 3
@@ -66,6 +68,9 @@ class _SeqState:
         self.kd = np.zeros((cap32, hk, nb), dtype=np.float16)
         self.vu = np.zeros((cap32, hk, d), dtype=np.uint8)
         self.vd = np.zeros((cap32, hk, nb), dtype=np.float16)
+        # qN_1 bodies: the block minima (zero rows for a qN_0 side, never read)
+        self.km = np.zeros((cap32, hk, nb), dtype=np.float16)
+        self.vm = np.zeros((cap32, hk, nb), dtype=np.float16)
         if cfg.get("index_dim", 0):
             self.ikey = np.zeros((cap32, indexer.POOLED), dtype=np.uint16)   # pooled index keys, bf16 bits
         r = lay["ring_slots"]
@@ -89,6 +94,8 @@ class OracleCache:
         self.R = self.lay["ring_slots"]
         self.tail = cfg["tail_dtype"] if self.W > 0 else TAIL_NONE
         self.rows = cfg.get("layout", LAYOUT_TILES) == LAYOUT_ROWS   # V stored as rows, like K
+        self.k_min = bool(cfg.get("k_min", 0))   # qN_1 bodies (scale and minimum per block)
+        self.v_min = bool(cfg.get("v_min", 0))
         self.state = {}
 
     # ------------------------------------------------------------------ helpers
@@ -128,8 +135,14 @@ class OracleCache:
         if self.cfg["kvarn"]:
             k32 = normalize(k32, s.sigma[:, 0, :])
             v32 = normalize(v32, s.sigma[:, 1, :])
-        s.ku[pos], s.kd[pos] = quantize_blocks(k32, self.cfg["k_bits"])
-        s.vu[pos], s.vd[pos] = quantize_blocks(v32, self.cfg["v_bits"])
+        if self.k_min:
+            s.ku[pos], s.kd[pos], s.km[pos] = quantize_blocks_min(k32, self.cfg["k_bits"])
+        else:
+            s.ku[pos], s.kd[pos] = quantize_blocks(k32, self.cfg["k_bits"])
+        if self.v_min:
+            s.vu[pos], s.vd[pos], s.vm[pos] = quantize_blocks_min(v32, self.cfg["v_bits"])
+        else:
+            s.vu[pos], s.vd[pos] = quantize_blocks(v32, self.cfg["v_bits"])
 
     def _write_ring(self, s: _SeqState, pos: np.ndarray, k_bits, v_bits):
         if len(pos) == 0:
@@ -254,8 +267,10 @@ class OracleCache:
         in_body = positions < s.body_len
         pb = positions[in_body]
         if len(pb):
-            kb = dequantize_blocks(s.ku[pb], s.kd[pb], self.cfg["k_bits"])
-            vb = dequantize_blocks(s.vu[pb], s.vd[pb], self.cfg["v_bits"])
+            kb = (dequantize_blocks_min(s.ku[pb], s.kd[pb], s.km[pb]) if self.k_min
+                  else dequantize_blocks(s.ku[pb], s.kd[pb], self.cfg["k_bits"]))
+            vb = (dequantize_blocks_min(s.vu[pb], s.vd[pb], s.vm[pb]) if self.v_min
+                  else dequantize_blocks(s.vu[pb], s.vd[pb], self.cfg["v_bits"]))
             if self.cfg["kvarn"]:
                 kb = kb * s.sigma[:, 0, :].astype(np.float64)
                 vb = vb * s.sigma[:, 1, :].astype(np.float64)
@@ -275,18 +290,21 @@ class OracleCache:
         s = self.st(layer, seq)
         kb, vb = self.cfg["k_bits"], self.cfg["v_bits"]
         d = self.cfg["head_dim"]
+        km = s.km[lo:hi, head] if self.k_min else None
+        vm = s.vm[lo:hi, head] if self.v_min else None
         if region == "k_body" and not self.rows:
             assert lo % TILE == 0 and hi % TILE == 0
-            return pack_k_tiles(s.ku[lo:hi, head].reshape(-1, TILE, d), s.kd[lo:hi, head].reshape(-1, TILE, d // 32), kb)
+            return pack_k_tiles(s.ku[lo:hi, head].reshape(-1, TILE, d), s.kd[lo:hi, head].reshape(-1, TILE, d // 32), kb,
+                                None if km is None else km.reshape(-1, TILE, d // 32))
         if region == "k_ring" and not self.rows:
             assert lo % TILE == 0 and hi % TILE == 0
             if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return pack_bf16_k_tiles(s.rk[lo:hi, head].reshape(-1, TILE, d))
             return pack_k_tiles(s.rku[lo:hi, head].reshape(-1, TILE, d), s.rkd[lo:hi, head].reshape(-1, TILE, d // 32), 8)
         if region == "k_body":
-            return pack_k_rows(s.ku[lo:hi, head], s.kd[lo:hi, head], kb)
+            return pack_k_rows(s.ku[lo:hi, head], s.kd[lo:hi, head], kb, km)
         if region == "v_body" and self.rows:
-            return pack_k_rows(s.vu[lo:hi, head], s.vd[lo:hi, head], vb)
+            return pack_k_rows(s.vu[lo:hi, head], s.vd[lo:hi, head], vb, vm)
         if region == "v_ring" and self.rows:
             if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return np.ascontiguousarray(s.rv[lo:hi, head]).view(np.uint8)
@@ -295,7 +313,7 @@ class OracleCache:
             assert lo % TILE == 0 and hi % TILE == 0
             u = s.vu[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"])
             d = s.vd[lo:hi, head].reshape(-1, TILE, self.cfg["head_dim"] // 32)
-            return pack_v_tiles(u, d, vb)
+            return pack_v_tiles(u, d, vb, None if vm is None else vm.reshape(-1, TILE, self.cfg["head_dim"] // 32))
         if region == "k_ring":
             if self.tail in _TAIL_16:   # 16-bit values, packed alike
                 return np.ascontiguousarray(s.rk[lo:hi, head]).view(np.uint8)

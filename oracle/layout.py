@@ -37,6 +37,13 @@ n = 0..NT-1 (NT * w bytes); they are interleaved across lanes in units of
 u = min(16, NT * w) bytes: [chunk][lane][u]. Then the NB x 32 fp16 scales,
 [block][position]. Tile bytes = 32 * NB * (4N + 2).
 
+qN_1 bodies (codes with a scale and a minimum per block): the codes are placed as
+above (u itself, 0 .. 2^N - 1, is what the planes hold); a K or V row ends with the NB
+fp16 scales and then the NB fp16 minima, both in block order (row bytes
+NB * (4N + 4)); a K tile ends with the scales [block][position] and then the
+minima [position][block]; a V tile with the scales and then the minima, both
+[block][position] (tile bytes 32 * NB * (4N + 4)).
+
 bf16 tail ring (tile layout): K tiles of 32 slots hold, for subtile s and block b,
 lane l = 16j + m's 8 bf16 values of channels 32b + 8j .. +7 of slot 16s + m:
 [s][b][lane][8 x bf16]; V tiles hold, for n-tile n and lane l, the 8 bf16 values
@@ -75,8 +82,10 @@ def _round_up(x: int, m: int) -> int:
     return (x + m - 1) // m * m
 
 
-def row_bytes(n_bits: int, head_dim: int) -> int:
-    return head_dim // BLOCK * (4 * n_bits + 2)
+def row_bytes(n_bits: int, head_dim: int, with_min: bool = False) -> int:
+    """Bytes of one K or V row: NB * (4N + 2), plus 2 * NB for the minima of a qN_1 row."""
+    nb = head_dim // BLOCK
+    return nb * (4 * n_bits + 2 + (2 if with_min else 0))
 
 
 def tile_positions() -> np.ndarray:
@@ -125,8 +134,9 @@ def unpack_pieces(b: np.ndarray, w: int, m: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- K rows
 
-def pack_k_rows(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
-    """Codes u [..., D] (uint8) and scales d16 [..., D/32] -> K rows [..., row_bytes]."""
+def pack_k_rows(u: np.ndarray, d16: np.ndarray, n_bits: int, m16=None) -> np.ndarray:
+    """Codes u [..., D] (uint8), scales d16 [..., D/32] and (qN_1) minima m16 [..., D/32] -> K rows
+    [..., row_bytes]."""
     u = np.asarray(u, dtype=np.uint8)
     d = u.shape[-1]
     nb = d // BLOCK
@@ -138,11 +148,14 @@ def pack_k_rows(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
         parts.append(pack_pieces(v, w).reshape(*u.shape[:-1], 4 * nb * w))
     parts.append(np.ascontiguousarray(np.asarray(d16, dtype=np.float16)).view(np.uint8)
                  .reshape(*u.shape[:-1], 2 * nb))
+    if m16 is not None:
+        parts.append(np.ascontiguousarray(np.asarray(m16, dtype=np.float16)).view(np.uint8)
+                     .reshape(*u.shape[:-1], 2 * nb))
     return np.concatenate(parts, axis=-1)
 
 
 def unpack_k_rows(rows: np.ndarray, n_bits: int, head_dim: int):
-    """K rows [..., row_bytes] -> (u [..., D], d16 [..., D/32])."""
+    """K rows [..., row_bytes] -> (u [..., D], d16 [..., D/32]) (the minima of a qN_1 row follow the scales)."""
     rows = np.asarray(rows, dtype=np.uint8)
     nb = head_dim // BLOCK
     lead = rows.shape[:-1]
@@ -172,8 +185,9 @@ def _k_tile_parts(n_bits: int, head_dim: int):
     return parts
 
 
-def pack_k_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
-    """Codes u [n_tiles, 32, D] and scales [n_tiles, 32, D/32] -> K tiles [n_tiles, tile_bytes]."""
+def pack_k_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int, m16=None) -> np.ndarray:
+    """Codes u [n_tiles, 32, D], scales [n_tiles, 32, D/32] and (qN_1) minima [n_tiles, 32, D/32] -> K tiles
+    [n_tiles, tile_bytes]."""
     u = np.asarray(u, dtype=np.uint8)
     ntl, tt, d = u.shape
     assert tt == TILE
@@ -189,6 +203,8 @@ def pack_k_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
         out.append(runs.reshape(ntl, 64, lb // cu, cu).transpose(0, 2, 1, 3).reshape(ntl, 64 * lb))
     sc = np.ascontiguousarray(np.asarray(d16, dtype=np.float16).transpose(0, 2, 1))   # [ntl, b, t]
     out.append(sc.view(np.uint8).reshape(ntl, 2 * nb * TILE))
+    if m16 is not None:   # minima [position][block]
+        out.append(np.ascontiguousarray(np.asarray(m16, dtype=np.float16)).view(np.uint8).reshape(ntl, 2 * nb * TILE))
     return np.concatenate(out, axis=-1)
 
 
@@ -242,8 +258,8 @@ def _v_gather_index(head_dim: int):
     return t_idx, d_idx
 
 
-def pack_v_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
-    """Codes u [n_tiles, 32, D] and scales [n_tiles, 32, D/32] -> tiles [n_tiles, tile_bytes]."""
+def pack_v_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int, m16=None) -> np.ndarray:
+    """Codes u [n_tiles, 32, D], scales [n_tiles, 32, D/32] and (qN_1) minima -> tiles [n_tiles, tile_bytes]."""
     u = np.asarray(u, dtype=np.uint8)
     ntl, tt, d = u.shape
     assert tt == TILE
@@ -260,6 +276,9 @@ def pack_v_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:
         parts.append(x.reshape(ntl, 64 * lb))
     sc = np.ascontiguousarray(np.asarray(d16, dtype=np.float16).transpose(0, 2, 1))   # [ntl, b, t]
     parts.append(sc.view(np.uint8).reshape(ntl, -1))
+    if m16 is not None:   # minima [block][position]
+        mn = np.ascontiguousarray(np.asarray(m16, dtype=np.float16).transpose(0, 2, 1))
+        parts.append(mn.view(np.uint8).reshape(ntl, -1))
     return np.concatenate(parts, axis=-1)
 
 
@@ -317,8 +336,8 @@ def slab_layout(cfg: dict) -> dict:
     d = cfg["head_dim"]
     hk = cfg["n_kv_heads"]
     cap32 = _round_up(cfg["capacity"], TILE)
-    rk = row_bytes(cfg["k_bits"], d)
-    rv = row_bytes(cfg["v_bits"], d)
+    rk = row_bytes(cfg["k_bits"], d, bool(cfg.get("k_min", 0)))
+    rv = row_bytes(cfg["v_bits"], d, bool(cfg.get("v_min", 0)))
     r = ring_slots(cfg)
     if cfg["tail_len"] > 0 and cfg["tail_dtype"] in (1, 3):   # bf16 or f16 values
         ring_rk = ring_rv = 2 * d

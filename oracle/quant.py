@@ -1,4 +1,4 @@
-"""qN_0 block quantizer and KVarN normalization (oracle; test infrastructure only).
+"""qN_0 and qN_1 block quantizers and KVarN normalization (oracle; test infrastructure only).
 
 Block quantizer (BeeLlama.cpp v0.4.1 page, list of standard KV cache types
 q2_0 .. q8_0; KVarN benchmark page, cache-size column): a block is 32
@@ -11,6 +11,16 @@ qmax = 2^(N-1) - 1, computed in IEEE fp32 and rounded to fp16 (round to nearest
 even, saturating at 65504); codes are rne(x / d16) against the *stored* fp16
 scale, clamped to [-qmax, qmax]; a block whose fp16 scale is 0 stores all-zero
 codes. The stored code is the biased value u = c + 2^(N-1).
+
+qN_1 blocks (BeeLlama.cpp v0.4.1 page, added types q2_1, q3_1, q6_1 beside q5_1; KVarN
+benchmark page, cache-size column: q5_1 = 37.5 % and q8_0-q5_1 = 45.3 % of bf16, i.e.
+N bits per value plus two fp16 numbers per 32 values): a scale and a minimum. Reading
+(the pages give no formula): mn, mx are the block's smallest and largest value;
+d = (mx - mn) / (2^N - 1) in IEEE fp32, saturating at 65504, rounded to fp16 (nearest
+even); the stored minimum m16 is mn rounded to fp16 (nearest even, saturating at
++/-65504); codes u = rne((x - m16) / d16), the subtraction and the division in IEEE
+fp32, clamped to [0, 2^N - 1]; a block whose fp16 scale is 0 stores all-zero codes.
+The value of a code is d16 * u + m16.
 
 KVarN (BeeLlama.cpp v0.4.1 page: "variance-normalized KV-cache quantization";
 KVarN benchmark page, TL;DR): before block quantization each channel is divided
@@ -59,6 +69,41 @@ def quantize_blocks(x: np.ndarray, n_bits: int):
     # a zero scale is stored as +0
     d16 = np.where(d16 == 0, np.float16(0), d16)
     return u.reshape(x.shape), d16
+
+
+def quantize_blocks_min(x: np.ndarray, n_bits: int):
+    """qN_1: quantize fp32 values along the last axis in blocks of 32 with a scale and a minimum.
+
+    x: float32 [..., D] with D % 32 == 0.
+    Returns (u, d16, m16): u uint8 [..., D] codes in [0, 2^N - 1]; d16, m16 float16 [..., D/32].
+    """
+    assert 2 <= n_bits <= 8
+    x = np.asarray(x, dtype=np.float32)
+    d_total = x.shape[-1]
+    assert d_total % BLOCK == 0
+    xb = x.reshape(*x.shape[:-1], d_total // BLOCK, BLOCK)
+    levels = np.float32((1 << n_bits) - 1)
+    mn = np.min(xb, axis=-1)                                   # exact
+    mx = np.max(xb, axis=-1)
+    d = (mx - mn) / levels                                     # IEEE fp32 subtraction and division
+    d = np.minimum(d, F16_MAX)
+    d16 = f16_rne(d)
+    m16 = f16_rne(np.clip(mn, -F16_MAX, F16_MAX))
+    d32 = d16.astype(np.float32)
+    m32 = m16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = (xb - m32[..., None]) / d32[..., None]             # IEEE fp32 subtraction, then division
+    c = np.clip(np.rint(q), np.float32(0), levels)
+    c = np.where((d16 == 0)[..., None], np.float32(0), c)
+    d16 = np.where(d16 == 0, np.float16(0), d16)
+    return c.astype(np.uint8).reshape(x.shape), d16, m16
+
+
+def dequantize_blocks_min(u: np.ndarray, d16: np.ndarray, m16: np.ndarray) -> np.ndarray:
+    """fp64 values d16 * u + m16 for qN_1 codes [..., D], scales and minima [..., D/32]."""
+    d = np.repeat(np.asarray(d16, dtype=np.float64), BLOCK, axis=-1)
+    m = np.repeat(np.asarray(m16, dtype=np.float64), BLOCK, axis=-1)
+    return np.asarray(u, dtype=np.float64) * d + m
 
 
 def dequantize_blocks(u: np.ndarray, d16: np.ndarray, n_bits: int) -> np.ndarray:

@@ -5,7 +5,8 @@ The offload page counts the bytes a step reads: a bf16 QSA row is 2 KV heads x
 positions reads 4 MiB per layer (offload page, byte arithmetic and QSA paragraph).
 The same count applies to a quantized cache with the row size of its format
 (BeeLlama.cpp v0.4.1 page, KV MiB column: N bits per value plus one fp16 scale per
-32 values).
+32 values; a qN_1 type adds one fp16 minimum per 32 values, KVarN benchmark page,
+cache-size column of q5_1 and q8_0-q5_1).
 
 A call's algorithmic bytes are the rows it must read (every attended position's K
 and V row of each KV head, from the body or the ring), the KVarN scales of each
@@ -17,9 +18,10 @@ from __future__ import annotations
 from .layout import row_bytes  # noqa: F401  (re-exported)
 
 
-def kv_token_bytes(n_bits_k: int, n_bits_v: int, n_kv_heads: int, head_dim: int) -> int:
-    """Bytes of one token in one layer: every KV head, K and V."""
-    return n_kv_heads * (row_bytes(n_bits_k, head_dim) + row_bytes(n_bits_v, head_dim))
+def kv_token_bytes(n_bits_k: int, n_bits_v: int, n_kv_heads: int, head_dim: int, k_min: bool = False,
+                   v_min: bool = False) -> int:
+    """Bytes of one token in one layer: every KV head, K and V (a qN_1 side adds an fp16 minimum per block)."""
+    return n_kv_heads * (row_bytes(n_bits_k, head_dim, k_min) + row_bytes(n_bits_v, head_dim, v_min))
 
 
 def ring_token_bytes(tail_dtype: int, n_kv_heads: int, head_dim: int) -> int:
@@ -34,7 +36,7 @@ def ring_token_bytes(tail_dtype: int, n_kv_heads: int, head_dim: int) -> int:
 def decode_kv_bytes(cfg: dict, lengths, body_lengths) -> int:
     """Cache bytes one dense decode call reads: body rows + ring rows (+ the KVarN scales per sequence)."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
-    body = kv_token_bytes(cfg["k_bits"], cfg["v_bits"], hk, d)
+    body = kv_token_bytes(cfg["k_bits"], cfg["v_bits"], hk, d, bool(cfg.get("k_min", 0)), bool(cfg.get("v_min", 0)))
     ring = ring_token_bytes(cfg["tail_dtype"] if cfg["tail_len"] > 0 else 0, hk, d)
     total = 0
     for ln, bl in zip(lengths, body_lengths):
@@ -57,7 +59,8 @@ def decode_bytes(cfg: dict, lengths, body_lengths) -> int:
 def sparse_kv_bytes(cfg: dict, n_body: int, n_ring: int) -> int:
     """Cache bytes of a sparse read of n_body body positions and n_ring ring positions."""
     hk, d = cfg["n_kv_heads"], cfg["head_dim"]
-    return (n_body * kv_token_bytes(cfg["k_bits"], cfg["v_bits"], hk, d)
+    return (n_body * kv_token_bytes(cfg["k_bits"], cfg["v_bits"], hk, d, bool(cfg.get("k_min", 0)),
+                                    bool(cfg.get("v_min", 0)))
             + n_ring * ring_token_bytes(cfg["tail_dtype"] if cfg.get("tail_len", 0) > 0 else 0, hk, d))
 
 

@@ -562,11 +562,12 @@ __device__ inline void step_writes(const DecodeArgs& a, const DecodeSeq& S, int 
     const StepWriteView w{a.g, a.k_in, a.v_in, 1, 1,
                           {WriteItem{S.slab, S.app_pos, S.app_pos + 1, S.app_pos, si, S.app_pos / kTile, 0}}};
     if (a.g.tail_dtype != 2) bf16_ring_write_wg(w, 0, head);   // bf16 or f16 values
-    else body_write_wg(w, 0, head, codes);
+    else body_write_wg<StepWriteView, false>(w, 0, head, codes);
   } else if (!is_ring && split == S.n_body_splits - 1 && S.ev1 > S.ev0) {
+    // (a cache with a qN_1 body never runs the fused step: the host plans it as separate calls)
     const StepWriteView w{a.g, a.k_in, a.v_in, 0, 1,
                           {WriteItem{S.slab, S.ev0, S.ev1, S.len, 0, S.ev0 / kTile, 0}}};
-    body_write_wg(w, 0, head, codes);
+    body_write_wg<StepWriteView, false>(w, 0, head, codes);
   } else {
     return;
   }

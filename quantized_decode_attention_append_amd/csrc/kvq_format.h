@@ -20,6 +20,10 @@
 //   j = l>>4) owns pieces n = 0..NT-1, piece (l,n) = channel 16n+d16 at tile positions
 //   T(j,i) = 4j+i (i<4), 16+4j+i-4 (i>=4); lanes' bytes are interleaved in units of
 //   min(16, NT*w) bytes ([chunk][lane][unit]); then the NB x 32 fp16 scales [block][position].
+// * qN_1 bodies (a scale and a minimum per block; the planes hold the code u in 0..2^N-1 itself): a row ends
+//   with the NB scales and then the NB fp16 minima; a K tile with the scales [block][position] and then the
+//   minima [position][block] (the MFMA A operand of the minimum term: one 16-byte run per position); a V tile
+//   with the scales and the minima, both [block][position].
 // * bf16 tail ring: K tiles hold, per subtile s and block b, lane (j, m)'s 8 bf16 values of channels
 //   32b+8j.. of slot 16s+m: [s][b][lane][8 x bf16]; V tiles hold, per n-tile and lane, the 8 bf16 values
 //   of channel 16n+d16 at positions T(j,i): [n][lane][8 x bf16].
@@ -79,8 +83,11 @@ KVQ_HD int plane_offset(int n, int p, int pieces) {
 }
 
 KVQ_HD size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
-KVQ_HD int row_bytes(int n_bits, int head_dim) { return head_dim / kBlock * (4 * n_bits + 2); }
-KVQ_HD int tile_bytes(int n_bits, int head_dim) { return kTile * row_bytes(n_bits, head_dim); }
+// with_min: a qN_1 row (one fp16 minimum per block after the scales)
+KVQ_HD int row_bytes(int n_bits, int head_dim, int with_min = 0) {
+  return head_dim / kBlock * (4 * n_bits + 2 + (with_min ? 2 : 0));
+}
+KVQ_HD int tile_bytes(int n_bits, int head_dim, int with_min = 0) { return kTile * row_bytes(n_bits, head_dim, with_min); }
 KVQ_HD int tile_pos(int j, int i) { return i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4); }
 
 // Offset of lane l's byte `b` of its run of `lb` bytes in a lane-interleaved tile part: runs are stored in
@@ -105,12 +112,14 @@ struct SlabLayout {
 };
 
 // tail_dtype: 0 none, 1 bf16, 2 q8_0, 3 f16. index: 0 none, else the cache holds pooled index keys.
+// k_min / v_min: qN_1 bodies.
 KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_bits, int v_bits,
-                              int kvarn, int tail_len, int tail_slack, int tail_dtype, int index) {
+                              int kvarn, int tail_len, int tail_slack, int tail_dtype, int index, int k_min = 0,
+                              int v_min = 0) {
   SlabLayout L{};
   L.cap32 = (int)round_up((size_t)capacity, kTile);
-  L.row_k = row_bytes(k_bits, head_dim);
-  L.row_v = row_bytes(v_bits, head_dim);
+  L.row_k = row_bytes(k_bits, head_dim, k_min);
+  L.row_v = row_bytes(v_bits, head_dim, v_min);
   L.ring_slots = tail_len > 0 ? tail_len + tail_slack : 0;
   if (tail_len > 0 && (tail_dtype == 1 || tail_dtype == 3)) {   // 16-bit values
     L.ring_row_k = L.ring_row_v = 2 * head_dim;

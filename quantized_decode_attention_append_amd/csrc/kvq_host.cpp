@@ -88,7 +88,7 @@ hipError_t timed(kvq_cache* c, int kind, hipStream_t stream, F launch) {
 
 SlabLayout layout_of(const kvq_config& c) {
   return kvq::slab_layout(c.capacity, c.n_kv_heads, c.head_dim, c.k_bits, c.v_bits, c.kvarn, c.tail_len,
-                          c.tail_slack, c.tail_dtype, c.index_dim > 0 ? 1 : 0);
+                          c.tail_slack, c.tail_dtype, c.index_dim > 0 ? 1 : 0, c.k_min, c.v_min);
 }
 
 kvq_status validate(const kvq_config* c) {
@@ -107,6 +107,10 @@ kvq_status validate(const kvq_config* c) {
   if (c->k_bits < 2 || c->k_bits > 8 || c->v_bits < 2 || c->v_bits > 8)
     return fail(KVQ_E_INVALID, "k_bits and v_bits must be in [2, 8] (got %d, %d)", c->k_bits, c->v_bits);
   if (c->kvarn != 0 && c->kvarn != 1) return fail(KVQ_E_INVALID, "kvarn must be 0 or 1");
+  if ((c->k_min != 0 && c->k_min != 1) || (c->v_min != 0 && c->v_min != 1))
+    return fail(KVQ_E_INVALID, "k_min and v_min must be 0 or 1 (got %d, %d)", c->k_min, c->v_min);
+  if ((c->k_min || c->v_min) && c->layout != KVQ_LAYOUT_TILES)
+    return fail(KVQ_E_INVALID, "qN_1 bodies (k_min / v_min) need KVQ_LAYOUT_TILES");
   if (c->tail_len < 0 || c->tail_slack < 0) return fail(KVQ_E_INVALID, "tail_len and tail_slack must be >= 0");
   if (c->layout != KVQ_LAYOUT_TILES && c->layout != KVQ_LAYOUT_ROWS)
     return fail(KVQ_E_INVALID, "layout must be KVQ_LAYOUT_TILES or KVQ_LAYOUT_ROWS (got %d)", c->layout);
@@ -154,6 +158,8 @@ kvq::Geometry geometry(const kvq_cache* c) {
   g.v_bits = c->cfg.v_bits;
   g.kvarn = c->cfg.kvarn;
   g.tail_dtype = c->cfg.tail_len > 0 ? c->cfg.tail_dtype : 0;
+  g.k_min = c->cfg.k_min;
+  g.v_min = c->cfg.v_min;
   return g;
 }
 
@@ -723,11 +729,24 @@ namespace {
 
 // Dense decode of n entries, entry i reading sequence ids[i] over positions [0, len[i]) (its body range
 // [0, min(body_len, len[i])) and the ring rows after it): the query and output rows follow the entries.
+kvq_status run_mq(kvq_cache* c, int layer, int n, const int32_t* ids, const int* q0, const int* nq, const void* q_bf16,
+                  float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
+
 kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, const int* len, const void* q_bf16,
                       float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream,
                       bool ring_extra = false) {
   if (c->cfg.layout == KVQ_LAYOUT_ROWS)
     return run_gather(c, layer, n, ids, q_bf16, nullptr, 0, len, out, softmax_scale, workspace, ws_bytes, stream);
+  if (c->cfg.k_min || c->cfg.v_min) {
+    // qN_1 bodies are read by the multi-query kernel (its cooperative tile decode carries the block minima): each
+    // entry is a block of one query at the last of its positions
+    int q0[KVQ_MAX_BATCH], nq[KVQ_MAX_BATCH];
+    for (int i = 0; i < n; ++i) {
+      q0[i] = len[i] - 1;
+      nq[i] = 1;
+    }
+    return run_mq(c, layer, n, ids, q0, nq, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
+  }
   int bl[KVQ_MAX_BATCH];
   for (int i = 0; i < n; ++i) bl[i] = std::min(c->body_len[c->idx(layer, ids[i])], len[i]);
   kvq::DecodeArgs a{};
@@ -998,7 +1017,8 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   // One launch when every sequence's step is a ring write plus the requantization of at most the rows of one
   // position tile that were in the ring before the call (the tiles the writes touch then belong to the last
   // ring split and the last body split, which write before they read); otherwise the calls run in turn.
-  bool fuse = W > 0 && c->cfg.layout == KVQ_LAYOUT_TILES && k_bf16 && v_bf16 && q_bf16 && out && workspace &&
+  bool fuse = W > 0 && c->cfg.layout == KVQ_LAYOUT_TILES && !c->cfg.k_min && !c->cfg.v_min && k_bf16 && v_bf16 &&
+              q_bf16 && out && workspace &&
               ((uintptr_t)workspace) % 256 == 0 && std::isfinite(softmax_scale);
   int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH], target[KVQ_MAX_BATCH];
   for (int i = 0; i < n_seqs && fuse; ++i) {

@@ -22,6 +22,7 @@ struct Geometry {
   int cap32, row_k, row_v, tile_k, tile_v, ring_row_k, ring_row_v, ring_tile_k, ring_tile_v, ring_slots;
   int n_kv_heads, head_dim, k_bits, v_bits, kvarn, tail_dtype;
   int layout;                                      // 0: V tiles, 1: V rows
+  int k_min, v_min;                                // qN_1 K / V body (scale and minimum per block)
 };
 
 // ---------------------------------------------------------------- append side

@@ -1,5 +1,6 @@
 // Multi-query attention over the quantized cache: blocks of up to 8 consecutive query positions of a sequence
-// attend causally to the cache, each K / V tile read from HBM and decoded once for all of them. It serves the
+// attend causally to the cache, each K / V tile read from HBM and decoded once for all of them. It also serves
+// single-query decode of caches with qN_1 bodies (a scale and a minimum per block, BeeLlama page q2_1 .. q6_1). It serves the
 // verification of drafted tokens (Qwen3.8-27B page, decode-speed paragraph: the engine drafts up to 7 tokens per
 // step with MTP heads) and chunked prefill over the quantized cache (the KVarN benchmark page and the
 // Qwen3.8-27B page measure prompt processing per cache type).
@@ -26,13 +27,15 @@ namespace kvq {
 namespace {
 
 constexpr int kMqWaves = 8;
-constexpr int kRawChunks = 2 * 32 * 272 / 16;   // 16-byte pieces of the largest qN_0 tile pair (q8_0 K + V)
+constexpr int kRawChunks = 2 * 32 * 288 / 16;   // 16-byte pieces of the largest quantized tile pair (q8_1 K + V)
 
 struct MqOps {                 // one tile's MFMA operands in LDS
   u32x4 k[2 * 8 * 64];         // K operands [subtile][block][lane]: 8 codes (or 16-bit values) per lane
-  u32x4 v[16 * 64];            // V operands [n-tile][lane]: code x scale, fp16 rounded (or 16-bit values)
-  u32x4 vl[16 * 64];           // V operands, the remainders: code x scale - v, fp16 (exact)
+  u32x4 v[16 * 64];            // V operands [n-tile][lane]: code x scale (+ offset), fp16 rounded (or 16-bit values)
+  u32x4 vl[16 * 64];           // V operands, the remainders, fp16
   uint16_t ks[8 * 32];         // K scales [block][position]
+  u32x4 kmin[2 * 64];          // qN_1 K: A operand of the offset term [subtile][lane] (rows: positions; k 0-7:
+                               // the blocks' offsets, fp16 hi parts; k 8-15: lo parts; k 16-31: zero)
 };
 
 enum { kKindQ = 0, kKindQ8Ring = 1, kKindBf16Ring = 2, kKindF16Ring = 3 };
@@ -116,10 +119,26 @@ __device__ inline void scale_v_piece(half8 c, const uint32_t* dv, u32x4& hi, u32
   }
 }
 
+// qN_1: a V piece's values code x scale + offset (offset = minimum + 2^(N-1) x scale: the codes are decoded
+// signed, c = u - 2^(N-1)) in fp32, as fp16 rounded values and remainders (to ~22 bits).
+__device__ inline void scale_v_piece_min(half8 c, const uint32_t* dv, const float* off, u32x4& hi, u32x4& lo) {
+  const u32x4 r = __builtin_bit_cast(u32x4, c);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const half2v cv = as_h2(r[k]), d = as_h2(dv[k]);
+    const float x0 = fmaf((float)cv[0], (float)d[0], off[2 * k]);
+    const float x1 = fmaf((float)cv[1], (float)d[1], off[2 * k + 1]);
+    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+    hi[k] = as_u(half2v{h0, h1});
+    lo[k] = as_u(half2v{(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)});
+  }
+}
+
 // V operands of one tile: thread t decodes n-tiles 2(t / 64) and 2(t / 64) + 1 (block t / 64) of lane t % 64;
-// vscale: the tile's V scales [block][position].
+// vscale: the tile's V scales [block][position]; vmin: a qN_1 tile's minima [block][position], else null.
 template <int N>
-__device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, MqOps& ops, uint32_t magic) {
+__device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, const uint8_t* vmin, MqOps& ops,
+                                     uint32_t magic) {
   constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
   const int t = threadIdx.x;
   const int lane = t & 63, np = t >> 6, g = lane >> 4;
@@ -132,6 +151,26 @@ __device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, 
   const u32x2 d1 = *(const u32x2*)(vscale + 2 * (np * 32 + 16 + 4 * g));
   const uint32_t dv[4] = {d0[0], d0[1], d1[0], d1[1]};
   const int o = 2 * np * 64 + lane;
+  if (vmin) {
+    const u32x2 m0 = *(const u32x2*)(vmin + 2 * (np * 32 + 4 * g));
+    const u32x2 m1 = *(const u32x2*)(vmin + 2 * (np * 32 + 16 + 4 * g));
+    const uint32_t mw[4] = {m0[0], m0[1], m1[0], m1[1]};
+    float off[8];
+    constexpr float bias = (float)(1 << (N - 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      off[2 * k] = fmaf(bias, lo_h(dv[k]), lo_h(mw[k]));
+      off[2 * k + 1] = fmaf(bias, hi_h(dv[k]), hi_h(mw[k]));
+    }
+#define KVQ_VPM(P)                                                                                                 \
+  case P:                                                                                                          \
+    scale_v_piece_min(decode_run_piece<N, 2 * P>(r0, r1, r2, magic), dv, off, ops.v[o], ops.vl[o]);               \
+    scale_v_piece_min(decode_run_piece<N, 2 * P + 1>(r0, r1, r2, magic), dv, off, ops.v[o + 64], ops.vl[o + 64]); \
+    break;
+    switch (np) { KVQ_VPM(0) KVQ_VPM(1) KVQ_VPM(2) KVQ_VPM(3) KVQ_VPM(4) KVQ_VPM(5) KVQ_VPM(6) default: KVQ_VPM(7) }
+#undef KVQ_VPM
+    return;
+  }
 #define KVQ_VP(P)                                                                                        \
   case P:                                                                                                \
     scale_v_piece(decode_run_piece<N, 2 * P>(r0, r1, r2, magic), dv, ops.v[o], ops.vl[o]);                \
@@ -141,14 +180,49 @@ __device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, 
 #undef KVQ_VP
 }
 
+// qN_1 K: the A operand of the offset term for subtile s, lane (g, m16): row = position 16s + m16; g = 0 holds
+// the fp16 hi parts of the 8 blocks' offsets (minimum + 2^(N-1) x scale, fp32), g = 1 the lo parts, g = 2, 3 zero.
+// kscale: the tile's K scales [block][position]; kmin: its minima [position][block]. Threads 0-127.
+template <int N>
+__device__ inline void kmin_operand(const uint8_t* kscale, const uint8_t* kmin, MqOps& ops) {
+  const int t = threadIdx.x;
+  const int s = t >> 6, lane = t & 63, g = lane >> 4;
+  const int pos = 16 * s + (lane & 15);
+  u32x4 out = {0u, 0u, 0u, 0u};
+  if (g < 2) {
+    const u32x4 mw = *(const u32x4*)(kmin + 16 * pos);
+    constexpr float bias = (float)(1 << (N - 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float d0 = h2f(((const uint16_t*)kscale)[(2 * k) * 32 + pos]);
+      const float d1 = h2f(((const uint16_t*)kscale)[(2 * k + 1) * 32 + pos]);
+      const float o0 = fmaf(bias, d0, lo_h(mw[k])), o1 = fmaf(bias, d1, hi_h(mw[k]));
+      const _Float16 h0 = (_Float16)o0, h1 = (_Float16)o1;
+      out[k] = g == 0 ? as_u(half2v{h0, h1})
+                      : as_u(half2v{(_Float16)(o0 - (float)h0), (_Float16)(o1 - (float)h1)});
+    }
+  }
+  ops.kmin[s * 64 + lane] = out;
+}
+
 // ---------------------------------------------------------------------------- per-wave compute
 
 // QK of a qN_0 (or q8_0 ring) tile for this wave's query: block by block one MFMA per 16-row subtile, the K scale
 // of each (position, block) applied to the fp32 result. x[4s + r]: position 16s + 4g + r.
-__device__ inline void mq_qk_q(const MqOps& ops, const half8* qop, float qmul, float* x) {
+__device__ inline void mq_qk_q(const MqOps& ops, const half8* qop, float qmul, float* x, const u32x4* qsum) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   float sc[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (qsum) {   // qN_1: sum over blocks of offset x the query's block sum, one MFMA per subtile
+    const half8 b = __builtin_bit_cast(half8, *qsum);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ops.kmin[s * 64 + lane]), b,
+                                                               floatx4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[s][r] = c[r];
+    }
+  }
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const floatx4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ops.k[b * 64 + lane]), qop[b],
@@ -283,13 +357,15 @@ __device__ inline void load_pieces(const TileRef& r, u32x4* reg) {
 
 // Hi / lo fp16 query operand of one block (columns 0-7: hi parts of the group's heads, 8-15: lo parts), the
 // query times `sig` (KVarN sigma of K, or 1) and 2^-e.
-__device__ inline void build_qop_f16(const uint16_t* qrow, const uint16_t* sig, int b, int e, bool head_ok, bool lo_lane,
-                                     half8& out) {
+// Returns the sum of this lane's 8 (exact) operand values, for the block sums of a qN_1 K.
+__device__ inline float build_qop_f16(const uint16_t* qrow, const uint16_t* sig, int b, int e, bool head_ok,
+                                      bool lo_lane, half8& out) {
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4;
   const u32x4 qw = *(const u32x4*)(qrow + 32 * b + 8 * gq);
   u32x4 sw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
   if (sig) sw = *(const u32x4*)(sig + 32 * b + 8 * gq);
+  float sum = 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float x0 = ldexpf(__uint_as_float(qw[k] << 16) * lo_h(sw[k]), -e);          // exact: 8 + 11 bits
@@ -298,7 +374,9 @@ __device__ inline void build_qop_f16(const uint16_t* qrow, const uint16_t* sig, 
     const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
     out[2 * k] = head_ok ? (lo_lane ? l0 : h0) : (_Float16)0.0f;
     out[2 * k + 1] = head_ok ? (lo_lane ? l1 : h1) : (_Float16)0.0f;
+    sum += x0 + x1;
   }
+  return head_ok ? sum : 0.0f;
 }
 
 // Exponent shift of a query: its |q sigma| maximum over the group's heads brought below 2^9.
@@ -329,6 +407,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int D = 256;
   __shared__ MqOps s_ops[2];
   __shared__ u32x4 s_raw[kRawChunks];
+  __shared__ u32x4 s_qsum[kMqWaves * 64];   // qN_1 K: each wave's B operand of the offset term
   const Geometry& g = a.g;
   // work-group -> (sequence, query block, KV head, split)
   int si = 0;
@@ -388,9 +467,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (kind == kKindQ || kind == kKindQ8Ring) {
       const uint16_t* sg = kind == kKindQ ? sig : nullptr;
       const int e = query_shift(qgroup, a.group, sg);
+      float bsum[8];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) build_qop_f16(qrow, sg, b, e, head_ok, lo_lane, qop[b]);
+      for (int b = 0; b < 8; ++b) bsum[b] = build_qop_f16(qrow, sg, b, e, head_ok, lo_lane, qop[b]);
       qmul = a.scale * kLog2e * ldexpf(1.0f, e);
+      if (kind == kKindQ && g.k_min) {
+        // qN_1 K: the B operand of the offset term, lane (g, m16): k = 8g + b (g = 0, 1) is the block-b sum of
+        // the operand values of head m16 & 7 (over the 4 lane groups), its fp16 hi part in columns 0-7 and its
+        // lo part in columns 8-15; g = 2, 3 zero
+        half8 qs;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const float t = sum_xor32(sum_xor16(bsum[b]));
+          const _Float16 h = (_Float16)t;
+          const _Float16 part = lo_lane ? (_Float16)(t - (float)h) : h;
+          qs[b] = (lane >> 4) < 2 ? part : (_Float16)0.0f;
+        }
+        s_qsum[wave * 64 + lane] = __builtin_bit_cast(u32x4, qs);
+      }
     } else if (kind == kKindF16Ring) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) build_qop_f16(qrow, nullptr, b, 0, head_ok, lo_lane, qop[b]);
@@ -451,15 +545,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     if (!raw16) {
       const uint8_t* raw = (const uint8_t*)s_raw;
-      const uint8_t* vscale = raw + r.kbytes + r.vbytes - 512;   // the V tile's last 512 bytes
-      if (r.kind == kKindQ) {
+      // a quantized tile: the codes (1024 N bytes), the scales [block][position], then for a qN_1 body the minima
+      const bool qb = r.kind == kKindQ;
+      const int kcodes = 1024 * (qb ? NK : 8), vcodes = 1024 * (qb ? NV : 8);
+      const uint8_t* vscale = raw + r.kbytes + vcodes;
+      if (qb) {
         decode_k_tile<NK>(raw, ops, magic);
-        decode_v_tile<NV>(raw + r.kbytes, vscale, ops, magic);
+        decode_v_tile<NV>(raw + r.kbytes, vscale, g.v_min ? vscale + 512 : nullptr, ops, magic);
+        if (g.k_min && tid < 128) kmin_operand<NK>(raw + kcodes, raw + kcodes + 512, ops);
       } else {
         decode_k_tile<8>(raw, ops, magic);
-        decode_v_tile<8>(raw + r.kbytes, vscale, ops, magic);
+        decode_v_tile<8>(raw + r.kbytes, vscale, nullptr, ops, magic);
       }
-      if (tid < 32) ((u32x4*)ops.ks)[tid] = s_raw[nk - 32 + tid];              // the K tile's last 512 bytes
+      if (tid < 32) ((u32x4*)ops.ks)[tid] = s_raw[kcodes / 16 + tid];
       __syncthreads();
     }
     // this wave's query over the tile: positions [lo, hi) of the tile's segment, causally up to qpos
@@ -470,7 +568,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (r.pos0 < hi && r.pos0 + kTile > lo) {
         if (r.kind != qop_kind) build_qop(r.kind);
         float x[8], p[8];
-        if (body || r.kind == kKindQ8Ring) mq_qk_q(ops, qop, qmul, x);
+        if (body || r.kind == kKindQ8Ring) mq_qk_q(ops, qop, qmul, x, body && g.k_min ? &s_qsum[wave * 64 + lane] : nullptr);
         else if (r.kind == kKindF16Ring) mq_qk_16<true>(ops, (const u32x4*)qop, qmul, x);
         else mq_qk_16<false>(ops, (const u32x4*)qop, qmul, x);
         const int g4 = lane >> 4;

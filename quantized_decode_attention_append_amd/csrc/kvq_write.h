@@ -1,4 +1,4 @@
-// Device code of the cache writes (qN_0 quantization into the body or the q8_0 ring, the bf16 ring copy, the
+// Device code of the cache writes (qN_0 or qN_1 quantization into the body, q8_0 into the 8-bit ring, the bf16 ring copy, the
 // requantization of ring rows that leave the window), shared by the append kernels and by the decode kernel
 // of a fused decode step. Quantization follows the symmetric qN_0 block format of the BeeLlama page (32
 // values, one fp16 scale, no offset): d = amax / qmax in IEEE fp32, fp16 round-to-nearest-even saturating at
@@ -57,6 +57,42 @@ __device__ inline uint32_t quant_lane(float x, int n_bits, uint16_t* d16_bits) {
   c = fminf(fmaxf(c, -qmax), qmax);
   *d16_bits = __builtin_bit_cast(uint16_t, h);
   return (uint32_t)((int)c + off);
+}
+
+__device__ inline float block_min(float v) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float block_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// qN_1 (a scale and a minimum per block; BeeLlama page, q2_1 .. q6_1 beside q5_1): d = (max - min) / (2^N - 1)
+// in IEEE fp32, fp16 round-to-nearest-even saturating at 65504; the stored minimum is the block minimum rounded
+// to fp16 (saturating at +/-65504); codes rne((x - m16) / d16) clamped to [0, 2^N - 1], zero when d16 is 0.
+// All 32 lanes of the block call this together. Returns the code; *d16_bits, *m16_bits receive scale and minimum.
+__device__ inline uint32_t quant_lane_min(float x, int n_bits, uint16_t* d16_bits, uint16_t* m16_bits) {
+#pragma clang fp contract(off)
+  const float mn = block_min(x);
+  const float mx = block_max(x);
+  const float levels = (float)((1 << n_bits) - 1);
+  float d = (mx - mn) / levels;                 // correctly rounded (see build flags)
+  d = fminf(d, 65504.0f);
+  const _Float16 h = (_Float16)d;               // RNE
+  const _Float16 mh = (_Float16)fminf(fmaxf(mn, -65504.0f), 65504.0f);
+  *m16_bits = __builtin_bit_cast(uint16_t, mh);
+  const float dh = (float)h;
+  if (dh == 0.0f) {
+    *d16_bits = 0;
+    return 0u;
+  }
+  float c = rintf((x - (float)mh) / dh);        // round half to even
+  c = fminf(fmaxf(c, 0.0f), levels);
+  *d16_bits = __builtin_bit_cast(uint16_t, h);
+  return (uint32_t)c;
 }
 
 // fp32 ring representation r(x) of one value: the bf16 value itself, its f16 rounding, or its q8_0 round trip.
@@ -164,7 +200,8 @@ typedef uint8_t WriteCodes[2][kTile][256];
 // One work-group of 512 threads per (position tile, KV head): thread (kv, c) quantizes channel c of K (kv = 0)
 // or V (kv = 1) for every position of the tile that the call writes. A: WriteArgs, or one role of StepArgs
 // (the kernel argument itself, so that the item list is read in place). codes: the caller's LDS buffer.
-template <class A>
+// kMin = false compiles the qN_1 quantizer out (for callers that never write qN_1 bodies).
+template <class A, bool kMin = true>
 __device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& codes) {
 #pragma clang fp contract(off)
   const Geometry& g = a.g;
@@ -228,14 +265,23 @@ __device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& c
       x = ring_value(g, slab, kv, head, p, c);
     }
     if (!a.dst_ring && g.kvarn) x = x / sig;
-    uint16_t dq;
-    const uint32_t u = quant_lane(x, nb, &dq);
+    uint16_t dq, dm = 0;
+    const bool with_min = kMin && !a.dst_ring && (kv ? g.v_min : g.k_min);   // uniform over each 256-thread half
+    const uint32_t u = with_min ? quant_lane_min(x, nb, &dq, &dm) : quant_lane(x, nb, &dq);
     if (direct) or_code(kv ? vrow_of(p) : krow_of(p), kv ? vtile : ktile, vrows, kv, nb, t, c, u, D);
     else codes[kv][t][c] = (uint8_t)u;
     if ((c % kBlock) == 0) {
-      if (vrows) ((uint16_t*)(kv ? vrow_of(p) + NB * 4 * NV : krow_of(p) + NB * 4 * NK))[b] = dq;
-      else if (kv == 0) ((uint16_t*)(ktile + 4 * D * NK))[b * kTile + t] = dq;   // [block][position]
-      else ((uint16_t*)(vtile + 4 * D * NV))[b * kTile + t] = dq;
+      if (vrows) {
+        uint16_t* sc = (uint16_t*)(kv ? vrow_of(p) + NB * 4 * NV : krow_of(p) + NB * 4 * NK);
+        sc[b] = dq;
+        if (with_min) sc[NB + b] = dm;                                               // minima after the scales
+      } else if (kv == 0) {
+        ((uint16_t*)(ktile + 4 * D * NK))[b * kTile + t] = dq;                       // [block][position]
+        if (with_min) ((uint16_t*)(ktile + 4 * D * NK + 2 * NB * kTile))[t * NB + b] = dm;   // [position][block]
+      } else {
+        ((uint16_t*)(vtile + 4 * D * NV))[b * kTile + t] = dq;
+        if (with_min) ((uint16_t*)(vtile + 4 * D * NV + 2 * NB * kTile))[b * kTile + t] = dm;
+      }
     }
   }
   if (direct) return;   // uniform over the work-group

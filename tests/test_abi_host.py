@@ -49,7 +49,7 @@ def _random_cfgs(n=60):
                    capacity=int(rng.integers(1, 300000)), n_kv_heads=hk, n_q_heads=hk * int(rng.integers(1, 9)),
                    k_bits=int(rng.integers(2, 9)), v_bits=int(rng.integers(2, 9)), kvarn=int(rng.integers(0, 2)),
                    tail_len=w, tail_slack=int(rng.choice([0, 32, 512])) if w else 0,
-                   tail_dtype=int(rng.integers(1, 4)))
+                   tail_dtype=int(rng.integers(1, 4)), k_min=int(rng.integers(0, 2)), v_min=int(rng.integers(0, 2)))
 
 
 def test_cache_bytes_and_regions_match_oracle():
@@ -78,6 +78,7 @@ def test_kv_mib_table_through_the_library():
     dict(head_dim=100), dict(k_bits=1), dict(v_bits=9), dict(kvarn=2), dict(tail_len=-1),
     dict(tail_len=64, tail_slack=31), dict(tail_len=64, tail_dtype=0), dict(tail_len=64, tail_dtype=4),
     dict(index_dim=128, index_pool=3), dict(index_dim=96, index_pool=4), dict(index_dim=128, index_pool=0),
+    dict(k_min=2), dict(v_min=-1), dict(k_min=1, layout=1), dict(v_min=1, layout=1),
 ])
 def test_validation_rejects(bad):
     from quantized_decode_attention_append_amd import kvq

@@ -255,3 +255,46 @@ def test_truncate_keeps_to_the_ring():
         o.truncate(0, [0], [n + 1])
     o.truncate(0, [0], [body])
     assert o.lengths(0, 0) == (body, body)
+
+
+@pytest.mark.parametrize("k_min,v_min,tail_dtype", [(1, 0, 0), (0, 1, 1), (1, 1, 2), (1, 1, 3)])
+def test_qn1_body_reproduces_values_on_its_grid(k_min, v_min, tail_dtype):
+    """Inputs that lie on a power-of-two grid with an offset (every block spanning all 2^N levels) are stored
+    exactly by a qN_1 side, through the ring and after eviction; a qN_0 side keeps its own rounding."""
+    nk, nv = 4, 3
+    n = 100
+    rng = np.random.default_rng(7 + 4 * k_min + 2 * v_min + tail_dtype)
+
+    def grid(bits, off, k):
+        c = rng.integers(0, 1 << bits, size=(n, 2, 8, 32))
+        c[..., 0] = 0
+        c[..., 1] = (1 << bits) - 1
+        return ((c + off) * 2.0 ** k).reshape(n, 2, 256).astype(np.float32)
+
+    kx, vx = grid(nk, -5, -3), grid(nv, 2, 1)
+    from workloads import bf16_bits
+    kb, vb = bf16_bits(kx), bf16_bits(vx)
+    assert np.array_equal(bf16_to_f32(kb), kx) and np.array_equal(bf16_to_f32(vb), vx)   # exact in bf16
+    cfg = dict(n_layers=1, max_seqs=1, capacity=256, n_q_heads=4, n_kv_heads=2, head_dim=256, k_bits=nk,
+               v_bits=nv, kvarn=0, tail_len=16 if tail_dtype else 0, tail_slack=16, tail_dtype=tail_dtype,
+               k_min=k_min, v_min=v_min)
+    o = OracleCache(cfg)
+    o.append(0, [0], [60], kb[:60], vb[:60])
+    o.tail_evict(0, [0])
+    o.append(0, [0], [40], kb[60:], vb[60:])
+    o.tail_evict(0, [0])
+    n_len, body = o.lengths(0, 0)
+    assert n_len == n and (body == n if not tail_dtype else body == n - 16)
+    k, v = o.dequantized(0, 0)
+    below = np.arange(body)
+    if tail_dtype == 2:   # body rows went through the q8_0 ring first: only their own grid survives exactly
+        return
+    if k_min:
+        assert np.array_equal(k[below], kx[below].astype(np.float64))
+    else:
+        assert not np.array_equal(k[below], kx[below].astype(np.float64))
+    if v_min:
+        assert np.array_equal(v[below], vx[below].astype(np.float64))
+    lay = slab_layout(cfg)
+    img = o.slab_image(0, 0)
+    assert img.shape[0] == lay["slab"]

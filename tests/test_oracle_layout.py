@@ -23,6 +23,7 @@ def _csv(name):
 
 
 BITS = {"q4_0": 4, "q5_0": 5, "q6_0": 6, "q8_0": 8}
+TYPES = {**{k: (v, False) for k, v in BITS.items()}, "q5_1": (5, True)}   # (bits, scale + minimum)
 
 
 def _cfg(**kw):
@@ -41,12 +42,12 @@ def test_kv_mib_table_exact(row):
 
 @pytest.mark.parametrize("row", _csv("p3_cache_size.csv"), ids=lambda r: f"{r['k_type']}-{r['v_type']}")
 def test_cache_size_percent_of_bf16(row):
-    k, v = BITS[row["k_type"]], BITS[row["v_type"]]
-    q = sizes.kv_token_bytes(k, v, 4, 256)
+    (k, kmin), (v, vmin) = TYPES[row["k_type"]], TYPES[row["v_type"]]
+    q = sizes.kv_token_bytes(k, v, 4, 256, kmin, vmin)
     bf = sizes.bf16_token_bytes(4, 256)
     assert round(100.0 * q / bf, 1) == float(row["percent"])
     # and the whole cache at the table's shape keeps the same ratio exactly
-    cfg = _cfg(k_bits=k, v_bits=v)
+    cfg = _cfg(k_bits=k, v_bits=v, k_min=int(kmin), v_min=int(vmin))
     assert layout.cache_bytes(cfg) * bf == q * 16 * 65536 * bf
 
 
@@ -210,3 +211,32 @@ def test_slab_regions_are_disjoint_and_aligned():
             assert off % 256 == 0 and off >= end
             end = off + size
         assert lay["slab"] >= end and lay["slab"] % 256 == 0
+
+
+def test_qn1_rows_and_tiles_carry_the_minima_after_the_scales():
+    """Hand-worked placement: a qN_1 K row ends with the 8 scales then the 8 minima (block order); a K tile
+    ends with the scales [block][position] then the minima [position][block]; a V tile with the scales and then
+    the minima, both [block][position]."""
+    rng = np.random.default_rng(3)
+    n = 5
+    u = rng.integers(0, 32, size=(1, 32, 256)).astype(np.uint8)
+    d = (np.arange(32 * 8).reshape(1, 32, 8) + 1).astype(np.float16)
+    m = (-np.arange(32 * 8).reshape(1, 32, 8) - 0.5).astype(np.float16)
+    rb0 = layout.row_bytes(n, 256)
+    assert layout.row_bytes(n, 256, True) == rb0 + 16 == 8 * (4 * n + 4)
+    rows = layout.pack_k_rows(u[0], d[0], n, m[0])
+    assert rows.shape == (32, rb0 + 16)
+    assert np.array_equal(rows[:, :rb0], layout.pack_k_rows(u[0], d[0], n))
+    assert np.array_equal(rows[:, rb0:].copy().view(np.float16), m[0])
+    kt = layout.pack_k_tiles(u, d, n, m)
+    tb0 = 32 * rb0
+    assert kt.shape == (1, tb0 + 512)
+    assert np.array_equal(kt[:, :tb0], layout.pack_k_tiles(u, d, n))
+    assert np.array_equal(kt[0, tb0:].copy().view(np.float16).reshape(32, 8), m[0])      # [position][block]
+    vt = layout.pack_v_tiles(u, d, n, m)
+    assert np.array_equal(vt[:, :tb0], layout.pack_v_tiles(u, d, n))
+    assert np.array_equal(vt[0, tb0:].copy().view(np.float16).reshape(8, 32), m[0].T)    # [block][position]
+    lay0 = layout.slab_layout(_cfg(k_bits=n, v_bits=n))
+    lay1 = layout.slab_layout(_cfg(k_bits=n, v_bits=n, v_min=1))
+    assert lay1["v_body"][1] == lay0["v_body"][1] * (4 * n + 4) // (4 * n + 2)
+    assert lay1["k_body"][1] == lay0["k_body"][1]

@@ -211,3 +211,84 @@ def test_kvarn_normalized_round_trip():
     c = u.astype(np.float64) - 8
     err = np.abs(y.astype(np.float64) - c * np.repeat(d16.astype(np.float64), 32, axis=-1))
     assert np.all(err <= np.repeat(d16.astype(np.float64), 32, axis=-1) / 2 + 2.0 ** -24 * np.abs(y))
+
+
+# ---- qN_1: a scale and a minimum per block (codes 0 .. 2^N - 1, value d16 * u + m16)
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+@pytest.mark.parametrize("scale", [0.05, 1.0, 37.0])
+def test_qn1_round_trip_within_half_scale(n_bits, scale):
+    x = _blocks(500 + n_bits * 7 + int(scale * 10), 300, scale, outliers=(n_bits % 2 == 1))
+    x = x + np.float32(scale)                     # an offset the minimum absorbs
+    u, d16, m16 = quant.quantize_blocks_min(x, n_bits)
+    d = d16.astype(np.float64)[:, 0]
+    m = m16.astype(np.float64)[:, 0]
+    mn = x.astype(np.float64).min(axis=1)
+    assert np.all(d >= 2.0 ** -14) and np.all(d < 65504)
+    assert np.all(u <= (1 << n_bits) - 1)
+    err = np.abs(x.astype(np.float64) - (u * d[:, None] + m[:, None]))
+    # d16/2 to the nearest level, |m16 - mn| where the rounded minimum lies above the block's smallest value,
+    # a few fp32 roundings of x - m16 and of the quotient
+    bound = d[:, None] / 2 + np.abs(m - mn)[:, None] + 2.0 ** -22 * (np.abs(x) + np.abs(m)[:, None])
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_qn1_scale_and_minimum_are_rne_fp16_of_the_exact_quantities(n_bits):
+    x = _blocks(600 + n_bits, 50, 3.0) + np.float32(1.25)
+    _, d16, m16 = quant.quantize_blocks_min(x, n_bits)
+    levels = (1 << n_bits) - 1
+    for b in range(x.shape[0]):
+        mn = min(float(v) for v in x[b])
+        mx = max(float(v) for v in x[b])
+        diff = _round_f32(Fraction(mx) - Fraction(mn))           # the fp32 subtraction
+        d32 = _round_f32(Fraction(diff) / levels)                 # then the fp32 division
+        assert float(d16[b, 0]) == _round_f16(d32)
+        assert float(m16[b, 0]) == _round_f16(mn)
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_qn1_codes_are_nearest_level_by_exhaustive_search(n_bits):
+    x = _blocks(700 + n_bits, 30, 2.0) - np.float32(0.75)
+    u, d16, m16 = quant.quantize_blocks_min(x, n_bits)
+    levels = (1 << n_bits) - 1
+    for b in range(x.shape[0]):
+        d = Fraction(float(d16[b, 0]))
+        m = Fraction(float(m16[b, 0]))
+        for i in range(32):
+            xv = Fraction(float(x[b, i]))
+            dists = sorted((abs(xv - (m + c * d)), c) for c in range(levels + 1))
+            best, c_best = dists[0]
+            if dists[1][0] == best:
+                c_best = dists[0][1] if dists[0][1] % 2 == 0 else dists[1][1]
+            q = (xv - m) / d
+            frac = q - math.floor(q)
+            if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 18):
+                continue                      # fp32 arithmetic may legitimately land on either side of a tie
+            assert int(u[b, i]) == c_best, (b, i)
+
+
+@pytest.mark.parametrize("n_bits", range(2, 9))
+def test_qn1_power_of_two_grid_with_offset_is_exact(n_bits):
+    levels = (1 << n_bits) - 1
+    rng = np.random.default_rng(40 + n_bits)
+    for k, off in ((-6, -3), (0, 5), (3, -2)):
+        c = rng.integers(0, levels + 1, size=(6, 32))
+        c[:, 0] = 0
+        c[:, 7] = levels                     # the block spans the whole range
+        x = ((c + off) * 2.0 ** k).astype(np.float32)
+        u, d16, m16 = quant.quantize_blocks_min(x, n_bits)
+        assert np.all(d16.astype(np.float64) == 2.0 ** k)
+        assert np.all(m16.astype(np.float64) == off * 2.0 ** k)
+        assert np.array_equal(u.astype(np.int64), c)
+        assert np.array_equal(quant.dequantize_blocks_min(u, d16, m16), x.astype(np.float64))
+
+
+def test_qn1_constant_block_stores_its_value_as_the_minimum():
+    x = np.full((3, 32), 0.3125, dtype=np.float32)
+    x[1] = -7.0
+    x[2] = 0.0
+    u, d16, m16 = quant.quantize_blocks_min(x, 4)
+    assert np.all(u == 0)
+    assert np.all(d16.view(np.uint16) == 0)
+    assert list(m16[:, 0].astype(np.float64)) == [0.3125, -7.0, 0.0]
