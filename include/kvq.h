@@ -82,6 +82,12 @@ typedef struct {
                            per 32 values, value = scale x code + minimum with codes 0..2^N-1 (BeeLlama page,
                            q2_1 .. q6_1; KVarN benchmark page, q5_1 and q8_0-q5_1). Needs KVQ_LAYOUT_TILES.   */
   int32_t v_min;        /* 0/1: the same for the V body                                                    */
+  int32_t k_axis;       /* 0: a K block is 32 channels of one position; 1: token axis, a K block is the 32
+                           positions of one channel in a position tile (KIVI-style per-channel K, Qwen3.8-27B
+                           page, reader comment). A tile's K is quantized once all its positions are known, so
+                           the body grows by whole tiles and the ring holds the window plus the tile still
+                           filling: needs KVQ_LAYOUT_TILES, tail_len >= 1 and tail_slack >= 32; kvq_tail_evict
+                           then keeps between tail_len and tail_len + 31 positions in the ring.            */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache;

@@ -15,6 +15,12 @@ Test infrastructure only. Follows, step by step:
   window the output equals a q8_0 cache (Qwen3.8-27B page, KV low-bit section).
   Reading: ring rows are q8_0 blocks; eviction requantizes the dequantized q8_0
   values (double quantization).
+* Token-axis K (Qwen3.8-27B page, reader comment on KIVI-style per-channel K): a K
+  block is the 32 positions of one channel in a position tile. Reading: such a block
+  can only be quantized once all its positions are known, so the body grows by whole
+  tiles: tokens leave the ring a tile at a time (the ring holds the window plus the
+  tile still filling, so it needs at least 32 slots of slack), and tail_evict keeps
+  between W and W + 31 positions in the ring. V stays per token.
 * Tokens leaving the window are requantized into the low-bit body; this needs two
   KV paths per layer and per-position branching (Qwen3.8-27B page, reader comment
   on the window boundary).
@@ -32,8 +38,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layout import (pack_k_rows, pack_k_tiles, pack_bf16_k_tiles, pack_v_tiles, pack_bf16_v_tiles,
-                     slab_layout, TILE)
+from .layout import (pack_k_rows, pack_k_tiles, pack_k_tiles_token_axis, pack_bf16_k_tiles, pack_v_tiles,
+                     pack_bf16_v_tiles, slab_layout, TILE)
 from .quant import quantize_blocks, quantize_blocks_min, kvarn_sigma, normalize, dequantize_blocks, dequantize_blocks_min
 from . import indexer
 
@@ -71,6 +77,9 @@ class _SeqState:
         # qN_1 bodies: the block minima (zero rows for a qN_0 side, never read)
         self.km = np.zeros((cap32, hk, nb), dtype=np.float16)
         self.vm = np.zeros((cap32, hk, nb), dtype=np.float16)
+        # token-axis K: one scale (and minimum) per (position tile, KV head, channel)
+        self.ktd = np.zeros((cap32 // 32, hk, d), dtype=np.float16)
+        self.ktm = np.zeros((cap32 // 32, hk, d), dtype=np.float16)
         if cfg.get("index_dim", 0):
             self.ikey = np.zeros((cap32, indexer.POOLED), dtype=np.uint16)   # pooled index keys, bf16 bits
         r = lay["ring_slots"]
@@ -96,6 +105,7 @@ class OracleCache:
         self.rows = cfg.get("layout", LAYOUT_TILES) == LAYOUT_ROWS   # V stored as rows, like K
         self.k_min = bool(cfg.get("k_min", 0))   # qN_1 bodies (scale and minimum per block)
         self.v_min = bool(cfg.get("v_min", 0))
+        self.k_tok = bool(cfg.get("k_axis", 0))  # token-axis K: blocks of 32 positions of one channel
         self.state = {}
 
     # ------------------------------------------------------------------ helpers
@@ -135,7 +145,21 @@ class OracleCache:
         if self.cfg["kvarn"]:
             k32 = normalize(k32, s.sigma[:, 0, :])
             v32 = normalize(v32, s.sigma[:, 1, :])
-        if self.k_min:
+        if self.k_tok:
+            # whole position tiles only: quantize each channel's 32 values of a tile as one block
+            assert pos[0] % TILE == 0 and len(pos) % TILE == 0 and np.all(np.diff(pos) == 1)
+            ntl = len(pos) // TILE
+            hk, d = k32.shape[1], k32.shape[2]
+            xt = np.ascontiguousarray(k32.reshape(ntl, TILE, hk, d).transpose(0, 2, 3, 1))   # [tile, head, ch, pos]
+            tl = pos[::TILE] // TILE
+            if self.k_min:
+                u, d16, m16 = quantize_blocks_min(xt, self.cfg["k_bits"])
+                s.ktm[tl] = m16[..., 0]
+            else:
+                u, d16 = quantize_blocks(xt, self.cfg["k_bits"])
+            s.ktd[tl] = d16[..., 0]
+            s.ku[pos] = u.transpose(0, 3, 1, 2).reshape(len(pos), hk, d)
+        elif self.k_min:
             s.ku[pos], s.kd[pos], s.km[pos] = quantize_blocks_min(k32, self.cfg["k_bits"])
         else:
             s.ku[pos], s.kd[pos] = quantize_blocks(k32, self.cfg["k_bits"])
@@ -193,6 +217,22 @@ class OracleCache:
                 s.len = s.body_len = new_len
                 continue
             new_body = max(s.body_len, new_len - self.R)
+            if self.k_tok:
+                # the body grows by whole tiles: positions of a tile leave the ring together, ring rows and new
+                # tokens behind the window in one write
+                new_body = max(s.body_len, -(-(new_len - self.R) // TILE) * TILE)
+                if new_body > s.body_len:
+                    p_all = np.arange(s.body_len, new_body)
+                    old_p = p_all[p_all < s.len]
+                    new_p = p_all[p_all >= s.len]
+                    k_old, v_old = self._ring_value(s, old_p % self.R)
+                    k_new, v_new = self._ring_rep_of_input(kb[new_p - s.len], vb[new_p - s.len])
+                    self._write_body(s, p_all, np.concatenate([k_old, k_new]), np.concatenate([v_old, v_new]))
+                keep = pos[pos >= new_body]
+                self._write_ring(s, keep, kb[keep - s.len], vb[keep - s.len])
+                s.len = new_len
+                s.body_len = new_body
+                continue
             # oldest ring rows leave first (only when the ring would overflow)
             self._evict_to(s, min(new_body, s.len))
             # new tokens already behind the window: through the ring representation
@@ -211,7 +251,10 @@ class OracleCache:
             s = self.st(layer, sid)
             if self.tail == TAIL_NONE:
                 continue
-            self._evict_to(s, max(s.body_len, s.len - self.W))
+            target = s.len - self.W
+            if self.k_tok:   # whole tiles only
+                target = target // TILE * TILE
+            self._evict_to(s, max(s.body_len, target))
 
     def truncate(self, layer: int, seq_ids, new_lens):
         """Drop the newest positions of each sequence down to new_lens[i], which must lie in [body_len, len]: only
@@ -267,8 +310,16 @@ class OracleCache:
         in_body = positions < s.body_len
         pb = positions[in_body]
         if len(pb):
-            kb = (dequantize_blocks_min(s.ku[pb], s.kd[pb], s.km[pb]) if self.k_min
-                  else dequantize_blocks(s.ku[pb], s.kd[pb], self.cfg["k_bits"]))
+            if self.k_tok:
+                tl = pb // TILE
+                c = s.ku[pb].astype(np.float64)
+                if self.k_min:
+                    kb = c * s.ktd[tl].astype(np.float64) + s.ktm[tl].astype(np.float64)
+                else:
+                    kb = (c - (1 << (self.cfg["k_bits"] - 1))) * s.ktd[tl].astype(np.float64)
+            else:
+                kb = (dequantize_blocks_min(s.ku[pb], s.kd[pb], s.km[pb]) if self.k_min
+                      else dequantize_blocks(s.ku[pb], s.kd[pb], self.cfg["k_bits"]))
             vb = (dequantize_blocks_min(s.vu[pb], s.vd[pb], s.vm[pb]) if self.v_min
                   else dequantize_blocks(s.vu[pb], s.vd[pb], self.cfg["v_bits"]))
             if self.cfg["kvarn"]:
@@ -292,6 +343,10 @@ class OracleCache:
         d = self.cfg["head_dim"]
         km = s.km[lo:hi, head] if self.k_min else None
         vm = s.vm[lo:hi, head] if self.v_min else None
+        if region == "k_body" and not self.rows and self.k_tok:
+            assert lo % TILE == 0 and hi % TILE == 0
+            return pack_k_tiles_token_axis(s.ku[lo:hi, head].reshape(-1, TILE, d), s.ktd[lo // TILE:hi // TILE, head], kb,
+                                           s.ktm[lo // TILE:hi // TILE, head] if self.k_min else None)
         if region == "k_body" and not self.rows:
             assert lo % TILE == 0 and hi % TILE == 0
             return pack_k_tiles(s.ku[lo:hi, head].reshape(-1, TILE, d), s.kd[lo:hi, head].reshape(-1, TILE, d // 32), kb,

@@ -44,6 +44,11 @@ NB * (4N + 4)); a K tile ends with the scales [block][position] and then the
 minima [position][block]; a V tile with the scales and then the minima, both
 [block][position] (tile bytes 32 * NB * (4N + 4)).
 
+Token-axis K (KIVI-style; Qwen3.8-27B page, reader comment on quantizing K along the token
+axis): a K block is the 32 positions of one channel within a position tile. The codes of a
+K tile are placed as above; the tile ends with the D fp16 scales [channel] (and, for a qN_1
+K, the D fp16 minima [channel]): the same bytes as a per-token tile.
+
 bf16 tail ring (tile layout): K tiles of 32 slots hold, for subtile s and block b,
 lane l = 16j + m's 8 bf16 values of channels 32b + 8j .. +7 of slot 16s + m:
 [s][b][lane][8 x bf16]; V tiles hold, for n-tile n and lane l, the 8 bf16 values
@@ -206,6 +211,19 @@ def pack_k_tiles(u: np.ndarray, d16: np.ndarray, n_bits: int, m16=None) -> np.nd
     if m16 is not None:   # minima [position][block]
         out.append(np.ascontiguousarray(np.asarray(m16, dtype=np.float16)).view(np.uint8).reshape(ntl, 2 * nb * TILE))
     return np.concatenate(out, axis=-1)
+
+
+def pack_k_tiles_token_axis(u: np.ndarray, d16: np.ndarray, n_bits: int, m16=None) -> np.ndarray:
+    """Token-axis K: codes u [n_tiles, 32, D], scales d16 [n_tiles, D] (one per channel and tile) and (qN_1)
+    minima [n_tiles, D] -> K tiles [n_tiles, tile_bytes]: the codes placed as in a per-token tile, then the
+    scales [channel], then the minima [channel]."""
+    u = np.asarray(u, dtype=np.uint8)
+    ntl, _, d = u.shape
+    codes = pack_k_tiles(u, np.zeros((ntl, TILE, d // BLOCK), dtype=np.float16), n_bits)[:, :TILE * d * n_bits // 8]
+    parts = [codes, np.ascontiguousarray(np.asarray(d16, dtype=np.float16)).view(np.uint8).reshape(ntl, 2 * d)]
+    if m16 is not None:
+        parts.append(np.ascontiguousarray(np.asarray(m16, dtype=np.float16)).view(np.uint8).reshape(ntl, 2 * d))
+    return np.concatenate(parts, axis=-1)
 
 
 def unpack_k_tiles(tiles: np.ndarray, n_bits: int, head_dim: int):

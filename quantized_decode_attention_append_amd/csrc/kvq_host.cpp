@@ -111,6 +111,9 @@ kvq_status validate(const kvq_config* c) {
     return fail(KVQ_E_INVALID, "k_min and v_min must be 0 or 1 (got %d, %d)", c->k_min, c->v_min);
   if ((c->k_min || c->v_min) && c->layout != KVQ_LAYOUT_TILES)
     return fail(KVQ_E_INVALID, "qN_1 bodies (k_min / v_min) need KVQ_LAYOUT_TILES");
+  if (c->k_axis != 0 && c->k_axis != 1) return fail(KVQ_E_INVALID, "k_axis must be 0 or 1 (got %d)", c->k_axis);
+  if (c->k_axis && (c->layout != KVQ_LAYOUT_TILES || c->tail_len < 1 || c->tail_slack < kvq::kTile))
+    return fail(KVQ_E_INVALID, "token-axis K (k_axis) needs KVQ_LAYOUT_TILES, tail_len >= 1 and tail_slack >= 32");
   if (c->tail_len < 0 || c->tail_slack < 0) return fail(KVQ_E_INVALID, "tail_len and tail_slack must be >= 0");
   if (c->layout != KVQ_LAYOUT_TILES && c->layout != KVQ_LAYOUT_ROWS)
     return fail(KVQ_E_INVALID, "layout must be KVQ_LAYOUT_TILES or KVQ_LAYOUT_ROWS (got %d)", c->layout);
@@ -160,6 +163,7 @@ kvq::Geometry geometry(const kvq_cache* c) {
   g.tail_dtype = c->cfg.tail_len > 0 ? c->cfg.tail_dtype : 0;
   g.k_min = c->cfg.k_min;
   g.v_min = c->cfg.v_min;
+  g.k_axis = c->cfg.k_axis;
   return g;
 }
 
@@ -572,7 +576,10 @@ kvq_status kvq_append(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t
       b1 = len + n;
       new_body[i] = len + n;
     } else {
-      const int nb = std::max(bl, len + n - R);
+      // token-axis K: the body grows by whole tiles (a tile's K blocks need all its positions)
+      const int over = len + n - R;
+      const int nb = std::max(bl, c->cfg.k_axis ? (over > 0 ? (over + kvq::kTile - 1) / kvq::kTile * kvq::kTile : 0)
+                                               : over);
       b0 = bl;
       b1 = nb;
       r0 = std::max(len, nb);
@@ -645,7 +652,9 @@ kvq_status kvq_tail_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const int
   for (int i = 0; i < n_seqs; ++i) {
     const int k = c->idx(layer, seq_ids[i]);
     const int len = c->len[k], bl = c->body_len[k];
-    target[i] = std::max(bl, len - W);
+    int t = len - W;
+    if (c->cfg.k_axis) t = t > 0 ? t / kvq::kTile * kvq::kTile : 0;   // whole tiles only
+    target[i] = std::max(bl, t);
     if (target[i] > bl) {
       kvq::WriteItem& it = body.items[body.n_items++];
       it = kvq::WriteItem{slab_offset(c, layer, seq_ids[i]), bl, target[i], len, 0, bl / kvq::kTile, wgs};
@@ -670,7 +679,7 @@ kvq_status kvq_append_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const i
   const int R = c->lay.ring_slots;
   // One launch only for a pure ring write plus an evict of rows that were in the ring before the call:
   // then the ring writes and the body writes touch disjoint bytes and neither reads what the other writes.
-  bool fuse = W > 0 && n_seqs <= kvq::kStepBatch;
+  bool fuse = W > 0 && n_seqs <= kvq::kStepBatch && !c->cfg.k_axis;
   long total = 0;
   for (int i = 0; i < n_seqs && fuse; ++i) {
     if (n_new[i] < 0) { fuse = false; break; }   // reported by kvq_append
@@ -737,9 +746,9 @@ kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, co
                       bool ring_extra = false) {
   if (c->cfg.layout == KVQ_LAYOUT_ROWS)
     return run_gather(c, layer, n, ids, q_bf16, nullptr, 0, len, out, softmax_scale, workspace, ws_bytes, stream);
-  if (c->cfg.k_min || c->cfg.v_min) {
-    // qN_1 bodies are read by the multi-query kernel (its cooperative tile decode carries the block minima): each
-    // entry is a block of one query at the last of its positions
+  if (c->cfg.k_min || c->cfg.v_min || c->cfg.k_axis) {
+    // qN_1 bodies and token-axis K are read by the multi-query kernel (its cooperative tile decode carries the
+    // block minima and the per-channel K scales): each entry is a block of one query at the last of its positions
     int q0[KVQ_MAX_BATCH], nq[KVQ_MAX_BATCH];
     for (int i = 0; i < n; ++i) {
       q0[i] = len[i] - 1;
@@ -782,7 +791,9 @@ constexpr int kMqBlock = 8;
 int body_len_after(const kvq_cache* c, int layer, int seq, int n) {
   const int k = c->idx(layer, seq);
   if (c->cfg.tail_len == 0) return c->len[k] + n;
-  return std::max(c->body_len[k], c->len[k] + n - c->lay.ring_slots);
+  const int over = c->len[k] + n - c->lay.ring_slots;
+  if (c->cfg.k_axis) return std::max(c->body_len[k], over > 0 ? (over + kvq::kTile - 1) / kvq::kTile * kvq::kTile : 0);
+  return std::max(c->body_len[k], over);
 }
 
 long mq_budget(const kvq_cache* c) { return std::min(kDecodeWgsPerCu * c->n_cu, kMaxWgBudget); }
@@ -1017,7 +1028,8 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   // One launch when every sequence's step is a ring write plus the requantization of at most the rows of one
   // position tile that were in the ring before the call (the tiles the writes touch then belong to the last
   // ring split and the last body split, which write before they read); otherwise the calls run in turn.
-  bool fuse = W > 0 && c->cfg.layout == KVQ_LAYOUT_TILES && !c->cfg.k_min && !c->cfg.v_min && k_bf16 && v_bf16 &&
+  bool fuse = W > 0 && c->cfg.layout == KVQ_LAYOUT_TILES && !c->cfg.k_min && !c->cfg.v_min && !c->cfg.k_axis &&
+              k_bf16 && v_bf16 &&
               q_bf16 && out && workspace &&
               ((uintptr_t)workspace) % 256 == 0 && std::isfinite(softmax_scale);
   int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH], target[KVQ_MAX_BATCH];

@@ -23,6 +23,7 @@ struct Geometry {
   int n_kv_heads, head_dim, k_bits, v_bits, kvarn, tail_dtype;
   int layout;                                      // 0: V tiles, 1: V rows
   int k_min, v_min;                                // qN_1 K / V body (scale and minimum per block)
+  int k_axis;                                      // 1: token-axis K (a block = 32 positions of one channel)
 };
 
 // ---------------------------------------------------------------- append side

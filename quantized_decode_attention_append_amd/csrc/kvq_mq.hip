@@ -1,6 +1,7 @@
 // Multi-query attention over the quantized cache: blocks of up to 8 consecutive query positions of a sequence
 // attend causally to the cache, each K / V tile read from HBM and decoded once for all of them. It also serves
-// single-query decode of caches with qN_1 bodies (a scale and a minimum per block, BeeLlama page q2_1 .. q6_1). It serves the
+// single-query decode of caches with qN_1 bodies (a scale and a minimum per block, BeeLlama page q2_1 .. q6_1)
+// and with token-axis K (KIVI-style per-channel K blocks, Qwen3.8-27B page, reader comment). It serves the
 // verification of drafted tokens (Qwen3.8-27B page, decode-speed paragraph: the engine drafts up to 7 tokens per
 // step with MTP heads) and chunked prefill over the quantized cache (the KVarN benchmark page and the
 // Qwen3.8-27B page measure prompt processing per cache type).
@@ -36,6 +37,7 @@ struct MqOps {                 // one tile's MFMA operands in LDS
   uint16_t ks[8 * 32];         // K scales [block][position]
   u32x4 kmin[2 * 64];          // qN_1 K: A operand of the offset term [subtile][lane] (rows: positions; k 0-7:
                                // the blocks' offsets, fp16 hi parts; k 8-15: lo parts; k 16-31: zero)
+  u32x4 kl[2 * 8 * 64];        // token-axis K: the remainders of the scaled K values (k holds the rounded ones)
 };
 
 enum { kKindQ = 0, kKindQ8Ring = 1, kKindBf16Ring = 2, kKindF16Ring = 3 };
@@ -178,6 +180,82 @@ __device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, 
     break;
   switch (np) { KVQ_VP(0) KVQ_VP(1) KVQ_VP(2) KVQ_VP(3) KVQ_VP(4) KVQ_VP(5) KVQ_VP(6) default: KVQ_VP(7) }
 #undef KVQ_VP
+}
+
+// Token-axis K operands of one tile (a block is the 32 positions of one channel: one scale, and for qN_1 one
+// minimum, per channel): thread t as in decode_k_tile, its 16 channels' values code x scale (+ offset) as fp16
+// rounded values and remainders. kscale / kmin: the tile's scales and minima [channel] (kmin null for qN_0).
+template <int N>
+__device__ inline void decode_k_tile_tok(const uint8_t* raw, const uint8_t* kscale, const uint8_t* kmin, MqOps& ops,
+                                         uint32_t magic) {
+  constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
+  const int t = threadIdx.x;
+  const int s = t >> 8, lane = (t >> 2) & 63, bp = t & 3, g = lane >> 4;
+  uint32_t r0[2 * w0], r1[w1 ? 2 * w1 : 1], r2[w2 ? 2 * w2 : 1];
+  const int sub = 512 * N * s;
+  raw_k_run<w0>(raw, sub, lane, r0);
+  if constexpr (w1 > 0) raw_k_run<w1>(raw, sub + 512 * w0, lane, r1);
+  if constexpr (w2 > 0) raw_k_run<w2>(raw, sub + 512 * (w0 + w1), lane, r2);
+  half8 c[2];
+  switch (bp) {
+    case 0: c[0] = decode_run_piece<N, 0>(r0, r1, r2, magic); c[1] = decode_run_piece<N, 1>(r0, r1, r2, magic); break;
+    case 1: c[0] = decode_run_piece<N, 2>(r0, r1, r2, magic); c[1] = decode_run_piece<N, 3>(r0, r1, r2, magic); break;
+    case 2: c[0] = decode_run_piece<N, 4>(r0, r1, r2, magic); c[1] = decode_run_piece<N, 5>(r0, r1, r2, magic); break;
+    default: c[0] = decode_run_piece<N, 6>(r0, r1, r2, magic); c[1] = decode_run_piece<N, 7>(r0, r1, r2, magic); break;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = 2 * bp + h;
+    const int ch0 = 32 * b + 8 * g;   // the piece's 8 channels
+    const u32x4 dw = *(const u32x4*)(kscale + 2 * ch0);
+    const u32x4 cw = __builtin_bit_cast(u32x4, c[h]);
+    u32x4 hi, lo;
+    if (kmin) {
+      const u32x4 mw = *(const u32x4*)(kmin + 2 * ch0);
+      constexpr float bias = (float)(1 << (N - 1));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const half2v cv = as_h2(cw[k]), d = as_h2(dw[k]), m = as_h2(mw[k]);
+        const float x0 = fmaf((float)cv[0], (float)d[0], fmaf(bias, (float)d[0], (float)m[0]));
+        const float x1 = fmaf((float)cv[1], (float)d[1], fmaf(bias, (float)d[1], (float)m[1]));
+        const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+        hi[k] = as_u(half2v{h0, h1});
+        lo[k] = as_u(half2v{(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)});
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {   // code x scale has at most 19 significant bits: value + exact remainder
+        const half2v pr = as_h2(cw[k]) * as_h2(dw[k]);
+        hi[k] = as_u(pr);
+        lo[k] = as_u(__builtin_elementwise_fma(as_h2(cw[k]), as_h2(dw[k]), -pr));
+      }
+    }
+    const int o = (s * 8 + b) * 64 + lane;
+    ops.k[o] = hi;
+    ops.kl[o] = lo;
+  }
+}
+
+// QK of a token-axis K tile: the scaled values and their remainders against the query operand, all blocks into one
+// accumulator per subtile (the scales are already in the operands).
+__device__ inline void mq_qk_tok(const MqOps& ops, const half8* qop, float qmul, float* x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    floatx4 c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ops.k[(s * 8 + b) * 64 + lane]), qop[b], c0,
+                                                  0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ops.kl[(s * 8 + b) * 64 + lane]), qop[b], c1,
+                                                  0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = c0[r] + c1[r];
+      x[4 * s + r] = (v + dpp_ror8(v)) * qmul;
+    }
+  }
 }
 
 // qN_1 K: the A operand of the offset term for subtile s, lane (g, m16): row = position 16s + m16; g = 0 holds
@@ -471,7 +549,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int b = 0; b < 8; ++b) bsum[b] = build_qop_f16(qrow, sg, b, e, head_ok, lo_lane, qop[b]);
       qmul = a.scale * kLog2e * ldexpf(1.0f, e);
-      if (kind == kKindQ && g.k_min) {
+      if (kind == kKindQ && g.k_min && !g.k_axis) {
         // qN_1 K: the B operand of the offset term, lane (g, m16): k = 8g + b (g = 0, 1) is the block-b sum of
         // the operand values of head m16 & 7 (over the 4 lane groups), its fp16 hi part in columns 0-7 and its
         // lo part in columns 8-15; g = 2, 3 zero
@@ -550,9 +628,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int kcodes = 1024 * (qb ? NK : 8), vcodes = 1024 * (qb ? NV : 8);
       const uint8_t* vscale = raw + r.kbytes + vcodes;
       if (qb) {
-        decode_k_tile<NK>(raw, ops, magic);
+        if (g.k_axis) {
+          decode_k_tile_tok<NK>(raw, raw + kcodes, g.k_min ? raw + kcodes + 512 : nullptr, ops, magic);
+        } else {
+          decode_k_tile<NK>(raw, ops, magic);
+          if (g.k_min && tid < 128) kmin_operand<NK>(raw + kcodes, raw + kcodes + 512, ops);
+        }
         decode_v_tile<NV>(raw + r.kbytes, vscale, g.v_min ? vscale + 512 : nullptr, ops, magic);
-        if (g.k_min && tid < 128) kmin_operand<NK>(raw + kcodes, raw + kcodes + 512, ops);
       } else {
         decode_k_tile<8>(raw, ops, magic);
         decode_v_tile<8>(raw + r.kbytes, vscale, nullptr, ops, magic);
@@ -568,7 +650,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (r.pos0 < hi && r.pos0 + kTile > lo) {
         if (r.kind != qop_kind) build_qop(r.kind);
         float x[8], p[8];
-        if (body || r.kind == kKindQ8Ring) mq_qk_q(ops, qop, qmul, x, body && g.k_min ? &s_qsum[wave * 64 + lane] : nullptr);
+        if (body && g.k_axis) mq_qk_tok(ops, qop, qmul, x);
+        else if (body || r.kind == kKindQ8Ring)
+          mq_qk_q(ops, qop, qmul, x, body && g.k_min ? &s_qsum[wave * 64 + lane] : nullptr);
         else if (r.kind == kKindF16Ring) mq_qk_16<true>(ops, (const u32x4*)qop, qmul, x);
         else mq_qk_16<false>(ops, (const u32x4*)qop, qmul, x);
         const int g4 = lane >> 4;

@@ -95,6 +95,48 @@ __device__ inline uint32_t quant_lane_min(float x, int n_bits, uint16_t* d16_bit
   return (uint32_t)c;
 }
 
+// Token-axis K (a block is the 32 positions of one channel in a position tile): quantize the block held by one
+// thread, xs[0..31], with the rules of quant_lane (symmetric qN_0) or quant_lane_min (qN_1). Writes the 32 codes
+// (biased for qN_0) and the block's fp16 scale (and minimum).
+__device__ inline void quant_block_local(const float* xs, int n_bits, bool with_min, uint8_t* u, uint16_t* d16_bits,
+                                         uint16_t* m16_bits) {
+#pragma clang fp contract(off)
+  if (with_min) {
+    float mn = xs[0], mx = xs[0];
+    for (int t = 1; t < kTile; ++t) {
+      mn = fminf(mn, xs[t]);
+      mx = fmaxf(mx, xs[t]);
+    }
+    const float levels = (float)((1 << n_bits) - 1);
+    float d = (mx - mn) / levels;
+    d = fminf(d, 65504.0f);
+    const _Float16 h = (_Float16)d;
+    const _Float16 mh = (_Float16)fminf(fmaxf(mn, -65504.0f), 65504.0f);
+    *m16_bits = __builtin_bit_cast(uint16_t, mh);
+    const float dh = (float)h;
+    *d16_bits = dh == 0.0f ? 0 : __builtin_bit_cast(uint16_t, h);
+    for (int t = 0; t < kTile; ++t) {
+      float c = dh == 0.0f ? 0.0f : rintf((xs[t] - (float)mh) / dh);
+      u[t] = (uint8_t)fminf(fmaxf(c, 0.0f), levels);
+    }
+    return;
+  }
+  float amax = 0.0f;
+  for (int t = 0; t < kTile; ++t) amax = fmaxf(amax, fabsf(xs[t]));
+  const float qmax = (float)((1 << (n_bits - 1)) - 1);
+  float d = amax / qmax;
+  d = fminf(d, 65504.0f);
+  const _Float16 h = (_Float16)d;
+  const float dh = (float)h;
+  const int off = 1 << (n_bits - 1);
+  *d16_bits = dh == 0.0f ? 0 : __builtin_bit_cast(uint16_t, h);
+  for (int t = 0; t < kTile; ++t) {
+    float c = dh == 0.0f ? 0.0f : rintf(xs[t] / dh);
+    c = fminf(fmaxf(c, -qmax), qmax);
+    u[t] = (uint8_t)((int)c + off);
+  }
+}
+
 // fp32 ring representation r(x) of one value: the bf16 value itself, its f16 rounding, or its q8_0 round trip.
 __device__ inline float ring_rep(float x, int tail_dtype) {
 #pragma clang fp contract(off)
@@ -200,7 +242,7 @@ typedef uint8_t WriteCodes[2][kTile][256];
 // One work-group of 512 threads per (position tile, KV head): thread (kv, c) quantizes channel c of K (kv = 0)
 // or V (kv = 1) for every position of the tile that the call writes. A: WriteArgs, or one role of StepArgs
 // (the kernel argument itself, so that the item list is read in place). codes: the caller's LDS buffer.
-// kMin = false compiles the qN_1 quantizer out (for callers that never write qN_1 bodies).
+// kMin = false compiles the qN_1 and token-axis K quantizers out (for callers that never write such bodies).
 template <class A, bool kMin = true>
 __device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& codes) {
 #pragma clang fp contract(off)
@@ -255,7 +297,8 @@ __device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& c
                         : 1.0f;
   // few positions of the body (a decode step's evict): OR the codes in directly, no LDS round trip
   const bool direct = !a.dst_ring && t1 - t0 <= kDirectPositions;
-  for (int t = t0; t < t1; ++t) {
+  // the value of channel c at tile position t, as the body quantizes it
+  auto value_at = [&](int t) {
     const int p = tile * kTile + t;
     float x;
     if (p >= w.len_old) {
@@ -265,6 +308,22 @@ __device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& c
       x = ring_value(g, slab, kv, head, p, c);
     }
     if (!a.dst_ring && g.kvarn) x = x / sig;
+    return x;
+  };
+  if (kMin && kv == 0 && !a.dst_ring && g.k_axis) {
+    // token-axis K: this thread's channel over the whole tile is one block (the host writes whole tiles here)
+    float xs[kTile];
+    for (int t = 0; t < kTile; ++t) xs[t] = value_at(t);
+    uint8_t us[kTile];
+    uint16_t dq, dm = 0;
+    quant_block_local(xs, nb, g.k_min, us, &dq, &dm);
+    for (int t = 0; t < kTile; ++t) codes[0][t][c] = us[t];
+    ((uint16_t*)(ktile + 4 * D * NK))[c] = dq;                                          // scales [channel]
+    if (g.k_min) ((uint16_t*)(ktile + 4 * D * NK + 2 * D))[c] = dm;                     // minima [channel]
+  } else
+  for (int t = t0; t < t1; ++t) {
+    const int p = tile * kTile + t;
+    const float x = value_at(t);
     uint16_t dq, dm = 0;
     const bool with_min = kMin && !a.dst_ring && (kv ? g.v_min : g.k_min);   // uniform over each 256-thread half
     const uint32_t u = with_min ? quant_lane_min(x, nb, &dq, &dm) : quant_lane(x, nb, &dq);

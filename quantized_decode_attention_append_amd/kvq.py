@@ -23,7 +23,8 @@ REGION = {"k_body": 0, "v_body": 1, "k_ring": 2, "v_ring": 3, "sigma": 4, "slab"
 MAX_BATCH = 64
 
 _FIELDS = ("n_layers", "max_seqs", "capacity", "n_q_heads", "n_kv_heads", "head_dim", "k_bits", "v_bits",
-           "kvarn", "tail_len", "tail_slack", "tail_dtype", "layout", "index_dim", "index_pool", "k_min", "v_min")
+           "kvarn", "tail_len", "tail_slack", "tail_dtype", "layout", "index_dim", "index_pool", "k_min", "v_min",
+           "k_axis")
 
 SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_init", "kvq_cache_destroy",
            "kvq_seq_reset", "kvq_seq_truncate", "kvq_seq_lengths", "kvq_workspace_bytes", "kvq_append", "kvq_tail_evict",
@@ -31,7 +32,8 @@ SYMBOLS = ("kvq_config_validate", "kvq_cache_bytes", "kvq_region", "kvq_cache_in
 KERNEL = {"decode": 0, "gather": 1, "combine": 2, "append": 3, "evict": 4, "append_evict": 5, "index": 6, "mq": 7}
 
 
-_OPTIONAL = ("layout", "index_dim", "index_pool", "k_min", "v_min")
+_OPTIONAL = ("layout", "index_dim", "index_pool", "k_min", "v_min",
+           "k_axis")
 
 
 class Config(ctypes.Structure):

@@ -45,11 +45,13 @@ def _random_cfgs(n=60):
         hk = int(rng.choice([1, 2, 4, 8]))
         w = int(rng.choice([0, 32, 1024, 2048]))
         pool = int(rng.choice([0, 1, 2, 4, 8, 16]))
+        slack = int(rng.choice([0, 32, 512])) if w else 0
         yield _cfg(index_dim=32 * pool, index_pool=pool, n_layers=int(rng.integers(1, 17)), max_seqs=int(rng.integers(1, 9)),
                    capacity=int(rng.integers(1, 300000)), n_kv_heads=hk, n_q_heads=hk * int(rng.integers(1, 9)),
                    k_bits=int(rng.integers(2, 9)), v_bits=int(rng.integers(2, 9)), kvarn=int(rng.integers(0, 2)),
-                   tail_len=w, tail_slack=int(rng.choice([0, 32, 512])) if w else 0,
-                   tail_dtype=int(rng.integers(1, 4)), k_min=int(rng.integers(0, 2)), v_min=int(rng.integers(0, 2)))
+                   tail_len=w, tail_slack=slack,
+                   tail_dtype=int(rng.integers(1, 4)), k_min=int(rng.integers(0, 2)), v_min=int(rng.integers(0, 2)),
+                   k_axis=int(slack >= 32 and rng.integers(0, 2)))
 
 
 def test_cache_bytes_and_regions_match_oracle():
@@ -79,6 +81,7 @@ def test_kv_mib_table_through_the_library():
     dict(tail_len=64, tail_slack=31), dict(tail_len=64, tail_dtype=0), dict(tail_len=64, tail_dtype=4),
     dict(index_dim=128, index_pool=3), dict(index_dim=96, index_pool=4), dict(index_dim=128, index_pool=0),
     dict(k_min=2), dict(v_min=-1), dict(k_min=1, layout=1), dict(v_min=1, layout=1),
+    dict(k_axis=2), dict(k_axis=1, layout=1), dict(k_axis=1, tail_len=0), dict(k_axis=1, tail_slack=16),
 ])
 def test_validation_rejects(bad):
     from quantized_decode_attention_append_amd import kvq

@@ -298,3 +298,79 @@ def test_qn1_body_reproduces_values_on_its_grid(k_min, v_min, tail_dtype):
     lay = slab_layout(cfg)
     img = o.slab_image(0, 0)
     assert img.shape[0] == lay["slab"]
+
+
+# ---- token-axis K (a block is the 32 positions of one channel in a position tile)
+
+def _tok_cfg(**kw):
+    c = dict(n_layers=1, max_seqs=1, capacity=512, n_q_heads=4, n_kv_heads=2, head_dim=256, k_bits=4, v_bits=5,
+             kvarn=0, tail_len=40, tail_slack=56, tail_dtype=1, k_axis=1)
+    c.update(kw)
+    return c
+
+
+def test_token_axis_k_stores_per_channel_grids_exactly():
+    """K values that are, per (tile, channel), integer codes times a channel-specific power of two spanning the
+    full code range are stored exactly along the token axis, though every position mixes 256 different scales
+    (which a per-token block of 32 channels could not represent exactly)."""
+    rng = np.random.default_rng(5)
+    n = 192
+    qmax = 7
+    c = rng.integers(-qmax, qmax + 1, size=(n // 32, 32, 2, 256))
+    c[:, 3] = qmax
+    c[:, 9] = -qmax
+    ex = rng.integers(-6, 4, size=(n // 32, 1, 2, 256))
+    kx = (c * 2.0 ** ex).reshape(n, 2, 256).astype(np.float32)
+    from workloads import bf16_bits
+    kb = bf16_bits(kx)
+    assert np.array_equal(bf16_to_f32(kb), kx)
+    _, vb = small_tokens(9, n, 2, 256)
+    o = OracleCache(_tok_cfg(tail_dtype=1))
+    o.append(0, [0], [n], kb, vb)
+    o.tail_evict(0, [0])
+    ln, body = o.lengths(0, 0)
+    assert body == (n - 40) // 32 * 32 == 128
+    k, _ = o.dequantized(0, 0, np.arange(body))
+    assert np.array_equal(k, kx[:body].astype(np.float64))
+    per_token = OracleCache(_tok_cfg(k_axis=0, tail_len=0, tail_slack=0, tail_dtype=0))
+    per_token.append(0, [0], [n], kb, vb)
+    k2, _ = per_token.dequantized(0, 0, np.arange(body))
+    assert not np.array_equal(k2, kx[:body].astype(np.float64))
+
+
+@pytest.mark.parametrize("k_min,tail_dtype", [(0, 1), (1, 2), (0, 3), (1, 1)])
+def test_token_axis_body_grows_by_whole_tiles_and_is_chunk_invariant(k_min, tail_dtype):
+    k, v = small_tokens(21 + tail_dtype, 300, 2, 256)
+    cfg = _tok_cfg(k_min=k_min, tail_dtype=tail_dtype)
+    a = OracleCache(cfg)
+    a.append(0, [0], [300], k, v)
+    a.tail_evict(0, [0])
+    b = OracleCache(cfg)
+    off = 0
+    for n in (1, 37, 90, 3, 64, 105):
+        b.append(0, [0], [n], k[off:off + n], v[off:off + n])
+        off += n
+        ln, body = b.lengths(0, 0)
+        assert body % 32 == 0 and ln - body <= cfg["tail_len"] + cfg["tail_slack"]
+        if n <= 3:
+            b.tail_evict(0, [0])
+            ln, body = b.lengths(0, 0)
+            assert cfg["tail_len"] <= ln - body < cfg["tail_len"] + 32 or ln < cfg["tail_len"]
+    b.tail_evict(0, [0])
+    assert a.lengths(0, 0) == b.lengths(0, 0)
+    ka, va = a.dequantized(0, 0)
+    kb2, vb2 = b.dequantized(0, 0)
+    assert np.array_equal(ka, kb2) and np.array_equal(va, vb2)
+    bl = a.lengths(0, 0)[1]
+    sa, sb = a.st(0, 0), b.st(0, 0)
+    assert np.array_equal(sa.ku[:bl], sb.ku[:bl]) and np.array_equal(sa.ktd[:bl // 32], sb.ktd[:bl // 32])
+    # the body's K is within half a channel scale of the ring representation of the input
+    ln, body = a.lengths(0, 0)
+    kin = bf16_to_f32(k[:body]).astype(np.float64)
+    if tail_dtype == 2:
+        return
+    st = a.st(0, 0)
+    d = np.repeat(st.ktd[:body // 32].astype(np.float64), 32, axis=0)      # [pos, head, ch]
+    extra = 0 if not k_min else np.abs(np.repeat(st.ktm[:body // 32].astype(np.float64), 32, axis=0)
+                                       - kin.reshape(-1, 32, 2, 256).min(axis=1).repeat(32, axis=0))
+    assert np.all(np.abs(ka[:body] - kin) <= d / 2 + extra + 2.0 ** -22 * (np.abs(kin) + 1))
