@@ -50,8 +50,10 @@ typedef enum {
 typedef enum {
   KVQ_LAYOUT_TILES = 0, /* V (and q8_0 ring V) stored in 32-position tiles ordered for the decode kernel's
                            matrix operands: the fastest dense decode; no sparse decode              */
-  KVQ_LAYOUT_ROWS = 1   /* every K and V position stored as one contiguous row, so that a sparse
-                           layer gathers exactly the rows it attends (offload page, QSA paragraph)  */
+  KVQ_LAYOUT_ROWS = 1   /* every K and V position stored as one row, position-major: a position's K and V
+                           rows of all KV heads are one contiguous run (the K body / K ring regions hold
+                           them; the V regions are empty), so that a sparse layer gathers exactly the rows
+                           it attends in whole runs (offload page, QSA paragraph)                     */
 } kvq_layout;
 
 /* Maximum number of sequences one call may name. */

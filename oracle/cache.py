@@ -392,7 +392,20 @@ class OracleCache:
         img = np.zeros(lay["slab"], dtype=np.uint8)
         hk = self.cfg["n_kv_heads"]
         cap32 = lay["cap32"]
-        for region, n in (("k_body", cap32), ("v_body", cap32), ("k_ring", self.R), ("v_ring", self.R)):
+        if self.rows:
+            # position-major: [position][head][K row, V row] in the body and in the ring region
+            for kreg, vreg, region, n in (("k_body", "v_body", "k_body", cap32), ("k_ring", "v_ring", "k_ring", self.R)):
+                off, size = lay[region]
+                if size == 0:
+                    continue
+                runs = np.stack([np.concatenate([self.region_bytes(layer, seq, kreg, h, 0, n).reshape(n, -1),
+                                                 self.region_bytes(layer, seq, vreg, h, 0, n).reshape(n, -1)], axis=1)
+                                 for h in range(hk)], axis=1)            # [n, head, K row + V row]
+                img[off:off + size] = runs.reshape(-1)
+            regions = ()
+        else:
+            regions = (("k_body", cap32), ("v_body", cap32), ("k_ring", self.R), ("v_ring", self.R))
+        for region, n in regions:
             off, size = lay[region]
             if size == 0:
                 continue

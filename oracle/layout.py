@@ -55,9 +55,12 @@ lane l = 16j + m's 8 bf16 values of channels 32b + 8j .. +7 of slot 16s + m:
 of channel 16*n + d16 at tile positions T(j, i): [n][lane][8 x bf16].
 
 Row layout (a cache option for sparse layers): V is stored exactly like K, one
-row per position, and K stays in rows (body and q8_0 ring: the K row format
-above; bf16 ring: the D bf16 values), so a position is one contiguous K row and
-one V row. The region sizes equal those of the tile layout.
+row per position (body and q8_0 ring: the K row format above; bf16 / f16 ring: the
+D 16-bit values), and the rows are position-major: for each position, for each KV
+head, the K row and then the V row. One position of every KV head is one contiguous
+run (q8_0 with 2 KV heads: 1,088 bytes), so a gather of listed positions reads whole
+runs. The body region holds [capacity32][head][K row, V row] and the ring region
+[R][head][K row, V row]; the separate V regions are empty.
 
 Arena: slabs of [layer][sequence]; each slab holds, in order and 256-byte
 aligned: K body [head][capacity32/32][tile], V body [head][capacity32/32][tile],
@@ -363,11 +366,12 @@ def slab_layout(cfg: dict) -> dict:
         ring_rk = ring_rv = row_bytes(8, d)
     else:
         ring_rk = ring_rv = 0
+    rows = cfg.get("layout", 0) == 1     # position-major K and V rows in the K regions
     sizes = {
-        "k_body": hk * cap32 * rk,
-        "v_body": hk * cap32 * rv,
-        "k_ring": hk * r * ring_rk,
-        "v_ring": hk * r * ring_rv,
+        "k_body": hk * cap32 * (rk + rv if rows else rk),
+        "v_body": 0 if rows else hk * cap32 * rv,
+        "k_ring": hk * r * (ring_rk + ring_rv if rows else ring_rk),
+        "v_ring": 0 if rows else hk * r * ring_rv,
         "sigma": hk * 2 * d * 2 if cfg["kvarn"] else 0,
         "index": cap32 * 64 if cfg.get("index_dim", 0) else 0,
     }

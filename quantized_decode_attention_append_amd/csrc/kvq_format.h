@@ -28,8 +28,9 @@
 //   32b+8j.. of slot 16s+m: [s][b][lane][8 x bf16]; V tiles hold, per n-tile and lane, the 8 bf16 values
 //   of channel 16n+d16 at positions T(j,i): [n][lane][8 x bf16].
 // * Row layout (a cache option for sparse layers): V is stored exactly like K, one row per position
-//   (body, q8_0 ring) or plain bf16 rows (bf16 ring), so every position is one contiguous row of K and
-//   one of V. Region sizes are the same in both layouts.
+//   (body, q8_0 ring) or plain 16-bit rows (bf16 / f16 ring), position-major: for each position, for each KV
+//   head, the K row and then the V row, so one position of every head is one contiguous run. The body region
+//   holds [cap32][head][K row, V row], the ring region [R][head][K row, V row]; the V regions are empty.
 // * Arena: [layer][seq] slabs; a slab holds (256-byte aligned) K body [head][cap32/32][tile],
 //   V body [head][cap32/32][tile], K ring [head][R/32][tile], V ring [head][R/32][tile] (row layout:
 //   [head][positions][row] for K and V), KVarN sigma [head][K,V][D] fp16, and for a cache with an indexer the
@@ -104,6 +105,13 @@ KVQ_HD int vtile_lane_byte(int lane, int b, int nt, int w) {
   return (b / unit) * 64 * unit + lane * unit + (b % unit);
 }
 
+// Row layout: byte offsets (within the body or ring region) of the K row of (position or slot p, head h) and
+// of its V row; pair = row_k + row_v (or ring_row_k + ring_row_v).
+KVQ_HD size_t rows_k_off(size_t p, int h, int n_kv_heads, int pair) { return (p * n_kv_heads + h) * (size_t)pair; }
+KVQ_HD size_t rows_v_off(size_t p, int h, int n_kv_heads, int pair, int row_k) {
+  return rows_k_off(p, h, n_kv_heads, pair) + row_k;
+}
+
 struct SlabLayout {
   size_t k_body, v_body, k_ring, v_ring, sigma, index;   // region offsets within a slab
   size_t k_body_sz, v_body_sz, k_ring_sz, v_ring_sz, sigma_sz, index_sz;
@@ -115,7 +123,7 @@ struct SlabLayout {
 // k_min / v_min: qN_1 bodies.
 KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_bits, int v_bits,
                               int kvarn, int tail_len, int tail_slack, int tail_dtype, int index, int k_min = 0,
-                              int v_min = 0) {
+                              int v_min = 0, int rows = 0) {
   SlabLayout L{};
   L.cap32 = (int)round_up((size_t)capacity, kTile);
   L.row_k = row_bytes(k_bits, head_dim, k_min);
@@ -127,10 +135,17 @@ KVQ_HD SlabLayout slab_layout(int capacity, int n_kv_heads, int head_dim, int k_
     L.ring_row_k = L.ring_row_v = row_bytes(8, head_dim);
   }
   size_t hk = (size_t)n_kv_heads;
-  L.k_body_sz = hk * L.cap32 * L.row_k;
-  L.v_body_sz = hk * L.cap32 * L.row_v;
-  L.k_ring_sz = hk * L.ring_slots * L.ring_row_k;
-  L.v_ring_sz = hk * L.ring_slots * L.ring_row_v;
+  if (rows) {   // position-major K and V rows in the K regions
+    L.k_body_sz = hk * L.cap32 * (L.row_k + L.row_v);
+    L.v_body_sz = 0;
+    L.k_ring_sz = hk * L.ring_slots * (L.ring_row_k + L.ring_row_v);
+    L.v_ring_sz = 0;
+  } else {
+    L.k_body_sz = hk * L.cap32 * L.row_k;
+    L.v_body_sz = hk * L.cap32 * L.row_v;
+    L.k_ring_sz = hk * L.ring_slots * L.ring_row_k;
+    L.v_ring_sz = hk * L.ring_slots * L.ring_row_v;
+  }
   L.sigma_sz = kvarn ? hk * 2 * head_dim * 2 : 0;
   L.index_sz = index ? (size_t)L.cap32 * kIndexWidth * 2 : 0;
   size_t off = 0;

@@ -82,10 +82,10 @@ __device__ inline void load_k_qrow(KRaw& r, const uint8_t* row, int j) {
 #pragma unroll
   for (int k = 0; k < n0; k += (n0 >= 4 ? 4 : 2)) {
     if constexpr (n0 >= 4) {
-      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(p0 + 4 * k));
+      const u32x4 v = *((const u32x4*)(p0 + 4 * k));
       r.w[k] = v[0]; r.w[k + 1] = v[1]; r.w[k + 2] = v[2]; r.w[k + 3] = v[3];
     } else {
-      const u32x2 v = __builtin_nontemporal_load((const u32x2*)(p0 + 4 * k));
+      const u32x2 v = *((const u32x2*)(p0 + 4 * k));
       r.w[k] = v[0]; r.w[k + 1] = v[1];
     }
   }
@@ -94,26 +94,26 @@ __device__ inline void load_k_qrow(KRaw& r, const uint8_t* row, int j) {
 #pragma unroll
     for (int k = 0; k < n1; k += (n1 >= 4 ? 4 : 2)) {
       if constexpr (n1 >= 4) {
-        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(p1 + 4 * k));
+        const u32x4 v = *((const u32x4*)(p1 + 4 * k));
         r.w[16 + k] = v[0]; r.w[16 + k + 1] = v[1]; r.w[16 + k + 2] = v[2]; r.w[16 + k + 3] = v[3];
       } else {
-        const u32x2 v = __builtin_nontemporal_load((const u32x2*)(p1 + 4 * k));
+        const u32x2 v = *((const u32x2*)(p1 + 4 * k));
         r.w[16 + k] = v[0]; r.w[16 + k + 1] = v[1];
       }
     }
   }
   if constexpr (P::n >= 3) {
-    const u32x2 v = __builtin_nontemporal_load((const u32x2*)(row + 4 * NB * (w0 + w1) + j * NB * w2));
+    const u32x2 v = *((const u32x2*)(row + 4 * NB * (w0 + w1) + j * NB * w2));
     r.w[24] = v[0]; r.w[25] = v[1];
   }
-  const u32x4 sc = __builtin_nontemporal_load((const u32x4*)(row + 4 * NB * N));
+  const u32x4 sc = *((const u32x4*)(row + 4 * NB * N));
   r.w[28] = sc[0]; r.w[29] = sc[1]; r.w[30] = sc[2]; r.w[31] = sc[3];
 }
 
 __device__ inline void load_k_bf16(KRaw& r, const uint8_t* row, int j) {
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(row + (32 * b + 8 * j) * 2));
+    const u32x4 v = *((const u32x4*)(row + (32 * b + 8 * j) * 2));
     r.w[4 * b] = v[0]; r.w[4 * b + 1] = v[1]; r.w[4 * b + 2] = v[2]; r.w[4 * b + 3] = v[3];
   }
 }
@@ -194,15 +194,15 @@ __device__ inline void load_v_qrow(VRaw& r, const uint8_t* row, int c) {
   const int b = c >> 3, j = (c & 7) >> 1;
   const int pc = j * NB + b;
   if constexpr (N == 8) {
-    r.w[0] = __builtin_nontemporal_load((const uint32_t*)(row + pc * 8 + 4 * (c & 1)));
+    r.w[0] = *((const uint32_t*)(row + pc * 8 + 4 * (c & 1)));
   } else {
-    r.w[0] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * ((pc * w0) / 4)));
+    r.w[0] = *((const uint32_t*)(row + 4 * ((pc * w0) / 4)));
     if constexpr (P::n >= 2)
-      r.w[1] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * NB * w0 + 4 * ((pc * w1) / 4)));
+      r.w[1] = *((const uint32_t*)(row + 4 * NB * w0 + 4 * ((pc * w1) / 4)));
     if constexpr (P::n >= 3)
-      r.w[2] = __builtin_nontemporal_load((const uint32_t*)(row + 4 * NB * (w0 + w1) + 4 * ((pc * w2) / 4)));
+      r.w[2] = *((const uint32_t*)(row + 4 * NB * (w0 + w1) + 4 * ((pc * w2) / 4)));
   }
-  r.w[3] = __builtin_nontemporal_load((const uint16_t*)(row + 4 * NB * N + 2 * b));
+  r.w[3] = *((const uint16_t*)(row + 4 * NB * N + 2 * b));
 }
 
 template <int N>
@@ -236,10 +236,12 @@ struct StepRows {
   VRaw vr[16];
 };
 
+// Row sources of one (sequence, KV head): the K and V rows of position (or slot) 0 and the byte stride from one
+// position to the next (the rows are position-major: every head's K and V rows of a position sit together).
 struct RowSrc {
   const uint8_t *kbody, *vbody, *kring, *vring;
   const int32_t* plist;
-  int len, body_len, R, tail, row_k, row_v, ring_row_k, ring_row_v;
+  int len, body_len, R, tail, body_stride, ring_stride;
 };
 
 __device__ inline void load_pos(StepRows& st, const RowSrc& rs, int g0, int ie) {
@@ -261,10 +263,10 @@ __device__ inline void load_rows(StepRows& st, const RowSrc& rs) {
   const bool body = valid && pos < rs.body_len;
   KRaw kr;   // (no zero fill: merging it with the loads would wait for them here)
   if (body) {
-    load_k_qrow<NK>(kr, rs.kbody + (size_t)pos * rs.row_k, j);
+    load_k_qrow<NK>(kr, rs.kbody + (size_t)pos * rs.body_stride, j);
   } else if (valid) {
-    if (rs.tail == 2) load_k_qrow<8>(kr, rs.kring + (size_t)(pos % rs.R) * rs.ring_row_k, j);
-    else load_k_bf16(kr, rs.kring + (size_t)(pos % rs.R) * rs.ring_row_k, j);
+    if (rs.tail == 2) load_k_qrow<8>(kr, rs.kring + (size_t)(pos % rs.R) * rs.ring_stride, j);
+    else load_k_bf16(kr, rs.kring + (size_t)(pos % rs.R) * rs.ring_stride, j);
   }
   // V rows of the 16 entries (lane = channel group)
   uint32_t vmask = 0, bmask = 0;
@@ -276,11 +278,11 @@ __device__ inline void load_rows(StepRows& st, const RowSrc& rs) {
       vmask |= 1u << t;
       if (pt < rs.body_len) {
         bmask |= 1u << t;
-        load_v_qrow<NV>(vr, rs.vbody + (size_t)pt * rs.row_v, lane);
+        load_v_qrow<NV>(vr, rs.vbody + (size_t)pt * rs.body_stride, lane);
       } else if (rs.tail == 2) {
-        load_v_qrow<8>(vr, rs.vring + (size_t)(pt % rs.R) * rs.ring_row_v, lane);
+        load_v_qrow<8>(vr, rs.vring + (size_t)(pt % rs.R) * rs.ring_stride, lane);
       } else {
-        const u32x2 x = __builtin_nontemporal_load((const u32x2*)(rs.vring + (size_t)(pt % rs.R) * rs.ring_row_v + 8 * lane));
+        const u32x2 x = *((const u32x2*)(rs.vring + (size_t)(pt % rs.R) * rs.ring_stride + 8 * lane));
         vr.w[0] = x[0];
         vr.w[1] = x[1];
       }
@@ -333,7 +335,8 @@ __device__ inline void sparse_step_write(const GatherArgs& a, const GatherSeq& S
     if (g.kvarn) x = x / f16_to_f32(((const uint16_t*)(slab + g.sigma))[((size_t)head * 2 + kv) * D + c]);
     uint16_t dq;
     const uint32_t u = quant_lane(x, nb, &dq);
-    uint8_t* row = slab + (kv ? g.v_body : g.k_body) + ((size_t)head * g.cap32 + p) * (kv ? g.row_v : g.row_k);
+    uint8_t* row = slab + g.k_body + (kv ? rows_v_off(p, head, g.n_kv_heads, g.row_k + g.row_v, g.row_k)
+                                         : rows_k_off(p, head, g.n_kv_heads, g.row_k + g.row_v));
     or_code(row, nullptr, true, kv, nb, 0, c, u, D);   // the row was zeroed with its slab
     if ((c % kBlock) == 0) ((uint16_t*)(row + 4 * (D / kBlock) * nb))[c / kBlock] = dq;
     if (img_k) {
@@ -378,12 +381,13 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
   const int j = lane >> 4, e16 = lane & 15;
   const int ib = (int)((long)split * S.n_list / S.n_splits);
   const int ie = (int)((long)(split + 1) * S.n_list / S.n_splits);
-  const RowSrc rs{slab + g.k_body + (size_t)head * g.cap32 * g.row_k,
-                  slab + g.v_body + (size_t)head * g.cap32 * g.row_v,
-                  slab + g.k_ring + (size_t)head * R * g.ring_row_k,
-                  slab + g.v_ring + (size_t)head * R * g.ring_row_v,
+  const int body_pair = g.row_k + g.row_v, ring_pair = g.ring_row_k + g.ring_row_v;
+  const RowSrc rs{slab + g.k_body + rows_k_off(0, head, g.n_kv_heads, body_pair),
+                  slab + g.k_body + rows_v_off(0, head, g.n_kv_heads, body_pair, g.row_k),
+                  slab + g.k_ring + rows_k_off(0, head, g.n_kv_heads, ring_pair),
+                  slab + g.k_ring + rows_v_off(0, head, g.n_kv_heads, ring_pair, g.ring_row_k),
                   a.positions ? a.positions + (size_t)si * a.pos_stride : nullptr,
-                  S.len, S.body_len, R, tail, g.row_k, g.row_v, g.ring_row_k, g.ring_row_v};
+                  S.len, S.body_len, R, tail, g.n_kv_heads * body_pair, g.n_kv_heads * ring_pair};
   // ---- query operands: wave w builds blocks w + NW k (channels 32 b + 8j + i) for row e16 of the A operand
   constexpr int BPW = 8 / NW;   // blocks per wave
   const int hh = e16 & 7;

@@ -88,7 +88,8 @@ hipError_t timed(kvq_cache* c, int kind, hipStream_t stream, F launch) {
 
 SlabLayout layout_of(const kvq_config& c) {
   return kvq::slab_layout(c.capacity, c.n_kv_heads, c.head_dim, c.k_bits, c.v_bits, c.kvarn, c.tail_len,
-                          c.tail_slack, c.tail_dtype, c.index_dim > 0 ? 1 : 0, c.k_min, c.v_min);
+                          c.tail_slack, c.tail_dtype, c.index_dim > 0 ? 1 : 0, c.k_min, c.v_min,
+                          c.layout == KVQ_LAYOUT_ROWS ? 1 : 0);
 }
 
 kvq_status validate(const kvq_config* c) {

@@ -165,8 +165,12 @@ __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int k
   if (g.tail_dtype == 1 || g.tail_dtype == 3) {   // 16-bit values: bf16 or f16
     const bool f16 = g.tail_dtype == 3;
     auto cv = [&](uint16_t bits) { return f16 ? f16_to_f32(bits) : bf16_to_f32(bits); };
-    if (g.layout == 1)
-      return cv(((const uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c]);
+    if (g.layout == 1) {   // position-major [slot][head][K row, V row]
+      const int pair = g.ring_row_k + g.ring_row_v;
+      const size_t off = kv ? rows_v_off(slot, head, g.n_kv_heads, pair, g.ring_row_k)
+                            : rows_k_off(slot, head, g.n_kv_heads, pair);
+      return cv(((const uint16_t*)(slab + g.k_ring + off))[c]);
+    }
     if (kv == 0) {
       const uint16_t* kt = (const uint16_t*)(slab + g.k_ring + rt * g.ring_tile_k);
       return cv(kt[(((t / 16) * NB + b) * 64 + klane) * 8 + (c % 8)]);
@@ -175,7 +179,9 @@ __device__ inline float ring_value(const Geometry& g, const uint8_t* slab, int k
     return cv(*((const uint16_t*)(tile + (size_t)(c / 16) * 64 * 16 + lane * 16) + e));
   }
   if (g.layout == 1) {
-    const uint8_t* row = slab + (kv ? g.v_ring : g.k_ring) + ((size_t)head * R + slot) * g.ring_row_k;
+    const int pair = g.ring_row_k + g.ring_row_v;
+    const uint8_t* row = slab + g.k_ring + (kv ? rows_v_off(slot, head, g.n_kv_heads, pair, g.ring_row_k)
+                                               : rows_k_off(slot, head, g.n_kv_heads, pair));
     const float dh = f16_to_f32(((const uint16_t*)(row + NB * 32))[b]);
     return (float)((int)row[(j * NB + b) * 8 + (c % 8)] - 128) * dh;
   }
@@ -261,27 +267,30 @@ __device__ inline void body_write_wg(const A& a, int wg, int head, WriteCodes& c
 
   const bool vrows = g.layout == 1;
   int row_k, row_v;
-  uint8_t* kbase;
-  uint8_t* vbase;   // row layout: V rows of this head
-  uint8_t* vtile;   // tile layout: this work-group's V tile
-  uint8_t* ktile;   // tile layout: this work-group's K tile
+  size_t row_stride;   // row layout: bytes from one position's rows to the next one's (all heads' K and V rows)
+  uint8_t* kbase;      // row layout: K row of position 0 of this head
+  uint8_t* vbase;      // row layout: V row of position 0 of this head
+  uint8_t* vtile;      // tile layout: this work-group's V tile
+  uint8_t* ktile;      // tile layout: this work-group's K tile
   if (a.dst_ring) {
     row_k = row_v = g.ring_row_k;
-    kbase = slab + g.k_ring + (size_t)head * R * row_k;
-    vbase = slab + g.v_ring + (size_t)head * R * row_v;
+    row_stride = (size_t)g.n_kv_heads * (row_k + row_v);
+    kbase = slab + g.k_ring + rows_k_off(0, head, g.n_kv_heads, row_k + row_v);
+    vbase = kbase + row_k;
     const size_t rt = (size_t)head * (R / kTile) + ((tile * kTile) % R) / kTile;
     ktile = slab + g.k_ring + rt * g.ring_tile_k;
     vtile = slab + g.v_ring + rt * g.ring_tile_v;
   } else {
     row_k = g.row_k;
     row_v = g.row_v;
-    kbase = slab + g.k_body + (size_t)head * g.cap32 * row_k;
-    vbase = slab + g.v_body + (size_t)head * g.cap32 * row_v;
+    row_stride = (size_t)g.n_kv_heads * (row_k + row_v);
+    kbase = slab + g.k_body + rows_k_off(0, head, g.n_kv_heads, row_k + row_v);
+    vbase = kbase + row_k;
     ktile = slab + g.k_body + ((size_t)head * (g.cap32 / kTile) + tile) * g.tile_k;
     vtile = slab + g.v_body + ((size_t)head * (g.cap32 / kTile) + tile) * g.tile_v;
   }
-  auto krow_of = [&](int p) { return kbase + (size_t)(a.dst_ring ? p % R : p) * row_k; };
-  auto vrow_of = [&](int p) { return vbase + (size_t)(a.dst_ring ? p % R : p) * row_v; };
+  auto krow_of = [&](int p) { return kbase + (size_t)(a.dst_ring ? p % R : p) * row_stride; };
+  auto vrow_of = [&](int p) { return vbase + (size_t)(a.dst_ring ? p % R : p) * row_stride; };
   const int t0 = max(w.p0 - tile * kTile, 0);
   const int t1 = min(w.p1 - tile * kTile, kTile);
 
@@ -503,8 +512,11 @@ __device__ inline void bf16_ring_write_wg(const A& a, int wg, int head) {
     uint16_t v = in[((size_t)(w.src_row + p - w.len_old) * g.n_kv_heads + head) * D + c];
     if (g.tail_dtype == 3) v = bf16_to_f16_bits(v);   // f16 tail
     const int slot = p % R;
-    if (g.layout == 1) {
-      ((uint16_t*)(slab + (kv ? g.v_ring : g.k_ring)))[((size_t)head * R + slot) * D + c] = v;
+    if (g.layout == 1) {   // position-major [slot][head][K row, V row]
+      const int pair = g.ring_row_k + g.ring_row_v;
+      const size_t off = kv ? rows_v_off(slot, head, g.n_kv_heads, pair, g.ring_row_k)
+                            : rows_k_off(slot, head, g.n_kv_heads, pair);
+      ((uint16_t*)(slab + g.k_ring + off))[c] = v;
     } else if (kv == 0) {
       // [s][b][lane][8]: lane 16 j + slot % 16 holds channels 32b + 8j .. +7
       const int ts = slot % kTile;

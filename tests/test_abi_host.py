@@ -46,12 +46,14 @@ def _random_cfgs(n=60):
         w = int(rng.choice([0, 32, 1024, 2048]))
         pool = int(rng.choice([0, 1, 2, 4, 8, 16]))
         slack = int(rng.choice([0, 32, 512])) if w else 0
-        yield _cfg(index_dim=32 * pool, index_pool=pool, n_layers=int(rng.integers(1, 17)), max_seqs=int(rng.integers(1, 9)),
+        km, vm = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+        ka = int(slack >= 32 and rng.integers(0, 2))
+        rows = int(not (km or vm or ka) and rng.integers(0, 2))
+        yield _cfg(layout=rows, index_dim=32 * pool, index_pool=pool, n_layers=int(rng.integers(1, 17)), max_seqs=int(rng.integers(1, 9)),
                    capacity=int(rng.integers(1, 300000)), n_kv_heads=hk, n_q_heads=hk * int(rng.integers(1, 9)),
                    k_bits=int(rng.integers(2, 9)), v_bits=int(rng.integers(2, 9)), kvarn=int(rng.integers(0, 2)),
                    tail_len=w, tail_slack=slack,
-                   tail_dtype=int(rng.integers(1, 4)), k_min=int(rng.integers(0, 2)), v_min=int(rng.integers(0, 2)),
-                   k_axis=int(slack >= 32 and rng.integers(0, 2)))
+                   tail_dtype=int(rng.integers(1, 4)), k_min=km, v_min=vm, k_axis=ka)
 
 
 def test_cache_bytes_and_regions_match_oracle():
