@@ -33,6 +33,7 @@ UNITS = [
     ("kvq_scratch.hip", ["-ffp-contract=off"]),
     ("kvq_index.hip", ["-ffp-contract=off"]),
     ("kvq_mq.hip", ["-ffp-contract=fast"]),
+    ("kvq_mq_var.hip", ["-ffp-contract=fast"]),
 ]
 PROBE_UNITS = [("kvq_probe.hip", [])]
 
