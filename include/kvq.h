@@ -216,9 +216,9 @@ kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, cons
  * dropped afterwards with kvq_seq_truncate, which requires them to still be ring rows: tail_len >= T - 1, and
  * any kvq_tail_evict (or fused step) comes after the verification, not before it. With KVQ_LAYOUT_TILES
  * and T >= 2 one multi-query launch reads and decodes every tile of a sequence once for all T queries (a
- * work-group of 8 waves, one query per wave, over a range of the tiles, the decoded operands shared through
- * LDS); T = 1 runs exactly as kvq_decode_attn; with KVQ_LAYOUT_ROWS each (sequence, query) pair is an entry
- * of the gather launch.
+ * work-group of 8 waves over a range of the tiles, the decoded operands shared through LDS; two queries per wave,
+ * or one with KVarN, a qN_1 body or token-axis K); T = 1 runs exactly as kvq_decode_attn; with KVQ_LAYOUT_ROWS
+ * each (sequence, query) pair is an entry of the gather launch.
  * Errors: KVQ_E_INVALID if T is outside [1, KVQ_MAX_QUERIES] or n_seqs * T > KVQ_MAX_BATCH; KVQ_E_STATE if
  * a sequence holds fewer than T positions; others as kvq_decode_attn. */
 kvq_status kvq_decode_attn_multi(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
@@ -231,8 +231,8 @@ kvq_status kvq_decode_attn_multi(kvq_cache* cache, int32_t layer, int32_t n_seqs
  * attends to positions [0, p] through the stored representation of every position, the chunk's own tokens
  * included (the KVarN benchmark page and the Qwen3.8-27B page measure prompt processing per cache type).
  * k_bf16, v_bf16: device bf16 [sum n_new][Hkv][D]; q_bf16: device bf16 [sum n_new][Hq][D]; out: device fp32
- * [sum n_new][Hq][D]; all packed in call order. Queries run in blocks of 8 through the multi-query kernel, each
- * tile read and decoded once per block. workspace: kvq_prefill_workspace_bytes(cache, n_seqs, max n_new, max
+ * [sum n_new][Hq][D]; all packed in call order. Queries run in blocks of 16 (8 with KVarN, a qN_1 body or
+ * token-axis K) through the multi-query kernel, each tile read and decoded once per block. workspace: kvq_prefill_workspace_bytes(cache, n_seqs, max n_new, max
  * length after the call) bytes, 256-byte aligned (NULL allowed when that size is 256).
  * Errors: as kvq_append; KVQ_E_INVALID for a KVQ_LAYOUT_ROWS cache; KVQ_E_SIZE if the workspace is too small
  * (checked before anything is appended). */

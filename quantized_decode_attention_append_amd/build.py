@@ -34,6 +34,7 @@ UNITS = [
     ("kvq_index.hip", ["-ffp-contract=off"]),
     ("kvq_mq.hip", ["-ffp-contract=fast"]),
     ("kvq_mq_var.hip", ["-ffp-contract=fast"]),
+    ("kvq_mq_pair.hip", ["-ffp-contract=fast"]),
 ]
 PROBE_UNITS = [("kvq_probe.hip", [])]
 

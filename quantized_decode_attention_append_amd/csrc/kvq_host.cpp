@@ -13,6 +13,7 @@
 
 #include "../../include/kvq.h"
 #include "kvq_kernels.h"
+#include "kvq_mq_plan.h"
 
 using kvq::SlabLayout;
 
@@ -782,11 +783,11 @@ kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, co
   return launch_combine_for(c, n, n_splits, p.max_splits, out, workspace, (hipStream_t)stream);
 }
 
-// ---- multi-query attention (kvq_decode_attn_multi for T >= 2, kvq_prefill_attn): queries in blocks of 8, each
-// (block, KV head) split so that the launch has about one work-group per CU. Without KVarN a split covers any range
-// of the block's tile list (body tiles, then ring tiles), so with one split per block the kernel writes the
-// outputs itself; with KVarN the body and ring tiles go to separate splits (the body's V values carry sigma_V).
-constexpr int kMqBlock = 8;
+// ---- multi-query attention (kvq_decode_attn_multi for T >= 2, kvq_prefill_attn): queries in blocks of 16 (two
+// per wave) or, with KVarN, a qN_1 body or token-axis K, of 8 (one per wave), each (block, KV head) split so that
+// the launch has about one work-group per CU. Without KVarN a split covers any range of the block's tile list (body
+// tiles, then ring tiles), so with one split per block the kernel writes the outputs itself; with KVarN the body
+// and ring tiles go to separate splits (the body's V values carry sigma_V).
 
 // body length of a sequence after kvq_append of n tokens (the rule kvq_append applies)
 int body_len_after(const kvq_cache* c, int layer, int seq, int n) {
@@ -807,8 +808,9 @@ struct MqPlan {
 MqPlan plan_mq(const kvq_cache* c, int n, const int* len, const int* body_len, const int* q0, const int* nq,
                kvq::MqSeq* out) {
   const int hk = c->cfg.n_kv_heads;
+  const int qb = kvq::mq_block_queries(geometry(c));
   long blocks = 0;
-  for (int i = 0; i < n; ++i) blocks += (nq[i] + kMqBlock - 1) / kMqBlock;
+  for (int i = 0; i < n; ++i) blocks += (nq[i] + qb - 1) / qb;
   const long entries = std::max(1L, blocks * hk);
   // at most the dense decode's per-head budget per entry (so kvq_workspace_bytes(cache, n_seqs * T, len) covers
   // kvq_decode_attn_multi), and rows x splits <= 8 x budget / Hkv (kvq_prefill_workspace_bytes)
@@ -833,7 +835,7 @@ MqPlan plan_mq(const kvq_cache* c, int n, const int* len, const int* body_len, c
     S.n_splits = ns;
     S.n_ring_splits = nr;
     S.wg_begin = p.total_wgs;
-    p.total_wgs += ((nq[i] + kMqBlock - 1) / kMqBlock) * hk * ns;
+    p.total_wgs += ((nq[i] + qb - 1) / qb) * hk * ns;
     p.max_splits = std::max(p.max_splits, ns);
     p.partials = p.partials || ns > 1;
     p.rows += nq[i];
@@ -963,13 +965,13 @@ kvq_status kvq_decode_attn_multi(kvq_cache* c, int32_t layer, int32_t n_seqs, co
 
 size_t kvq_prefill_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_new, int32_t max_len) {
   if (!c || n_seqs < 1 || n_seqs > KVQ_MAX_BATCH || max_new < 1 || max_len < 1) return 0;
-  // partial records = rows x KV heads x the largest split count. A block holds at most 8 rows and gets at most
-  // budget / entries splits (entries >= blocks x Hkv), so rows x splits <= 8 x budget / Hkv; a KVarN block with
+  // partial records = rows x KV heads x the largest split count. A block holds at most 16 rows and gets at most
+  // budget / entries splits (entries >= blocks x Hkv), so rows x splits <= 16 x budget / Hkv; a KVarN block with
   // body and ring tiles takes at least 2 splits; no block takes more splits than its tiles.
   const long rows = (long)n_seqs * std::min(max_new, max_len);
   const long tiles = (max_len + kvq::kTile - 1) / kvq::kTile + 1;
   const long cap = std::max(2L, std::min(tiles, mq_budget(c) / c->cfg.n_kv_heads));
-  const long records = std::min(rows * cap, std::max(2 * rows, kMqBlock * mq_budget(c) / c->cfg.n_kv_heads));
+  const long records = std::min(rows * cap, std::max(2 * rows, kvq::kMqBlockPair * mq_budget(c) / c->cfg.n_kv_heads));
   return std::max<size_t>((size_t)records * c->cfg.n_kv_heads * kPartialFloats(c->cfg.head_dim) * sizeof(float), 256);
 }
 

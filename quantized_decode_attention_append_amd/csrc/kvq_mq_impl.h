@@ -91,12 +91,14 @@ __device__ inline void k_two_pieces(const uint32_t* r0, const uint32_t* r1, cons
   dst[64] = __builtin_bit_cast(u32x4, decode_run_piece<N, I0 + 1>(r0, r1, r2, magic));
 }
 
-// K operands of one tile: thread t decodes blocks 2(t % 4) and 2(t % 4) + 1 of lane (t / 4) % 64 of subtile t / 256.
+// K operands of one tile, as 512 threads t (the work-group's threads, or its last 256 taking two t each): the
+// wave w = t / 64 decodes blocks 2(w % 4) and 2(w % 4) + 1 of subtile w / 4 (the block pair is uniform across the
+// wave, so the wave runs one of the four decode variants), thread t lane t % 64.
 template <int N, class Ops>
-__device__ inline void decode_k_tile(const uint8_t* raw, Ops& ops, uint32_t magic) {
+__device__ inline void decode_k_tile(const uint8_t* raw, Ops& ops, uint32_t magic, int t) {
   constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
-  const int t = threadIdx.x;
-  const int s = t >> 8, lane = (t >> 2) & 63, bp = t & 3;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int s = wv >> 2, bp = wv & 3, lane = t & 63;
   uint32_t r0[2 * w0], r1[w1 ? 2 * w1 : 1], r2[w2 ? 2 * w2 : 1];
   const int sub = 512 * N * s;
   raw_k_run<w0>(raw, sub, lane, r0);
@@ -139,14 +141,14 @@ __device__ inline void scale_v_piece_min(half8 c, const uint32_t* dv, const floa
   }
 }
 
-// V operands of one tile: thread t decodes n-tiles 2(t / 64) and 2(t / 64) + 1 (block t / 64) of lane t % 64;
-// vscale: the tile's V scales [block][position]; vmin: a qN_1 tile's minima [block][position], else null.
+// V operands of one tile, as 512 threads t: thread t decodes n-tiles 2(t / 64) and 2(t / 64) + 1 (block t / 64)
+// of lane t % 64; vscale: the tile's V scales [block][position]; vmin: a qN_1 tile's minima [block][position],
+// else null.
 template <int N, class Ops>
 __device__ inline void decode_v_tile(const uint8_t* raw, const uint8_t* vscale, const uint8_t* vmin, Ops& ops,
-                                     uint32_t magic) {
+                                     uint32_t magic, int t) {
   constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
-  const int t = threadIdx.x;
-  const int lane = t & 63, np = t >> 6, g = lane >> 4;
+  const int lane = t & 63, np = __builtin_amdgcn_readfirstlane(t >> 6), g = lane >> 4;
   uint32_t r0[4 * w0], r1[w1 ? 4 * w1 : 1], r2[w2 ? 4 * w2 : 1];
   raw_v_run<w0>(raw, 0, lane, r0);
   if constexpr (w1 > 0) raw_v_run<w1>(raw, 1024 * w0, lane, r1);
@@ -193,7 +195,8 @@ __device__ inline void decode_k_tile_tok(const uint8_t* raw, const uint8_t* ksca
                                          uint32_t magic) {
   constexpr int w0 = Planes<N>::w[0], w1 = Planes<N>::w[1], w2 = Planes<N>::w[2];
   const int t = threadIdx.x;
-  const int s = t >> 8, lane = (t >> 2) & 63, bp = t & 3, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int s = wv >> 2, bp = wv & 3, lane = t & 63, g = lane >> 4;
   uint32_t r0[2 * w0], r1[w1 ? 2 * w1 : 1], r2[w2 ? 2 * w2 : 1];
   const int sub = 512 * N * s;
   raw_k_run<w0>(raw, sub, lane, r0);
@@ -640,16 +643,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if (k_axis) {
             decode_k_tile_tok<NK>(raw, raw + kcodes, k_min ? raw + kcodes + 512 : nullptr, ops, magic);
           } else {
-            decode_k_tile<NK>(raw, ops, magic);
+            decode_k_tile<NK>(raw, ops, magic, tid);
             if (k_min && tid < 128) kmin_operand<NK>(raw + kcodes, raw + kcodes + 512, ops);
           }
         } else {
-          decode_k_tile<NK>(raw, ops, magic);
+          decode_k_tile<NK>(raw, ops, magic, tid);
         }
-        decode_v_tile<NV>(raw + r.kbytes, vscale, v_min ? vscale + 512 : nullptr, ops, magic);
+        decode_v_tile<NV>(raw + r.kbytes, vscale, v_min ? vscale + 512 : nullptr, ops, magic, tid);
       } else {
-        decode_k_tile<8>(raw, ops, magic);
-        decode_v_tile<8>(raw + r.kbytes, vscale, nullptr, ops, magic);
+        decode_k_tile<8>(raw, ops, magic, tid);
+        decode_v_tile<8>(raw + r.kbytes, vscale, nullptr, ops, magic, tid);
       }
       if (tid < 32) ((u32x4*)ops.ks)[tid] = s_raw[kcodes / 16 + tid];
       __syncthreads();

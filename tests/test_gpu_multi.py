@@ -48,6 +48,22 @@ def test_multi_query_matches_oracle(layout, tail_dtype, kvarn, n_q):
     assert max_err(got, want) <= TOL, max_err(got, want)
 
 
+@pytest.mark.parametrize("tail_dtype,n_q,hq,k_bits,v_bits", [
+    (0, 3, 16, 6, 5), (1, 7, 16, 2, 8), (2, 6, 8, 8, 3), (3, 3, 2, 4, 4), (1, 2, 4, 7, 2), (2, 8, 16, 3, 6)])
+def test_odd_query_counts_and_group_sizes(tail_dtype, n_q, hq, k_bits, v_bits):
+    """Two queries per wave without KVarN: an odd T leaves a wave with one query, and groups of 1, 2 and 4 query
+    heads per KV head leave columns unused; every ring kind, several widths."""
+    tail = dict(tail_len=64, tail_slack=32, tail_dtype=tail_dtype) if tail_dtype else {}
+    p = Pair(cfg(n_q_heads=hq, k_bits=k_bits, v_bits=v_bits, **tail))
+    seed = 90 + 7 * tail_dtype + n_q + hq
+    k, v = small_tokens(seed, 900, 2, 256)
+    p.append(1, [0, 1, 2], [260, 33, 401], k[:694], v[:694])
+    p.evict(1, [0, 1, 2])
+    p.append(1, [0, 1, 2], [n_q] * 3, k[694:694 + 3 * n_q], v[694:694 + 3 * n_q])
+    got, want = run_multi(p, 1, [0, 1, 2], mq(seed, 3, n_q, hq))
+    assert max_err(got, want) <= TOL, max_err(got, want)
+
+
 def test_multi_query_of_one_equals_decode_attn_bit_for_bit():
     p = Pair(cfg(tail_len=64, tail_slack=32, tail_dtype=1))
     k, v = small_tokens(3, 400, 2, 256)
