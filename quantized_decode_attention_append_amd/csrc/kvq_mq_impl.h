@@ -405,7 +405,7 @@ __device__ inline void mq_pv_16(WaveState& st, const Ops& ops, const float* p, b
 
 // ---------------------------------------------------------------------------- the kernel
 
-__device__ inline TileRef tile_ref(const MqArgs& a, const MqSeq& S, int head, int i, int n_body) {
+__device__ __attribute__((always_inline)) inline TileRef tile_ref(const MqArgs& a, const MqSeq& S, int head, int i, int n_body) {
   const Geometry& g = a.g;
   const uint8_t* slab = g.arena + S.slab;
   TileRef r;

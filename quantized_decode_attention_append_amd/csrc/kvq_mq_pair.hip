@@ -211,10 +211,64 @@ __device__ inline void pair_pv_16(WaveState& st, const MqOpsT<false>& ops, const
   }
 }
 
-// ---- the decode of one tile by waves 4-7 alone: wave 4 + c decodes K blocks 2c and 2c + 1 of both 16-position
-// subtiles and V blocks c and c + 4, each thread reading only the words of its lane's plane runs that its pieces
-// sit in (a piece: 8 codes of one plane, w bytes; [chunk][lane][unit] runs of 8 K pieces, unit = min(16, 8w)
-// bytes, or of 16 V pieces, unit = 16 bytes), so the two halves of the work interleave in one block of code.
+// Where the tiles of one (sequence, KV head) live: tile_ref's addressing with the per-head bases precomputed, held by
+// value (so the decode waves' loops take no reference to the kernel's argument block).
+struct TileAddr {
+  const uint8_t* kbody;   // the head's body tile 0
+  const uint8_t* vbody;
+  const uint8_t* kring;   // the head's ring tile 0
+  const uint8_t* vring;
+  int tile_k, tile_v, ring_tile_k, ring_tile_v;
+  int n_body, ring_t0, ring_tiles, ring_kind;
+
+  __device__ inline TileRef operator()(int i) const {
+    TileRef r;
+    if (i < n_body) {
+      r.k = kbody + (size_t)i * tile_k;
+      r.v = vbody + (size_t)i * tile_v;
+      r.kbytes = tile_k;
+      r.vbytes = tile_v;
+      r.kind = kKindQ;
+      r.pos0 = i * kTile;
+    } else {
+      const int t = ring_t0 + (i - n_body);
+      const int slot = t % ring_tiles;
+      r.k = kring + (size_t)slot * ring_tile_k;
+      r.v = vring + (size_t)slot * ring_tile_v;
+      r.kbytes = ring_tile_k;
+      r.vbytes = ring_tile_v;
+      r.kind = ring_kind;
+      r.pos0 = t * kTile;
+    }
+    return r;
+  }
+};
+
+__device__ inline TileAddr tile_addr(const MqArgs& a, const MqSeq& S, int head, int n_body) {
+  const Geometry& g = a.g;
+  const uint8_t* slab = g.arena + S.slab;
+  TileAddr t;
+  const size_t bt = (size_t)head * (g.cap32 / kTile);
+  t.kbody = slab + g.k_body + bt * g.tile_k;
+  t.vbody = slab + g.v_body + bt * g.tile_v;
+  t.ring_tiles = g.ring_slots / kTile;
+  const size_t rt = (size_t)head * t.ring_tiles;
+  t.kring = slab + g.k_ring + rt * g.ring_tile_k;
+  t.vring = slab + g.v_ring + rt * g.ring_tile_v;
+  t.tile_k = g.tile_k;
+  t.tile_v = g.tile_v;
+  t.ring_tile_k = g.ring_tile_k;
+  t.ring_tile_v = g.ring_tile_v;
+  t.n_body = n_body;
+  t.ring_t0 = S.body_len / kTile;
+  t.ring_kind = g.tail_dtype == 2 ? kKindQ8Ring : g.tail_dtype == 1 ? kKindBf16Ring : kKindF16Ring;
+  return t;
+}
+
+// ---- the decode of one tile by waves 4-7 alone: wave 4 + C decodes K blocks 2C and 2C + 1 of both 16-position
+// subtiles and V blocks C and C + 4, each thread loading from global memory only the words of its lane's plane
+// runs that its pieces sit in (a piece: 8 codes of one plane, w bytes; the runs are [chunk][lane][unit] with 8 K
+// pieces per run and unit = min(16, 8w) bytes, or 16 V pieces per run and unit = 16 bytes), two tiles ahead.
 
 template <int W, bool KRUN>
 __device__ inline uint32_t run_word(const uint8_t* plane, int lane, int wd) {
@@ -237,54 +291,86 @@ __device__ inline void fetch_piece_words(const uint8_t* base, int lane, uint32_t
   }
 }
 
+// One decode thread's share of a tile in registers: its K and V words, its V scales and (wave 4, lanes 0-31) a
+// 16-byte piece of the K scales.
 template <int NKt, int NVt, int C>
-__device__ inline void decode_tile_quarter(const uint8_t* raw, int kbytes, const uint8_t* vscale, MqOpsT<false>& ops,
-                                           uint32_t magic, int lane) {
-  // K: blocks 2C, 2C + 1 of subtiles 0 and 1
-  constexpr int a0 = Planes<NKt>::w[0], a1 = Planes<NKt>::w[1], a2 = Planes<NKt>::w[2];
-  constexpr int n0 = NKt == 8 ? 16 : 2 * a0, n1 = a1 ? 2 * a1 : 1, n2 = a2 ? 2 * a2 : 1;
-  uint32_t k0[2][n0] = {}, k1[2][n1] = {}, k2[2][n2] = {};
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    fetch_piece_words<NKt, 2 * C, true>(raw + 512 * NKt * s, lane, k0[s], k1[s], k2[s]);
-    fetch_piece_words<NKt, 2 * C + 1, true>(raw + 512 * NKt * s, lane, k0[s], k1[s], k2[s]);
-  }
-  // V: n-tiles 2C, 2C + 1 (block C) and 2C + 8, 2C + 9 (block C + 4)
-  constexpr int b0 = Planes<NVt>::w[0], b1 = Planes<NVt>::w[1], b2 = Planes<NVt>::w[2];
-  constexpr int m0 = NVt == 8 ? 32 : 4 * b0, m1 = b1 ? 4 * b1 : 1, m2 = b2 ? 4 * b2 : 1;
-  uint32_t v0[m0] = {}, v1[m1] = {}, v2[m2] = {};
-  const uint8_t* vraw = raw + kbytes;
-  fetch_piece_words<NVt, 2 * C, false>(vraw, lane, v0, v1, v2);
-  fetch_piece_words<NVt, 2 * C + 1, false>(vraw, lane, v0, v1, v2);
-  fetch_piece_words<NVt, 2 * C + 8, false>(vraw, lane, v0, v1, v2);
-  fetch_piece_words<NVt, 2 * C + 9, false>(vraw, lane, v0, v1, v2);
-  const int g = lane >> 4;
+struct QuarterWords {
+  static constexpr int a0 = Planes<NKt>::w[0], a1 = Planes<NKt>::w[1], a2 = Planes<NKt>::w[2];
+  static constexpr int b0 = Planes<NVt>::w[0], b1 = Planes<NVt>::w[1], b2 = Planes<NVt>::w[2];
+  uint32_t k0[2][NKt == 8 ? 16 : 2 * a0], k1[2][a1 ? 2 * a1 : 1], k2[2][a2 ? 2 * a2 : 1];
+  uint32_t v0[NVt == 8 ? 32 : 4 * b0], v1[b1 ? 4 * b1 : 1], v2[b2 ? 4 * b2 : 1];
   uint32_t dv[2][4];
+  u32x4 ks;
+
+  __device__ __attribute__((always_inline)) inline void load(const TileRef& r, int lane, bool ks_lane) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {   // the scales of operand rows 8g..8g+7 of block C + 4h
-    const int blk = C + 4 * h;
-    const u32x2 d0 = *(const u32x2*)(vscale + 2 * (blk * 32 + 4 * g));
-    const u32x2 d1 = *(const u32x2*)(vscale + 2 * (blk * 32 + 16 + 4 * g));
-    dv[h][0] = d0[0]; dv[h][1] = d0[1]; dv[h][2] = d1[0]; dv[h][3] = d1[1];
+    for (int s = 0; s < 2; ++s) {
+      fetch_piece_words<NKt, 2 * C, true>(r.k + 512 * NKt * s, lane, k0[s], k1[s], k2[s]);
+      fetch_piece_words<NKt, 2 * C + 1, true>(r.k + 512 * NKt * s, lane, k0[s], k1[s], k2[s]);
+    }
+    fetch_piece_words<NVt, 2 * C, false>(r.v, lane, v0, v1, v2);
+    fetch_piece_words<NVt, 2 * C + 1, false>(r.v, lane, v0, v1, v2);
+    fetch_piece_words<NVt, 2 * C + 8, false>(r.v, lane, v0, v1, v2);
+    fetch_piece_words<NVt, 2 * C + 9, false>(r.v, lane, v0, v1, v2);
+    const uint8_t* vscale = r.v + 1024 * NVt;
+    const int g = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // the scales of operand rows 8g..8g+7 of block C + 4h
+      const int blk = C + 4 * h;
+      const u32x2 d0 = *(const u32x2*)(vscale + 2 * (blk * 32 + 4 * g));
+      const u32x2 d1 = *(const u32x2*)(vscale + 2 * (blk * 32 + 16 + 4 * g));
+      dv[h][0] = d0[0]; dv[h][1] = d0[1]; dv[h][2] = d1[0]; dv[h][3] = d1[1];
+    }
+    if (ks_lane) ks = *(const u32x4*)(r.k + 1024 * NKt + 16 * lane);
   }
+
+  __device__ __attribute__((always_inline)) inline void decode(MqOpsT<false>& ops, uint32_t magic, int lane,
+                                                               bool ks_lane) const {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-    k_two_pieces<NKt, 2 * C>(k0[s], k1[s], k2[s], magic, ops.k + (s * 8 + 2 * C) * 64 + lane);
-  const int o0 = 2 * C * 64 + lane, o1 = 2 * (C + 4) * 64 + lane;
-  scale_v_piece(decode_run_piece<NVt, 2 * C>(v0, v1, v2, magic), dv[0], ops.v[o0], ops.vl[o0]);
-  scale_v_piece(decode_run_piece<NVt, 2 * C + 1>(v0, v1, v2, magic), dv[0], ops.v[o0 + 64], ops.vl[o0 + 64]);
-  scale_v_piece(decode_run_piece<NVt, 2 * C + 8>(v0, v1, v2, magic), dv[1], ops.v[o1], ops.vl[o1]);
-  scale_v_piece(decode_run_piece<NVt, 2 * C + 9>(v0, v1, v2, magic), dv[1], ops.v[o1 + 64], ops.vl[o1 + 64]);
+    for (int s = 0; s < 2; ++s)
+      k_two_pieces<NKt, 2 * C>(k0[s], k1[s], k2[s], magic, ops.k + (s * 8 + 2 * C) * 64 + lane);
+    const int o0 = 2 * C * 64 + lane, o1 = 2 * (C + 4) * 64 + lane;
+    scale_v_piece(decode_run_piece<NVt, 2 * C>(v0, v1, v2, magic), dv[0], ops.v[o0], ops.vl[o0]);
+    scale_v_piece(decode_run_piece<NVt, 2 * C + 1>(v0, v1, v2, magic), dv[0], ops.v[o0 + 64], ops.vl[o0 + 64]);
+    scale_v_piece(decode_run_piece<NVt, 2 * C + 8>(v0, v1, v2, magic), dv[1], ops.v[o1], ops.vl[o1]);
+    scale_v_piece(decode_run_piece<NVt, 2 * C + 9>(v0, v1, v2, magic), dv[1], ops.v[o1 + 64], ops.vl[o1 + 64]);
+    if (ks_lane) ((u32x4*)ops.ks)[lane] = ks;
+  }
+};
+
+// The decode waves' side of a run of quantized tiles [t0, t1) of one kind (qN_0 body: NK / NV bits; q8_0 ring: 8 / 8):
+// one barrier to publish tile t0, then per tile one barrier, matching the compute waves' loop. Tile j is decoded
+// into operand buffer j % 2 in the phase before the one that computes it, from words loaded one phase earlier.
+template <int NKt, int NVt, int C>
+__device__ __attribute__((always_inline)) inline void decode_run(int t0, int t1, const TileAddr ref,
+                                                                 MqOpsT<false>* s_ops, uint32_t magic, int lane) {
+  const bool ks_lane = C == 0 && lane < 32;
+  QuarterWords<NKt, NVt, C> x, y;   // tiles t0, t0 + 2, ... and t0 + 1, t0 + 3, ...
+  x.load(ref(t0), lane, ks_lane);
+  if (t0 + 1 < t1) y.load(ref(t0 + 1), lane, ks_lane);
+  x.decode(s_ops[t0 & 1], magic, lane, ks_lane);
+  __syncthreads();
+  // phase of tile p (computed by the other waves): load tile p + 2 into the set tile p used, decode tile p + 1
+  for (int p = t0; p < t1; p += 2) {
+    if (p + 2 < t1) x.load(ref(p + 2), lane, ks_lane);
+    if (p + 1 < t1) y.decode(s_ops[(p + 1) & 1], magic, lane, ks_lane);
+    __syncthreads();
+    if (p + 1 >= t1) break;
+    if (p + 3 < t1) y.load(ref(p + 3), lane, ks_lane);
+    if (p + 2 < t1) x.decode(s_ops[p & 1], magic, lane, ks_lane);
+    __syncthreads();
+  }
 }
 
 template <int NKt, int NVt>
-__device__ inline void decode_tile_quarter_of(int c, const uint8_t* raw, int kbytes, const uint8_t* vscale,
-                                              MqOpsT<false>& ops, uint32_t magic, int lane) {
+__device__ __attribute__((always_inline)) inline void decode_run_of(int c, int t0, int t1, const TileAddr ref,
+                                                                    MqOpsT<false>* s_ops, uint32_t magic,
+                                     int lane) {
   switch (c) {
-    case 0: decode_tile_quarter<NKt, NVt, 0>(raw, kbytes, vscale, ops, magic, lane); break;
-    case 1: decode_tile_quarter<NKt, NVt, 1>(raw, kbytes, vscale, ops, magic, lane); break;
-    case 2: decode_tile_quarter<NKt, NVt, 2>(raw, kbytes, vscale, ops, magic, lane); break;
-    default: decode_tile_quarter<NKt, NVt, 3>(raw, kbytes, vscale, ops, magic, lane); break;
+    case 0: decode_run<NKt, NVt, 0>(t0, t1, ref, s_ops, magic, lane); break;
+    case 1: decode_run<NKt, NVt, 1>(t0, t1, ref, s_ops, magic, lane); break;
+    case 2: decode_run<NKt, NVt, 2>(t0, t1, ref, s_ops, magic, lane); break;
+    default: decode_run<NKt, NVt, 3>(t0, t1, ref, s_ops, magic, lane); break;
   }
 }
 
@@ -360,6 +446,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // 16-bit ring tiles come after every quantized tile of the split: [tb, tq) quantized, [tq, te) 16-bit
   const bool ring16 = g.tail_dtype == 1 || g.tail_dtype == 3;
   const int tq = ring16 ? max(tb, min(te, n_body)) : te;
+  const TileAddr ref = tile_addr(a, S, head, n_body);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -385,7 +472,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool apart = nqb <= 8;
   // the split's first tile is on its way while the query operand is built
   u32x4 reg[3];
-  if (!apart && tb < tq) load_part<3>(tile_ref(a, S, head, tb, n_body), reg, tid, 512);
+  if (!apart && tb < tq) load_part<3>(ref(tb), reg, tid, 512);
 
   half8 qop[8];
   float qmul = 0.0f;
@@ -414,7 +501,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // tile i of this wave's queries: QK, causal mask per column, online softmax, P.V
   auto compute = [&](int i, const MqOpsT<false>& ops) {
     if (!active) return;
-    const TileRef r = tile_ref(a, S, head, i, n_body);
+    const TileRef r = ref(i);
     const bool body = r.kind == kKindQ;
     const int lo = body ? 0 : S.body_len;
     const int lim = body ? blen : end;
@@ -442,7 +529,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // raw buffer j % 2 decoded into operand buffer j % 2, as the 512 decode threads t of the tile decoders
   auto decode_as = [&](int j, int t) {
-    const TileRef r = tile_ref(a, S, head, j, n_body);
+    const TileRef r = ref(j);
     MqOpsT<false>& ops = s_ops[j & 1];
     const uint8_t* raw = (const uint8_t*)s_raw[j & 1];
     const bool qb = r.kind == kKindQ;
@@ -457,20 +544,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (t < 32) ((u32x4*)ops.ks)[t] = s_raw[j & 1][kcodes / 16 + t];
   };
-  auto ref = [&](int j) { return tile_ref(a, S, head, j, n_body); };
-  // the same decode by waves 4-7 alone (wave 4 + c: its quarter c)
-  auto decode_quarter = [&](int j) {
-    const TileRef r = ref(j);
-    MqOpsT<false>& ops = s_ops[j & 1];
-    const uint8_t* raw = (const uint8_t*)s_raw[j & 1];
-    const bool qb = r.kind == kKindQ;
-    const int kcodes = 1024 * (qb ? NK : 8), vcodes = 1024 * (qb ? NV : 8);
-    const uint8_t* vscale = raw + r.kbytes + vcodes;
-    const int c = wave - 4;
-    if (qb) decode_tile_quarter_of<NK, NV>(c, raw, r.kbytes, vscale, ops, magic, lane);
-    else decode_tile_quarter_of<8, 8>(c, raw, r.kbytes, vscale, ops, magic, lane);
-    if (c == 0 && lane < 32) ((u32x4*)ops.ks)[lane] = s_raw[j & 1][kcodes / 16 + lane];
-  };
   // the bf16 ring's query operand is the bf16 query itself
   auto qop_bf16 = [&]() {
     if (active && g.tail_dtype == 1 && tb < tq) {
@@ -484,30 +557,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (i + 1) % 2 and operand buffer i % 2 hold what the phase before filled, and operand buffer (i + 1) % 2 and raw
   // buffer i % 2 were last read before that barrier. Then the 16-bit ring tiles [tq, te), one tile ahead.
   if (apart) {
+    // the quantized tiles in runs of one kind: the body tiles, then the q8_0 ring tiles
+    const int tm = min(max(tb, n_body), tq);
     if (wave >= 4) {
       const int t0 = tid - 256;
-      constexpr int P = 5;   // 16-byte pieces of a quantized tile pair (at most 1088) over 256 threads
-      u32x4 rq[P];
-      if (tb < tq) {
-        load_part<P>(ref(tb), rq, t0, 256);
-        stage_part<P>(ref(tb), s_raw[tb & 1], rq, t0, 256);
-        if (tb + 1 < tq) load_part<P>(ref(tb + 1), rq, t0, 256);
-        __syncthreads();
-        decode_quarter(tb);
-        if (tb + 1 < tq) {
-          stage_part<P>(ref(tb + 1), s_raw[(tb + 1) & 1], rq, t0, 256);
-          if (tb + 2 < tq) load_part<P>(ref(tb + 2), rq, t0, 256);
-        }
-        __syncthreads();
-        for (int i = tb; i < tq; ++i) {
-          if (i + 1 < tq) decode_quarter(i + 1);
-          if (i + 2 < tq) {
-            stage_part<P>(ref(i + 2), s_raw[i & 1], rq, t0, 256);
-            if (i + 3 < tq) load_part<P>(ref(i + 3), rq, t0, 256);
-          }
-          __syncthreads();
-        }
-      }
+      if (tb < tm) decode_run_of<NK, NV>(wave - 4, tb, tm, ref, s_ops, magic, lane);
+      if (tm < tq) decode_run_of<8, 8>(wave - 4, tm, tq, ref, s_ops, magic, lane);
       if (tq < te) {
         constexpr int P16 = 8;   // a 16-bit tile pair: 2048 pieces over 256 threads
         u32x4 r16[P16];
@@ -520,10 +575,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       return;
     }
-    if (tb < tq) {
+    for (int run = 0; run < 2; ++run) {
+      const int r0 = run == 0 ? tb : tm, r1 = run == 0 ? tm : tq;
+      if (r0 >= r1) continue;
       __syncthreads();
-      __syncthreads();
-      for (int i = tb; i < tq; ++i) {
+      for (int i = r0; i < r1; ++i) {
         compute(i, s_ops[i & 1]);
         __syncthreads();
       }
