@@ -442,16 +442,42 @@ __device__ inline void load_pieces(const TileRef& r, u32x4* reg) {
   }
 }
 
-// Hi / lo fp16 query operand of one block (columns 0-7: hi parts of the group's heads, 8-15: lo parts), the
-// query times `sig` (KVarN sigma of K, or 1) and 2^-e.
+// The lane's query words: channels 32b + 8g .. 32b + 8g + 7 of block b (g = lane / 16) of its head, bf16, and the
+// same channels of `sig` (KVarN sigma of K; fp16 1 without it). The lanes of a wave together hold every head of the
+// group, so one batch of loads serves the exponent shift and the operand.
+__device__ inline void query_words(const uint16_t* qrow, const uint16_t* sig, u32x4* qw, u32x4* sw) {
+  const int gq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    qw[b] = *(const u32x4*)(qrow + 32 * b + 8 * gq);
+    sw[b] = sig ? *(const u32x4*)(sig + 32 * b + 8 * gq) : u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  }
+}
+
+// Exponent shift of a query: its |q sigma| maximum over the group's heads brought below 2^9.
+__device__ inline int query_shift(const u32x4* qw, const u32x4* sw, bool head_ok) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(qw[b][k] << 16) * lo_h(sw[b][k])));
+      amax = fmaxf(amax, fabsf(__uint_as_float(qw[b][k] & 0xFFFF0000u) * hi_h(sw[b][k])));
+    }
+  if (!head_ok) amax = 0.0f;
+  amax = wave_max_16_32(amax);
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 8));
+  return amax > 0.0f ? ilogbf(amax) - 8 : 0;
+}
+
+// Hi / lo fp16 query operand of one block (columns 0-7: hi parts of the group's heads, 8-15: lo parts) from the
+// lane's words: the query times `sig` and 2^-e.
 // Returns the sum of this lane's 8 (exact) operand values, for the block sums of a qN_1 K.
-__device__ inline float build_qop_f16(const uint16_t* qrow, const uint16_t* sig, int b, int e, bool head_ok,
-                                      bool lo_lane, half8& out) {
-  const int lane = threadIdx.x & 63;
-  const int gq = lane >> 4;
-  const u32x4 qw = *(const u32x4*)(qrow + 32 * b + 8 * gq);
-  u32x4 sw = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-  if (sig) sw = *(const u32x4*)(sig + 32 * b + 8 * gq);
+__device__ inline float build_qop_f16(const u32x4& qw, const u32x4& sw, int e, bool head_ok, bool lo_lane,
+                                      half8& out) {
   float sum = 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -464,29 +490,6 @@ __device__ inline float build_qop_f16(const uint16_t* qrow, const uint16_t* sig,
     sum += x0 + x1;
   }
   return head_ok ? sum : 0.0f;
-}
-
-// Exponent shift of a query: its |q sigma| maximum over the group's heads brought below 2^9.
-__device__ inline int query_shift(const uint16_t* qgroup, int group, const uint16_t* sig) {
-  const int lane = threadIdx.x & 63;
-  float amax = 0.0f;
-  // lane covers channels 4 lane .. 4 lane + 3 of every head of the group
-  for (int h = 0; h < group; ++h) {
-    const u32x2 qw = *(const u32x2*)(qgroup + h * 256 + 4 * lane);
-    u32x2 sw = {0x3C003C00u, 0x3C003C00u};
-    if (sig) sw = *(const u32x2*)(sig + 4 * lane);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(qw[k] << 16) * lo_h(sw[k])));
-      amax = fmaxf(amax, fabsf(__uint_as_float(qw[k] & 0xFFFF0000u) * hi_h(sw[k])));
-    }
-  }
-  amax = wave_max_16_32(amax);
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-  amax = fmaxf(amax, __shfl_xor(amax, 8));
-  return amax > 0.0f ? ilogbf(amax) - 8 : 0;
 }
 
 // VAR: the instantiation that reads qN_1 bodies and token-axis K (the plain one compiles those paths out)
@@ -555,10 +558,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto build_qop = [&](int kind) {
     if (kind == kKindQ || kind == kKindQ8Ring) {
       const uint16_t* sg = kind == kKindQ ? sig : nullptr;
-      const int e = query_shift(qgroup, a.group, sg);
+      u32x4 qw[8], sw[8];
+      query_words(qrow, sg, qw, sw);
+      const int e = query_shift(qw, sw, head_ok);
       float bsum[8];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) bsum[b] = build_qop_f16(qrow, sg, b, e, head_ok, lo_lane, qop[b]);
+      for (int b = 0; b < 8; ++b) bsum[b] = build_qop_f16(qw[b], sw[b], e, head_ok, lo_lane, qop[b]);
       qmul = a.scale * kLog2e * ldexpf(1.0f, e);
       if (kind == kKindQ && k_min && !k_axis) {
         // qN_1 K: the B operand of the offset term, lane (g, m16): k = 8g + b (g = 0, 1) is the block-b sum of
@@ -575,8 +580,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s_qsum[wave * 64 + lane] = __builtin_bit_cast(u32x4, qs);
       }
     } else if (kind == kKindF16Ring) {
+      u32x4 qw[8], sw[8];
+      query_words(qrow, nullptr, qw, sw);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) build_qop_f16(qrow, nullptr, b, 0, head_ok, lo_lane, qop[b]);
+      for (int b = 0; b < 8; ++b) build_qop_f16(qw[b], sw[b], 0, head_ok, lo_lane, qop[b]);
       qmul = a.scale * kLog2e;
     } else {
       const int gq = lane >> 4;

@@ -27,41 +27,41 @@ namespace {
 
 constexpr int kPairQueries = kMqBlockPair;
 
-// Largest |q| over the group's heads of one query row (lane covers channels 4 lane .. 4 lane + 3 of each head).
-__device__ inline float query_absmax(const uint16_t* qgroup, int group) {
-  const int lane = threadIdx.x & 63;
-  float amax = 0.0f;
-  for (int h = 0; h < group; ++h) {
-    const u32x2 qw = *(const u32x2*)(qgroup + h * 256 + 4 * lane);
+// The lane's share of its column's query: channels 32b + 8g .. 32b + 8g + 7 of every block b (g = lane / 16), the
+// bf16 words as they are (zero for an unused column). The four lanes of a column together hold its whole row, so
+// the wave's 64 lanes hold both queries' heads: one batch of loads serves the exponent shift and the operand.
+__device__ inline void pair_query_words(const uint16_t* qrow, bool col_ok, u32x4* qw) {
+  const int gq = (threadIdx.x & 63) >> 4;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(qw[k] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(qw[k] & 0xFFFF0000u)));
-    }
-  }
+  for (int b = 0; b < 8; ++b) qw[b] = col_ok ? *(const u32x4*)(qrow + 32 * b + 8 * gq) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Exponent shift of the wave's queries: their largest |q| brought below 2^9.
+__device__ inline int pair_query_shift(const u32x4* qw) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(qw[b][k] << 16)), fabsf(__uint_as_float(qw[b][k] & 0xFFFF0000u))));
   amax = wave_max_16_32(amax);
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   amax = fmaxf(amax, __shfl_xor(amax, 4));
   amax = fmaxf(amax, __shfl_xor(amax, 8));
-  return amax;
+  return amax > 0.0f ? ilogbf(amax) - 8 : 0;
 }
 
-// Query operand of block b for the lane's column: the query row's head times 2^-e in fp16 (zero for an unused
-// column); `bf16`: the bf16 query as it is (for a bf16 ring).
-__device__ inline void pair_qop(const uint16_t* qrow, int b, int e, bool col_ok, bool bf16, half8& out) {
-  const int gq = (threadIdx.x & 63) >> 4;
-  u32x4 qw = *(const u32x4*)(qrow + 32 * b + 8 * gq);
-  if (!col_ok) qw = u32x4{0u, 0u, 0u, 0u};
-  if (bf16) {
-    out = __builtin_bit_cast(half8, qw);
-    return;
-  }
+// Query operand of block b: the words times 2^-e in fp16, or (`bf16`, for a bf16 ring) the bf16 words as they are.
+__device__ inline half8 pair_qop(const u32x4& qw, int e, bool bf16) {
+  if (bf16) return __builtin_bit_cast(half8, qw);
+  half8 out;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     out[2 * k] = (_Float16)ldexpf(__uint_as_float(qw[k] << 16), -e);
     out[2 * k + 1] = (_Float16)ldexpf(__uint_as_float(qw[k] & 0xFFFF0000u), -e);
   }
+  return out;
 }
 
 // QK of a quantized tile (qN_0 body or q8_0 ring): one MFMA per (block, 16-row subtile), the K scale of each
@@ -268,7 +268,7 @@ __device__ inline TileAddr tile_addr(const MqArgs& a, const MqSeq& S, int head, 
 // ---- the decode of one tile by waves 4-7 alone: wave 4 + C decodes K blocks 2C and 2C + 1 of both 16-position
 // subtiles and V blocks C and C + 4, each thread loading from global memory only the words of its lane's plane
 // runs that its pieces sit in (a piece: 8 codes of one plane, w bytes; the runs are [chunk][lane][unit] with 8 K
-// pieces per run and unit = min(16, 8w) bytes, or 16 V pieces per run and unit = 16 bytes), two tiles ahead.
+// pieces per run and unit = min(16, 8w) bytes, or 16 V pieces per run and unit = 16 bytes), three tiles ahead.
 
 template <int W, bool KRUN>
 __device__ inline uint32_t run_word(const uint8_t* plane, int lane, int wd) {
@@ -340,24 +340,30 @@ struct QuarterWords {
 
 // The decode waves' side of a run of quantized tiles [t0, t1) of one kind (qN_0 body: NK / NV bits; q8_0 ring: 8 / 8):
 // one barrier to publish tile t0, then per tile one barrier, matching the compute waves' loop. Tile j is decoded
-// into operand buffer j % 2 in the phase before the one that computes it, from words loaded one phase earlier.
+// into operand buffer j % 2 in the phase before the one that computes it, from words whose loads went out two
+// phases earlier (three register sets in rotation).
 template <int NKt, int NVt, int C>
 __device__ __attribute__((always_inline)) inline void decode_run(int t0, int t1, const TileAddr ref,
                                                                  MqOpsT<false>* s_ops, uint32_t magic, int lane) {
   const bool ks_lane = C == 0 && lane < 32;
-  QuarterWords<NKt, NVt, C> x, y;   // tiles t0, t0 + 2, ... and t0 + 1, t0 + 3, ...
+  QuarterWords<NKt, NVt, C> x, y, z;   // tiles t0 + 3m, t0 + 3m + 1, t0 + 3m + 2
   x.load(ref(t0), lane, ks_lane);
   if (t0 + 1 < t1) y.load(ref(t0 + 1), lane, ks_lane);
+  if (t0 + 2 < t1) z.load(ref(t0 + 2), lane, ks_lane);
   x.decode(s_ops[t0 & 1], magic, lane, ks_lane);
   __syncthreads();
-  // phase of tile p (computed by the other waves): load tile p + 2 into the set tile p used, decode tile p + 1
-  for (int p = t0; p < t1; p += 2) {
-    if (p + 2 < t1) x.load(ref(p + 2), lane, ks_lane);
+  // the phase that computes tile p: load tile p + 3 into the set tile p used, decode tile p + 1
+  for (int p = t0; p < t1; p += 3) {
+    if (p + 3 < t1) x.load(ref(p + 3), lane, ks_lane);
     if (p + 1 < t1) y.decode(s_ops[(p + 1) & 1], magic, lane, ks_lane);
     __syncthreads();
     if (p + 1 >= t1) break;
-    if (p + 3 < t1) y.load(ref(p + 3), lane, ks_lane);
-    if (p + 2 < t1) x.decode(s_ops[p & 1], magic, lane, ks_lane);
+    if (p + 4 < t1) y.load(ref(p + 4), lane, ks_lane);
+    if (p + 2 < t1) z.decode(s_ops[p & 1], magic, lane, ks_lane);
+    __syncthreads();
+    if (p + 2 >= t1) break;
+    if (p + 5 < t1) z.load(ref(p + 5), lane, ks_lane);
+    if (p + 3 < t1) x.decode(s_ops[(p + 1) & 1], magic, lane, ks_lane);
     __syncthreads();
   }
 }
@@ -476,17 +482,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   half8 qop[8];
   float qmul = 0.0f;
-  int qexp = 0;
   if (active && tb < te) {
-    float amax = query_absmax(a.q + ((size_t)(row_base + 2 * wave) * a.n_q_heads + (size_t)head * a.group) * D,
-                              a.group);
-    if (nqw > 1)
-      amax = fmaxf(amax, query_absmax(a.q + ((size_t)(row_base + 2 * wave + 1) * a.n_q_heads +
-                                             (size_t)head * a.group) * D, a.group));
-    qexp = amax > 0.0f ? ilogbf(amax) - 8 : 0;   // |q| 2^-e < 2^9
+    u32x4 qw[8];
+    pair_query_words(qrow, col_ok, qw);
+    const int qexp = pair_query_shift(qw);   // |q| 2^-e < 2^9
     const bool bf16 = tq == tb && g.tail_dtype == 1;   // a split of bf16 ring tiles only
 #pragma unroll
-    for (int b = 0; b < 8; ++b) pair_qop(qrow, b, bf16 ? 0 : qexp, col_ok, bf16, qop[b]);
+    for (int b = 0; b < 8; ++b) qop[b] = pair_qop(qw[b], bf16 ? 0 : qexp, bf16);
     qmul = a.scale * kLog2e * (bf16 ? 1.0f : ldexpf(1.0f, qexp));
   }
 
@@ -547,8 +549,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the bf16 ring's query operand is the bf16 query itself
   auto qop_bf16 = [&]() {
     if (active && g.tail_dtype == 1 && tb < tq) {
+      u32x4 qw[8];
+      pair_query_words(qrow, col_ok, qw);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) pair_qop(qrow, b, 0, col_ok, true, qop[b]);
+      for (int b = 0; b < 8; ++b) qop[b] = pair_qop(qw[b], 0, true);
       qmul = a.scale * kLog2e;
     }
   };
