@@ -71,7 +71,7 @@ __device__ inline void pair_qk_q(const MqOpsT<false>& ops, const half8* qop, flo
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   float sc[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  constexpr int G = 4;   // blocks per group
+  constexpr int G = 8;   // blocks per group
 #pragma unroll
   for (int b0 = 0; b0 < 8; b0 += G) {
     u32x4 k0[G], k1[G];
@@ -147,22 +147,34 @@ __device__ inline void pair_pv_q(WaveState& st, const MqOpsT<false>& ops, const 
     ah[i] = h;
     al[i] = (_Float16)(p[i] - (float)h);
   }
-  // n-tiles in groups: the group's LDS reads first, then its MFMAs with each accumulator's three products G apart
+  // n-tiles in groups of 4, the next group's LDS reads issued before this group's MFMAs (each accumulator's three
+  // products 4 apart)
   constexpr int G = 4;
+  half8 v[2][G], vl[2][G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    v[0][j] = __builtin_bit_cast(half8, ops.v[j * 64 + lane]);
+    vl[0][j] = __builtin_bit_cast(half8, ops.vl[j * 64 + lane]);
+  }
 #pragma unroll
   for (int n0 = 0; n0 < 16; n0 += G) {
-    half8 v[G], vl[G];
+    const int cb = (n0 / G) & 1;
+    if (n0 + G < 16) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      v[j] = __builtin_bit_cast(half8, ops.v[(n0 + j) * 64 + lane]);
-      vl[j] = __builtin_bit_cast(half8, ops.vl[(n0 + j) * 64 + lane]);
+      for (int j = 0; j < G; ++j) {
+        v[cb ^ 1][j] = __builtin_bit_cast(half8, ops.v[(n0 + G + j) * 64 + lane]);
+        vl[cb ^ 1][j] = __builtin_bit_cast(half8, ops.vl[(n0 + G + j) * 64 + lane]);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j) st.o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, v[j], st.o[n0 + j], 0, 0, 0);
+    for (int j = 0; j < G; ++j)
+      st.o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, v[cb][j], st.o[n0 + j], 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < G; ++j) st.o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, v[j], st.o[n0 + j], 0, 0, 0);
+    for (int j = 0; j < G; ++j)
+      st.o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, v[cb][j], st.o[n0 + j], 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < G; ++j) st.o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, vl[j], st.o[n0 + j], 0, 0, 0);
+    for (int j = 0; j < G; ++j)
+      st.o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, vl[cb][j], st.o[n0 + j], 0, 0, 0);
   }
 }
 
@@ -340,8 +352,8 @@ struct QuarterWords {
 
 // The decode waves' side of a run of quantized tiles [t0, t1) of one kind (qN_0 body: NK / NV bits; q8_0 ring: 8 / 8):
 // one barrier to publish tile t0, then per tile one barrier, matching the compute waves' loop. Tile j is decoded
-// into operand buffer j % 2 in the phase before the one that computes it, from words whose loads went out two
-// phases earlier (three register sets in rotation).
+// into operand buffer j % 2 in the phase before the one that computes it, from words whose loads went out at the
+// end of the phase two before that (three register sets in rotation).
 template <int NKt, int NVt, int C>
 __device__ __attribute__((always_inline)) inline void decode_run(int t0, int t1, const TileAddr ref,
                                                                  MqOpsT<false>* s_ops, uint32_t magic, int lane) {
@@ -352,18 +364,19 @@ __device__ __attribute__((always_inline)) inline void decode_run(int t0, int t1,
   if (t0 + 2 < t1) z.load(ref(t0 + 2), lane, ks_lane);
   x.decode(s_ops[t0 & 1], magic, lane, ks_lane);
   __syncthreads();
-  // the phase that computes tile p: load tile p + 3 into the set tile p used, decode tile p + 1
+  // the phase that computes tile p: decode tile p + 1, then load tile p + 3 into the set tile p used (decoding
+  // first, a wait for the words of tile p + 1 never covers loads issued in the same phase)
   for (int p = t0; p < t1; p += 3) {
-    if (p + 3 < t1) x.load(ref(p + 3), lane, ks_lane);
     if (p + 1 < t1) y.decode(s_ops[(p + 1) & 1], magic, lane, ks_lane);
+    if (p + 3 < t1) x.load(ref(p + 3), lane, ks_lane);
     __syncthreads();
     if (p + 1 >= t1) break;
-    if (p + 4 < t1) y.load(ref(p + 4), lane, ks_lane);
     if (p + 2 < t1) z.decode(s_ops[p & 1], magic, lane, ks_lane);
+    if (p + 4 < t1) y.load(ref(p + 4), lane, ks_lane);
     __syncthreads();
     if (p + 2 >= t1) break;
-    if (p + 5 < t1) z.load(ref(p + 5), lane, ks_lane);
     if (p + 3 < t1) x.decode(s_ops[(p + 1) & 1], magic, lane, ks_lane);
+    if (p + 5 < t1) z.load(ref(p + 5), lane, ks_lane);
     __syncthreads();
   }
 }
