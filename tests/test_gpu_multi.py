@@ -197,6 +197,20 @@ def test_multi_query_at_the_64k_workload_size():
     assert max_err(got, want) <= TOL, max_err(got, want)
 
 
+def test_multi_query_at_the_262k_workload_size():
+    """T = 8 over layer 0 of the K6/V5 + q8_0 ring workload at 262,144 positions, the size bench.py --config 4
+    --verify-queries 8 times: splits of ~64 tiles, the last of them crossing from body tiles into q8_0 ring tiles
+    (the decode waves switch from the 6/5-bit decode to the 8-bit one within a split)."""
+    from tests.test_gpu_fullsize import prefill_all
+    wl = W.workload(4)
+    p = Pair(dict(wl.cache_config(), n_layers=1))
+    prefill_all(p, wl, 0)
+    k, v = _drafts(wl, 0, 0, 8)
+    p.append(0, [0], [8], k, v)
+    got, want = run_multi(p, 0, [0], _workload_queries(wl, 0, 1, 8))
+    assert max_err(got, want) <= TOL, max_err(got, want)
+
+
 def test_multi_query_64_entries_at_the_eight_stream_workload_size():
     """8 streams x 8 queries (64 entries: ring segments planned outside the per-head budget) over layer 0 of the
     KVarN K4/V4 + bf16 tail workload at its full contexts (16k-64k), the size bench.py --config 3
