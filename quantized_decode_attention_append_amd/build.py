@@ -35,6 +35,7 @@ UNITS = [
     ("kvq_mq.hip", ["-ffp-contract=fast"]),
     ("kvq_mq_var.hip", ["-ffp-contract=fast"]),
     ("kvq_mq_pair.hip", ["-ffp-contract=fast"]),
+    ("kvq_mq_pair_kv.hip", ["-ffp-contract=fast"]),
 ]
 PROBE_UNITS = [("kvq_probe.hip", [])]
 
