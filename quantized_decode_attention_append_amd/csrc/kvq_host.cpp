@@ -741,7 +741,8 @@ namespace {
 // Dense decode of n entries, entry i reading sequence ids[i] over positions [0, len[i]) (its body range
 // [0, min(body_len, len[i])) and the ring rows after it): the query and output rows follow the entries.
 kvq_status run_mq(kvq_cache* c, int layer, int n, const int32_t* ids, const int* q0, const int* nq, const void* q_bf16,
-                  float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream);
+                  float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream,
+                  bool balance = false);
 
 kvq_status run_decode(kvq_cache* c, int32_t layer, int n, const int32_t* ids, const int* len, const void* q_bf16,
                       float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream,
@@ -805,15 +806,30 @@ struct MqPlan {
   bool partials = false;
 };
 
+// Tiles of sequence i's prefix up to position end (body tiles, then ring tiles).
+void mq_tiles(int body_len, int end, int& bt, int& rt) {
+  bt = (std::min(body_len, end) + kvq::kTile - 1) / kvq::kTile;
+  rt = end > body_len ? (end + kvq::kTile - 1) / kvq::kTile - body_len / kvq::kTile : 0;
+}
+
+// balance (one block per sequence, kvq_decode_attn_multi): each sequence's splits in proportion to its tiles, at
+// most the per-head budget and its tile count (what kvq_workspace_bytes(cache, n_seqs * T, len) provides for);
+// otherwise (prefill) every entry the same share, so that rows x splits <= 16 x budget / Hkv
+// (kvq_prefill_workspace_bytes).
 MqPlan plan_mq(const kvq_cache* c, int n, const int* len, const int* body_len, const int* q0, const int* nq,
-               kvq::MqSeq* out) {
+               kvq::MqSeq* out, bool balance = false) {
   const int hk = c->cfg.n_kv_heads;
   const int qb = kvq::mq_block_queries(geometry(c));
-  long blocks = 0;
-  for (int i = 0; i < n; ++i) blocks += (nq[i] + qb - 1) / qb;
+  long blocks = 0, all_tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    blocks += (nq[i] + qb - 1) / qb;
+    int bt, rt;
+    mq_tiles(body_len[i], q0[i] + nq[i], bt, rt);
+    all_tiles += bt + rt;
+  }
+  balance = balance && blocks == n && all_tiles > 0;
   const long entries = std::max(1L, blocks * hk);
-  // at most the dense decode's per-head budget per entry (so kvq_workspace_bytes(cache, n_seqs * T, len) covers
-  // kvq_decode_attn_multi), and rows x splits <= 8 x budget / Hkv (kvq_prefill_workspace_bytes)
+  const long budget_h = std::max(1L, mq_budget(c) / hk);
   const int per_entry = (int)std::max(1L, mq_budget(c) / entries);
   MqPlan p;
   for (int i = 0; i < n; ++i) {
@@ -823,10 +839,11 @@ MqPlan plan_mq(const kvq_cache* c, int n, const int* len, const int* body_len, c
     S.q0 = q0[i];
     S.nq = nq[i];
     S.row0 = p.rows;
-    const int end = q0[i] + nq[i];
-    const int bt = (std::min(body_len[i], end) + kvq::kTile - 1) / kvq::kTile;
-    const int rt = end > body_len[i] ? (end + kvq::kTile - 1) / kvq::kTile - body_len[i] / kvq::kTile : 0;
+    int bt, rt;
+    mq_tiles(body_len[i], q0[i] + nq[i], bt, rt);
     int ns = std::min(per_entry, std::max(1, bt + rt));
+    if (balance)
+      ns = (int)std::max(1L, std::min({budget_h * (bt + rt) / all_tiles, budget_h, (long)std::max(1, bt + rt)}));
     int nr = 0;
     if (c->cfg.kvarn && rt > 0) {   // separate body and ring splits
       ns = std::max(ns, bt > 0 ? 2 : 1);
@@ -849,7 +866,8 @@ size_t mq_partials_bytes(const kvq_cache* c, const MqPlan& p) {
 }
 
 kvq_status run_mq(kvq_cache* c, int layer, int n, const int32_t* ids, const int* q0, const int* nq, const void* q_bf16,
-                  float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+                  float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream,
+                  bool balance) {
   kvq::MqArgs a{};
   a.g = geometry(c);
   int len[KVQ_MAX_BATCH], bl[KVQ_MAX_BATCH];
@@ -858,7 +876,7 @@ kvq_status run_mq(kvq_cache* c, int layer, int n, const int32_t* ids, const int*
     len[i] = c->len[k];
     bl[i] = c->body_len[k];
   }
-  const MqPlan p = plan_mq(c, n, len, bl, q0, nq, a.seqs);
+  const MqPlan p = plan_mq(c, n, len, bl, q0, nq, a.seqs, balance);
   const size_t need = mq_partials_bytes(c, p);
   if (need && (!workspace || ws_bytes < need)) return fail(KVQ_E_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   for (int i = 0; i < n; ++i) a.seqs[i].slab = slab_offset(c, layer, ids[i]);
@@ -955,7 +973,8 @@ kvq_status kvq_decode_attn_multi(kvq_cache* c, int32_t layer, int32_t n_seqs, co
       q0[i] = c->len[c->idx(layer, seq_ids[i])] - n_queries;
       nq[i] = n_queries;
     }
-    return run_mq(c, layer, n_seqs, seq_ids, q0, nq, q_bf16, out, softmax_scale, workspace, ws_bytes, stream);
+    return run_mq(c, layer, n_seqs, seq_ids, q0, nq, q_bf16, out, softmax_scale, workspace, ws_bytes, stream,
+                  true);
   }
   // one query per sequence plans (and computes) exactly as kvq_decode_attn; a row-layout cache runs every
   // (sequence, query) pair as an entry of the gather launch
