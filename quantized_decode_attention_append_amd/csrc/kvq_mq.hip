@@ -14,7 +14,7 @@ hipError_t launch_mq(const MqArgs& a, int grid_x, hipStream_t s, hipEvent_t e0, 
 }
 
 hipError_t launch_mq_combine(const MqArgs& a, int rows, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_k(mq_combine_kernel, dim3(rows * a.g.n_kv_heads, a.group, 256 / 16), dim3(256), s, e0, e1, a);
+  return launch_k(mq_combine_kernel, dim3(rows * a.g.n_kv_heads, a.group), dim3(1024), s, e0, e1, a);
 }
 
 }  // namespace kvq

@@ -745,11 +745,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Merge of the split partials of every query row: one work-group per (row, KV head, query head, 16-channel chunk).
-__global__ __launch_bounds__(256) void mq_combine_kernel(MqArgs a) {
+// Merge of the split partials of every query row: one work-group per (row, KV head, query head), 16 groups of 64
+// threads, thread t of a group owning channels 4t .. 4t + 3 of a strided share of the splits (online log-sum-exp,
+// exp2 domain); then the 16 groups are merged: out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+__global__ __launch_bounds__(1024) void mq_combine_kernel(MqArgs a) {
   constexpr int D = 256;
   constexpr size_t rec = kPartialHeads * (D + 2);
-  __shared__ float s_m[16], s_l[16], s_o[16][17];
+  __shared__ float s_m[16], s_l[16];
+  __shared__ floatx4 s_o[16][64];
   const int hk = a.g.n_kv_heads;
   const int row = blockIdx.x / hk;
   const int head = blockIdx.x % hk;
@@ -759,37 +762,45 @@ __global__ __launch_bounds__(256) void mq_combine_kernel(MqArgs a) {
   if (ns == 1) return;   // that sequence's queries were written by the split kernel itself
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int c = blockIdx.z * 16 + (tid & 15);
-  const int grp = tid >> 4;
+  const int grp = tid >> 6, t = tid & 63;
   const float* base = a.partials + ((size_t)row * hk + head) * a.max_splits * rec;
-  float M = kNegBig, L = 0.0f, O = 0.0f;
+  float M = kNegBig, L = 0.0f;
+  floatx4 O = {0, 0, 0, 0};
+#pragma unroll 2
   for (int sp = grp; sp < ns; sp += 16) {
     const float* pr = base + sp * rec;
-    const float m = pr[h], l = pr[kPartialHeads + h], o = pr[2 * kPartialHeads + h * D + c];
+    const float m = pr[h], l = pr[kPartialHeads + h];
+    const floatx4 o = *(const floatx4*)(pr + 2 * kPartialHeads + h * D + 4 * t);
     const float mn = fmaxf(M, m);
     const float fa = __builtin_amdgcn_exp2f(M - mn), fb = __builtin_amdgcn_exp2f(m - mn);
     L = L * fa + l * fb;
-    O = O * fa + o * fb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) O[k] = O[k] * fa + o[k] * fb;
     M = mn;
   }
-  if ((tid & 15) == 0) {
+  if (t == 0) {
     s_m[grp] = M;
     s_l[grp] = L;
   }
-  s_o[grp][tid & 15] = O;
+  s_o[grp][t] = O;
   __syncthreads();
-  if (tid < 16) {
+  if (grp == 0) {
     float Mx = kNegBig;
 #pragma unroll
     for (int k = 0; k < 16; ++k) Mx = fmaxf(Mx, s_m[k]);
-    float Ls = 0.0f, Os = 0.0f;
+    float Ls = 0.0f;
+    floatx4 Os = {0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float f = __builtin_amdgcn_exp2f(s_m[k] - Mx);
       Ls += s_l[k] * f;
-      Os += s_o[k][tid] * f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Os[c] += s_o[k][t][c] * f;
     }
-    a.out[((size_t)row * a.n_q_heads + head * a.group + h) * D + blockIdx.z * 16 + tid] = Ls > 0.0f ? Os / Ls : 0.0f;
+    floatx4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = Ls > 0.0f ? Os[c] / Ls : 0.0f;
+    *(floatx4*)(a.out + ((size_t)row * a.n_q_heads + head * a.group + h) * D + 4 * t) = r;
   }
 }
 
