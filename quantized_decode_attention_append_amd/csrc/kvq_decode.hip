@@ -291,8 +291,8 @@ __device__ inline const uint8_t* tile_ptr(const uint8_t* vbase, int tile_v, bool
 template <int NK, int NV, bool UNROLL>
 __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, TileRaw<NK, NV>& nxt, const half8* qb,
                                        float qmul, const uint8_t* kbase, int tile_k, bool ring, int R,
-                                       const uint8_t* vbase, int tile_v, int t, int tile_end, int lo, int hi,
-                                       uint32_t lane_mask, u32x4* s_buf, int* s_next) {
+                                       const uint8_t* vbase, int tile_v, int tb, int ts, int t, int tile_end, int lo,
+                                       int hi, uint32_t lane_mask, u32x4* s_buf, int* s_next) {
   const int lane = threadIdx.x & 63;
   if (t >= tile_end) return;
   uint32_t magic = kMagic;
@@ -306,13 +306,13 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     for (;;) {
       int nt = grab_tile(s_next);
       bool more = nt < tile_end;
-      load_tile_k<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
+      load_tile_k<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, tb + (more ? nt : t) * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + (more ? nt : t) * ts), tile_v,
                           more);
       stage(cur, s_buf);
       {
         float x[8], p[8];
-        qk_part<NK, NV>(cur, s_buf, qb, qmul, t, lo, hi, x);
-        load_tile_v<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+        qk_part<NK, NV>(cur, s_buf, qb, qmul, tb + t * ts, lo, hi, x);
+        load_tile_v<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, tb + (more ? nt : t) * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + (more ? nt : t) * ts),
                             tile_v, more);
         softmax_update(st, x, p);
         pv_part<NK, NV>(st, cur, s_buf, p, lane_mask, magic);
@@ -321,13 +321,13 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
       t = nt;
       nt = grab_tile(s_next);
       more = nt < tile_end;
-      load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
+      load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, tb + (more ? nt : t) * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + (more ? nt : t) * ts), tile_v,
                           more);
       stage(nxt, s_buf + 64);
       {
         float x[8], p[8];
-        qk_part<NK, NV>(nxt, s_buf + 64, qb, qmul, t, lo, hi, x);
-        load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+        qk_part<NK, NV>(nxt, s_buf + 64, qb, qmul, tb + t * ts, lo, hi, x);
+        load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, tb + (more ? nt : t) * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + (more ? nt : t) * ts),
                             tile_v, more);
         softmax_update(st, x, p);
         pv_part<NK, NV>(st, nxt, s_buf + 64, p, lane_mask, magic);
@@ -343,13 +343,13 @@ __device__ inline void run_quant_tiles(WaveState& st, TileRaw<NK, NV>& cur, Tile
     // the next tile's loads go out before this tile's scales are staged (which waits for this tile only)
     const int nt = grab_tile(s_next);
     const bool more = nt < tile_end;
-    load_tile_k<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t), tile_v,
+    load_tile_k<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, tb + (more ? nt : t) * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + (more ? nt : t) * ts), tile_v,
                         more);
     stage(cur, sb);
     {
       float x[8], p[8];
-      qk_part<NK, NV>(cur, sb, qb, qmul, t, lo, hi, x);
-      load_tile_v<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, more ? nt : t), tile_k, tile_ptr(vbase, tile_v, ring, R, more ? nt : t),
+      qk_part<NK, NV>(cur, sb, qb, qmul, tb + t * ts, lo, hi, x);
+      load_tile_v<NK, NV>(nxt, tile_ptr(kbase, tile_k, ring, R, tb + (more ? nt : t) * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + (more ? nt : t) * ts),
                           tile_v, more);
       softmax_update(st, x, p);
       pv_part<NK, NV>(st, cur, sb, p, lane_mask, magic);
@@ -473,8 +473,8 @@ struct QArgs {
 // operands (times KVarN sigma) in LDS, then run the tile loop. All waves of the work-group call this.
 template <int NK, int NV, bool EARLY>
 __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, const uint8_t* kbase, int tile_k,
-                                  bool ring, int R, const uint8_t* vbase, int tile_v, int wb, int we, int lo, int hi,
-                                  uint32_t lane_mask, u32x4* sbuf, int* s_next, float* s_amax) {
+                                  bool ring, int R, const uint8_t* vbase, int tile_v, int tb, int ts, int wb, int we,
+                                  int lo, int hi, uint32_t lane_mask, u32x4* sbuf, int* s_next, float* s_amax) {
   constexpr int NB = 8;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile addresses stay scalar
@@ -491,8 +491,8 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   KVQ_SB
   const int t0 = wb < we ? wb : we - 1;
   if constexpr (EARLY) {
-    load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
-    load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+    load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, tb + t0 * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + t0 * ts), tile_v, wb < we);
+    load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, tb + t0 * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + t0 * ts), tile_v, wb < we);
   }
   float x[8];
 #pragma unroll
@@ -534,11 +534,11 @@ __device__ inline void quant_path(WaveState& st, const QArgs& qa, half8* s_qb, c
   }
   __syncthreads();
   if constexpr (!EARLY) {
-    load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
-    load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, t0), tile_k, tile_ptr(vbase, tile_v, ring, R, t0), tile_v, wb < we);
+    load_tile_k<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, tb + t0 * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + t0 * ts), tile_v, wb < we);
+    load_tile_v<NK, NV>(cur, tile_ptr(kbase, tile_k, ring, R, tb + t0 * ts), tile_k, tile_ptr(vbase, tile_v, ring, R, tb + t0 * ts), tile_v, wb < we);
   }
   const float qmul = qa.scale * kLog2e * ldexpf(1.0f, e + 24);
-  run_quant_tiles<NK, NV, unroll_tiles(NK, NV)>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, wb, we, lo, hi, lane_mask,
+  run_quant_tiles<NK, NV, unroll_tiles(NK, NV)>(st, cur, nxt, s_qb, qmul, kbase, tile_k, ring, R, vbase, tile_v, tb, ts, wb, we, lo, hi, lane_mask,
                           sbuf, s_next);
 }
 
@@ -633,23 +633,34 @@ void decode_kernel(DecodeArgs a) {
     lo = S.body_len;
     hi = S.len;
   }
-  // this split's tiles [tb, te): wave w starts with tile tb + w, further tiles come from s_next. A body split
-  // that also requantizes rows of a fused decode step starts late: the last body split then takes the tiles
-  // from last_tb on and the others share [0, last_tb) evenly.
-  int tb, te;
-  if (!is_ring && S.last_tb > 0 && nsp > 1) {
-    tb = sp == nsp - 1 ? S.last_tb : (int)((long)sp * S.last_tb / (nsp - 1));
-    te = sp == nsp - 1 ? seg_tiles : (int)((long)(sp + 1) * S.last_tb / (nsp - 1));
+  // this split's tiles are tb + k * ts for k in [0, n_tiles): wave w starts with k = w, further k come from
+  // s_next. Body splits interleave: split sp < nsp - 1 takes every (nsp - 1)-th tile of [0, L) from tile sp on,
+  // so that at any time the work-groups of a KV head stream one window of the body together, and the last split
+  // takes the contiguous tiles [L, seg_tiles) at the end, which hold the rows a fused decode step requantizes
+  // (that split writes them before it reads anything; last_tb > 0 gives it fewer tiles for the time it spends
+  // writing). The ring segment is split into contiguous ranges; its last split holds the appended position.
+  int tb, te, ts = 1;
+  if (!is_ring && nsp > 1) {
+    const int L = S.last_tb > 0 ? S.last_tb : seg_tiles - (seg_tiles / nsp > 1 ? seg_tiles / nsp : 1);
+    if (sp == nsp - 1) {
+      tb = L;
+      te = seg_tiles;
+    } else {
+      tb = sp;
+      te = L;
+      ts = nsp - 1;
+    }
   } else {
     tb = seg_begin + (int)((long)sp * seg_tiles / nsp);
     te = seg_begin + (int)((long)(sp + 1) * seg_tiles / nsp);
   }
+  const int n_tiles = te > tb ? (te - tb + ts - 1) / ts : 0;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses stay scalar
   const int lane = tid & 63;
-  const int wb = tb + wave;
-  const int we = te;
-  if (tid == 0) s_next = tb + NW;   // published by the work-group barrier before the first tile loop
+  const int wb = wave;
+  const int we = n_tiles;
+  if (tid == 0) s_next = NW;   // published by the work-group barrier before the first tile loop
 
   const int m16 = lane & 15;
   const int gq = lane >> 4;
@@ -692,7 +703,8 @@ void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
     const float qmul = a.scale * kLog2e;
-    for (int t = wb; t < we; t = grab_tile(&s_next)) {
+    for (int k = wb; k < we; k = grab_tile(&s_next)) {
+      const int t = tb + k * ts;
       const size_t rt = (size_t)head * (R / kTile) + ((t * kTile) % R) / kTile;
       const uint8_t* kt = slab + g.k_ring + rt * g.ring_tile_k;
       const uint8_t* vt = slab + g.v_ring + rt * g.ring_tile_v;
@@ -710,19 +722,19 @@ void decode_kernel(DecodeArgs a) {
       // waves 0-3 (one per SIMD) request their first tile at once, waves 4-7 only once the query is set
       // up: a smaller first burst reaches every SIMD sooner
       if (wave < 4)
-        quant_path<NK, NV, true>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
+        quant_path<NK, NV, true>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, tb, ts, wb, we, lo, hi, lane_mask,
                                  sbuf, &s_next, s_amax);
       else {
         // the later-starting wave of each SIMD gets issue priority, so that both finish together
         __builtin_amdgcn_s_setprio(1);
-        quant_path<NK, NV, false>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, wb, we, lo, hi, lane_mask,
+        quant_path<NK, NV, false>(st, qa, s_qb, kbase, g.tile_k, false, 1, vbase, g.tile_v, tb, ts, wb, we, lo, hi, lane_mask,
                                   sbuf, &s_next, s_amax);
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
       const uint8_t* kbase = slab + g.k_ring + (size_t)head * (R / kTile) * g.ring_tile_k;
       const uint8_t* vbase = slab + g.v_ring + (size_t)head * (R / kTile) * g.ring_tile_v;
-      quant_path<8, 8, true>(st, qa, s_qb, kbase, g.ring_tile_k, true, R, vbase, g.ring_tile_v, wb, we, lo, hi,
+      quant_path<8, 8, true>(st, qa, s_qb, kbase, g.ring_tile_k, true, R, vbase, g.ring_tile_v, tb, ts, wb, we, lo, hi,
                              lane_mask, sbuf, &s_next, s_amax);
     }
   }
