@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kGroup = 16;    // list entries per wave step
 constexpr int kGWaves = kGatherWaves;
+static_assert(64 * kGWaves == 256, "the fused append gives each thread one channel of K and V");
 constexpr int kImgRow = 288;   // bytes per LDS row image (a q8_0 row is 272)
 
 __device__ inline float f16f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
@@ -317,33 +318,39 @@ __device__ inline void image_v(StepRows& st, const uint8_t* img_v, int app) {
 }
 
 // The append of a fused sparse decode step (a cache without a ring): one token of this sequence and KV head
-// quantized into body row app_pos, K and V, as the body write of an append does it (thread c
-// owns channel c of K and V, or of K or V; a block's 32 values are the 32 lanes of a half-wave).
-// With img_k / img_v (zeroed LDS row images) the same bytes go there too.
-template <int NTHREADS>
-__device__ inline void sparse_step_write(const GatherArgs& a, const GatherSeq& S, int si, int head, uint8_t* img_k,
-                                         uint8_t* img_v) {
+// quantized into body row app_pos, K and V, as the body write of an append does it (thread c owns channel c of
+// K and V; a block's 32 values are the 32 lanes of a half-wave). sparse_step_inputs loads the thread's two input
+// values (divided by KVarN sigma); sparse_step_emit quantizes them into the body row in global memory
+// (to_global) or into the zeroed LDS row images img_k / img_v.
+__device__ inline void sparse_step_inputs(const GatherArgs& a, const GatherSeq& S, int si, int head, float* x) {
+  const Geometry& g = a.g;
+  constexpr int D = 256;
+  const int c = threadIdx.x & (D - 1);
+  const uint8_t* slab = g.arena + S.slab;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint16_t* in = kv ? a.v_in : a.k_in;
+    x[kv] = bf16_to_f32(in[((size_t)si * g.n_kv_heads + head) * D + c]);
+    if (g.kvarn) x[kv] = x[kv] / f16_to_f32(((const uint16_t*)(slab + g.sigma))[((size_t)head * 2 + kv) * D + c]);
+  }
+}
+__device__ inline void sparse_step_emit(const GatherArgs& a, const GatherSeq& S, int head, const float* x,
+                                        bool to_global, uint8_t* img_k, uint8_t* img_v) {
   const Geometry& g = a.g;
   constexpr int D = 256;
   const int c = threadIdx.x & (D - 1);
   uint8_t* slab = g.arena + S.slab;
   const int p = S.app_pos;
-  for (int kv = threadIdx.x / D; kv < 2; kv += NTHREADS / D) {
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
     const int nb = kv ? g.v_bits : g.k_bits;
-    const uint16_t* in = kv ? a.v_in : a.k_in;
-    float x = bf16_to_f32(in[((size_t)si * g.n_kv_heads + head) * D + c]);
-    if (g.kvarn) x = x / f16_to_f32(((const uint16_t*)(slab + g.sigma))[((size_t)head * 2 + kv) * D + c]);
     uint16_t dq;
-    const uint32_t u = quant_lane(x, nb, &dq);
-    uint8_t* row = slab + g.k_body + (kv ? rows_v_off(p, head, g.n_kv_heads, g.row_k + g.row_v, g.row_k)
-                                         : rows_k_off(p, head, g.n_kv_heads, g.row_k + g.row_v));
-    or_code(row, nullptr, true, kv, nb, 0, c, u, D);   // the row was zeroed with its slab
+    const uint32_t u = quant_lane(x[kv], nb, &dq);
+    uint8_t* row = to_global ? slab + g.k_body + (kv ? rows_v_off(p, head, g.n_kv_heads, g.row_k + g.row_v, g.row_k)
+                                                     : rows_k_off(p, head, g.n_kv_heads, g.row_k + g.row_v))
+                             : (kv ? img_v : img_k);
+    or_code(row, nullptr, true, kv, nb, 0, c, u, D);   // the row was zeroed with its slab (the image in LDS)
     if ((c % kBlock) == 0) ((uint16_t*)(row + 4 * (D / kBlock) * nb))[c / kBlock] = dq;
-    if (img_k) {
-      uint8_t* im = kv ? img_v : img_k;
-      or_code(im, nullptr, true, kv, nb, 0, c, u, D);
-      if ((c % kBlock) == 0) ((uint16_t*)(im + 4 * (D / kBlock) * nb))[c / kBlock] = dq;
-    }
   }
 }
 
@@ -393,12 +400,14 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
   const int hh = e16 & 7;
   const bool lo_row = e16 >= 8, head_ok = hh < a.group;
   int g0 = ib + kGroup * wave;
-  // fused append (a.step): the new position's rows are written by the first split of the KV head and by every
-  // work-group whose range lists the position; such a work-group also builds the rows in LDS and reads those
-  // entries from there (so no work-group waits for another's writes)
+  // fused append (a.step): every work-group whose range lists the new position builds its K and V rows in LDS
+  // and reads those entries from there; the first split of the KV head writes the rows to global memory at its
+  // end (so no work-group waits for another's writes, and none waits for the write)
   const int app = a.step ? S.app_pos : -1;
   bool hit = false;
+  float app_x[2] = {0.0f, 0.0f};
   if (app >= 0) {
+    sparse_step_inputs(a, S, si, head, app_x);
     for (int idx = ib + tid; idx < ie; idx += 64 * NW) hit |= (rs.plist ? rs.plist[idx] : idx) == app;
     for (int w = tid; w < 2 * kImgRow / 4; w += 64 * NW) ((uint32_t*)s_img)[w] = 0u;
   }
@@ -436,8 +445,7 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
     }
     if (app >= 0) hit = __syncthreads_or(hit);   // (also publishes s_amax and the zeroed row images)
     else __syncthreads();
-    if (app >= 0 && (hit || split == 0))
-      sparse_step_write<64 * NW>(a, S, si, head, hit ? s_img : nullptr, hit ? s_img + kImgRow : nullptr);
+    if (app >= 0 && hit) sparse_step_emit(a, S, head, app_x, false, s_img, s_img + kImgRow);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       am = fmaxf(am, s_amax[w][0]);
@@ -641,6 +649,9 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
     part[tid] = M;
     part[G + tid] = L;
   }
+  // the new position's rows in global memory, once per KV head (no work-group of this launch reads them from
+  // there: those that list the position read the LDS image), after the split's own work
+  if (app >= 0 && split == 0) sparse_step_emit(a, S, head, app_x, true, nullptr, nullptr);
 }
 
 template <int NK, int NV>
