@@ -259,9 +259,10 @@ kvq_status kvq_sparse_decode_attn(kvq_cache* cache, int32_t layer, int32_t n_seq
  * [n_seqs][Hkv][D]), then sparse decode attention over positions (which index the cache after the append:
  * the new token is at the old length), with the results of kvq_append (n_new = 1 each) followed by
  * kvq_sparse_decode_attn. Without a tail ring and with no KVarN calibration pending, the new rows are
- * quantized into the body inside the sparse decode launch (by the first work-group of each KV head and by
- * every work-group whose list range holds the new position, before it reads any row; they write the same
- * bytes); otherwise the calls run in turn. Arguments and errors as those calls; the workspace size
+ * quantized into the body inside the sparse decode launch (every work-group whose list range holds the new
+ * position builds its rows in LDS and reads that entry from there; the first work-group of each KV head writes
+ * them to the body after its own work, and no work-group of the launch reads them from the body); otherwise the
+ * calls run in turn. Arguments and errors as those calls; the workspace size
  * (kvq_workspace_bytes(cache, n_seqs, budget)) is checked before any write. */
 kvq_status kvq_sparse_decode_step(kvq_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                   const void* k_bf16, const void* v_bf16, const void* q_bf16,
