@@ -25,7 +25,8 @@ the MALL), `copy_ceiling_gbs` (a plain 1 GiB device copy, bytes read + written p
 streaming-read probe). With --verify-queries T, `multi_query` times multi-query decode of the last T
 positions of every sequence (verification of T - 1 drafted tokens) over every layer. With --prefill, `prefill`
 times chunked prefill attention (append + causal attention of each 4096-token chunk) of layer 0 of the first
-sequence over its whole context.
+sequence over its whole context. With --dense-rows (sparse workload), `dense_rows` times dense decode of its
+row-layout cache over every position (the gather kernel).
 """
 from __future__ import annotations
 
@@ -415,6 +416,41 @@ def cold_calls(torch, cache, seqs, q, out, ws, n: int) -> dict:
             "how": "each decode call after a 512 MiB device write (L2 and MALL evicted)"}
 
 
+def dense_rows_leg(torch, cache, cfg, L, seqs, q, out, ws, reps):
+    """Dense decode of a row-layout cache (the sparse workload's): one kvq_decode_attn per layer over every
+    position, which runs the gather kernel with the whole cache as its list; reps passes over the layers. Reports
+    the wall time per pass and the gather kernel's rate in algorithmic bytes (every K and V row once)."""
+    lens = [cache.lengths(0, s) for s in seqs]
+    call_bytes = decode_call_bytes(cfg, [x[0] for x in lens], [x[1] for x in lens])
+
+    def run():
+        for layer in range(L):
+            cache.decode_attn(layer, seqs, q[layer], out=out[layer], workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    cache.timing(True)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms, n = cache.timing_read("gather")
+    cms, cn = cache.timing_read("combine")
+    cache.timing(False)
+    kernel_s = ms / 1e3 / max(n, 1)
+    achieved = call_bytes / kernel_s / 1e9
+    return {"ms_per_pass": round(elapsed * 1e3 / reps, 4), "kernel": "gather",
+            "kernel_us": round(kernel_s * 1e6, 3), "combine_us": round(cms * 1e3 / max(cn, 1), 3),
+            "bytes_per_call": int(call_bytes), "achieved_GBs": round(achieved, 2),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "value_GBs": round(call_bytes * L * reps / elapsed / 1e9, 2),
+            "how": "per layer one kvq_decode_attn over all positions of the row-layout cache (gather kernel "
+                   "with every position as its list); no append"}
+
+
 def multi_query_leg(torch, cache, cfg, L, seqs, qin, n_q, reps, dev):
     """Multi-query decode (the last n_q cached positions of every sequence, causal among them) over every layer,
     reps times: wall time per pass over the layers, the split kernel's dispatch-stamped average, and that kernel's
@@ -594,6 +630,9 @@ def main() -> int:
                     help="dense workloads: also time chunked prefill attention of layer 0 of the first sequence over "
                          "its whole context (append + causal attention of each 4096-token chunk), reported as the "
                          "line's prefill object")
+    ap.add_argument("--dense-rows", action="store_true",
+                    help="sparse workload: also time dense decode of its row-layout cache over every position "
+                         "(the gather kernel), reported as the line's dense_rows object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
@@ -747,6 +786,9 @@ def main() -> int:
     cold = cold_calls(torch, cache, seqs, qin_d[0, 0], out[0], ws, args.steps) if (L == 1 and not appends) else None
 
     indexed = indexer_leg(torch, cache, cfg, wl, L, seqs, total_steps, index_steps, ws, dev) if use_index else None
+    dense_rows = None
+    if args.dense_rows and cfg.get("layout", 0) == 1:
+        dense_rows = dense_rows_leg(torch, cache, cfg, L, seqs, qin_d[0], out, ws, max(2, args.steps // 4))
     multi = None
     if args.verify_queries and not sparse:
         multi = multi_query_leg(torch, cache, cfg, L, seqs, qin, args.verify_queries, args.steps, dev)
@@ -797,6 +839,8 @@ def main() -> int:
     }
     if multi is not None:
         res["multi_query"] = multi
+    if dense_rows is not None:
+        res["dense_rows"] = dense_rows
     if indexed is not None:
         res["indexer"] = indexed
     if pre is not None:
