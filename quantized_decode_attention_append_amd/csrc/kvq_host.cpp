@@ -736,6 +736,7 @@ kvq_status kvq_append_evict(kvq_cache* c, int32_t layer, int32_t n_seqs, const i
   return KVQ_OK;
 }
 
+extern "C++" {   // internal helpers between the exported entry points: C++ linkage
 namespace {
 
 // Dense decode of n entries, entry i reading sequence ids[i] over positions [0, len[i]) (its body range
@@ -908,6 +909,7 @@ kvq_status check_decode_args(const void* q_bf16, const float* out, const void* w
 }
 
 }  // namespace
+}  // extern "C++"
 
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q_bf16,
                            float* out, float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
@@ -1150,9 +1152,11 @@ kvq_status kvq_index_write(kvq_cache* c, int32_t layer, int32_t n_seqs, const in
   return KVQ_OK;
 }
 
+extern "C++" {
 namespace {
 int index_wgs(int m) { return std::max(1, (m + kvq::kIndexChunk - 1) / kvq::kIndexChunk); }
 }  // namespace
+}  // extern "C++"
 
 size_t kvq_index_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t max_len) {
   if (!c || n_seqs < 1 || max_len < 0) return 0;

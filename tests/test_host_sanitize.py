@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not ava
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=undefined"]
 FLAGS = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "--offload-arch=gfx950",
-         "-Wno-unused-command-line-argument", "-Wno-return-type-c-linkage",
+         "-Wno-unused-command-line-argument",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
