@@ -3,9 +3,10 @@
 // Decode is bandwidth-bound: every step streams the whole cache of a full-attention layer (offload page, on
 // the bytes a decode step reads), so the kernel is built around one pass over HBM per call:
 //
-// * grid (split, KV head, sequence); a work-group of 8 waves (two per SIMD) owns a contiguous range of 32-position tiles
-//   of either the qN_0 body or the tail ring (two KV paths per layer, Qwen3.8-27B page) and emits one
-//   partial (m, l, o) per query head of the group;
+// * grid (split, KV head, sequence); a work-group of 8 waves (two per SIMD) owns a set of 32-position tiles of
+//   either the qN_0 body (every G-th tile, so that a KV head's work-groups stream one window of the body
+//   together) or the tail ring (two KV paths per layer, Qwen3.8-27B page) and emits one partial (m, l, o) per
+//   query head of the group;
 // * each wave streams its tiles with 128-bit loads straight into registers: K rows are laid out so that
 //   lane (row, j) reads the 8-code pieces of one position contiguously, V tiles so that lane (d16, j)
 //   reads the MFMA B operand of P.V directly (no LDS transpose);
