@@ -77,3 +77,31 @@ def test_sparse_decode_full_size():
         got, want = p.sparse(0, [0], q, pos)
         err = max_err(got, want)
         assert err <= TOL, f"{wl.name} step {st}: max abs error {err:.3e}"
+
+
+def test_sparse_step_and_dense_rows_full_size():
+    """The sparse workload's layer 0 as bench.py runs it: fused sparse steps (append inside the gather launch,
+    the new position sometimes in the list), the slab byte-exact afterwards, then dense decode of the whole
+    262,144-position row-layout cache (the gather kernel over every position) against the oracle."""
+    import torch
+    wl = W.workload(5)
+    cfg = dict(wl.cache_config(), n_layers=1)
+    p = Pair(cfg)
+    prefill_all(p, wl, 0)
+    n = wl.contexts[0]
+    for st in range(2):
+        k, v, q = step_inputs(wl, 0, st)
+        pos = W.sparse_positions(wl.cfg, 0, 0, st, n + st + 1, wl.budget, wl.recent)[None]
+        assert (pos == n + st).any()   # the newest positions are forced: the appended one is listed
+        pos_d = torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).to("cuda")
+        got = p.gpu.sparse_decode_step(0, [0], dev(k), dev(v), dev(q), pos_d).cpu().numpy()
+        p.ora.append(0, [0], [1], k, v)
+        want = oracle.sparse_reference(p.ora, 0, [0], q, pos)
+        err = max_err(got, want)
+        assert err <= TOL, f"{wl.name} fused step {st}: max abs error {err:.3e}"
+    p.lengths_match(0, 0)
+    p.assert_slab_equal(0, 0)
+    q = W.query(wl.cfg, 0, 0, 7)[None]
+    got, want = p.decode(0, [0], q)
+    err = max_err(got, want)
+    assert err <= TOL, f"{wl.name} dense decode of the row layout: max abs error {err:.3e}"
