@@ -34,6 +34,7 @@ namespace {
 constexpr int kGroup = 16;    // list entries per wave step
 constexpr int kGWaves = kGatherWaves;
 static_assert(64 * kGWaves == 256, "the fused append gives each thread one channel of K and V");
+static_assert(2 * (32 * 8 + 16) / 16 <= 64 * kGWaves, "one 16-byte store per thread covers both row images");
 constexpr int kImgRow = 288;   // bytes per LDS row image (a q8_0 row is 272)
 
 __device__ inline float f16f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
@@ -320,8 +321,8 @@ __device__ inline void image_v(StepRows& st, const uint8_t* img_v, int app) {
 // The append of a fused sparse decode step (a cache without a ring): one token of this sequence and KV head
 // quantized into body row app_pos, K and V, as the body write of an append does it (thread c owns channel c of
 // K and V; a block's 32 values are the 32 lanes of a half-wave). sparse_step_inputs loads the thread's two input
-// values (divided by KVarN sigma); sparse_step_emit quantizes them into the body row in global memory
-// (to_global) or into the zeroed LDS row images img_k / img_v.
+// values (divided by KVarN sigma); sparse_step_emit quantizes them into the zeroed LDS row images img_k / img_v
+// (the body row layout), from which the kernel stores them to the body.
 __device__ inline void sparse_step_inputs(const GatherArgs& a, const GatherSeq& S, int si, int head, float* x) {
   const Geometry& g = a.g;
   constexpr int D = 256;
@@ -334,22 +335,17 @@ __device__ inline void sparse_step_inputs(const GatherArgs& a, const GatherSeq& 
     if (g.kvarn) x[kv] = x[kv] / f16_to_f32(((const uint16_t*)(slab + g.sigma))[((size_t)head * 2 + kv) * D + c]);
   }
 }
-__device__ inline void sparse_step_emit(const GatherArgs& a, const GatherSeq& S, int head, const float* x,
-                                        bool to_global, uint8_t* img_k, uint8_t* img_v) {
+__device__ inline void sparse_step_emit(const GatherArgs& a, const float* x, uint8_t* img_k, uint8_t* img_v) {
   const Geometry& g = a.g;
   constexpr int D = 256;
   const int c = threadIdx.x & (D - 1);
-  uint8_t* slab = g.arena + S.slab;
-  const int p = S.app_pos;
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const int nb = kv ? g.v_bits : g.k_bits;
     uint16_t dq;
     const uint32_t u = quant_lane(x[kv], nb, &dq);
-    uint8_t* row = to_global ? slab + g.k_body + (kv ? rows_v_off(p, head, g.n_kv_heads, g.row_k + g.row_v, g.row_k)
-                                                     : rows_k_off(p, head, g.n_kv_heads, g.row_k + g.row_v))
-                             : (kv ? img_v : img_k);
-    or_code(row, nullptr, true, kv, nb, 0, c, u, D);   // the row was zeroed with its slab (the image in LDS)
+    uint8_t* row = kv ? img_v : img_k;
+    or_code(row, nullptr, true, kv, nb, 0, c, u, D);   // the image was zeroed
     if ((c % kBlock) == 0) ((uint16_t*)(row + 4 * (D / kBlock) * nb))[c / kBlock] = dq;
   }
 }
@@ -445,7 +441,7 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
     }
     if (app >= 0) hit = __syncthreads_or(hit);   // (also publishes s_amax and the zeroed row images)
     else __syncthreads();
-    if (app >= 0 && hit) sparse_step_emit(a, S, head, app_x, false, s_img, s_img + kImgRow);
+    if (app >= 0 && hit) sparse_step_emit(a, app_x, s_img, s_img + kImgRow);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       am = fmaxf(am, s_amax[w][0]);
@@ -650,8 +646,19 @@ __global__ __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(kG
     part[G + tid] = L;
   }
   // the new position's rows in global memory, once per KV head (no work-group of this launch reads them from
-  // there: those that list the position read the LDS image), after the split's own work
-  if (app >= 0 && split == 0) sparse_step_emit(a, S, head, app_x, true, nullptr, nullptr);
+  // there: those that list the position read the LDS image), after the split's own work: the rows are built in
+  // the LDS images (already there if this work-group lists the position) and stored with 16-byte writes
+  if (app >= 0 && split == 0) {
+    if (!hit) sparse_step_emit(a, app_x, s_img, s_img + kImgRow);
+    __syncthreads();
+    const int body_pair = g.row_k + g.row_v, nk16 = g.row_k / 16, nv16 = g.row_v / 16;
+    uint8_t* rows = g.arena + S.slab + g.k_body;
+    if (tid < nk16)
+      ((u32x4*)(rows + rows_k_off(app, head, g.n_kv_heads, body_pair)))[tid] = ((const u32x4*)s_img)[tid];
+    else if (tid < nk16 + nv16)
+      ((u32x4*)(rows + rows_v_off(app, head, g.n_kv_heads, body_pair, g.row_k)))[tid - nk16] =
+          ((const u32x4*)(s_img + kImgRow))[tid - nk16];
+  }
 }
 
 template <int NK, int NV>
